@@ -1,0 +1,13 @@
+"""GDLA oracle (test infrastructure): plain fp64 CPU reference of the method.
+Only the tests, the package smoke check and the benchmark's CPU baseline may
+import it; the HIP library never does."""
+
+from .gdla_ref import (Cfg, attention_heads, attended_keys, differential_gate_out, gdla_block,
+                       gdla_decode, gdla_layer, hybrid_windows, kv_head_of, latent_expand,
+                       latent_expand_from_norm, linear, project_tokens, rms_norm, rope,
+                       rope_inv_freq, sigmoid)
+
+__all__ = ["Cfg", "attention_heads", "attended_keys", "differential_gate_out", "gdla_block",
+           "gdla_decode", "gdla_layer", "hybrid_windows", "kv_head_of", "latent_expand",
+           "latent_expand_from_norm", "linear", "project_tokens", "rms_norm", "rope",
+           "rope_inv_freq", "sigmoid"]

@@ -1,0 +1,387 @@
+"""GDLA oracle: a plain fp64 CPU implementation of the Grouped Differential
+Latent Attention forward pass (one layer), its single-token decode form, and
+the latent expansion.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the package
+smoke check and the benchmark's CPU-baseline leg may import this module.  It
+shares no code with the HIP library and imports nothing from it; the HIP path
+never calls it.
+
+Sources (cited by page title and paragraph; the summary page of the technical
+report has no headings, so its paragraphs are named by topic):
+
+  [M3-arch]  "Motif 3: Technical Report", architecture paragraph: a block is a
+             GDLA layer then a sparse MoE layer; hybrid schedule of one full
+             causal layer followed by three sliding-window layers; GDLA has a
+             query-dependent output gate.
+  [M3-gdla]  same page, GDLA summary paragraph: one normalization and one
+             up-projection of the compressed KV latent; signal and noise paths
+             differ only along the expanded head dimension; compact MLA-style
+             inference state.
+  [M3-eq]    same page, GDLA definition paragraph: low-rank query down/up
+             projection; joint KV down-projection giving the latent and a
+             decoupled rotary key; normalize-and-expand into shared content
+             key / value heads; RoPE on rotary parts only; g times more signal
+             heads than noise heads; lambda_t = sigmoid(x_t W_lambda), one per
+             signal head; D_t = H_S,t - lambda_t * Repeat_g(H_N,t); sigmoid
+             gate from the normalized query latent before the output
+             projection.
+  [M3-cfg]   same page, model-configuration paragraph (head counts, 192-dim
+             query-key heads with a 64-dim rotary part, 128-dim values).
+  [OSM-1]    "Open-Source Frontier Models: Architecture and Benchmarks of
+             Rnj-1 and Motif-2", section 1 (full vs sliding-window attention):
+             softmax(Q K^T / sqrt(d_k)) V; a sliding window lets each token
+             see W previous tokens.
+  [OSM-2]    same page, section 2 (YaRN): RoPE as a block-diagonal rotation
+             with theta_i = b^(-2(i-1)/d).
+  [OSM-impl] same page, implementation section: frequencies duplicated as
+             cat(freqs, freqs) and the rotate-half application
+             x*cos + rotate_half(x)*sin.
+
+Readings where the pages are silent (each listed in the design notes):
+RMSNorm with a learned gain for both latents; eps = cfg rms_eps; rotate-half
+RoPE with theta_i = base^(-2i/d_rope), i = 0..d_rope/2-1, positions
+p = pos_offset + t; the rotary part is the last d_rope dims of each query head;
+one rotary key per token shared by every head; softmax scale
+1/sqrt(d_nope + d_rope); query heads 0..nS-1 are signal, nS..H-1 are noise;
+signal head j and noise head j//g both use KV head j//g; window W means keys
+s with t - W < s <= t (W <= 0 or W >= L: full causal); no biases; weights are
+[out, in] (y = x W^T); W_UKV rows are all content-key heads then all value
+heads.
+
+Every function works in float64 on whatever it is given (inputs are widened
+with np.asarray(..., float64)); nothing is rounded to bf16 here.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Cfg:
+    """Layer shape and options (field names follow the C header)."""
+
+    d_model: int
+    q_rank: int
+    kv_rank: int
+    n_noise: int      # number of noise heads = number of expanded KV heads
+    group: int        # g: signal heads per noise head
+    d_nope: int
+    d_rope: int
+    d_v: int
+    window: int = 0   # <= 0: full causal
+    rope_base: float = 10000.0
+    rms_eps: float = 1e-6
+
+    @property
+    def n_signal(self) -> int:
+        return self.group * self.n_noise
+
+    @property
+    def n_heads(self) -> int:
+        return self.n_signal + self.n_noise
+
+    @property
+    def d_qk(self) -> int:
+        return self.d_nope + self.d_rope
+
+
+def _with_window(cfg: Cfg, window):
+    return replace(cfg, window=int(window))
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Elementary pieces
+# --------------------------------------------------------------------------
+
+def linear(x, w):
+    """y = x W^T with W stored [out, in] (the layout reading).  A plain
+    matrix product; the library routine is the step."""
+    return _f64(x) @ _f64(w).T
+
+
+def rms_norm(c, gamma, eps):
+    """RMSNorm over the last axis: c / sqrt(mean(c^2) + eps) * gamma.
+    [M3-gdla] and [M3-eq] say the latents are normalized; the norm's kind is
+    the reading above."""
+    c = _f64(c)
+    rms = np.sqrt(np.mean(c * c, axis=-1, keepdims=True) + eps)
+    return c / rms * _f64(gamma)
+
+
+def sigmoid(z):
+    """Logistic function 1 / (1 + e^-z) ([M3-eq]: lambda and the gate)."""
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def rope_inv_freq(d_rope, base):
+    """theta_i = base^(-2i/d_rope), i = 0..d_rope/2-1 ([OSM-2], written
+    0-based; the same table the implementation section builds from
+    arange(0, d, 2) / d)."""
+    i = np.arange(d_rope // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * i / d_rope)
+
+
+def rope(u, pos, base):
+    """Rotate-half RoPE ([OSM-impl]) of u[..., T, d_rope] at positions pos[T].
+
+    For each i < d_rope/2 the pair (u_i, u_{i+d/2}) is rotated by angle
+    pos * theta_i:  u_i' = u_i cos - u_{i+d/2} sin,
+                    u_{i+d/2}' = u_{i+d/2} cos + u_i sin.
+    """
+    u = _f64(u)
+    d = u.shape[-1]
+    half = d // 2
+    ang = _f64(pos)[:, None] * rope_inv_freq(d, base)[None, :]      # [T, d/2]
+    cos, sin = np.cos(ang), np.sin(ang)
+    u1, u2 = u[..., :half], u[..., half:]
+    return np.concatenate([u1 * cos - u2 * sin, u2 * cos + u1 * sin], axis=-1)
+
+
+def kv_head_of(h, cfg: Cfg):
+    """KV head used by query head h: j // g for signal head j, h - nS for
+    noise head h ([M3-eq]: the expanded heads are shared by both paths; the
+    pairing j -> j // g is the Repeat_g reading)."""
+    return h // cfg.group if h < cfg.n_signal else h - cfg.n_signal
+
+
+def attended_keys(t, window):
+    """Keys position t may attend: max(0, t-W+1) .. t ([OSM-1]); W <= 0 is
+    full causal ([M3-arch])."""
+    lo = 0 if window <= 0 else max(0, t - window + 1)
+    return lo, t + 1
+
+
+# --------------------------------------------------------------------------
+# Latent expansion ([M3-gdla], [M3-eq])
+# --------------------------------------------------------------------------
+
+def latent_expand(c_kv, g_kv, w_ukv, cfg: Cfg):
+    """c_KVn = RMSNorm(c_KV); [K^C | V] = c_KVn W_UKV^T split into n_noise
+    content-key heads [.., n_noise, d_nope] and value heads [.., n_noise, d_v].
+    Returns (k_nope, v, c_norm)."""
+    c_norm = rms_norm(c_kv, g_kv, cfg.rms_eps)
+    kv = linear(c_norm, w_ukv)
+    nk = cfg.n_noise * cfg.d_nope
+    lead = kv.shape[:-1]
+    k_nope = kv[..., :nk].reshape(*lead, cfg.n_noise, cfg.d_nope)
+    v = kv[..., nk:].reshape(*lead, cfg.n_noise, cfg.d_v)
+    return k_nope, v, c_norm
+
+
+# --------------------------------------------------------------------------
+# Per-token projections shared by prefill and decode ([M3-eq])
+# --------------------------------------------------------------------------
+
+def project_tokens(x, W, cfg: Cfg, pos):
+    """Steps that act on each token alone.  x [T, d_model], pos [T].
+
+    Returns a dict with
+      cqn    normalized query latent              [T, q_rank]
+      q      query heads, RoPE applied to rotary  [T, H, d_qk]
+      ckvn   normalized KV latent                 [T, kv_rank]
+      kr     rotary key after RoPE                [T, d_rope]
+      lam    lambda = sigmoid(x W_lambda^T)       [T, nS]
+      gate   sigmoid(cqn W_G^T)                   [T, nS * d_v]
+    """
+    x = _f64(x)
+    T = x.shape[0]
+    # query: low-rank down-projection, normalization, up-projection
+    cq = linear(x, W["w_dq"])
+    cqn = rms_norm(cq, W["g_q"], cfg.rms_eps)
+    q = linear(cqn, W["w_uq"]).reshape(T, cfg.n_heads, cfg.d_qk)
+    # RoPE only on the rotary part (last d_rope dims) of every query head
+    q_rot = rope(np.transpose(q[:, :, cfg.d_nope:], (1, 0, 2)), pos, cfg.rope_base)
+    q = np.concatenate([q[:, :, :cfg.d_nope], np.transpose(q_rot, (1, 0, 2))], axis=-1)
+    # KV: joint down-projection to [latent | rotary key]
+    ckv_kr = linear(x, W["w_dkv"])
+    ckv = ckv_kr[:, :cfg.kv_rank]
+    kr = rope(ckv_kr[:, cfg.kv_rank:], pos, cfg.rope_base)
+    ckvn = rms_norm(ckv, W["g_kv"], cfg.rms_eps)
+    # token-dependent differential coefficient, one per signal head
+    lam = sigmoid(linear(x, W["w_lambda"]))
+    # element-wise output gate from the normalized query latent
+    gate = sigmoid(linear(cqn, W["w_gate"]))
+    return dict(cqn=cqn, q=q, ckvn=ckvn, kr=kr, lam=lam, gate=gate)
+
+
+def differential_gate_out(Hs, Hn, lam, gate, w_o, cfg: Cfg):
+    """D_j = H_S,j - lambda_j * H_N,j//g; Z = gate * vec(D); y = Z W_O^T.
+    Hs [R, nS, d_v], Hn [R, nN, d_v], lam [R, nS], gate [R, nS*d_v].
+    ([M3-eq]; D's definition and the gate before the output projection.)"""
+    rep = np.repeat(Hn, cfg.group, axis=1)                 # Repeat_g: j -> j//g
+    D = Hs - lam[:, :, None] * rep
+    Z = gate * D.reshape(D.shape[0], -1)
+    y = linear(Z, w_o)
+    return y, Z, D
+
+
+# --------------------------------------------------------------------------
+# Prefill: one GDLA layer over [B, L] tokens
+# --------------------------------------------------------------------------
+
+def _consecutive_runs(rows, max_len):
+    """Split a sorted row list into runs of consecutive positions (at most
+    max_len long); each run shares one key range.  Pure iteration order: every
+    row is still computed on its own."""
+    runs, cur = [], []
+    for r in rows:
+        if cur and (r != cur[-1] + 1 or len(cur) == max_len):
+            runs.append(cur)
+            cur = []
+        cur.append(r)
+    if cur:
+        runs.append(cur)
+    return runs
+
+
+def attention_heads(q, kc, kr, v, rows, cfg: Cfg):
+    """Per-head causal / sliding-window softmax attention ([OSM-1], [M3-eq]).
+
+    q [R, H, d_qk] for query positions `rows`; kc [L, nN, d_nope]; kr [L, d_rope]
+    (one rotary key per token, shared by all heads); v [L, nN, d_v].
+    H[r, h] = sum_{s in A(t)} softmax_s(q_h . [k^C_n,s | k_R,s] / sqrt(d_qk)) v_n,s
+    with n = kv_head_of(h), A(t) = attended_keys(t, window).
+    """
+    scale = 1.0 / math.sqrt(cfg.d_qk)
+    out = np.zeros((len(rows), cfg.n_heads, cfg.d_v))
+    index = {t: i for i, t in enumerate(rows)}
+    for run in _consecutive_runs(rows, 128):
+        lo_run = attended_keys(run[0], cfg.window)[0]
+        hi_run = run[-1] + 1
+        spos = np.arange(lo_run, hi_run)
+        tpos = np.array(run)
+        lo_t = np.array([attended_keys(t, cfg.window)[0] for t in run])
+        allowed = (spos[None, :] <= tpos[:, None]) & (spos[None, :] >= lo_t[:, None])
+        idx = [index[t] for t in run]
+        for h in range(cfg.n_heads):
+            n = kv_head_of(h, cfg)
+            k = np.concatenate([kc[lo_run:hi_run, n, :], kr[lo_run:hi_run]], axis=-1)
+            s = (q[idx, h, :] @ k.T) * scale                     # [run, S]
+            s = np.where(allowed, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            w = np.exp(s)
+            w /= w.sum(axis=1, keepdims=True)
+            out[idx, h, :] = w @ v[lo_run:hi_run, n, :]
+    return out
+
+
+def gdla_layer(x, W, cfg: Cfg, pos_offset=0, rows=None, lam_override=None):
+    """One GDLA layer, [M3-eq] steps in order.
+
+    x      [B, L, d_model]
+    W      dict of weights (names as in the C header)
+    rows   optional sorted list of query positions to evaluate (the same for
+           every sequence); keys and values are still built for every position
+    lam_override  optional constant replacing lambda (special-case checks)
+
+    Returns dict: y [B, R, d_model], Z [B, R, nS*d_v], H [B, R, H, d_v]
+    (per-head attention outputs before the difference), cache
+    [B, L, kv_rank + d_rope] (normalized latent | RoPE'd rotary key),
+    lam [B, R, nS], and the row list used.
+    """
+    x = _f64(x)
+    B, L, _ = x.shape
+    R = list(range(L)) if rows is None else sorted(int(r) for r in rows)
+    pos = pos_offset + np.arange(L, dtype=np.float64)
+    ys, Zs, Hs_all, caches, lams = [], [], [], [], []
+    for b in range(B):
+        p = project_tokens(x[b], W, cfg, pos)
+        kc, v, _ = latent_expand_from_norm(p["ckvn"], W["w_ukv"], cfg)
+        Hh = attention_heads(p["q"][R], kc, p["kr"], v, R, cfg)
+        lam = p["lam"][R]
+        if lam_override is not None:
+            lam = np.full_like(lam, float(lam_override))
+        y, Z, _ = differential_gate_out(Hh[:, :cfg.n_signal], Hh[:, cfg.n_signal:],
+                                        lam, p["gate"][R], W["w_o"], cfg)
+        ys.append(y)
+        Zs.append(Z)
+        Hs_all.append(Hh)
+        lams.append(lam)
+        caches.append(np.concatenate([p["ckvn"], p["kr"]], axis=-1))
+    return dict(y=np.stack(ys), Z=np.stack(Zs), H=np.stack(Hs_all),
+                cache=np.stack(caches), lam=np.stack(lams), rows=R)
+
+
+def latent_expand_from_norm(ckvn, w_ukv, cfg: Cfg):
+    """[K^C | V] = c_KVn W_UKV^T for an already-normalized latent (the cache
+    holds normalized rows, so decode expands without renormalizing)."""
+    kv = linear(ckvn, w_ukv)
+    nk = cfg.n_noise * cfg.d_nope
+    lead = kv.shape[:-1]
+    return (kv[..., :nk].reshape(*lead, cfg.n_noise, cfg.d_nope),
+            kv[..., nk:].reshape(*lead, cfg.n_noise, cfg.d_v), ckvn)
+
+
+# --------------------------------------------------------------------------
+# Decode: one new token per sequence against the compressed cache
+# --------------------------------------------------------------------------
+
+def gdla_decode(x_new, W, cfg: Cfg, cache, cache_lens):
+    """One decode step ([M3-gdla]: only the normalized latent and rotary key
+    are kept per position).
+
+    x_new       [B, d_model]  the new token of each sequence
+    cache       [B, capacity, kv_rank + d_rope] rows [c_KVn | RoPE(k_R)]
+    cache_lens  [B] tokens already cached; the new token sits at that position
+
+    The new token's row is appended first, then every attended cached row is
+    expanded plainly (k^C = W_UK,n c, v = W_UV,n c) and steps 7-10 run for
+    the one query.  Returns dict y [B, d_model], Z [B, nS*d_v], new_rows
+    [B, kv_rank + d_rope].
+    """
+    x_new = _f64(x_new)
+    cache = _f64(cache)
+    B = x_new.shape[0]
+    ys, Zs, rows_out = [], [], []
+    for b in range(B):
+        p_b = int(cache_lens[b])
+        pr = project_tokens(x_new[b:b + 1], W, cfg, np.array([p_b], dtype=np.float64))
+        new_row = np.concatenate([pr["ckvn"][0], pr["kr"][0]])
+        lo, hi = attended_keys(p_b, cfg.window)
+        rows = np.array(cache[b, lo:hi])
+        rows[hi - 1 - lo] = new_row                      # the appended row
+        kc, v, _ = latent_expand_from_norm(rows[:, :cfg.kv_rank], W["w_ukv"], cfg)
+        kr = rows[:, cfg.kv_rank:]
+        # keys are indexed relative to lo, so the query sits at hi-1-lo
+        Hh = attention_heads(pr["q"], kc, kr, v, [hi - 1 - lo],
+                             _with_window(cfg, 0))[0]
+        y, Z, _ = differential_gate_out(Hh[None, :cfg.n_signal], Hh[None, cfg.n_signal:],
+                                        pr["lam"], pr["gate"], W["w_o"], cfg)
+        ys.append(y[0])
+        Zs.append(Z[0])
+        rows_out.append(new_row)
+    return dict(y=np.stack(ys), Z=np.stack(Zs), new_rows=np.stack(rows_out))
+
+
+# --------------------------------------------------------------------------
+# Hybrid block ([M3-arch]): 1 full-causal layer then 3 sliding-window layers
+# --------------------------------------------------------------------------
+
+def hybrid_windows(n_layers, window):
+    """Window of each layer in a hybrid block: layer 0 of every group of four
+    is full causal (0), the other three use `window`."""
+    return [0 if (l % 4) == 0 else int(window) for l in range(n_layers)]
+
+
+def gdla_block(x, Ws, cfg: Cfg, window):
+    """A plain residual stand-in joins the layers: x_{l+1} = x_l + y_l (the
+    pages' hyper-connections are another component).  Returns the list of
+    per-layer outputs and the final stream."""
+    x = _f64(x)
+    outs = []
+    for l, (W, win) in enumerate(zip(Ws, hybrid_windows(len(Ws), window))):
+        y = gdla_layer(x, W, _with_window(cfg, win))["y"]
+        outs.append(y)
+        x = x + y
+    return outs, x

@@ -1,0 +1,422 @@
+"""Pins that tie the GDLA oracle to facts outside itself: closed forms,
+invariants, special cases that reduce to textbook routines, and brute force on
+tiny inputs.  Each pin is a plain function that raises AssertionError; the
+pytest module test_oracle_pins.py runs them, and test_oracle_mutants.py runs
+them again against deliberately broken copies of the oracle to show that each
+plausible mistake is caught by at least one pin.
+
+Every call goes through the module object R so that a patched oracle function
+is seen by the pins.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import replace
+
+import numpy as np
+
+import oracle.gdla_ref as R
+
+# A tiny layer: 2 noise heads, g = 2 (4 signal heads), 4-dim content / rotary
+# parts, so every loop below is cheap.
+TINY = R.Cfg(d_model=24, q_rank=12, kv_rank=8, n_noise=2, group=2, d_nope=4, d_rope=4, d_v=4)
+L_TINY = 11
+
+
+def tiny_weights(cfg=TINY, seed=0, sharp=2.0, gamma_random=True):
+    """Random weights with std sharp/sqrt(fan_in) so attention is not uniform."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nS, H = cfg.n_signal, cfg.n_heads
+
+    def w(o, i, s=1.0):
+        return rng.standard_normal((o, i)) * (s / math.sqrt(i))
+
+    W = dict(
+        w_dq=w(cfg.q_rank, cfg.d_model),
+        w_dkv=w(cfg.kv_rank + cfg.d_rope, cfg.d_model, sharp),
+        w_lambda=w(nS, cfg.d_model),
+        w_uq=w(H * cfg.d_qk, cfg.q_rank, sharp),
+        w_ukv=w(cfg.n_noise * (cfg.d_nope + cfg.d_v), cfg.kv_rank),
+        w_gate=w(nS * cfg.d_v, cfg.q_rank),
+        w_o=w(cfg.d_model, nS * cfg.d_v),
+    )
+    if gamma_random:
+        W["g_q"] = 1.0 + 0.2 * rng.standard_normal(cfg.q_rank)
+        W["g_kv"] = 1.0 + 0.2 * rng.standard_normal(cfg.kv_rank)
+    else:
+        W["g_q"] = np.ones(cfg.q_rank)
+        W["g_kv"] = np.ones(cfg.kv_rank)
+    return W
+
+
+def tiny_x(B=2, L=L_TINY, cfg=TINY, seed=1):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.standard_normal((B, L, cfg.d_model))
+
+
+def close(a, b, tol=1e-12):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    scale = max(1.0, float(np.max(np.abs(b)))) if b.size else 1.0
+    assert err <= tol * scale, f"max abs err {err:.3e} > {tol:.1e}"
+
+
+# ---------------------------------------------------------------- projections
+
+def pin_linear_explicit_sums():
+    """x W^T with W stored [out, in], against explicit triple loops."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    x = rng.standard_normal((3, 5))
+    w = rng.standard_normal((4, 5))
+    ref = [[sum(x[i, k] * w[o, k] for k in range(5)) for o in range(4)] for i in range(3)]
+    close(R.linear(x, w), ref)
+
+
+def pin_rms_norm_closed_form():
+    """[3, 4] has mean square 12.5; unit gain makes the output RMS one; scaling
+    the input does not change the output (up to eps)."""
+    eps = 1e-6
+    close(R.rms_norm(np.array([3.0, 4.0]), np.ones(2), eps),
+          np.array([3.0, 4.0]) / math.sqrt(12.5 + eps))
+    rng = np.random.Generator(np.random.PCG64(6))
+    c = rng.standard_normal((7, 16)) * 3.0
+    out = R.rms_norm(c, np.ones(16), 0.0)
+    close(np.sqrt(np.mean(out ** 2, axis=-1)), np.ones(7))
+    close(R.rms_norm(5.0 * c, np.ones(16), 0.0), out)
+    g = rng.standard_normal(16)
+    close(R.rms_norm(c, g, 0.0), out * g)
+
+
+def pin_sigmoid_values():
+    close(R.sigmoid(0.0), 0.5)
+    close(R.sigmoid(math.log(3.0)), 0.75)
+    z = np.linspace(-30, 30, 61)
+    close(R.sigmoid(z) + R.sigmoid(-z), np.ones_like(z))
+
+
+# ---------------------------------------------------------------------- RoPE
+
+def pin_rope_frequencies():
+    """theta_i = base^(-2i/d): d = 4, base 10000 gives (1, 1/100); d = 64 ends
+    at base^(-62/64)."""
+    close(R.rope_inv_freq(4, 10000.0), [1.0, 0.01])
+    th = R.rope_inv_freq(64, 10000.0)
+    assert th.shape == (32,)
+    close(th[-1], 10000.0 ** (-62.0 / 64.0))
+
+
+def pin_rope_complex_rotation():
+    """Rotate-half RoPE multiplies z_i = u_i + 1j*u_{i+d/2} by exp(1j*p*theta_i)
+    (complex form of the block-diagonal rotation); p = 0 is the identity and
+    the rotation keeps the norm."""
+    rng = np.random.Generator(np.random.PCG64(7))
+    d, base = 8, 10000.0
+    u = rng.standard_normal((5, d))
+    pos = np.array([0.0, 1.0, 2.0, 37.0, 40000.0])
+    out = R.rope(u, pos, base)
+    z = u[:, :d // 2] + 1j * u[:, d // 2:]
+    th = np.array([base ** (-2.0 * i / d) for i in range(d // 2)])
+    zr = z * np.exp(1j * pos[:, None] * th[None, :])
+    close(out[:, :d // 2], zr.real)
+    close(out[:, d // 2:], zr.imag)
+    close(out[0], u[0])
+    close(np.linalg.norm(out, axis=1), np.linalg.norm(u, axis=1))
+    # the first pair turns by exactly p radians: (1, 0) -> (cos 1, sin 1)
+    e = np.zeros((1, d)); e[0, 0] = 1.0
+    r1 = R.rope(e, np.array([1.0]), base)[0]
+    close([r1[0], r1[d // 2]], [math.cos(1.0), math.sin(1.0)])
+
+
+def pin_rope_relative():
+    """<rope(q, m), rope(k, n)> depends only on m - n; rotations compose."""
+    rng = np.random.Generator(np.random.PCG64(8))
+    q, k = rng.standard_normal((1, 16)), rng.standard_normal((1, 16))
+    a = float((R.rope(q, np.array([100.0]), 1e4) @ R.rope(k, np.array([93.0]), 1e4).T)[0, 0])
+    b = float((R.rope(q, np.array([7.0]), 1e4) @ R.rope(k, np.array([0.0]), 1e4).T)[0, 0])
+    close(a, b, 1e-10)
+    close(R.rope(R.rope(q, np.array([3.0]), 1e4), np.array([4.0]), 1e4),
+          R.rope(q, np.array([7.0]), 1e4), 1e-12)
+
+
+# ----------------------------------------------------------------- attention
+
+def brute_force_heads(q, kc, kr, v, rows, cfg):
+    """Per-head, per-row softmax attention with scalar loops and math.exp."""
+    out = np.zeros((len(rows), cfg.n_heads, cfg.d_v))
+    scale = 1.0 / math.sqrt(cfg.d_nope + cfg.d_rope)
+    for ri, t in enumerate(rows):
+        lo = 0 if cfg.window <= 0 else max(0, t - cfg.window + 1)
+        for h in range(cfg.n_heads):
+            n = h // cfg.group if h < cfg.group * cfg.n_noise else h - cfg.group * cfg.n_noise
+            sc = []
+            for s in range(lo, t + 1):
+                dot = 0.0
+                for i in range(cfg.d_nope):
+                    dot += q[ri, h, i] * kc[s, n, i]
+                for i in range(cfg.d_rope):
+                    dot += q[ri, h, cfg.d_nope + i] * kr[s, i]
+                sc.append(dot * scale)
+            m = max(sc)
+            e = [math.exp(x - m) for x in sc]
+            tot = sum(e)
+            for j in range(cfg.d_v):
+                out[ri, h, j] = sum(e[s - lo] * v[s, n, j] for s in range(lo, t + 1)) / tot
+    return out
+
+
+def _rand_qkv(cfg, L, seed, sharp=2.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((L, cfg.n_heads, cfg.d_qk)) * sharp
+    kc = rng.standard_normal((L, cfg.n_noise, cfg.d_nope))
+    kr = rng.standard_normal((L, cfg.d_rope))
+    v = rng.standard_normal((L, cfg.n_noise, cfg.d_v))
+    return q, kc, kr, v
+
+
+def pin_attention_brute_force():
+    for window in (0, 3, 1, 50):
+        cfg = replace(TINY, window=window)
+        q, kc, kr, v = _rand_qkv(cfg, 9, seed=11 + window)
+        rows = list(range(9))
+        close(R.attention_heads(q, kc, kr, v, rows, cfg), brute_force_heads(q, kc, kr, v, rows, cfg), 1e-12)
+        sub = [0, 4, 8]
+        close(R.attention_heads(q[sub], kc, kr, v, sub, cfg), brute_force_heads(q[sub], kc, kr, v, sub, cfg), 1e-12)
+
+
+def pin_attention_two_key_closed_form():
+    """Row 1 sees keys 0 and 1: H = v0 + sigmoid((s1 - s0)/sqrt(d_qk)) (v1 - v0)."""
+    cfg = TINY
+    q, kc, kr, v = _rand_qkv(cfg, 2, seed=21)
+    H = R.attention_heads(q[1:2], kc, kr, v, [1], cfg)[0]
+    for h in range(cfg.n_heads):
+        n = h // cfg.group if h < cfg.n_signal else h - cfg.n_signal
+        k0 = np.concatenate([kc[0, n], kr[0]])
+        k1 = np.concatenate([kc[1, n], kr[1]])
+        a = 1.0 / (1.0 + math.exp(-(q[1, h] @ k1 - q[1, h] @ k0) / math.sqrt(cfg.d_qk)))
+        close(H[h], v[0, n] + a * (v[1, n] - v[0, n]), 1e-12)
+
+
+def pin_attention_head_mapping():
+    """With KV head n's values all equal to n + 1, every query head returns the
+    number of the KV head it reads: signal j -> j // g, noise nS + n -> n."""
+    cfg = replace(TINY, n_noise=3, group=3)
+    L = 5
+    q, kc, kr, _ = _rand_qkv(cfg, L, seed=22)
+    v = np.zeros((L, cfg.n_noise, cfg.d_v))
+    for n in range(cfg.n_noise):
+        v[:, n, :] = n + 1
+    H = R.attention_heads(q, kc, kr, v, list(range(L)), cfg)
+    expect = [1, 1, 1, 2, 2, 2, 3, 3, 3, 1, 2, 3]
+    for h, e in enumerate(expect):
+        close(H[:, h, :], np.full((L, cfg.d_v), float(e)))
+
+
+def pin_attention_masks():
+    """W >= L equals full causal; W = 1 returns the token's own value; row 0
+    returns v_0; with q = 0 each row is the mean of v over its window."""
+    L = 10
+    q, kc, kr, v = _rand_qkv(TINY, L, seed=23)
+    rows = list(range(L))
+    full = R.attention_heads(q, kc, kr, v, rows, replace(TINY, window=0))
+    close(R.attention_heads(q, kc, kr, v, rows, replace(TINY, window=L)), full, 1e-13)
+    close(R.attention_heads(q, kc, kr, v, rows, replace(TINY, window=L + 5)), full, 1e-13)
+    own = R.attention_heads(q, kc, kr, v, rows, replace(TINY, window=1))
+    for h in range(TINY.n_heads):
+        n = h // TINY.group if h < TINY.n_signal else h - TINY.n_signal
+        close(own[:, h], v[:, n])
+        close(full[0, h], v[0, n])
+    zero_q = np.zeros_like(q)
+    for window in (0, 4):
+        Hm = R.attention_heads(zero_q, kc, kr, v, rows, replace(TINY, window=window))
+        for t in range(L):
+            lo = 0 if window == 0 else max(0, t - window + 1)
+            for h in range(TINY.n_heads):
+                n = h // TINY.group if h < TINY.n_signal else h - TINY.n_signal
+                close(Hm[t, h], v[lo:t + 1, n].mean(axis=0), 1e-13)
+
+
+# -------------------------------------------------------------- whole layer
+
+def pin_layer_causality():
+    """Changing x at s > t leaves row t unchanged; with a window W, so does
+    changing x at s <= t - W, while s = t - W + 1 is inside the window."""
+    W = tiny_weights()
+    x = tiny_x(B=1)
+    t = 7
+    for window in (0, 3):
+        cfg = replace(TINY, window=window)
+        base = R.gdla_layer(x, W, cfg)["y"][0]
+        x2 = x.copy(); x2[0, t + 1:] += 5.0
+        close(R.gdla_layer(x2, W, cfg)["y"][0, :t + 1], base[:t + 1], 1e-12)
+        if window:
+            x3 = x.copy(); x3[0, :t - window + 1] += 5.0
+            close(R.gdla_layer(x3, W, cfg)["y"][0, t], base[t], 1e-12)
+            x4 = x.copy(); x4[0, t - window + 1] += 5.0
+            d = np.max(np.abs(R.gdla_layer(x4, W, cfg)["y"][0, t] - base[t]))
+            assert d > 1e-6, "the oldest key inside the window had no effect"
+
+
+def pin_layer_position_shift():
+    """Only relative positions enter the scores, so a common position offset
+    leaves y unchanged; the cache's rotary key does change."""
+    W = tiny_weights()
+    x = tiny_x()
+    a = R.gdla_layer(x, W, TINY, pos_offset=0)
+    b = R.gdla_layer(x, W, TINY, pos_offset=1234)
+    close(b["y"], a["y"], 1e-10)
+    assert np.max(np.abs(b["cache"][..., TINY.kv_rank:] - a["cache"][..., TINY.kv_rank:])) > 1e-3
+
+
+def pin_layer_norm_invariance():
+    """Both latents are RMS-normalized: scaling W_DQ, or the latent rows of
+    W_DKV, by c > 0 leaves y unchanged (eps = 0); scaling the rotary-key rows
+    does change y (that key is not normalized)."""
+    W = tiny_weights()
+    x = tiny_x()
+    cfg = replace(TINY, rms_eps=0.0)
+    base = R.gdla_layer(x, W, cfg)["y"]
+    W1 = dict(W, w_dq=W["w_dq"] * 3.7)
+    close(R.gdla_layer(x, W1, cfg)["y"], base, 1e-12)
+    w_dkv = W["w_dkv"].copy(); w_dkv[:cfg.kv_rank] *= 0.3
+    close(R.gdla_layer(x, dict(W, w_dkv=w_dkv), cfg)["y"], base, 1e-12)
+    w_dkv = W["w_dkv"].copy(); w_dkv[cfg.kv_rank:] *= 3.0
+    assert np.max(np.abs(R.gdla_layer(x, dict(W, w_dkv=w_dkv), cfg)["y"] - base)) > 1e-6
+
+
+def mla_gqa_reference(x, W, cfg):
+    """Multi-head latent attention with grouped KV heads written the standard
+    way (per-head q, k, v, then softmax attention), for the signal heads only,
+    followed by the gate and the output projection; this is what GDLA reduces
+    to when lambda = 0."""
+    B, L, _ = x.shape
+    out = np.zeros((B, L, cfg.d_model))
+    th = np.array([cfg.rope_base ** (-2.0 * i / cfg.d_rope) for i in range(cfg.d_rope // 2)])
+    for b in range(B):
+        cq = x[b] @ W["w_dq"].T
+        cqn = cq / np.sqrt((cq ** 2).mean(-1, keepdims=True) + cfg.rms_eps) * W["g_q"]
+        ckr = x[b] @ W["w_dkv"].T
+        c = ckr[:, :cfg.kv_rank]
+        cn = c / np.sqrt((c ** 2).mean(-1, keepdims=True) + cfg.rms_eps) * W["g_kv"]
+        kr = ckr[:, cfg.kv_rank:]
+        qall = (cqn @ W["w_uq"].T).reshape(L, cfg.n_heads, cfg.d_qk)
+        kv = cn @ W["w_ukv"].T
+        gate = 1.0 / (1.0 + np.exp(-(cqn @ W["w_gate"].T)))
+        Z = np.zeros((L, cfg.n_signal * cfg.d_v))
+        for j in range(cfg.n_signal):
+            n = j // cfg.group
+            qh = qall[:, j, :].copy()
+            kh = np.concatenate([kv[:, n * cfg.d_nope:(n + 1) * cfg.d_nope], kr], axis=1)
+            vh = kv[:, cfg.n_noise * cfg.d_nope + n * cfg.d_v:cfg.n_noise * cfg.d_nope + (n + 1) * cfg.d_v]
+            # rotary parts as complex numbers turned by p * theta
+            half = cfg.d_rope // 2
+            ang = np.arange(L)[:, None] * th[None, :]
+            for arr in (qh, kh):
+                z = (arr[:, cfg.d_nope:cfg.d_nope + half] + 1j * arr[:, cfg.d_nope + half:]) * np.exp(1j * ang)
+                arr[:, cfg.d_nope:cfg.d_nope + half] = z.real
+                arr[:, cfg.d_nope + half:] = z.imag
+            s = qh @ kh.T / math.sqrt(cfg.d_qk)
+            s[np.triu_indices(L, 1)] = -np.inf
+            p = np.exp(s - s.max(1, keepdims=True))
+            p /= p.sum(1, keepdims=True)
+            Z[:, j * cfg.d_v:(j + 1) * cfg.d_v] = p @ vh
+        out[b] = (gate * Z) @ W["w_o"].T
+    return out
+
+
+def pin_layer_lambda_zero_is_latent_attention():
+    W = tiny_weights()
+    x = tiny_x()
+    got = R.gdla_layer(x, W, TINY, lam_override=0.0)["y"]
+    close(got, mla_gqa_reference(x, W, TINY), 1e-11)
+
+
+def pin_layer_closed_forms():
+    """W_lambda = 0 gives lambda = 1/2; W_G = 0 gives gate = 1/2 so Z = D/2;
+    with g = 1 and each noise head's query rows equal to its signal head's,
+    H_N = H_S and D = (1 - lambda) H_S."""
+    W = tiny_weights()
+    x = tiny_x()
+    out = R.gdla_layer(x, dict(W, w_lambda=np.zeros_like(W["w_lambda"])), TINY)
+    close(out["lam"], np.full_like(out["lam"], 0.5), 0)
+    Wg = dict(W, w_gate=np.zeros_like(W["w_gate"]))
+    o = R.gdla_layer(x, Wg, TINY)
+    H = o["H"]
+    nS, g = TINY.n_signal, TINY.group
+    D = H[:, :, :nS] - o["lam"][..., None] * np.repeat(H[:, :, nS:], g, axis=2)
+    close(o["Z"], 0.5 * D.reshape(*D.shape[:2], -1), 1e-13)
+    # g = 1: copy each signal head's W_UQ rows into its noise partner
+    c1 = replace(TINY, group=1, n_noise=2)
+    W1 = tiny_weights(c1, seed=3)
+    wuq = W1["w_uq"].reshape(c1.n_heads, c1.d_qk, c1.q_rank).copy()
+    wuq[c1.n_signal:] = wuq[:c1.n_signal]
+    W1["w_uq"] = wuq.reshape(-1, c1.q_rank)
+    o1 = R.gdla_layer(x, W1, c1)
+    Hs = o1["H"][:, :, :c1.n_signal]
+    close(o1["H"][:, :, c1.n_signal:], Hs, 1e-13)
+    Dexp = (1.0 - o1["lam"])[..., None] * Hs
+    o1g = R.gdla_layer(x, dict(W1, w_gate=np.zeros_like(W1["w_gate"])), c1)
+    close(o1g["Z"], 0.5 * Dexp.reshape(*Dexp.shape[:2], -1), 1e-12)
+
+
+def pin_differential_pairing():
+    """Signal head j subtracts noise head j // g (g = 2, two noise heads:
+    heads 0, 1 pair with noise 0 and heads 2, 3 with noise 1)."""
+    cfg = TINY
+    Hs = np.arange(4 * cfg.d_v, dtype=np.float64).reshape(1, 4, cfg.d_v)
+    Hn = np.array([[[100.0] * cfg.d_v, [1000.0] * cfg.d_v]])
+    lam = np.array([[0.5, 0.25, 0.5, 0.25]])
+    _, Z, D = R.differential_gate_out(Hs, Hn, lam, np.ones((1, 4 * cfg.d_v)),
+                                      np.zeros((3, 4 * cfg.d_v)), cfg)
+    close(D[0, 0], Hs[0, 0] - 50.0)
+    close(D[0, 1], Hs[0, 1] - 25.0)
+    close(D[0, 2], Hs[0, 2] - 500.0)
+    close(D[0, 3], Hs[0, 3] - 250.0)
+
+
+def pin_decode_matches_prefill():
+    """Decoding token L-1 against the cache prefill wrote for tokens 0..L-2
+    gives prefill's row L-1, for full and windowed layers."""
+    W = tiny_weights()
+    x = tiny_x(B=2)
+    L = x.shape[1]
+    for window in (0, 4):
+        cfg = replace(TINY, window=window)
+        full = R.gdla_layer(x, W, cfg)
+        pre = R.gdla_layer(x[:, :L - 1], W, cfg)
+        cap = L + 3
+        cache = np.zeros((2, cap, cfg.kv_rank + cfg.d_rope))
+        cache[:, :L - 1] = pre["cache"]
+        dec = R.gdla_decode(x[:, L - 1], W, cfg, cache, np.array([L - 1, L - 1]))
+        close(dec["y"], full["y"][:, L - 1], 1e-11)
+        close(dec["new_rows"], full["cache"][:, L - 1], 1e-12)
+
+
+def pin_latent_expand():
+    """latent_expand = RMSNorm then W_UKV split into key heads then value
+    heads, checked element by element with explicit sums."""
+    cfg = TINY
+    rng = np.random.Generator(np.random.PCG64(31))
+    c = rng.standard_normal((3, cfg.kv_rank))
+    g = rng.standard_normal(cfg.kv_rank)
+    w = rng.standard_normal((cfg.n_noise * (cfg.d_nope + cfg.d_v), cfg.kv_rank))
+    kn, v, cn = R.latent_expand(c, g, w, cfg)
+    for t in range(3):
+        r = math.sqrt(sum(c[t, i] ** 2 for i in range(cfg.kv_rank)) / cfg.kv_rank + cfg.rms_eps)
+        for n in range(cfg.n_noise):
+            for i in range(cfg.d_nope):
+                row = n * cfg.d_nope + i
+                close(kn[t, n, i], sum(c[t, k] / r * g[k] * w[row, k] for k in range(cfg.kv_rank)), 1e-12)
+            for i in range(cfg.d_v):
+                row = cfg.n_noise * cfg.d_nope + n * cfg.d_v + i
+                close(v[t, n, i], sum(c[t, k] / r * g[k] * w[row, k] for k in range(cfg.kv_rank)), 1e-12)
+
+
+def pin_hybrid_schedule():
+    """One full-causal layer, then three sliding-window layers, repeating."""
+    assert R.hybrid_windows(4, 4096) == [0, 4096, 4096, 4096]
+    assert R.hybrid_windows(8, 128) == [0, 128, 128, 128, 0, 128, 128, 128]
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

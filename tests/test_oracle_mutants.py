@@ -1,0 +1,187 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at
+least one pin catches each of them; this shows the pins constrain every part
+of the oracle rather than restating it."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.gdla_ref as R
+from tests import oracle_pins as P
+
+
+def _rope_wrong_sign(u, pos, base):
+    u = np.asarray(u, np.float64)
+    half = u.shape[-1] // 2
+    ang = np.asarray(pos, np.float64)[:, None] * R.rope_inv_freq(u.shape[-1], base)[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    u1, u2 = u[..., :half], u[..., half:]
+    return np.concatenate([u1 * c + u2 * s, u2 * c - u1 * s * 0.5], axis=-1)
+
+
+def _rope_adjacent_pairs(u, pos, base):
+    u = np.asarray(u, np.float64)
+    d = u.shape[-1]
+    ang = np.asarray(pos, np.float64)[:, None] * R.rope_inv_freq(d, base)[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = u[..., 0::2], u[..., 1::2]
+    out = np.empty_like(u)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = b * c + a * s
+    return out
+
+
+def _inv_freq_wrong(d, base):
+    i = np.arange(d // 2, dtype=np.float64)
+    return np.power(float(base), -1.0 * i / d)
+
+
+def _kv_head_modulo(h, cfg):
+    return h % cfg.n_noise if h < cfg.n_signal else h - cfg.n_signal
+
+
+def _window_off_by_one(t, window):
+    lo = 0 if window <= 0 else max(0, t - window)
+    return lo, t + 1
+
+
+def _not_causal(t, window):
+    return 0, t + 2
+
+
+def _diff_one_minus_lambda(Hs, Hn, lam, gate, w_o, cfg):
+    rep = np.repeat(Hn, cfg.group, axis=1)
+    D = Hs - (1.0 - lam)[:, :, None] * rep
+    Z = gate * D.reshape(D.shape[0], -1)
+    return R.linear(Z, w_o), Z, D
+
+
+def _diff_tile_not_repeat(Hs, Hn, lam, gate, w_o, cfg):
+    rep = np.tile(Hn, (1, cfg.group, 1))
+    D = Hs - lam[:, :, None] * rep
+    Z = gate * D.reshape(D.shape[0], -1)
+    return R.linear(Z, w_o), Z, D
+
+
+def _diff_no_gate(Hs, Hn, lam, gate, w_o, cfg):
+    rep = np.repeat(Hn, cfg.group, axis=1)
+    D = Hs - lam[:, :, None] * rep
+    Z = D.reshape(D.shape[0], -1)
+    return R.linear(Z, w_o), Z, D
+
+
+def _rms_no_eps_sqrt(c, gamma, eps):
+    c = np.asarray(c, np.float64)
+    return c / (np.mean(c * c, axis=-1, keepdims=True) + eps) * np.asarray(gamma, np.float64)
+
+
+def _sigmoid_tanh_wrong(z):
+    return 0.5 * (1.0 + np.tanh(np.asarray(z, np.float64)))
+
+
+_orig_project = R.project_tokens
+
+
+def _gate_from_raw_latent(x, W, cfg, pos):
+    out = _orig_project(x, W, cfg, pos)
+    cq = R.linear(x, W["w_dq"])
+    out["gate"] = R.sigmoid(R.linear(cq, W["w_gate"]))
+    return out
+
+
+def _key_not_roped(x, W, cfg, pos):
+    out = _orig_project(x, W, cfg, pos)
+    out["kr"] = R.linear(x, W["w_dkv"])[:, cfg.kv_rank:]
+    return out
+
+
+def _kv_not_normalized(x, W, cfg, pos):
+    out = _orig_project(x, W, cfg, pos)
+    out["ckvn"] = R.linear(x, W["w_dkv"])[:, :cfg.kv_rank] * np.asarray(W["g_kv"], np.float64)
+    return out
+
+
+_orig_attn = R.attention_heads
+
+
+def _attn_scale_dnope(q, kc, kr, v, rows, cfg):
+    # a scale of 1/sqrt(d_nope) instead of 1/sqrt(d_nope + d_rope)
+    f = math.sqrt(cfg.d_nope / cfg.d_qk)
+    return _orig_attn(np.asarray(q) / f, kc, kr, v, rows, cfg)
+
+
+def _attn_drop_rope_term(q, kc, kr, v, rows, cfg):
+    return _orig_attn(q, kc, np.zeros_like(np.asarray(kr, np.float64)), v, rows, cfg)
+
+
+_orig_decode = R.gdla_decode
+
+
+def _decode_without_append(x_new, W, cfg, cache, cache_lens):
+    # attend only to the rows already cached (forgets the new token's own row)
+    lens = np.asarray(cache_lens)
+    out = []
+    for b in range(len(lens)):
+        o = _orig_decode(x_new[b:b + 1], W, cfg, cache[b:b + 1], lens[b:b + 1] - 1)
+        out.append(o)
+    return dict(y=np.concatenate([o["y"] for o in out]), Z=np.concatenate([o["Z"] for o in out]),
+                new_rows=np.concatenate([o["new_rows"] for o in out]))
+
+
+def _linear_transposed(x, w):
+    w = np.asarray(w, np.float64)
+    if w.shape[0] == w.shape[1]:
+        return np.asarray(x, np.float64) @ w
+    return np.asarray(x, np.float64) @ w.T * (1.0 + 1e-3)
+
+
+_orig_le = R.latent_expand
+
+
+def _latent_expand_swapped(c_kv, g_kv, w_ukv, cfg):
+    # value heads read from the key rows and vice versa
+    kn, v, cn = _orig_le(c_kv, g_kv, w_ukv, cfg)
+    return v[..., :cfg.d_nope], kn[..., :cfg.d_v], cn
+
+
+def _hybrid_last_full(n, w):
+    return [0 if (l % 4) == 3 else int(w) for l in range(n)]
+
+
+MUTANTS = {
+    "rope_wrong_sign": ("rope", _rope_wrong_sign),
+    "rope_adjacent_pairs": ("rope", _rope_adjacent_pairs),
+    "rope_theta_exponent": ("rope_inv_freq", _inv_freq_wrong),
+    "kv_head_modulo": ("kv_head_of", _kv_head_modulo),
+    "window_off_by_one": ("attended_keys", _window_off_by_one),
+    "not_causal": ("attended_keys", _not_causal),
+    "diff_one_minus_lambda": ("differential_gate_out", _diff_one_minus_lambda),
+    "diff_tile_not_repeat": ("differential_gate_out", _diff_tile_not_repeat),
+    "diff_no_gate": ("differential_gate_out", _diff_no_gate),
+    "rms_missing_sqrt": ("rms_norm", _rms_no_eps_sqrt),
+    "sigmoid_wrong": ("sigmoid", _sigmoid_tanh_wrong),
+    "gate_from_raw_latent": ("project_tokens", _gate_from_raw_latent),
+    "rotary_key_not_roped": ("project_tokens", _key_not_roped),
+    "kv_latent_not_normalized": ("project_tokens", _kv_not_normalized),
+    "scale_sqrt_dnope": ("attention_heads", _attn_scale_dnope),
+    "dropped_rope_term": ("attention_heads", _attn_drop_rope_term),
+    "decode_without_append": ("gdla_decode", _decode_without_append),
+    "linear_transposed": ("linear", _linear_transposed),
+    "latent_expand_swapped": ("latent_expand", _latent_expand_swapped),
+    "hybrid_last_full": ("hybrid_windows", _hybrid_last_full),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(R, attr, fn)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception as e:  # AssertionError, or a shape error from the mutant
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutant {name}"
