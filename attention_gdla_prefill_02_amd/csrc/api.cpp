@@ -1,0 +1,347 @@
+// C ABI of libgdla: argument checks, workspace carving and the launch
+// sequence of one GDLA layer (prefill), one decode step, and the latent
+// expansion.  Every check runs before the first launch, so a non-OK return
+// has enqueued nothing.  Nothing here allocates or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/gdla.h"
+#include "decode.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdla_status fail(gdla_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+gdla_status hip_fail(hipError_t e, const char* where) {
+  return fail(GDLA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Dims {
+  int64_t d, rq, rkv, nN, g, dn, dr, dv, nS, H, dqk, ndown, nq, ngate;
+  int elt;   // bytes per element of the config dtype
+};
+
+Dims dims_of(const gdla_config* c) {
+  Dims D;
+  D.d = c->d_model; D.rq = c->q_rank; D.rkv = c->kv_rank; D.nN = c->n_noise; D.g = c->group;
+  D.dn = c->d_nope; D.dr = c->d_rope; D.dv = c->d_v;
+  D.nS = D.g * D.nN; D.H = D.nS + D.nN; D.dqk = D.dn + D.dr;
+  D.ndown = D.rq + D.rkv + D.dr + D.nS;
+  D.nq = D.H * D.dqk;
+  D.ngate = D.nS * D.dv;
+  D.elt = c->dtype == GDLA_BF16 ? 2 : 4;
+  return D;
+}
+
+// Shape checks shared by every entry point.
+gdla_status check_config(const gdla_config* c) {
+  if (!c) return fail(GDLA_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->dtype != GDLA_BF16 && c->dtype != GDLA_FP32) return fail(GDLA_ERR_INVALID_ARG, "unknown dtype %d", (int)c->dtype);
+  if (c->d_model <= 0 || c->q_rank <= 0 || c->kv_rank <= 0 || c->n_noise <= 0 || c->group <= 0 ||
+      c->d_nope <= 0 || c->d_rope <= 0 || c->d_v <= 0)
+    return fail(GDLA_ERR_INVALID_ARG, "every dimension must be positive");
+  if (c->d_rope % 2) return fail(GDLA_ERR_INVALID_ARG, "d_rope must be even (got %d)", c->d_rope);
+  if (!(c->rope_base > 0.f) || !std::isfinite(c->rope_base)) return fail(GDLA_ERR_INVALID_ARG, "rope_base must be positive");
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps)) return fail(GDLA_ERR_INVALID_ARG, "rms_eps must be >= 0");
+  const int64_t H = (int64_t)c->group * c->n_noise + c->n_noise;
+  if (H * (c->d_nope + c->d_rope) > (1 << 24)) return fail(GDLA_ERR_INVALID_ARG, "too many query heads");
+  if (c->dtype == GDLA_BF16) {
+    if (c->d_nope != 128 || c->d_rope != 64 || c->d_v != 128)
+      return fail(GDLA_ERR_UNSUPPORTED, "bf16 path needs d_nope=128, d_rope=64, d_v=128 (got %d, %d, %d)",
+                  c->d_nope, c->d_rope, c->d_v);
+    if (c->group > 4) return fail(GDLA_ERR_UNSUPPORTED, "bf16 path supports group <= 4 (got %d)", c->group);
+    if (c->d_model % 64 || c->q_rank % 64 || c->kv_rank % 64)
+      return fail(GDLA_ERR_UNSUPPORTED, "bf16 path needs d_model, q_rank, kv_rank multiples of 64");
+  } else {
+    if (c->d_nope + c->d_rope > 256 || c->d_v > 256)
+      return fail(GDLA_ERR_UNSUPPORTED, "fp32 path needs d_nope + d_rope <= 256 and d_v <= 256");
+  }
+  return GDLA_OK;
+}
+
+// Prefill workspace: every intermediate of the layer, each 256-byte aligned.
+struct PrefillLayout {
+  size_t down, cqn, ckvn, kr, lam, rope, q, gate, kc, vt, z, total;
+  int64_t vt_seq, vt_ld;
+};
+
+PrefillLayout prefill_layout(const Dims& D, int64_t B, int64_t L) {
+  PrefillLayout P;
+  const int64_t T = B * L;
+  const int e = D.elt;
+  P.vt_seq = (L + 63) / 64 * 64;
+  P.vt_ld = B * P.vt_seq;
+  size_t o = 0;
+  P.down = o; o = align256(o + (size_t)T * D.ndown * 4);
+  P.cqn = o;  o = align256(o + (size_t)T * D.rq * e);
+  P.ckvn = o; o = align256(o + (size_t)T * D.rkv * 2 * e);
+  P.kr = o;   o = align256(o + (size_t)T * D.dr * e);
+  P.lam = o;  o = align256(o + (size_t)T * D.nS * 4);
+  P.rope = o; o = align256(o + (size_t)T * D.dr * 4);
+  P.q = o;    o = align256(o + (size_t)T * D.nq * e);
+  P.gate = o; o = align256(o + (size_t)T * D.ngate * 4);
+  P.kc = o;   o = align256(o + (size_t)T * D.nN * D.dn * e);
+  P.vt = o;   o = align256(o + (size_t)D.nN * D.dv * P.vt_ld * e);
+  P.z = o;    o = align256(o + (size_t)T * D.nS * D.dv * e);
+  P.total = o;
+  return P;
+}
+
+gdla_status check_weights(const gdla_weights* w) {
+  if (!w) return fail(GDLA_ERR_INVALID_ARG, "weights is NULL");
+  const void* ps[] = {w->w_dq, w->g_q, w->w_dkv, w->g_kv, w->w_lambda, w->w_uq, w->w_ukv, w->w_gate, w->w_o};
+  const char* names[] = {"w_dq", "g_q", "w_dkv", "g_kv", "w_lambda", "w_uq", "w_ukv", "w_gate", "w_o"};
+  for (int i = 0; i < 9; ++i) {
+    if (!ps[i]) return fail(GDLA_ERR_INVALID_ARG, "weight %s is NULL", names[i]);
+    if (!aligned16(ps[i])) return fail(GDLA_ERR_INVALID_ARG, "weight %s is not 16-byte aligned", names[i]);
+  }
+  return GDLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdla_status_string(gdla_status s) {
+  switch (s) {
+    case GDLA_OK: return "GDLA_OK";
+    case GDLA_ERR_INVALID_ARG: return "GDLA_ERR_INVALID_ARG";
+    case GDLA_ERR_UNSUPPORTED: return "GDLA_ERR_UNSUPPORTED";
+    case GDLA_ERR_WORKSPACE: return "GDLA_ERR_WORKSPACE";
+    case GDLA_ERR_HIP: return "GDLA_ERR_HIP";
+  }
+  return "GDLA_ERR_UNKNOWN";
+}
+
+const char* gdla_last_error(void) { return g_err; }
+
+int32_t gdla_version(void) { return 100; }
+
+size_t gdla_prefill_workspace_size(const gdla_config* cfg, int32_t B, int32_t L) {
+  if (check_config(cfg) != GDLA_OK || B < 0 || L < 0) return 0;
+  return prefill_layout(dims_of(cfg), B, L).total;
+}
+
+gdla_status gdla_prefill_workspace_layout(const gdla_config* cfg, int32_t B, int32_t L, gdla_prefill_layout* out) {
+  gdla_status st = check_config(cfg);
+  if (st != GDLA_OK) return st;
+  if (!out) return fail(GDLA_ERR_INVALID_ARG, "out is NULL");
+  if (B < 0 || L < 0) return fail(GDLA_ERR_INVALID_ARG, "B and L must be >= 0");
+  const PrefillLayout P = prefill_layout(dims_of(cfg), B, L);
+  out->down = P.down; out->cqn = P.cqn; out->ckvn = P.ckvn; out->kr = P.kr; out->lam = P.lam;
+  out->rope = P.rope; out->q = P.q; out->gate = P.gate; out->kc = P.kc; out->vt = P.vt; out->z = P.z;
+  return GDLA_OK;
+}
+
+gdla_status gdla_prefill(const gdla_config* cfg, const gdla_weights* w, int32_t B, int32_t L, int64_t pos_offset,
+                         const void* x, void* y, const void* residual, void* cache, int32_t cache_capacity,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace gdla;
+  gdla_status st = check_config(cfg);
+  if (st != GDLA_OK) return st;
+  if (B < 0 || L < 0) return fail(GDLA_ERR_INVALID_ARG, "B and L must be >= 0 (got %d, %d)", B, L);
+  if (pos_offset < 0) return fail(GDLA_ERR_INVALID_ARG, "pos_offset must be >= 0");
+  if (B == 0 || L == 0) return GDLA_OK;
+  const bool bf = cfg->dtype == GDLA_BF16;
+  if (!bf && L > 8192) return fail(GDLA_ERR_UNSUPPORTED, "fp32 path supports L <= 8192 (got %d)", L);
+  if ((int64_t)B * L > ((int64_t)1 << 31) / 8) return fail(GDLA_ERR_UNSUPPORTED, "B*L too large");
+  st = check_weights(w);
+  if (st != GDLA_OK) return st;
+  if (!x || !y) return fail(GDLA_ERR_INVALID_ARG, "x and y must be non-NULL");
+  if (!aligned16(x) || !aligned16(y) || (residual && !aligned16(residual)) || (cache && !aligned16(cache)))
+    return fail(GDLA_ERR_INVALID_ARG, "x, y, residual and cache must be 16-byte aligned");
+  if (x == y) return fail(GDLA_ERR_INVALID_ARG, "y must not alias x");
+  if (cache && (int64_t)cache_capacity < pos_offset + L)
+    return fail(GDLA_ERR_INVALID_ARG, "cache_capacity %d < pos_offset + L = %lld", cache_capacity,
+                (long long)(pos_offset + L));
+  if (pos_offset + L > (int64_t)1 << 30) return fail(GDLA_ERR_INVALID_ARG, "positions beyond 2^30");
+  const Dims D = dims_of(cfg);
+  const PrefillLayout P = prefill_layout(D, B, L);
+  if (!workspace) return fail(GDLA_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", P.total);
+  if (((uintptr_t)workspace & 255) != 0) return fail(GDLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < P.total)
+    return fail(GDLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, P.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int64_t T = (int64_t)B * L;
+  const int e = D.elt;
+  auto gemm = bf ? gemm_bf16 : gemm_f32;
+  hipError_t err;
+
+  // 1. fused down-projection: [c_Q | c_KV k_R | lambda logit] = x [W_DQ; W_DKV; W_l]^T (fp32 out)
+  {
+    GemmArgs g{};
+    g.A = x; g.lda = D.d;
+    g.B = w->w_dq; g.ldb = D.d;
+    g.B2 = w->w_dkv; g.nb2 = (int)D.rq;
+    g.B3 = w->w_lambda; g.nb3 = (int)(D.rq + D.rkv + D.dr);
+    g.C = ws + P.down; g.ldc = D.ndown;
+    g.M = (int)T; g.N = (int)D.ndown; g.K = (int)D.d; g.batch = 1; g.epi = EPI_F32;
+    if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "down-projection");
+  }
+  // 2. row prep: norms, rotary key, lambda, RoPE table, cache rows
+  {
+    RowPrepArgs r{};
+    r.down = (const float*)(ws + P.down); r.ld_down = D.ndown;
+    r.T = T; r.L = L; r.pos_offset = pos_offset;
+    r.q_rank = (int)D.rq; r.kv_rank = (int)D.rkv; r.d_rope = (int)D.dr; r.nS = (int)D.nS;
+    r.g_q = w->g_q; r.g_kv = w->g_kv; r.eps = cfg->rms_eps; r.rope_base = cfg->rope_base;
+    r.cqn = ws + P.cqn; r.ckvn = ws + P.ckvn; r.kr = ws + P.kr; r.lam = (float*)(ws + P.lam);
+    r.rope = (float*)(ws + P.rope); r.cache = cache; r.cache_cap = cache_capacity;
+    r.split_kv = bf;
+    if ((err = rowprep(r, bf, s)) != hipSuccess) return hip_fail(err, "row prep");
+  }
+  // 3. latent expansion: K^C = c_KVn W_UK^T (token-major), V^T = W_UV c_KVn^T (per
+  //    sequence).  bf16: c_KVn enters as [hi | lo] over K = 2*kv_rank against the
+  //    weight read twice (K wrap), so the expansion does not round the latent.
+  {
+    const int64_t kk = bf ? 2 * D.rkv : D.rkv;
+    GemmArgs g{};
+    g.A = ws + P.ckvn; g.lda = kk;
+    g.B = w->w_ukv; g.ldb = D.rkv; g.kwrapB = bf ? (int)D.rkv : 0;
+    g.C = ws + P.kc; g.ldc = D.nN * D.dn;
+    g.M = (int)T; g.N = (int)(D.nN * D.dn); g.K = (int)kk; g.batch = 1; g.epi = EPI_STORE;
+    if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "latent expand (keys)");
+    GemmArgs v{};
+    v.A = (const char*)w->w_ukv + (size_t)D.nN * D.dn * D.rkv * e; v.lda = D.rkv; v.strideA = 0;
+    v.kwrapA = bf ? (int)D.rkv : 0;
+    v.B = ws + P.ckvn; v.ldb = kk; v.strideB = (int64_t)L * kk;
+    v.C = ws + P.vt; v.ldc = P.vt_ld; v.strideC = P.vt_seq;
+    v.M = (int)(D.nN * D.dv); v.N = L; v.K = (int)kk; v.batch = B; v.epi = EPI_STORE;
+    if ((err = gemm(v, s)) != hipSuccess) return hip_fail(err, "latent expand (values)");
+  }
+  // 4. query up-projection with RoPE on the rotary parts, and the sigmoid gate
+  //    (fp32): [Q | G] = c_Qn [W_UQ; W_G]^T
+  if (bf) {
+    GemmArgs g{};
+    g.A = ws + P.cqn; g.lda = D.rq;
+    g.B = w->w_uq; g.ldb = D.rq;
+    g.B2 = w->w_gate; g.nb2 = (int)D.nq;
+    g.C = ws + P.q; g.ldc = D.nq;
+    g.G = (float*)(ws + P.gate); g.ldg = D.ngate;
+    g.M = (int)T; g.N = (int)(D.nq + D.ngate); g.K = (int)D.rq; g.batch = 1; g.epi = EPI_QG;
+    g.rope = (const float*)(ws + P.rope); g.q_cols = (int)D.nq;
+    g.d_qk = (int)D.dqk; g.d_nope = (int)D.dn; g.d_rope = (int)D.dr;
+    if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "query/gate projection");
+  } else {
+    GemmArgs g{};
+    g.A = ws + P.cqn; g.lda = D.rq;
+    g.B = w->w_uq; g.ldb = D.rq;
+    g.C = ws + P.q; g.ldc = D.nq;
+    g.M = (int)T; g.N = (int)D.nq; g.K = (int)D.rq; g.batch = 1; g.epi = EPI_STORE;
+    if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "query projection");
+    g.B = w->w_gate; g.C = ws + P.gate; g.ldc = D.ngate; g.N = (int)D.ngate;
+    if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "gate projection");
+    if ((err = qg_finish((float*)(ws + P.q), D.nq, (float*)(ws + P.gate), D.ngate, T, (int)D.H, (int)D.ngate,
+                         (int)D.dqk, (int)D.dn, (int)D.dr, (const float*)(ws + P.rope), s)) != hipSuccess)
+      return hip_fail(err, "query/gate finish");
+  }
+  // 5. attention, signal + noise heads, fused differential and gate
+  {
+    AttnArgs a{};
+    a.q = ws + P.q; a.ld_q = D.nq;
+    a.gate = (const float*)(ws + P.gate); a.ld_gate = D.ngate;
+    a.kc = ws + P.kc; a.ld_kc = D.nN * D.dn;
+    a.kr = ws + P.kr;
+    a.vt = ws + P.vt; a.ld_vt = P.vt_ld; a.vt_seq = P.vt_seq;
+    a.lam = (const float*)(ws + P.lam);
+    a.z = ws + P.z;
+    a.B = B; a.L = L; a.nN = (int)D.nN; a.g = (int)D.g; a.window = cfg->window;
+    a.d_nope = (int)D.dn; a.d_rope = (int)D.dr; a.d_v = (int)D.dv;
+    a.scale = (float)(1.0 / std::sqrt((double)D.dqk));
+    if ((err = bf ? attn_bf16(a, s) : attn_f32(a, s)) != hipSuccess) return hip_fail(err, "attention");
+  }
+  // 6. output projection (+ residual)
+  {
+    GemmArgs g{};
+    g.A = ws + P.z; g.lda = D.nS * D.dv;
+    g.B = w->w_o; g.ldb = D.nS * D.dv;
+    g.C = y; g.ldc = D.d;
+    g.R = residual; g.ldr = D.d;
+    g.M = (int)T; g.N = (int)D.d; g.K = (int)(D.nS * D.dv); g.batch = 1; g.epi = EPI_STORE;
+    if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "output projection");
+  }
+  return GDLA_OK;
+}
+
+gdla_status gdla_latent_expand(const gdla_config* cfg, int64_t T, const void* c_kv, int64_t ld_c, const void* g_kv,
+                               const void* w_ukv, void* k_nope, void* v, void* c_norm, void* stream) {
+  using namespace gdla;
+  gdla_status st = check_config(cfg);
+  if (st != GDLA_OK) return st;
+  if (T < 0) return fail(GDLA_ERR_INVALID_ARG, "T must be >= 0");
+  if (T == 0) return GDLA_OK;
+  if (T > ((int64_t)1 << 31) / 8) return fail(GDLA_ERR_UNSUPPORTED, "T too large");
+  if (ld_c < cfg->kv_rank) return fail(GDLA_ERR_INVALID_ARG, "ld_c (%lld) < kv_rank (%d)", (long long)ld_c, cfg->kv_rank);
+  if (!c_kv || !g_kv || !w_ukv || !k_nope || !v || !c_norm)
+    return fail(GDLA_ERR_INVALID_ARG, "c_kv, g_kv, w_ukv, k_nope, v and c_norm must be non-NULL");
+  const void* ps[] = {c_kv, g_kv, w_ukv, k_nope, v, c_norm};
+  for (const void* p : ps)
+    if (!aligned16(p)) return fail(GDLA_ERR_INVALID_ARG, "all pointers must be 16-byte aligned");
+  const Dims D = dims_of(cfg);
+  if ((ld_c * D.elt) % 16) return fail(GDLA_ERR_INVALID_ARG, "ld_c rows must be 16-byte multiples");
+  const bool bf = cfg->dtype == GDLA_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err;
+  LatentNormArgs n{c_kv, ld_c, T, (int)D.rkv, g_kv, cfg->rms_eps, c_norm, nullptr};
+  if ((err = latent_norm(n, bf, s)) != hipSuccess) return hip_fail(err, "latent norm");
+  auto gemm = bf ? gemm_bf16 : gemm_f32;
+  GemmArgs g{};
+  g.A = c_norm; g.lda = D.rkv;
+  g.B = w_ukv; g.ldb = D.rkv;
+  g.C = k_nope; g.ldc = D.nN * D.dn;
+  g.M = (int)T; g.N = (int)(D.nN * D.dn); g.K = (int)D.rkv; g.batch = 1; g.epi = EPI_STORE;
+  if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "latent expand (keys)");
+  g.B = (const char*)w_ukv + (size_t)D.nN * D.dn * D.rkv * D.elt;
+  g.C = v; g.ldc = D.nN * D.dv; g.N = (int)(D.nN * D.dv);
+  if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "latent expand (values)");
+  return GDLA_OK;
+}
+
+size_t gdla_decode_workspace_size(const gdla_config* cfg, int32_t B) {
+  if (check_config(cfg) != GDLA_OK || B < 0 || cfg->dtype != GDLA_BF16) return 0;
+  return gdla::decode_workspace_bytes(cfg, B);
+}
+
+gdla_status gdla_decode(const gdla_config* cfg, const gdla_weights* w, int32_t B, const void* x, void* y, void* cache,
+                        const int32_t* cache_lens, int32_t capacity, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  gdla_status st = check_config(cfg);
+  if (st != GDLA_OK) return st;
+  if (cfg->dtype != GDLA_BF16) return fail(GDLA_ERR_UNSUPPORTED, "decode is bf16 only");
+  if (B < 0) return fail(GDLA_ERR_INVALID_ARG, "B must be >= 0");
+  if (B == 0) return GDLA_OK;
+  if (capacity <= 0) return fail(GDLA_ERR_INVALID_ARG, "capacity must be positive");
+  st = check_weights(w);
+  if (st != GDLA_OK) return st;
+  if (!x || !y || !cache || !cache_lens) return fail(GDLA_ERR_INVALID_ARG, "x, y, cache and cache_lens must be non-NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(cache) || ((uintptr_t)cache_lens & 3))
+    return fail(GDLA_ERR_INVALID_ARG, "x, y, cache must be 16-byte aligned, cache_lens 4-byte aligned");
+  const size_t need = gdla::decode_workspace_bytes(cfg, B);
+  if (!workspace) return fail(GDLA_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", need);
+  if (((uintptr_t)workspace & 255) != 0) return fail(GDLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need) return fail(GDLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  hipError_t err = gdla::decode_step(cfg, w, B, x, y, cache, cache_lens, capacity, workspace, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "decode");
+  return GDLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,411 @@
+// GDLA attention core with the fused differential + gate epilogue.
+//
+// What it computes ("Motif 3: Technical Report", GDLA definition paragraph;
+// softmax(QK^T/sqrt(d_k))V and the sliding window from "Open-Source Frontier
+// Models: Architecture and Benchmarks of Rnj-1 and Motif-2", section 1):
+//   for KV head n, its g signal heads j = n*g .. n*g+g-1 and noise head nS+n,
+//   H_h,t = sum_{s in A(t)} softmax_s(q_h,t . [k^C_n,s | k_R,s] / sqrt(d_qk)) v_n,s
+//   Z_t[j] = gate_t[j] * (H_j,t - lambda_t,j * H_{nS+n},t)
+// with A(t) = {s <= t} (full) or {t - W < s <= t} (window W).
+//
+// bf16 kernel (d_nope = 128, d_rope = 64, d_v = 128), one workgroup per
+// (sequence, KV head n, 64-query block):
+//  * 2(g+1) waves: wave w handles query head slot w/2 (g signal heads, then
+//    the noise head) for 32 consecutive queries.  All g+1 heads of the group
+//    read the same content key, rotary key and value, so each 64-key tile of
+//    [K^C | k_R] (64 x 192) and V^T (128 x 64) is staged in LDS once (double
+//    buffered, loads of tile j+1 in flight during tile j) and reused by every
+//    wave.
+//  * Scores are formed transposed, S^T = K Q^T, on the 32x32x16 bf16 MFMA:
+//    the 192-wide key row is the A operand (read from LDS), the wave's query
+//    rows are the B operand held in registers for the whole sweep.  Each lane
+//    then owns one query column, so the softmax row max needs one exchange
+//    with lane l^32 and the row sum needs none until the end.
+//  * Key rows are fed to the A operand with bits 2 and 3 of the in-tile index
+//    swapped; with that order the fp32 score registers of a lane, converted
+//    to bf16, are already the B operand of the P V product for 8 consecutive
+//    keys, and V^T fragments are single 16-byte LDS reads.
+//  * Online softmax in the exp2 domain with a lazy rescale: the running max
+//    is only raised (and O, l rescaled) when a tile's max exceeds it by more
+//    than 8 (so P <= 256); the decision is per query but the rescale branch is
+//    wave-uniform and rare after the first tiles.
+//  * Causal / window tile skipping: the workgroup walks only the key tiles
+//    that intersect [q0 - W + 1, q0 + 63]; masks are applied only on tiles
+//    that straddle a boundary, and a wave skips tiles none of its 32 queries
+//    sees.
+//  * Epilogue: H = O / l; the noise waves publish H_N through LDS, the signal
+//    waves form gate * (H_S - lambda * H_N) in fp32 and stage bf16 Z rows in
+//    LDS, then the workgroup writes 64 contiguous Z rows (g*d_v wide) with
+//    16-byte coalesced stores.
+//  * Workgroups are numbered so XCD x (blockIdx % 8) processes whole KV
+//    heads, query blocks in descending order (longest causal rows first);
+//    neighbouring query blocks of a head then stream the same key tiles
+//    through that XCD's L2.
+//
+// The fp32 kernel is a plain vector-ALU version (three passes per query and
+// head) for the fp32 configuration.
+#include "common.h"
+#include "kernels.h"
+
+namespace gdla {
+namespace {
+
+constexpr int DN = 128, DR = 64, DQK = DN + DR, DV = 128;
+constexpr int BQ = 64, BKV = 64;
+constexpr int K_LD = DQK + 8;        // LDS row of a key (elements), padded
+constexpr int V_LD = BKV + 8;        // LDS row of V^T (one value dim, 64 keys)
+constexpr int K_TILE = BKV * K_LD;   // elements
+constexpr int V_TILE = DV * V_LD;
+constexpr int KV_CHUNKS = BKV * (DQK / 8) + DV * (BKV / 8);   // 16-byte chunks per tile
+constexpr float NEG_INIT = -1.0e30f;
+
+__host__ __device__ constexpr int z_ld(int g) { return g * DV + 8; }
+__host__ __device__ constexpr size_t lds_bytes(int g) {
+  const size_t kv = 2 * (size_t)(K_TILE + V_TILE) * 2;
+  const size_t ep = (size_t)BQ * (DV + 4) * 4 + (size_t)BQ * z_ld(g) * 2;
+  return kv > ep ? kv : ep;
+}
+
+// Key offset (within a 32-key sub-tile) held by score element e = 4*i + j of
+// a lane in half `hi`: rows 8i + 4hi + j with bits 2 and 3 swapped.
+__device__ __forceinline__ int key_of(int e, int hi) {
+  const int i = e >> 2, j = e & 3;
+  return 16 * (i >> 1) + 8 * hi + 4 * (i & 1) + j;
+}
+
+template <int G>
+__global__ void __launch_bounds__(128 * (G + 1), 1)
+attn_bf16_kernel(AttnArgs a) {
+  constexpr int NW = 2 * (G + 1), NT = 64 * NW;
+  constexpr int CH = (KV_CHUNKS + NT - 1) / NT;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  bf16* sK = reinterpret_cast<bf16*>(smem_raw);          // [2][BKV][K_LD]
+  bf16* sV = sK + 2 * K_TILE;                              // [2][DV][V_LD]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hs = w >> 1, half = w & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int L = a.L, nN = a.nN, nS = G * nN, W = a.window;
+
+  // workgroup -> (sequence, KV head, query block)
+  const int HN = a.B * nN, nqb = cdiv(L, BQ);
+  int id = blockIdx.x, hn, qbi;
+  if ((HN & 7) == 0) {
+    const int hpx = HN >> 3, slot = id >> 3;
+    hn = (id & 7) + 8 * (slot % hpx);
+    qbi = slot / hpx;
+  } else {
+    hn = id % HN;
+    qbi = id / HN;
+  }
+  const int qb = nqb - 1 - qbi;
+  const int b = hn / nN, n = hn % nN;
+  const int q0 = qb * BQ;
+  const int64_t tb = (int64_t)b * L;
+  const int head = hs < G ? n * G + hs : nS + n;
+  const int qw0 = q0 + 32 * half;                 // first query of this wave
+  const int qme = qw0 + l32;                       // this lane's query
+  const int qlast = min(qw0 + 31, L - 1);
+  const float sc = a.scale * 1.4426950408889634f;  // exp2 domain
+
+  // this wave's query fragments, B operand: column = query, k = 16s + 8hi + e
+  bf16x8 qf[DQK / 16];
+  {
+    const bf16* qp = (const bf16*)a.q + (tb + min(qme, L - 1)) * a.ld_q + (int64_t)head * DQK + hi * 8;
+#pragma unroll
+    for (int s = 0; s < DQK / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+  }
+
+  // key tiles this workgroup visits
+  const int k_lo = W > 0 ? max(0, q0 - W + 1) : 0;
+  const int k_hi = min(L, q0 + BQ);
+  const int t_lo = k_lo / BKV, t_hi = cdiv(k_hi, BKV);
+
+  const bf16* kc = (const bf16*)a.kc + tb * a.ld_kc + (int64_t)n * DN;
+  const bf16* kr = (const bf16*)a.kr + tb * DR;
+  const bf16* vt = (const bf16*)a.vt + (int64_t)n * DV * a.ld_vt + (int64_t)b * a.vt_seq;
+
+  bf16x8 stg[CH];
+  const bf16x8 zero8 = {};
+  auto gload = [&](int tile) {
+    const int kb = tile * BKV;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + c * NT;
+      bf16x8 v = zero8;
+      if (idx < BKV * (DQK / 8)) {
+        const int r = idx / (DQK / 8), cc = idx % (DQK / 8);
+        const int key = kb + r;
+        if (key < L)
+          v = cc < DN / 8 ? *reinterpret_cast<const bf16x8*>(kc + (int64_t)key * a.ld_kc + cc * 8)
+                          : *reinterpret_cast<const bf16x8*>(kr + (int64_t)key * DR + (cc - DN / 8) * 8);
+      } else if (idx < KV_CHUNKS) {
+        const int j = idx - BKV * (DQK / 8);
+        const int d = j / (BKV / 8), cc = j % (BKV / 8);
+        const int key = kb + cc * 8;
+        const bf16* src = vt + (int64_t)d * a.ld_vt + key;
+        if (key + 8 <= L) {
+          v = *reinterpret_cast<const bf16x8*>(src);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = key + e < L ? src[e] : (bf16)0.0f;
+        }
+      }
+      stg[c] = v;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + c * NT;
+      if (idx < BKV * (DQK / 8)) {
+        const int r = idx / (DQK / 8), cc = idx % (DQK / 8);
+        *reinterpret_cast<bf16x8*>(sK + buf * K_TILE + r * K_LD + cc * 8) = stg[c];
+      } else if (idx < KV_CHUNKS) {
+        const int j = idx - BKV * (DQK / 8);
+        const int d = j / (BKV / 8), cc = j % (BKV / 8);
+        *reinterpret_cast<bf16x8*>(sV + buf * V_TILE + d * V_LD + cc * 8) = stg[c];
+      }
+    }
+  };
+
+  f32x16 o[DV / 32];
+#pragma unroll
+  for (int d = 0; d < DV / 32; ++d) o[d] = f32x16{};
+  float m = NEG_INIT, lsum = 0.f;
+
+  // key-row order of the A operand: bits 2 and 3 of the lane's row swapped
+  const int arow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+
+  gload(t_lo);
+  sstore(0);
+  __syncthreads();
+  for (int tile = t_lo; tile < t_hi; ++tile) {
+    const int buf = (tile - t_lo) & 1;
+    if (tile + 1 < t_hi) gload(tile + 1);
+    const int kb = tile * BKV;
+    const bool visible = kb <= qlast && (W <= 0 || kb + BKV - 1 > qw0 - W);
+    if (visible) {
+      const bool full = kb + BKV - 1 <= qw0 && kb + BKV <= L && (W <= 0 || kb > qlast - W);
+      const bf16* Kt = sK + buf * K_TILE + arow * K_LD + hi * 8;
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+      for (int s = 0; s < DQK / 16; ++s) {
+        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Kt + 16 * s);
+        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Kt + 32 * K_LD + 16 * s);
+        s0 = mfma32(k0, qf[s], s0);
+        s1 = mfma32(k1, qf[s], s1);
+      }
+      if (!full) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int k0 = kb + key_of(e, hi), k1 = k0 + 32;
+          const bool v0 = k0 <= qme && k0 < L && (W <= 0 || k0 > qme - W);
+          const bool v1 = k1 <= qme && k1 < L && (W <= 0 || k1 > qme - W);
+          s0[e] = v0 ? s0[e] : -INFINITY;
+          s1[e] = v1 ? s1[e] : -INFINITY;
+        }
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, fmaxf(s0[e], s1[e]));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sc;
+      const bool raise = mt > m + 8.0f;
+      if (__any(raise)) {
+        const float mn = raise ? mt : m;
+        const float alpha = fast_exp2(m - mn);
+        m = mn;
+        lsum *= alpha;
+#pragma unroll
+        for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
+      }
+      bf16x8 p[2][2];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p0 = fast_exp2(fmaf(s0[e], sc, -m));
+        const float p1 = fast_exp2(fmaf(s1[e], sc, -m));
+        lsum += p0 + p1;
+        p[0][e >> 3][e & 7] = (bf16)p0;
+        p[1][e >> 3][e & 7] = (bf16)p1;
+      }
+      const bf16* Vt = sV + buf * V_TILE + l32 * V_LD + hi * 8;
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + d * 32 * V_LD + 32 * ts + 16 * u);
+            o[d] = mfma32(vf, p[ts][u], o[d]);
+          }
+    }
+    if (tile + 1 < t_hi) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: H = O / l, Z = gate * (H_S - lambda * H_N)
+  const float l_tot = lsum + __shfl_xor(lsum, 32, 64);
+  const float inv = 1.0f / l_tot;
+  float* sH = reinterpret_cast<float*>(smem_raw);                          // [BQ][DV + 4]
+  bf16* sZ = reinterpret_cast<bf16*>(smem_raw + (size_t)BQ * (DV + 4) * 4);  // [BQ][g*DV + 8]
+  const int qrow = 32 * half + l32;
+  if (hs == G) {
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 h4 = {o[d][4 * i] * inv, o[d][4 * i + 1] * inv, o[d][4 * i + 2] * inv, o[d][4 * i + 3] * inv};
+        *reinterpret_cast<f32x4*>(sH + qrow * (DV + 4) + d * 32 + 8 * i + 4 * hi) = h4;
+      }
+  }
+  __syncthreads();
+  if (hs < G) {
+    const int64_t t = tb + min(qme, L - 1);
+    const int j = n * G + hs;
+    const float lam = a.lam[t * nS + j];
+    const float* gate = a.gate + t * a.ld_gate + (int64_t)j * DV;
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int dv = d * 32 + 8 * i + 4 * hi;
+        const f32x4 hn4 = *reinterpret_cast<const f32x4*>(sH + qrow * (DV + 4) + dv);
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(gate + dv);
+        bf16x4 z4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z4[e] = (bf16)(g4[e] * (o[d][4 * i + e] * inv - lam * hn4[e]));
+        *reinterpret_cast<bf16x4*>(sZ + qrow * z_ld(G) + hs * DV + dv) = z4;
+      }
+  }
+  __syncthreads();
+  {
+    constexpr int CPRZ = G * DV / 8;    // 16-byte chunks per Z row of this group
+    bf16* z = (bf16*)a.z;
+    for (int c = tid; c < BQ * CPRZ; c += NT) {
+      const int r = c / CPRZ, cc = c % CPRZ;
+      if (q0 + r < L)
+        *reinterpret_cast<bf16x8*>(z + (tb + q0 + r) * (int64_t)(nS * DV) + (int64_t)n * G * DV + cc * 8) =
+            *reinterpret_cast<const bf16x8*>(sZ + r * z_ld(G) + cc * 8);
+    }
+  }
+}
+
+// ------------------------------------------------------------ fp32 kernel
+// One workgroup per (query position, KV head, sequence).  Noise head first
+// (its H stays in LDS), then each signal head: scores into LDS, block max,
+// exp and sum, then H over value dims, then Z = gate * (H - lambda * H_N).
+__global__ void __launch_bounds__(256)
+attn_f32_kernel(AttnArgs a) {
+  extern __shared__ float fsm[];
+  const int L = a.L;
+  const int t = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
+  const int nS = a.g * a.nN, dqk = a.d_nope + a.d_rope, dv = a.d_v;
+  float* sc = fsm;             // [L]
+  float* hN = fsm + L;         // [dv]
+  float* red = hN + dv;        // [64]
+  const int64_t tb = (int64_t)b * L;
+  const int lo = a.window > 0 ? max(0, t - a.window + 1) : 0;
+  const float* qv = (const float*)a.q;
+  const float* kc = (const float*)a.kc;
+  const float* kr = (const float*)a.kr;
+  const float* vt = (const float*)a.vt;
+  for (int slot = a.g; slot >= 0; --slot) {
+    const int h = slot == a.g ? nS + n : n * a.g + slot;
+    const float* q = qv + (tb + t) * a.ld_q + (int64_t)h * dqk;
+    float mx = -INFINITY;
+    for (int s = lo + threadIdx.x; s <= t; s += blockDim.x) {
+      const float* k = kc + (tb + s) * a.ld_kc + (int64_t)n * a.d_nope;
+      const float* r = kr + (tb + s) * a.d_rope;
+      float dot = 0.f;
+      for (int i = 0; i < a.d_nope; ++i) dot += q[i] * k[i];
+      for (int i = 0; i < a.d_rope; ++i) dot += q[a.d_nope + i] * r[i];
+      dot *= a.scale;
+      sc[s - lo] = dot;
+      mx = fmaxf(mx, dot);
+    }
+    mx = wave_max(mx);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = red[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) mx = fmaxf(mx, red[i]);
+    __syncthreads();
+    float sum = 0.f;
+    for (int s = lo + threadIdx.x; s <= t; s += blockDim.x) {
+      const float e = expf(sc[s - lo] - mx);
+      sc[s - lo] = e;
+      sum += e;
+    }
+    sum = wave_sum(sum);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sum;
+    __syncthreads();
+    sum = 0.f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) sum += red[i];
+    for (int d = threadIdx.x; d < dv; d += blockDim.x) {
+      const float* v = vt + (int64_t)(n * dv + d) * a.ld_vt + (int64_t)b * a.vt_seq;
+      float acc = 0.f;
+      for (int s = lo; s <= t; ++s) acc += sc[s - lo] * v[s];
+      const float H = acc / sum;
+      if (slot == a.g) {
+        hN[d] = H;
+      } else {
+        const int j = n * a.g + slot;
+        const float lam = a.lam[(tb + t) * nS + j];
+        const float gte = a.gate[(tb + t) * a.ld_gate + (int64_t)j * dv + d];
+        ((float*)a.z)[(tb + t) * (int64_t)(nS * dv) + (int64_t)j * dv + d] = gte * (H - lam * hN[d]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int G>
+hipError_t launch_g(const AttnArgs& a, hipStream_t s) {
+  const size_t lds = lds_bytes(G);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<G>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int blocks = a.B * a.nN * cdiv(a.L, BQ);
+  hipLaunchKernelGGL(attn_bf16_kernel<G>, dim3(blocks), dim3(128 * (G + 1)), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_bf16_lds_bytes(int g) {
+  switch (g) {
+    case 1: return lds_bytes(1);
+    case 2: return lds_bytes(2);
+    case 3: return lds_bytes(3);
+    case 4: return lds_bytes(4);
+    default: return 0;
+  }
+}
+
+hipError_t attn_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.B <= 0 || a.L <= 0) return hipSuccess;
+  switch (a.g) {
+    case 1: return launch_g<1>(a, s);
+    case 2: return launch_g<2>(a, s);
+    case 3: return launch_g<3>(a, s);
+    case 4: return launch_g<4>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t attn_f32(const AttnArgs& a, hipStream_t s) {
+  if (a.B <= 0 || a.L <= 0) return hipSuccess;
+  const size_t lds = ((size_t)a.L + a.d_v + 64) * sizeof(float);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_f32_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(a.L, a.nN, a.B), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace gdla

@@ -1,0 +1,48 @@
+// Internal helpers shared by the gfx950 kernels of libgdla (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define GDLA_DEV __device__ __forceinline__
+
+// gfx950 matrix cores, bf16 inputs, fp32 accumulation.
+//   32x32x16: A lane l supplies row l%32, k = 8*(l/32)+e (e = vector element);
+//             B lane l supplies column l%32, the same k; D lane l holds
+//             column l%32, rows 8*i + 4*(l/32) + j in element 4*i + j.
+GDLA_DEV f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+//   16x16x32: A lane l supplies row l%16, k = 8*(l/16)+e; B column l%16;
+//             D lane l holds column l%16, rows 4*(l/16) + j.
+GDLA_DEV f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+GDLA_DEV float to_f32(bf16 v) { return (float)v; }
+GDLA_DEV float to_f32(float v) { return v; }
+template <class T> GDLA_DEV T from_f32(float v);
+template <> GDLA_DEV float from_f32<float>(float v) { return v; }
+template <> GDLA_DEV bf16 from_f32<bf16>(float v) { return (bf16)v; }   // round to nearest even
+
+GDLA_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+GDLA_DEV float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+GDLA_DEV float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+GDLA_DEV float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__host__ __device__ static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }

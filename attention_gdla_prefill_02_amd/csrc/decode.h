@@ -1,0 +1,16 @@
+// Internal interface of the decode path (one new token per sequence against
+// the compressed latent cache).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "../../include/gdla.h"
+
+namespace gdla {
+
+size_t decode_workspace_bytes(const gdla_config* cfg, int B);
+hipError_t decode_step(const gdla_config* cfg, const gdla_weights* w, int B, const void* x, void* y, void* cache,
+                       const int32_t* cache_lens, int capacity, void* workspace, hipStream_t s);
+
+}  // namespace gdla

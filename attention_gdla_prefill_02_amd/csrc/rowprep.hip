@@ -1,0 +1,135 @@
+// Per-token preparation between the fused down-projection and the
+// up-projections ("Motif 3: Technical Report", GDLA definition paragraph):
+//   c_Qn  = RMSNorm(c_Q) * g_q                      (feeds W_UQ and the gate)
+//   c_KVn = RMSNorm(c_KV) * g_kv                    (feeds W_UKV; cached)
+//   k_R   <- RoPE(k_R, p)                           (rotary key; cached)
+//   lambda = sigmoid(lambda logit)                  (one per signal head)
+// and the per-token RoPE table cos/sin(p * base^(-2i/d_rope)) used by the
+// query epilogue ("Open-Source Frontier Models: Architecture and Benchmarks
+// of Rnj-1 and Motif-2", section 2 and the rotate-half helper of its
+// implementation section).  Angles are formed and reduced in fp64: at
+// p = 262143 an fp32 angle would be off by ~0.03 rad.
+//
+// One wave per token; the row is read once (coalesced) and every output is a
+// contiguous row write.  Memory-bound and tiny next to the GEMMs.
+#include "common.h"
+#include "kernels.h"
+
+namespace gdla {
+namespace {
+
+template <class T>
+__global__ void __launch_bounds__(256)
+rowprep_kernel(RowPrepArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const float* row = a.down + t * a.ld_down;
+  const T* gq = (const T*)a.g_q;
+  const T* gkv = (const T*)a.g_kv;
+  int64_t seq, p;
+  if (a.pos_dev) {
+    seq = t;
+    p = a.pos_dev[t];
+  } else {
+    seq = t / a.L;
+    p = a.pos_offset + (t - seq * a.L);
+  }
+
+  // query latent
+  float ss = 0.f;
+  for (int i = lane; i < a.q_rank; i += 64) ss += row[i] * row[i];
+  float r = 1.0f / sqrtf(wave_sum(ss) / a.q_rank + a.eps);
+  T* cqn = (T*)a.cqn + t * a.q_rank;
+  for (int i = lane; i < a.q_rank; i += 64) cqn[i] = from_f32<T>(row[i] * r * to_f32(gq[i]));
+
+  // KV latent
+  const float* ckv = row + a.q_rank;
+  ss = 0.f;
+  for (int i = lane; i < a.kv_rank; i += 64) ss += ckv[i] * ckv[i];
+  r = 1.0f / sqrtf(wave_sum(ss) / a.kv_rank + a.eps);
+  // split rows: [hi | lo] with hi = round(c_KVn), lo = round(c_KVn - hi); the
+  // expansion then sees c_KVn to ~16 bits while the cache keeps hi
+  T* ckvn = (T*)a.ckvn + t * (a.split_kv ? 2 * a.kv_rank : a.kv_rank);
+  T* crow = a.cache ? (T*)a.cache + (seq * a.cache_cap + p) * (int64_t)(a.kv_rank + a.d_rope) : nullptr;
+  for (int i = lane; i < a.kv_rank; i += 64) {
+    const float f = ckv[i] * r * to_f32(gkv[i]);
+    const T v = from_f32<T>(f);
+    ckvn[i] = v;
+    if (a.split_kv) ckvn[a.kv_rank + i] = from_f32<T>(f - to_f32(v));
+    if (crow) crow[i] = v;
+  }
+
+  // rotary key and the RoPE table of this position
+  const float* kr = ckv + a.kv_rank;
+  const int half = a.d_rope / 2;
+  T* krow = (T*)a.kr + t * a.d_rope;
+  for (int i = lane; i < half; i += 64) {
+    const double theta = pow(a.rope_base, -2.0 * (double)i / (double)a.d_rope);
+    double sd, cd;
+    sincos((double)p * theta, &sd, &cd);
+    const float c = (float)cd, s = (float)sd;
+    a.rope[(t * half + i) * 2] = c;
+    a.rope[(t * half + i) * 2 + 1] = s;
+    const float x1 = kr[i], x2 = kr[i + half];
+    const T o1 = from_f32<T>(x1 * c - x2 * s), o2 = from_f32<T>(x2 * c + x1 * s);
+    krow[i] = o1;
+    krow[i + half] = o2;
+    if (crow) {
+      crow[a.kv_rank + i] = o1;
+      crow[a.kv_rank + i + half] = o2;
+    }
+  }
+
+  // lambda
+  const float* ll = kr + a.d_rope;
+  for (int i = lane; i < a.nS; i += 64) a.lam[t * a.nS + i] = sigmoidf_(ll[i]);
+}
+
+template <class T>
+__global__ void __launch_bounds__(256)
+latent_norm_kernel(LatentNormArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const T* c = (const T*)a.c + t * a.ldc;
+  const T* g = (const T*)a.g;
+  float ss = 0.f;
+  for (int i = lane; i < a.kv_rank; i += 64) {
+    const float v = to_f32(c[i]);
+    ss += v * v;
+  }
+  const float r = 1.0f / sqrtf(wave_sum(ss) / a.kv_rank + a.eps);
+  T* o = (T*)a.out + t * a.kv_rank;
+  T* lo = a.lo ? (T*)a.lo + t * a.kv_rank : nullptr;
+  for (int i = lane; i < a.kv_rank; i += 64) {
+    const float f = to_f32(c[i]) * r * to_f32(g[i]);
+    const T v = from_f32<T>(f);
+    o[i] = v;
+    if (lo) lo[i] = from_f32<T>(f - to_f32(v));
+  }
+}
+
+}  // namespace
+
+hipError_t rowprep(const RowPrepArgs& a, bool bf16, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv(a.T, 4)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(rowprep_kernel<__bf16>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(rowprep_kernel<float>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t latent_norm(const LatentNormArgs& a, bool bf16, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv(a.T, 4)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(latent_norm_kernel<__bf16>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(latent_norm_kernel<float>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace gdla

@@ -1,0 +1,202 @@
+/*
+ * gdla.h - C ABI of the MI355X (gfx950) GDLA forward-pass library, libgdla.so.
+ *
+ * GDLA (Grouped Differential Latent Attention) is the attention layer of
+ * "Motif 3: Technical Report".  Per token x_t of one layer:
+ *   - query: low-rank down-projection c_Q = x W_DQ^T, RMSNorm -> c_Qn, and
+ *     up-projection q = c_Qn W_UQ^T into H = nS + nN heads of d_nope + d_rope
+ *     dims (report, GDLA definition paragraph);
+ *   - KV: one joint down-projection [c_KV | k_R] = x W_DKV^T giving the
+ *     compressed latent and a decoupled rotary key; RMSNorm of the latent and
+ *     a single up-projection [K^C | V] = c_KVn W_UKV^T into nN content-key and
+ *     value heads shared by both query paths (report, GDLA summary and
+ *     definition paragraphs);
+ *   - RoPE on the rotary parts only (rotate-half form; "Open-Source Frontier
+ *     Models: Architecture and Benchmarks of Rnj-1 and Motif-2", section 2
+ *     and its implementation section);
+ *   - causal or sliding-window softmax attention for nS = g * nN signal heads
+ *     and nN noise heads (Rnj-1/Motif-2 page, section 1; report, definition
+ *     paragraph);
+ *   - D_t = H_S,t - lambda_t * Repeat_g(H_N,t), lambda_t = sigmoid(x_t W_l^T),
+ *     then an element-wise sigmoid gate from c_Qn and the output projection
+ *     y = (gate * D) W_O^T (report, definition paragraph).
+ *
+ * Conventions (readings where the report is silent):
+ *   - every weight is [out, in] row-major (y = x W^T);
+ *   - W_UQ rows: head h occupies rows h*(d_nope+d_rope) .. +d_nope+d_rope-1,
+ *     content part first, rotary part last; heads 0..nS-1 are signal heads,
+ *     nS..nS+nN-1 noise heads;
+ *   - W_UKV rows: all nN content-key heads (nN*d_nope rows) then all nN value
+ *     heads (nN*d_v rows);
+ *   - W_DKV rows: the kv_rank latent rows, then the d_rope rotary-key rows;
+ *   - signal head j and noise head j/g both attend with KV head j/g; signal
+ *     head j subtracts noise head j/g;
+ *   - RoPE angle for pair (i, i + d_rope/2) at position p is
+ *     p * rope_base^(-2i/d_rope); positions are pos_offset + t, 0-based;
+ *   - softmax scale 1/sqrt(d_nope + d_rope); window W > 0 lets position t
+ *     attend keys s with t - W < s <= t; W <= 0 is full causal;
+ *   - RMSNorm: c / sqrt(mean(c^2) + rms_eps) * gain.
+ *
+ * Ownership and threading: every buffer is device memory owned by the
+ * caller.  The library allocates nothing, keeps no state besides a
+ * thread-local error string, and never synchronizes: all work is enqueued on
+ * `stream` (a hipStream_t; NULL = the default stream) and inputs must stay
+ * valid until the stream reaches it.  Calls that share output or workspace
+ * buffers must be ordered on one stream.
+ *
+ * Errors: every argument is checked on the host before anything is enqueued;
+ * a call that returns non-OK has launched nothing.  GDLA_ERR_HIP means a
+ * launch failed; gdla_last_error() has the detail.  Faults that happen
+ * asynchronously in a kernel surface at the caller's next synchronization.
+ */
+#ifndef GDLA_H
+#define GDLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDLA_OK = 0,
+  GDLA_ERR_INVALID_ARG = 1,   /* null required pointer, bad size, misaligned pointer */
+  GDLA_ERR_UNSUPPORTED = 2,   /* shape / dtype combination no kernel covers */
+  GDLA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than *_workspace_size */
+  GDLA_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+} gdla_status;
+
+typedef enum {
+  GDLA_BF16 = 0,   /* bf16 storage, fp32 accumulation (MFMA path) */
+  GDLA_FP32 = 1    /* fp32 storage and arithmetic (vector-ALU path) */
+} gdla_dtype;
+
+typedef struct {
+  int32_t d_model;   /* token width */
+  int32_t q_rank;    /* query latent width */
+  int32_t kv_rank;   /* KV latent width */
+  int32_t n_noise;   /* nN: noise heads = expanded KV heads */
+  int32_t group;     /* g: signal heads per noise head; nS = g * nN */
+  int32_t d_nope;    /* content part of a query/key head */
+  int32_t d_rope;    /* rotary part of a query/key head (even) */
+  int32_t d_v;       /* value head width */
+  int32_t window;    /* <= 0: full causal; else keys t-window < s <= t */
+  float rope_base;   /* RoPE base, e.g. 10000 */
+  float rms_eps;     /* RMSNorm epsilon, e.g. 1e-6 */
+  gdla_dtype dtype;  /* one dtype for x, y, weights, gains and cache */
+} gdla_config;
+
+typedef struct {          /* device pointers, all [out, in] row-major, dtype of the config */
+  const void* w_dq;       /* [q_rank, d_model] */
+  const void* g_q;        /* [q_rank]            RMSNorm gain of the query latent */
+  const void* w_dkv;      /* [kv_rank + d_rope, d_model] */
+  const void* g_kv;       /* [kv_rank]           RMSNorm gain of the KV latent */
+  const void* w_lambda;   /* [nS, d_model] */
+  const void* w_uq;       /* [(nS + nN) * (d_nope + d_rope), q_rank] */
+  const void* w_ukv;      /* [nN * d_nope + nN * d_v, kv_rank] */
+  const void* w_gate;     /* [nS * d_v, q_rank] */
+  const void* w_o;        /* [d_model, nS * d_v] */
+} gdla_weights;
+
+/* Support limits of the bf16 path (the fp32 path takes any positive sizes with
+ * d_rope even, d_nope + d_rope <= 256, d_v <= 256, and L <= 8192):
+ *   d_nope = 128, d_rope = 64, d_v = 128, group + 1 <= 8,
+ *   d_model, q_rank, kv_rank and nS * d_v multiples of 64.            */
+
+/* Bytes of workspace gdla_prefill needs for B sequences of L tokens
+ * (0 if the configuration is invalid). */
+size_t gdla_prefill_workspace_size(const gdla_config* cfg, int32_t B, int32_t L);
+
+/* One GDLA layer over B sequences of L tokens (report, GDLA definition
+ * paragraph; hybrid schedules call it once per layer with that layer's window).
+ *   x          [B, L, d_model]  input tokens
+ *   y          [B, L, d_model]  output; y = residual + (gate * D) W_O^T when
+ *                               residual != NULL, else (gate * D) W_O^T.
+ *                               y may alias residual but not x otherwise.
+ *   residual   nullable [B, L, d_model]
+ *   pos_offset position of token 0 of every sequence (>= 0)
+ *   cache      nullable [B, cache_capacity, kv_rank + d_rope]: rows
+ *              pos_offset .. pos_offset + L - 1 of each sequence receive
+ *              [c_KVn | RoPE(k_R)], the layout gdla_decode reads
+ *   cache_capacity  rows per sequence in cache (>= pos_offset + L when cache
+ *              is given)
+ *   workspace  device buffer of at least gdla_prefill_workspace_size bytes,
+ *              256-byte aligned; its contents on return are the
+ *              intermediates listed by gdla_prefill_workspace_layout.
+ * All pointers 16-byte aligned. */
+gdla_status gdla_prefill(const gdla_config* cfg, const gdla_weights* w, int32_t B, int32_t L,
+                         int64_t pos_offset, const void* x, void* y, const void* residual,
+                         void* cache, int32_t cache_capacity, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Byte offsets of the intermediates inside the prefill workspace after a call
+ * (for inspection and tests).  T = B*L tokens; elements are in the config
+ * dtype unless marked fp32.
+ *   down   [T, q_rank + kv_rank + d_rope + nS] fp32: c_Q | c_KV | k_R | lambda logit
+ *   cqn    [T, q_rank]            normalized query latent
+ *   ckvn   bf16: [T, 2*kv_rank]   normalized KV latent as hi | lo, where
+ *                                 hi = bf16(c_KVn) and lo = bf16(c_KVn - hi);
+ *          fp32: [T, kv_rank]
+ *   kr     [T, d_rope]            RoPE'd rotary key
+ *   lam    [T, nS] fp32           lambda
+ *   rope   [T, d_rope/2, 2] fp32  cos, sin of each position's RoPE angles
+ *   q      [T, H*(d_nope+d_rope)] query heads, rotary parts RoPE'd
+ *   gate   [T, nS*d_v] fp32       sigmoid gate
+ *   kc     [T, nN*d_nope]         content keys
+ *   vt     [nN*d_v, B*Lp]         values transposed; sequence b's tokens at
+ *                                 columns b*Lp .. b*Lp+L-1, Lp = L rounded up to 64
+ *   z      [T, nS*d_v]            gate * D                                     */
+typedef struct {
+  int64_t down, cqn, ckvn, kr, lam, rope, q, gate, kc, vt, z;
+} gdla_prefill_layout;
+gdla_status gdla_prefill_workspace_layout(const gdla_config* cfg, int32_t B, int32_t L,
+                                          gdla_prefill_layout* out);
+
+/* Bytes of workspace gdla_decode needs for B sequences (0 if invalid). */
+size_t gdla_decode_workspace_size(const gdla_config* cfg, int32_t B);
+
+/* One decode step: one new token per sequence attends its cached context
+ * through the compressed latent (report, GDLA summary paragraph: only the
+ * normalized latent and the rotary key are kept per position).
+ *   x           [B, d_model]  the new tokens
+ *   y           [B, d_model]  output (gate * D) W_O^T
+ *   cache       [B, capacity, kv_rank + d_rope]; rows 0 .. cache_lens[b]-1 are
+ *               read, row cache_lens[b] is written with the new token's
+ *               [c_KVn | RoPE(k_R)] before it is attended
+ *   cache_lens  device int32 [B]: tokens already cached per sequence; the new
+ *               token's position.  Read on the device (never on the host); it
+ *               must be in [0, capacity - 1].  The caller advances it.
+ * bf16 only.  All pointers 16-byte aligned. */
+gdla_status gdla_decode(const gdla_config* cfg, const gdla_weights* w, int32_t B,
+                        const void* x, void* y, void* cache, const int32_t* cache_lens,
+                        int32_t capacity, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Latent expansion alone (report, GDLA summary and definition paragraphs):
+ * c_KVn = RMSNorm(c_KV) * g_kv, [K^C | V] = c_KVn W_UKV^T.
+ *   c_kv    [T, ld_c] raw latent (first kv_rank columns used), ld_c >= kv_rank
+ *   g_kv    [kv_rank] gain;  w_ukv  [nN*d_nope + nN*d_v, kv_rank]
+ *   k_nope  [T, nN, d_nope] out
+ *   v       [T, nN, d_v]    out
+ *   c_norm  [T, kv_rank]    out: c_KVn rounded to the dtype (the GEMM's input)
+ * Row-major, dtype of the config, 16-byte aligned; T >= 0 (T = 0 is a no-op).
+ * Unlike gdla_prefill (which feeds the expansion the latent split into bf16
+ * hi and lo parts), this standalone call expands the rounded c_norm. */
+gdla_status gdla_latent_expand(const gdla_config* cfg, int64_t T, const void* c_kv, int64_t ld_c,
+                               const void* g_kv, const void* w_ukv, void* k_nope, void* v,
+                               void* c_norm, void* stream);
+
+const char* gdla_status_string(gdla_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* gdla_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t gdla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDLA_H */

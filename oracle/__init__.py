@@ -4,10 +4,10 @@ import it; the HIP library never does."""
 
 from .gdla_ref import (Cfg, attention_heads, attended_keys, differential_gate_out, gdla_block,
                        gdla_decode, gdla_layer, hybrid_windows, kv_head_of, latent_expand,
-                       latent_expand_from_norm, linear, project_tokens, rms_norm, rope,
+                       kv_tokens, latent_expand_from_norm, linear, project_tokens, query_tokens, rms_norm, rope,
                        rope_inv_freq, sigmoid)
 
 __all__ = ["Cfg", "attention_heads", "attended_keys", "differential_gate_out", "gdla_block",
            "gdla_decode", "gdla_layer", "hybrid_windows", "kv_head_of", "latent_expand",
-           "latent_expand_from_norm", "linear", "project_tokens", "rms_norm", "rope",
+           "kv_tokens", "latent_expand_from_norm", "linear", "project_tokens", "query_tokens", "rms_norm", "rope",
            "rope_inv_freq", "sigmoid"]

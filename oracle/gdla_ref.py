@@ -183,36 +183,38 @@ def latent_expand(c_kv, g_kv, w_ukv, cfg: Cfg):
 # Per-token projections shared by prefill and decode ([M3-eq])
 # --------------------------------------------------------------------------
 
-def project_tokens(x, W, cfg: Cfg, pos):
-    """Steps that act on each token alone.  x [T, d_model], pos [T].
+def kv_tokens(x, W, cfg: Cfg, pos):
+    """KV side of each token ([M3-eq], [M3-gdla]): the joint down-projection
+    [c_KV | k_R] = x W_DKV^T, c_KVn = RMSNorm(c_KV), k_R <- RoPE(k_R, pos).
+    x [T, d_model], pos [T].  Returns (ckvn [T, kv_rank], kr [T, d_rope])."""
+    ckv_kr = linear(x, W["w_dkv"])
+    ckvn = rms_norm(ckv_kr[:, :cfg.kv_rank], W["g_kv"], cfg.rms_eps)
+    kr = rope(ckv_kr[:, cfg.kv_rank:], pos, cfg.rope_base)
+    return ckvn, kr
 
-    Returns a dict with
-      cqn    normalized query latent              [T, q_rank]
-      q      query heads, RoPE applied to rotary  [T, H, d_qk]
-      ckvn   normalized KV latent                 [T, kv_rank]
-      kr     rotary key after RoPE                [T, d_rope]
-      lam    lambda = sigmoid(x W_lambda^T)       [T, nS]
-      gate   sigmoid(cqn W_G^T)                   [T, nS * d_v]
-    """
-    x = _f64(x)
+
+def query_tokens(x, W, cfg: Cfg, pos):
+    """Query side of each token ([M3-eq]): c_Qn = RMSNorm(x W_DQ^T),
+    q = c_Qn W_UQ^T with RoPE on the last d_rope dims of every head,
+    lambda = sigmoid(x W_lambda^T), gate = sigmoid(c_Qn W_G^T).
+    x [T, d_model], pos [T].  Returns dict cqn, q [T, H, d_qk], lam, gate."""
     T = x.shape[0]
-    # query: low-rank down-projection, normalization, up-projection
-    cq = linear(x, W["w_dq"])
-    cqn = rms_norm(cq, W["g_q"], cfg.rms_eps)
+    cqn = rms_norm(linear(x, W["w_dq"]), W["g_q"], cfg.rms_eps)
     q = linear(cqn, W["w_uq"]).reshape(T, cfg.n_heads, cfg.d_qk)
-    # RoPE only on the rotary part (last d_rope dims) of every query head
     q_rot = rope(np.transpose(q[:, :, cfg.d_nope:], (1, 0, 2)), pos, cfg.rope_base)
     q = np.concatenate([q[:, :, :cfg.d_nope], np.transpose(q_rot, (1, 0, 2))], axis=-1)
-    # KV: joint down-projection to [latent | rotary key]
-    ckv_kr = linear(x, W["w_dkv"])
-    ckv = ckv_kr[:, :cfg.kv_rank]
-    kr = rope(ckv_kr[:, cfg.kv_rank:], pos, cfg.rope_base)
-    ckvn = rms_norm(ckv, W["g_kv"], cfg.rms_eps)
-    # token-dependent differential coefficient, one per signal head
     lam = sigmoid(linear(x, W["w_lambda"]))
-    # element-wise output gate from the normalized query latent
     gate = sigmoid(linear(cqn, W["w_gate"]))
-    return dict(cqn=cqn, q=q, ckvn=ckvn, kr=kr, lam=lam, gate=gate)
+    return dict(cqn=cqn, q=q, lam=lam, gate=gate)
+
+
+def project_tokens(x, W, cfg: Cfg, pos):
+    """Both per-token halves: dict cqn, q, ckvn, kr, lam, gate."""
+    x = _f64(x)
+    ckvn, kr = kv_tokens(x, W, cfg, pos)
+    out = query_tokens(x, W, cfg, pos)
+    out.update(ckvn=ckvn, kr=kr)
+    return out
 
 
 def differential_gate_out(Hs, Hn, lam, gate, w_o, cfg: Cfg):
@@ -296,19 +298,21 @@ def gdla_layer(x, W, cfg: Cfg, pos_offset=0, rows=None, lam_override=None):
     pos = pos_offset + np.arange(L, dtype=np.float64)
     ys, Zs, Hs_all, caches, lams = [], [], [], [], []
     for b in range(B):
-        p = project_tokens(x[b], W, cfg, pos)
-        kc, v, _ = latent_expand_from_norm(p["ckvn"], W["w_ukv"], cfg)
-        Hh = attention_heads(p["q"][R], kc, p["kr"], v, R, cfg)
-        lam = p["lam"][R]
+        # keys and values for every position; the query path only for rows R
+        ckvn, kr = kv_tokens(x[b], W, cfg, pos)
+        kc, v, _ = latent_expand_from_norm(ckvn, W["w_ukv"], cfg)
+        qp = query_tokens(x[b, R], W, cfg, pos[R])
+        Hh = attention_heads(qp["q"], kc, kr, v, R, cfg)
+        lam = qp["lam"]
         if lam_override is not None:
             lam = np.full_like(lam, float(lam_override))
         y, Z, _ = differential_gate_out(Hh[:, :cfg.n_signal], Hh[:, cfg.n_signal:],
-                                        lam, p["gate"][R], W["w_o"], cfg)
+                                        lam, qp["gate"], W["w_o"], cfg)
         ys.append(y)
         Zs.append(Z)
         Hs_all.append(Hh)
         lams.append(lam)
-        caches.append(np.concatenate([p["ckvn"], p["kr"]], axis=-1))
+        caches.append(np.concatenate([ckvn, kr], axis=-1))
     return dict(y=np.stack(ys), Z=np.stack(Zs), H=np.stack(Hs_all),
                 cache=np.stack(caches), lam=np.stack(lams), rows=R)
 

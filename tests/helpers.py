@@ -1,0 +1,59 @@
+"""Shared helpers of the parity tests: seeded inputs on the device, the oracle
+on the same bits, and the error metrics with the tolerances of the method
+(fp32: max-abs <= 1e-4; bf16: max-abs <= 2e-2 and rel-L2 <= 5e-3)."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from attention_gdla_prefill_02_amd import inputs
+from oracle import gdla_ref as R
+
+TOL = {"fp32": dict(max_abs=1e-4, rel_l2=1e-5), "bf16": dict(max_abs=2e-2, rel_l2=5e-3)}
+
+# bf16 shapes with the real head dims and small widths: spans several tiles of
+# every kernel while the oracle finishes in well under a second.
+SMALL = dict(d_model=256, q_rank=128, kv_rank=128, n_noise=2, group=3, d_nope=128, d_rope=64, d_v=128)
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = got - ref
+    max_abs = float(np.max(np.abs(d))) if d.size else 0.0
+    den = float(np.sqrt(np.sum(ref * ref)))
+    rel = float(np.sqrt(np.sum(d * d)) / den) if den > 0 else float(np.sqrt(np.sum(d * d)))
+    return max_abs, rel
+
+
+def assert_close(got, ref, dtype, what="", tol=None):
+    t = dict(TOL[dtype])
+    if tol:
+        t.update(tol)
+    ma, rl = errors(got, ref)
+    print(f"[parity] {what}: max_abs={ma:.3e} rel_l2={rl:.3e} (tol {t['max_abs']:.0e} / {t['rel_l2']:.0e})",
+          flush=True)
+    assert np.all(np.isfinite(np.asarray(got, np.float64))), f"{what}: non-finite output"
+    assert ma <= t["max_abs"], f"{what}: max_abs {ma:.3e} > {t['max_abs']:.1e}"
+    assert rl <= t["rel_l2"], f"{what}: rel_l2 {rl:.3e} > {t['rel_l2']:.1e}"
+
+
+def oracle_cfg(shapes, window=0, rope_base=10000.0, rms_eps=1e-6):
+    return R.Cfg(**shapes, window=int(window), rope_base=rope_base, rms_eps=rms_eps)
+
+
+def make_layer(shapes, seed, dtype, init="fan_in", gamma="ones"):
+    """CPU storage tensors, device copies and the float64 view for the oracle."""
+    Wc = inputs.make_weights(shapes, seed, dtype, init=init, gamma=gamma)
+    Wd = {k: v.to("cuda") for k, v in Wc.items()}
+    W64 = {k: inputs.widen(v) for k, v in Wc.items()}
+    return Wd, W64
+
+
+def to_dev(t: torch.Tensor):
+    return t.to("cuda")
+
+
+def host64(t: torch.Tensor):
+    return t.detach().to("cpu").to(torch.float64).numpy()

@@ -1,0 +1,153 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports
+every function include/gdla.h declares, the header compiles as C, and
+invalid arguments are rejected with the right status before any launch."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from attention_gdla_prefill_02_amd import configs, gdla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdla.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdla_[a-z_]+)\s*\(", src)))
+
+
+def lib():
+    if not os.path.exists(gdla.LIB_PATH):
+        pytest.skip("libgdla.so not built")
+    return gdla.load()
+
+
+def test_exports_every_declared_function():
+    L = lib()
+    names = header_functions()
+    assert set(names) == set(gdla.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", gdla.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (gdla_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "gdla.h"\nint main(void){ gdla_config c; (void)c; return 0; }\n')
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), "-c", str(src),
+                        "-o", str(tmp_path / "t.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings_and_version():
+    L = lib()
+    assert L.gdla_status_string(0) == b"GDLA_OK"
+    assert L.gdla_status_string(3) == b"GDLA_ERR_WORKSPACE"
+    assert L.gdla_version() >= 100
+
+
+def _cfg(**kw):
+    s = dict(configs.MOTIF_SHAPES)
+    s.update({k: v for k, v in kw.items() if k in s})
+    c = gdla.make_config(s, kw.get("window", 0), kw.get("dtype", "bf16"))
+    return c
+
+
+class FakeW:
+    """Non-null, 16-byte aligned fake pointers: validation never dereferences them."""
+
+    def __init__(self, misalign=None):
+        self.ptrs = {n: 0x10000 * (i + 1) for i, n in enumerate(gdla.WEIGHT_FIELDS)}
+        if misalign:
+            self.ptrs[misalign] += 2
+
+    def struct(self, null=None):
+        return gdla.Weights(*[0 if n == null else self.ptrs[n] for n in gdla.WEIGHT_FIELDS])
+
+
+def call_prefill(cfg, w, B=1, L=16, pos=0, x=0x100000, y=0x200000, res=None, cache=None, cap=0, ws=0x300000,
+                 wsb=None):
+    L_ = lib()
+    if wsb is None:
+        wsb = L_.gdla_prefill_workspace_size(ctypes.byref(cfg), B, L)
+    st = L_.gdla_prefill(ctypes.byref(cfg), ctypes.byref(w), B, L, pos, x, y, res, cache, cap, ws, wsb, None)
+    return st, L_.gdla_last_error().decode()
+
+
+def test_prefill_rejects_bad_arguments():
+    lib()
+    w = FakeW().struct()
+    st, msg = call_prefill(_cfg(), FakeW().struct(null="w_o"))
+    assert st == gdla.GDLA_ERR_INVALID_ARG and "w_o" in msg
+    assert call_prefill(_cfg(), FakeW(misalign="w_uq").struct())[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_prefill(_cfg(), w, x=0)[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_prefill(_cfg(), w, x=0x100002)[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_prefill(_cfg(), w, y=0x100000)[0] == gdla.GDLA_ERR_INVALID_ARG   # aliases x
+    assert call_prefill(_cfg(), w, B=-1)[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_prefill(_cfg(), w, pos=-3)[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_prefill(_cfg(), w, cache=0x400000, cap=15)[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_prefill(_cfg(), w, ws=0)[0] == gdla.GDLA_ERR_WORKSPACE
+    assert call_prefill(_cfg(), w, ws=0x300010)[0] == gdla.GDLA_ERR_INVALID_ARG   # not 256-aligned
+    st, msg = call_prefill(_cfg(), w, wsb=1024)
+    assert st == gdla.GDLA_ERR_WORKSPACE and "needs" in msg
+    assert call_prefill(_cfg(d_nope=96), w)[0] == gdla.GDLA_ERR_UNSUPPORTED
+    assert call_prefill(_cfg(group=5), w)[0] == gdla.GDLA_ERR_UNSUPPORTED
+    assert call_prefill(_cfg(d_model=4000), w)[0] == gdla.GDLA_ERR_UNSUPPORTED
+    assert call_prefill(_cfg(d_rope=63, dtype="fp32"), w)[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_prefill(_cfg(n_noise=0), w)[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_prefill(_cfg(dtype="fp32", d_nope=32, d_rope=16, d_v=32), w, L=9000)[0] == gdla.GDLA_ERR_UNSUPPORTED
+    bad = _cfg()
+    bad.dtype = 7
+    assert call_prefill(bad, w)[0] == gdla.GDLA_ERR_INVALID_ARG
+    st = lib().gdla_prefill(None, ctypes.byref(w), 1, 1, 0, 0x100000, 0x200000, None, None, 0, 0x300000, 1 << 30, None)
+    assert st == gdla.GDLA_ERR_INVALID_ARG
+
+
+def test_empty_inputs_are_noops():
+    w = FakeW().struct()
+    # B = 0 or L = 0: nothing to do, OK without touching any pointer
+    assert call_prefill(_cfg(), w, B=0, x=0, y=0, ws=0)[0] == gdla.GDLA_OK
+    assert call_prefill(_cfg(), w, L=0, x=0, y=0, ws=0)[0] == gdla.GDLA_OK
+    L_ = lib()
+    assert L_.gdla_decode(ctypes.byref(_cfg()), ctypes.byref(w), 0, None, None, None, None, 0, None, 0, None) == 0
+    assert L_.gdla_latent_expand(ctypes.byref(_cfg()), 0, None, 512, None, None, None, None, None, None) == 0
+
+
+def test_workspace_size_monotone_and_layout():
+    L_ = lib()
+    c = _cfg()
+    sizes = [L_.gdla_prefill_workspace_size(ctypes.byref(c), 1, L) for L in (1, 64, 65, 4096, 32768)]
+    assert all(a < b for a, b in zip(sizes, sizes[1:]))
+    assert L_.gdla_prefill_workspace_size(ctypes.byref(_cfg(d_nope=96)), 1, 64) == 0
+    lay = gdla.prefill_layout(c, 2, 100)
+    offs = sorted(lay.values())
+    assert offs[0] == 0 and all(o % 256 == 0 for o in offs)
+    assert offs[-1] < L_.gdla_prefill_workspace_size(ctypes.byref(c), 2, 100)
+
+
+def test_decode_and_expand_reject_bad_arguments():
+    L_ = lib()
+    w = FakeW().struct()
+    c = _cfg()
+    ws = L_.gdla_decode_workspace_size(ctypes.byref(c), 4)
+    assert ws > 0
+    st = L_.gdla_decode(ctypes.byref(_cfg(dtype="fp32", d_nope=32, d_rope=16, d_v=32)), ctypes.byref(w), 4,
+                        0x100000, 0x200000, 0x400000, 0x500000, 64, 0x300000, ws, None)
+    assert st == gdla.GDLA_ERR_UNSUPPORTED
+    assert L_.gdla_decode(ctypes.byref(c), ctypes.byref(w), 4, 0x100000, 0x200000, 0, 0x500000, 64, 0x300000, ws,
+                          None) == gdla.GDLA_ERR_INVALID_ARG
+    assert L_.gdla_decode(ctypes.byref(c), ctypes.byref(w), 4, 0x100000, 0x200000, 0x400000, 0x500000, 0, 0x300000,
+                          ws, None) == gdla.GDLA_ERR_INVALID_ARG
+    assert L_.gdla_decode(ctypes.byref(c), ctypes.byref(w), 4, 0x100000, 0x200000, 0x400000, 0x500000, 64, 0x300000,
+                          ws - 1, None) == gdla.GDLA_ERR_WORKSPACE
+    assert L_.gdla_latent_expand(ctypes.byref(c), 10, 0x100000, 100, 0x200000, 0x300000, 0x400000, 0x500000,
+                                 0x600000, None) == gdla.GDLA_ERR_INVALID_ARG   # ld_c < kv_rank
+    assert L_.gdla_latent_expand(ctypes.byref(c), 10, 0x100000, 512, 0x200000, 0x300000, 0x400000, 0x500000,
+                                 None, None) == gdla.GDLA_ERR_INVALID_ARG   # c_norm required

@@ -80,25 +80,36 @@ def _sigmoid_tanh_wrong(z):
     return 0.5 * (1.0 + np.tanh(np.asarray(z, np.float64)))
 
 
-_orig_project = R.project_tokens
+_orig_query = R.query_tokens
+_orig_kv = R.kv_tokens
 
 
 def _gate_from_raw_latent(x, W, cfg, pos):
-    out = _orig_project(x, W, cfg, pos)
+    out = _orig_query(x, W, cfg, pos)
     cq = R.linear(x, W["w_dq"])
     out["gate"] = R.sigmoid(R.linear(cq, W["w_gate"]))
     return out
 
 
 def _key_not_roped(x, W, cfg, pos):
-    out = _orig_project(x, W, cfg, pos)
-    out["kr"] = R.linear(x, W["w_dkv"])[:, cfg.kv_rank:]
-    return out
+    ckvn, _ = _orig_kv(x, W, cfg, pos)
+    return ckvn, R.linear(x, W["w_dkv"])[:, cfg.kv_rank:]
 
 
 def _kv_not_normalized(x, W, cfg, pos):
-    out = _orig_project(x, W, cfg, pos)
-    out["ckvn"] = R.linear(x, W["w_dkv"])[:, :cfg.kv_rank] * np.asarray(W["g_kv"], np.float64)
+    _, kr = _orig_kv(x, W, cfg, pos)
+    return R.linear(x, W["w_dkv"])[:, :cfg.kv_rank] * np.asarray(W["g_kv"], np.float64), kr
+
+
+def _query_rope_on_content(x, W, cfg, pos):
+    out = _orig_query(x, W, cfg, pos)
+    q = out["q"]
+    # rotate the first d_rope dims (content) instead of the last ones
+    rot = R.rope(np.transpose(q[:, :, :cfg.d_rope], (1, 0, 2)), pos, cfg.rope_base)
+    raw = R.linear(R.rms_norm(R.linear(x, W["w_dq"]), W["g_q"], cfg.rms_eps), W["w_uq"]).reshape(q.shape)
+    out["q"] = np.concatenate([np.transpose(R.rope(np.transpose(raw[:, :, :cfg.d_rope], (1, 0, 2)), pos, cfg.rope_base), (1, 0, 2)),
+                               raw[:, :, cfg.d_rope:]], axis=-1)
+    del rot
     return out
 
 
@@ -161,9 +172,10 @@ MUTANTS = {
     "diff_no_gate": ("differential_gate_out", _diff_no_gate),
     "rms_missing_sqrt": ("rms_norm", _rms_no_eps_sqrt),
     "sigmoid_wrong": ("sigmoid", _sigmoid_tanh_wrong),
-    "gate_from_raw_latent": ("project_tokens", _gate_from_raw_latent),
-    "rotary_key_not_roped": ("project_tokens", _key_not_roped),
-    "kv_latent_not_normalized": ("project_tokens", _kv_not_normalized),
+    "gate_from_raw_latent": ("query_tokens", _gate_from_raw_latent),
+    "rotary_key_not_roped": ("kv_tokens", _key_not_roped),
+    "kv_latent_not_normalized": ("kv_tokens", _kv_not_normalized),
+    "query_rope_on_content": ("query_tokens", _query_rope_on_content),
     "scale_sqrt_dnope": ("attention_heads", _attn_scale_dnope),
     "dropped_rope_term": ("attention_heads", _attn_drop_rope_term),
     "decode_without_append": ("gdla_decode", _decode_without_append),
