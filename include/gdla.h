@@ -130,6 +130,28 @@ gdla_status gdla_prefill(const gdla_config* cfg, const gdla_weights* w, int32_t 
                          void* cache, int32_t cache_capacity, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Stages of one prefill layer, in launch order.  gdla_prefill runs them all;
+ * gdla_prefill_stages runs a subset on the same workspace (for per-stage
+ * timing and profiling: later stages read what earlier calls left there). */
+enum {
+  GDLA_STAGE_DOWN = 1,     /* fused down-projection x -> [c_Q | c_KV | k_R | lambda logit] */
+  GDLA_STAGE_PREP = 2,     /* RMSNorms, rotary key, lambda, RoPE table, cache rows */
+  GDLA_STAGE_EXPAND = 4,   /* latent expansion into content keys and values */
+  GDLA_STAGE_QG = 8,       /* query up-projection (RoPE) and sigmoid gate */
+  GDLA_STAGE_ATTN = 16,    /* signal + noise attention, differential, gate -> Z */
+  GDLA_STAGE_OUT = 32,     /* output projection (+ residual) -> y */
+  GDLA_STAGE_ALL = 63
+};
+
+/* gdla_prefill restricted to the stages in the `stages` mask (same arguments,
+ * same checks).  A stage reads the workspace contents earlier stages of a
+ * call with the same cfg, B and L left there; running a stage whose inputs
+ * were never produced computes on undefined data (but stays in bounds). */
+gdla_status gdla_prefill_stages(const gdla_config* cfg, const gdla_weights* w, int32_t B, int32_t L,
+                                int64_t pos_offset, const void* x, void* y, const void* residual,
+                                void* cache, int32_t cache_capacity, void* workspace,
+                                size_t workspace_bytes, void* stream, uint32_t stages);
+
 /* Byte offsets of the intermediates inside the prefill workspace after a call
  * (for inspection and tests).  T = B*L tokens; elements are in the config
  * dtype unless marked fp32.
