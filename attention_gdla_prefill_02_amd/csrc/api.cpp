@@ -328,7 +328,7 @@ gdla_status gdla_latent_expand(const gdla_config* cfg, int64_t T, const void* c_
 }
 
 size_t gdla_decode_workspace_size(const gdla_config* cfg, int32_t B) {
-  if (check_config(cfg) != GDLA_OK || B < 0 || cfg->dtype != GDLA_BF16) return 0;
+  if (check_config(cfg) != GDLA_OK || B < 0 || !gdla::decode_supported(cfg)) return 0;
   return gdla::decode_workspace_bytes(cfg, B);
 }
 
@@ -338,6 +338,8 @@ gdla_status gdla_decode(const gdla_config* cfg, const gdla_weights* w, int32_t B
   gdla_status st = check_config(cfg);
   if (st != GDLA_OK) return st;
   if (cfg->dtype != GDLA_BF16) return fail(GDLA_ERR_UNSUPPORTED, "decode is bf16 only");
+  if (!gdla::decode_supported(cfg))
+    return fail(GDLA_ERR_UNSUPPORTED, "decode needs kv_rank in {128, 256, 512} and at most 80 query heads");
   if (B < 0) return fail(GDLA_ERR_INVALID_ARG, "B must be >= 0");
   if (B == 0) return GDLA_OK;
   if (capacity <= 0) return fail(GDLA_ERR_INVALID_ARG, "capacity must be positive");

@@ -9,6 +9,8 @@
 
 namespace gdla {
 
+// Shapes the decode kernels cover (bf16; kv_rank 128, 256 or 512; at most 80 query heads).
+bool decode_supported(const gdla_config* cfg);
 size_t decode_workspace_bytes(const gdla_config* cfg, int B);
 hipError_t decode_step(const gdla_config* cfg, const gdla_weights* w, int B, const void* x, void* y, void* cache,
                        const int32_t* cache_lens, int capacity, void* workspace, hipStream_t s);

@@ -51,8 +51,9 @@ struct RowPrepArgs {
   void* cqn; void* ckvn; void* kr; float* lam; float* rope;
   bool split_kv;                         // ckvn rows are [hi | lo] (2*kv_rank wide)
   void* cache; int cache_cap;            // nullable
-  const int32_t* pos_dev;                // decode: per-row positions (device), else null
-  int rows_per_seq;                      // decode: 1 (row b is sequence b)
+  const int32_t* pos_dev;                // decode: per-row positions (device), else null;
+                                         // row b is then sequence b at position pos_dev[b]
+  int nsplit; int64_t split_stride;      // down holds nsplit partial sums (elements apart); 0/1 = one
 };
 hipError_t rowprep(const RowPrepArgs& a, bool bf16, hipStream_t s);
 

@@ -21,16 +21,36 @@ namespace {
 template <class T>
 __global__ void __launch_bounds__(256)
 rowprep_kernel(RowPrepArgs a) {
+  extern __shared__ float rp_row[];                 // [4][ld_down] when the input is split
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
   const float* row = a.down + t * a.ld_down;
+  if (a.nsplit > 1) {
+    // sum the split-K partials of this row once
+    float* acc = rp_row + (threadIdx.x >> 6) * a.ld_down;
+    for (int i = lane; i < a.ld_down; i += 64) {
+      float v = 0.f;
+      for (int sp = 0; sp < a.nsplit; ++sp) v += row[sp * a.split_stride + i];
+      acc[i] = v;
+    }
+    // the row is re-read by other lanes of this wave only
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    row = acc;
+  }
   const T* gq = (const T*)a.g_q;
   const T* gkv = (const T*)a.g_kv;
   int64_t seq, p;
+  bool write_cache = a.cache != nullptr;
   if (a.pos_dev) {
     seq = t;
     p = a.pos_dev[t];
+    if (p < 0 || p >= a.cache_cap) {   // outside the cache: nothing is written there
+      write_cache = false;
+      p = p < 0 ? 0 : p;
+    }
   } else {
     seq = t / a.L;
     p = a.pos_offset + (t - seq * a.L);
@@ -51,7 +71,7 @@ rowprep_kernel(RowPrepArgs a) {
   // split rows: [hi | lo] with hi = round(c_KVn), lo = round(c_KVn - hi); the
   // expansion then sees c_KVn to ~16 bits while the cache keeps hi
   T* ckvn = (T*)a.ckvn + t * (a.split_kv ? 2 * a.kv_rank : a.kv_rank);
-  T* crow = a.cache ? (T*)a.cache + (seq * a.cache_cap + p) * (int64_t)(a.kv_rank + a.d_rope) : nullptr;
+  T* crow = write_cache ? (T*)a.cache + (seq * a.cache_cap + p) * (int64_t)(a.kv_rank + a.d_rope) : nullptr;
   for (int i = lane; i < a.kv_rank; i += 64) {
     const float f = ckv[i] * r * to_f32(gkv[i]);
     const T v = from_f32<T>(f);
@@ -115,10 +135,11 @@ latent_norm_kernel(LatentNormArgs a) {
 hipError_t rowprep(const RowPrepArgs& a, bool bf16, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   dim3 grid((unsigned)cdiv(a.T, 4)), block(256);
+  const size_t lds = a.nsplit > 1 ? 4 * (size_t)a.ld_down * sizeof(float) : 0;
   if (bf16)
-    hipLaunchKernelGGL(rowprep_kernel<__bf16>, grid, block, 0, s, a);
+    hipLaunchKernelGGL(rowprep_kernel<__bf16>, grid, block, lds, s, a);
   else
-    hipLaunchKernelGGL(rowprep_kernel<float>, grid, block, 0, s, a);
+    hipLaunchKernelGGL(rowprep_kernel<float>, grid, block, lds, s, a);
   return hipGetLastError();
 }
 
