@@ -151,6 +151,66 @@ def bench_prefill(args, torch, gdla, configs, inputs):
     return res, w, Wc[0], x_cpu
 
 
+def decode_bytes(s: dict, lens, window: int) -> int:
+    """Algorithmic HBM bytes of one decode step: attended cache rows, every
+    weight once, the appended rows, x and y."""
+    RL = s["kv_rank"] + s["d_rope"]
+    rows = sum(min(int(p) + 1, window) if window > 0 else int(p) + 1 for p in lens)
+    nS = s["group"] * s["n_noise"]
+    H = nS + s["n_noise"]
+    dqk = s["d_nope"] + s["d_rope"]
+    params = (s["d_model"] * (s["q_rank"] + s["kv_rank"] + s["d_rope"] + nS) + s["q_rank"] + s["kv_rank"]
+              + s["q_rank"] * (H * dqk + nS * s["d_v"]) + s["kv_rank"] * s["n_noise"] * (s["d_nope"] + s["d_v"])
+              + nS * s["d_v"] * s["d_model"])
+    B = len(lens)
+    return rows * RL * 2 + params * 2 + B * RL * 2 + B * s["d_model"] * 2 * 2
+
+
+def bench_decode(torch, gdla, configs, inputs, reps: int = 20):
+    """Batch-64 decode step against a 32768-row latent cache (contexts
+    U{1024..32768}), full-causal and W = 4096 layers, plus all contexts at
+    32768.  The 256 MB MALL is flushed (512 MB write) before every timed rep."""
+    w = configs.WORKLOADS["decode_b64"]
+    s = w.shapes
+    log(f"[bench] building decode state: {w.note}")
+    cache_c, lens = inputs.make_decode_state(w.B, w.capacity, s["kv_rank"], s["d_rope"], w.ctx_range, w.seed, "bf16")
+    cache = cache_c.to("cuda")
+    del cache_c
+    W = {k: v.to("cuda") for k, v in inputs.make_weights(s, configs.layer_seed(w, 0), "bf16").items()}
+    x = inputs.make_x(w.B, 1, s["d_model"], w.seed, "bf16")[:, 0].contiguous().to("cuda")
+    y = torch.empty_like(x)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    out = {}
+    cases = [("full", 0, lens), ("swa4096", 4096, lens),
+             ("full_ctx32768", 0, torch.full_like(lens, w.capacity - 1))]
+    for name, window, ln in cases:
+        cfg = gdla.make_config(s, window, "bf16")
+        ws = gdla.alloc_workspace(gdla.decode_workspace_size(cfg, w.B))
+        ln_d = ln.to("cuda")
+        for _ in range(3):
+            gdla.decode(cfg, W, x, cache, ln_d, y=y, workspace=ws)
+        times = []
+        for _ in range(reps):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            gdla.decode(cfg, W, x, cache, ln_d, y=y, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 1e3)
+        times.sort()
+        t = times[len(times) // 2]
+        nbytes = decode_bytes(s, ln.tolist(), window)
+        out[name] = {"us_per_step": round(t * 1e6, 1), "min_us": round(times[0] * 1e6, 1),
+                     "tokens_per_s": round(w.B / t, 1), "GB": round(nbytes / 1e9, 4),
+                     "GB_per_s": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] decode {name}: {out[name]}")
+    out["block_tokens_per_s"] = round(w.B / (out["full"]["us_per_step"] + 3 * out["swa4096"]["us_per_step"]) * 1e6, 1)
+    out["batch"] = w.B
+    out["contexts"] = "U{1024..32768} seeded (full, swa4096); all 32768 (full_ctx32768)"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +219,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true", help="time only the decode steps (for profiling)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -175,11 +236,14 @@ def main():
         sys.exit(1)
     gdla.load()
 
+    if args.decode_only:
+        print(json.dumps({"decode": bench_decode(torch, gdla, configs, inputs)}), flush=True)
+        return
     pf, w, Wc0, x_cpu = bench_prefill(args, torch, gdla, configs, inputs)
     log(f"[bench] prefill: {pf['ms_step']:.2f} ms/step, {pf['tflops']:.1f} TFLOP/s, attention "
         f"{pf['attn_tflops']:.1f} TFLOP/s, GEMMs+prep {pf['other_tflops']:.1f} TFLOP/s, stages {pf['kern']}")
 
-    decode = None
+    decode = None if args.no_decode else bench_decode(torch, gdla, configs, inputs)
 
     cpu = None
     if not args.no_cpu_baseline:
