@@ -258,23 +258,27 @@ def attention_heads(q, kc, kr, v, rows, cfg: Cfg):
     scale = 1.0 / math.sqrt(cfg.d_qk)
     out = np.zeros((len(rows), cfg.n_heads, cfg.d_v))
     index = {t: i for i, t in enumerate(rows)}
-    for run in _consecutive_runs(rows, 128):
-        lo_run = attended_keys(run[0], cfg.window)[0]
-        hi_run = run[-1] + 1
-        spos = np.arange(lo_run, hi_run)
-        tpos = np.array(run)
-        lo_t = np.array([attended_keys(t, cfg.window)[0] for t in run])
-        allowed = (spos[None, :] <= tpos[:, None]) & (spos[None, :] >= lo_t[:, None])
-        idx = [index[t] for t in run]
-        for h in range(cfg.n_heads):
-            n = kv_head_of(h, cfg)
-            k = np.concatenate([kc[lo_run:hi_run, n, :], kr[lo_run:hi_run]], axis=-1)
-            s = (q[idx, h, :] @ k.T) * scale                     # [run, S]
-            s = np.where(allowed, s, -np.inf)
-            s = s - s.max(axis=1, keepdims=True)
+    runs = _consecutive_runs(rows, 128)
+    for n in range(cfg.n_noise):
+        heads = [h for h in range(cfg.n_heads) if kv_head_of(h, cfg) == n]
+        k = np.concatenate([kc[:, n, :], kr], axis=-1)                 # [L, d_qk], KV head n
+        for run in runs:
+            lo_run = attended_keys(run[0], cfg.window)[0]
+            hi_run = run[-1] + 1
+            spos = np.arange(lo_run, hi_run)
+            tpos = np.array(run)
+            lo_t = np.array([attended_keys(t, cfg.window)[0] for t in run])
+            allowed = (spos[None, :] <= tpos[:, None]) & (spos[None, :] >= lo_t[:, None])
+            idx = [index[t] for t in run]
+            R_, G_ = len(run), len(heads)
+            qg = q[idx][:, heads, :].reshape(R_ * G_, cfg.d_qk)           # rows (t, head)
+            s = ((qg @ k[lo_run:hi_run].T) * scale).reshape(R_, G_, -1)  # [run, heads, S]
+            s = np.where(allowed[:, None, :], s, -np.inf)
+            s = s - s.max(axis=-1, keepdims=True)
             w = np.exp(s)
-            w /= w.sum(axis=1, keepdims=True)
-            out[idx, h, :] = w @ v[lo_run:hi_run, n, :]
+            w /= w.sum(axis=-1, keepdims=True)
+            o = w.reshape(R_ * G_, -1) @ v[lo_run:hi_run, n, :]
+            out[np.ix_(idx, heads)] = o.reshape(R_, G_, cfg.d_v)
     return out
 
 
