@@ -235,6 +235,7 @@ gdla_status gdla_prefill_stages(const gdla_config* cfg, const gdla_weights* w, i
     v.B = ws + P.ckvn; v.ldb = kk; v.strideB = (int64_t)L * kk;
     v.C = ws + P.vt; v.ldc = P.vt_ld; v.strideC = P.vt_seq;
     v.M = (int)(D.nN * D.dv); v.N = L; v.K = (int)kk; v.batch = B; v.epi = EPI_STORE;
+    v.Npad = (int)P.vt_seq;   // the attention kernel reads whole 64-key tiles: pad with zeros
     if ((err = gemm(v, s)) != hipSuccess) return hip_fail(err, "latent expand (values)");
   }
   // 4. query up-projection with RoPE on the rotary parts, and the sigmoid gate

@@ -51,9 +51,9 @@ namespace gdla {
 namespace {
 
 constexpr int DN = 128, DR = 64, DQK = DN + DR, DV = 128;
-constexpr int BQ = 64, BKV = 64;
+constexpr int BQ = 64, BKV = 32;
 constexpr int K_LD = DQK + 8;        // LDS row of a key (elements), padded
-constexpr int V_LD = BKV + 8;        // LDS row of V^T (one value dim, 64 keys)
+constexpr int V_LD = BKV + 8;        // LDS row of V^T (one value dim, BKV keys)
 constexpr int K_TILE = BKV * K_LD;   // elements
 constexpr int V_TILE = DV * V_LD;
 constexpr int KV_CHUNKS = BKV * (DQK / 8) + DV * (BKV / 8);   // 16-byte chunks per tile
@@ -61,7 +61,7 @@ constexpr float NEG_INIT = -1.0e30f;
 
 __host__ __device__ constexpr int z_ld(int g) { return g * DV + 8; }
 __host__ __device__ constexpr size_t lds_bytes(int g) {
-  const size_t kv = 2 * (size_t)(K_TILE + V_TILE) * 2;
+  const size_t kv = 3 * (size_t)(K_TILE + V_TILE) * 2;
   const size_t ep = (size_t)BQ * (DV + 4) * 4 + (size_t)BQ * z_ld(g) * 2;
   return kv > ep ? kv : ep;
 }
@@ -73,17 +73,47 @@ __device__ __forceinline__ int key_of(int e, int hi) {
   return 16 * (i >> 1) + 8 * hi + 4 * (i & 1) + j;
 }
 
+// max over 16 values with three-input max instructions
+__device__ __forceinline__ float max16(const f32x16& v) {
+  const float a = fmaxf(fmaxf(v[0], v[1]), v[2]), b = fmaxf(fmaxf(v[3], v[4]), v[5]);
+  const float c = fmaxf(fmaxf(v[6], v[7]), v[8]), d = fmaxf(fmaxf(v[9], v[10]), v[11]);
+  const float e = fmaxf(fmaxf(v[12], v[13]), v[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), v[15]));
+}
+
+// value of lane l ^ 32
+__device__ __forceinline__ float xor32(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  // r = {own or partner, partner or own}: the pair is the same set in both halves
+  const unsigned lane = __lane_id();
+  return __builtin_bit_cast(float, lane < 32 ? r[1] : r[0]);
+}
+
+// LDS tiles keep padded rows (keys: 192 + 8 elements = 25 chunks of 16 B;
+// values: 32 + 8 = 5 chunks), which makes the 16-byte fragment reads of 16
+// consecutive rows bank-conflict free with compile-time offsets.  Tiles are
+// filled with global_load_lds: lane i of a wave writes bytes 16i..16i+15 of a
+// 1 KB LDS block, so each lane fetches the global chunk that belongs at its
+// position; lanes on a pad chunk fetch a valid dummy chunk, lanes past the
+// tile end are switched off.
+constexpr int KROW_CH = K_LD / 8;                 // 25 chunks per padded key row
+constexpr int VROW_CH = V_LD / 8;                 // 5 chunks per padded value row
+constexpr int K_CHUNKS = BKV * KROW_CH;           // 800
+constexpr int T_CHUNKS = K_CHUNKS + DV * VROW_CH; // 1440
+constexpr int K_BYTES = K_CHUNKS * 16;            // 12.5 KB
+constexpr int TILE_BYTES = T_CHUNKS * 16;         // 22.5 KB
+constexpr int TILE_KB = (T_CHUNKS + 63) / 64;     // 23 load instructions per tile
+
 template <int G>
 __global__ void __launch_bounds__(128 * (G + 1), 1)
 attn_bf16_kernel(AttnArgs a) {
   constexpr int NW = 2 * (G + 1), NT = 64 * NW;
-  constexpr int CH = (KV_CHUNKS + NT - 1) / NT;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  bf16* sK = reinterpret_cast<bf16*>(smem_raw);          // [2][BKV][K_LD]
-  bf16* sV = sK + 2 * K_TILE;                              // [2][DV][V_LD]
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int hs = w >> 1, half = w & 1;
+  // wave w: query head slot w % (G+1), query half w / (G+1); waves w and w+4 share a SIMD
+  const int hs = w % (G + 1), half = w / (G + 1);
   const int l32 = lane & 31, hi = lane >> 5;
   const int L = a.L, nN = a.nN, nS = G * nN, W = a.window;
 
@@ -125,46 +155,27 @@ attn_bf16_kernel(AttnArgs a) {
   const bf16* kr = (const bf16*)a.kr + tb * DR;
   const bf16* vt = (const bf16*)a.vt + (int64_t)n * DV * a.ld_vt + (int64_t)b * a.vt_seq;
 
-  bf16x8 stg[CH];
-  const bf16x8 zero8 = {};
-  auto gload = [&](int tile) {
+  // issue the loads of one tile into LDS buffer buf (1 KB blocks round-robin over waves)
+  auto load_tile = [&](int tile, int buf) {
     const int kb = tile * BKV;
+    unsigned char* base = smem_raw + buf * TILE_BYTES;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + c * NT;
-      bf16x8 v = zero8;
-      if (idx < BKV * (DQK / 8)) {
-        const int r = idx / (DQK / 8), cc = idx % (DQK / 8);
-        const int key = kb + r;
-        if (key < L)
-          v = cc < DN / 8 ? *reinterpret_cast<const bf16x8*>(kc + (int64_t)key * a.ld_kc + cc * 8)
-                          : *reinterpret_cast<const bf16x8*>(kr + (int64_t)key * DR + (cc - DN / 8) * 8);
-      } else if (idx < KV_CHUNKS) {
-        const int j = idx - BKV * (DQK / 8);
-        const int d = j / (BKV / 8), cc = j % (BKV / 8);
-        const int key = kb + cc * 8;
-        const bf16* src = vt + (int64_t)d * a.ld_vt + key;
-        if (key + 8 <= L) {
-          v = *reinterpret_cast<const bf16x8*>(src);
+    for (int blk = w; blk < TILE_KB; blk += NW) {
+      const int pos = blk * 64 + lane;             // 16-byte chunk position in the tile
+      if (pos < T_CHUNKS) {
+        const void* src;
+        if (pos < K_CHUNKS) {
+          const int r = pos / KROW_CH, c = pos % KROW_CH;   // c == 24: pad chunk
+          const int key = min(kb + r, L - 1);      // rows past L repeat a valid row; masked to -inf
+          src = c < DN / 8 ? (const void*)(kc + (int64_t)key * a.ld_kc + c * 8)
+                           : (const void*)(kr + (int64_t)key * DR + min(c - DN / 8, DR / 8 - 1) * 8);
         } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = key + e < L ? src[e] : (bf16)0.0f;
+          const int pv = pos - K_CHUNKS;
+          const int d = pv / VROW_CH, c = min(pv % VROW_CH, VROW_CH - 2);   // pad chunk -> chunk 3
+          // value columns past L lie in the zero-filled padding of V^T
+          src = vt + (int64_t)d * a.ld_vt + kb + c * 8;
         }
-      }
-      stg[c] = v;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + c * NT;
-      if (idx < BKV * (DQK / 8)) {
-        const int r = idx / (DQK / 8), cc = idx % (DQK / 8);
-        *reinterpret_cast<bf16x8*>(sK + buf * K_TILE + r * K_LD + cc * 8) = stg[c];
-      } else if (idx < KV_CHUNKS) {
-        const int j = idx - BKV * (DQK / 8);
-        const int d = j / (BKV / 8), cc = j % (BKV / 8);
-        *reinterpret_cast<bf16x8*>(sV + buf * V_TILE + d * V_LD + cc * 8) = stg[c];
+        g2lds16(src, base + blk * 1024);
       }
     }
   };
@@ -174,78 +185,115 @@ attn_bf16_kernel(AttnArgs a) {
   for (int d = 0; d < DV / 32; ++d) o[d] = f32x16{};
   float m = NEG_INIT, lsum = 0.f;
 
-  // key-row order of the A operand: bits 2 and 3 of the lane's row swapped
+  // A-operand key row of this lane: bits 2 and 3 of l32 swapped (P then lands in
+  // the P V operand layout directly)
   const int arow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
 
-  gload(t_lo);
-  sstore(0);
-  __syncthreads();
-  for (int tile = t_lo; tile < t_hi; ++tile) {
-    const int buf = (tile - t_lo) & 1;
-    if (tile + 1 < t_hi) gload(tile + 1);
-    const int kb = tile * BKV;
-    const bool visible = kb <= qlast && (W <= 0 || kb + BKV - 1 > qw0 - W);
-    if (visible) {
-      const bool full = kb + BKV - 1 <= qw0 && kb + BKV <= L && (W <= 0 || kb > qlast - W);
-      const bf16* Kt = sK + buf * K_TILE + arow * K_LD + hi * 8;
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
+  // S^T tile of 32 keys: key kb + key_of(e, hi) in element e, column = this lane's query
+  auto qk = [&](int buf, f32x16& s) {
+    const bf16* K = reinterpret_cast<const bf16*>(smem_raw + buf * TILE_BYTES) + arow * K_LD + hi * 8;
+    s = f32x16{};
 #pragma unroll
-      for (int s = 0; s < DQK / 16; ++s) {
-        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Kt + 16 * s);
-        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Kt + 32 * K_LD + 16 * s);
-        s0 = mfma32(k0, qf[s], s0);
-        s1 = mfma32(k1, qf[s], s1);
-      }
-      if (!full) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int k0 = kb + key_of(e, hi), k1 = k0 + 32;
-          const bool v0 = k0 <= qme && k0 < L && (W <= 0 || k0 > qme - W);
-          const bool v1 = k1 <= qme && k1 < L && (W <= 0 || k1 > qme - W);
-          s0[e] = v0 ? s0[e] : -INFINITY;
-          s1[e] = v1 ? s1[e] : -INFINITY;
-        }
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, fmaxf(s0[e], s1[e]));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sc;
-      const bool raise = mt > m + 8.0f;
-      if (__any(raise)) {
-        const float mn = raise ? mt : m;
-        const float alpha = fast_exp2(m - mn);
-        m = mn;
-        lsum *= alpha;
-#pragma unroll
-        for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
-      }
-      bf16x8 p[2][2];
+    for (int st = 0; st < DQK / 16; ++st) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(K + 16 * st);
+      s = mfma32(kf, qf[st], s);
+    }
+  };
+  // softmax, first half: masks on boundary tiles, tile max, lazy rescale of O
+  // (branches; rare after the first tiles)
+  auto softmax_max = [&](f32x16& s, int kb) {
+    const bool full = kb + BKV - 1 <= qw0 && kb + BKV <= L && (W <= 0 || kb > qlast - W);
+    if (!full) {
+      const int lo_ok = W > 0 ? qme - W + 1 : 0;   // keys in [lo_ok, min(qme, L-1)] are visible
+      const unsigned span = (unsigned)(min(qme, L - 1) - lo_ok);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p0 = fast_exp2(fmaf(s0[e], sc, -m));
-        const float p1 = fast_exp2(fmaf(s1[e], sc, -m));
-        lsum += p0 + p1;
-        p[0][e >> 3][e & 7] = (bf16)p0;
-        p[1][e >> 3][e & 7] = (bf16)p1;
+        const int key = kb + key_of(e, hi);
+        s[e] = (unsigned)(key - lo_ok) <= span ? s[e] : -INFINITY;
       }
-      const bf16* Vt = sV + buf * V_TILE + l32 * V_LD + hi * 8;
-#pragma unroll
-      for (int d = 0; d < DV / 32; ++d)
-#pragma unroll
-        for (int ts = 0; ts < 2; ++ts)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + d * 32 * V_LD + 32 * ts + 16 * u);
-            o[d] = mfma32(vf, p[ts][u], o[d]);
-          }
     }
-    if (tile + 1 < t_hi) sstore(buf ^ 1);
+    float mt = max16(s);
+    mt = fmaxf(mt, xor32(mt)) * sc;
+    const bool raise = mt > m + 8.0f;
+    if (__any(raise)) {
+      const float mn = raise ? mt : m;
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
+    }
+  };
+  // softmax, second half: P = exp2(s*sc - m) in bf16 and the running sum (no branches)
+  auto softmax_exp = [&](const f32x16& s, bf16x8 (&p)[2]) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pe = fast_exp2(fmaf(s[e], sc, -m));
+      acc += pe;
+      p[e >> 3][e & 7] = (bf16)pe;
+    }
+    lsum += acc;
+  };
+  auto pv = [&](int buf, const bf16x8 (&p)[2]) {
+    const bf16* V = reinterpret_cast<const bf16*>(smem_raw + buf * TILE_BYTES + K_BYTES) + l32 * V_LD + hi * 8;
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(V + 32 * d * V_LD + 16 * u);
+        o[d] = mfma32(vf, p[u], o[d]);
+      }
+  };
+
+  // Pipeline over tiles, LDS buffer of tile t = t % 3, one barrier per tile.
+  // Step t issues the loads of tile t+2 (direct to LDS; buffer (t+2) % 3 last
+  // held tile t-1) and computes Q K^T of tile t+1, the softmax of tile t and
+  // P V of tile t.  Tile t+1 was loaded during step t-1 and published by that
+  // step's closing wait + barrier.  The two waves that share a SIMD (query
+  // halves 0 and 1 of one head) order the step differently -- half 0 starts
+  // with the Q K^T MFMAs, half 1 with the softmax on the vector ALU -- so the
+  // matrix cores and the vector ALU of the SIMD work at the same time.  Tiles
+  // a wave cannot see are still computed: their masked scores give P = 0.
+  const bool lead = half == 0;
+  f32x16 sA, sB;
+  bf16x8 p[2];
+  load_tile(t_lo, t_lo % 3);
+  if (t_lo + 1 < t_hi) load_tile(t_lo + 1, (t_lo + 1) % 3);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  qk(t_lo % 3, sA);
+  auto step = [&](int tile, f32x16& cur, f32x16& nxt, bool has_next) {
+    const int kb = tile * BKV;
+    if (tile + 2 < t_hi) load_tile(tile + 2, (tile + 2) % 3);
+    if (lead) {
+      if (has_next) qk((tile + 1) % 3, nxt);
+      softmax_max(cur, kb);
+      softmax_exp(cur, p);
+      pv(tile % 3, p);
+    } else {
+      softmax_max(cur, kb);
+      softmax_exp(cur, p);
+      pv(tile % 3, p);
+      if (has_next) qk((tile + 1) % 3, nxt);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  int tile = t_lo;
+  for (; tile + 2 < t_hi; tile += 2) {
+    step(tile, sA, sB, true);
+    step(tile + 1, sB, sA, true);
+  }
+  if (tile + 1 < t_hi) {
+    step(tile, sA, sB, true);
+    step(tile + 1, sB, sA, false);
+  } else {
+    step(tile, sA, sB, false);
   }
 
   // ---- epilogue: H = O / l, Z = gate * (H_S - lambda * H_N)
-  const float l_tot = lsum + __shfl_xor(lsum, 32, 64);
-  const float inv = 1.0f / l_tot;
+  const float inv = 1.0f / (lsum + xor32(lsum));
   float* sH = reinterpret_cast<float*>(smem_raw);                          // [BQ][DV + 4]
   bf16* sZ = reinterpret_cast<bf16*>(smem_raw + (size_t)BQ * (DV + 4) * 4);  // [BQ][g*DV + 8]
   const int qrow = 32 * half + l32;
@@ -254,7 +302,7 @@ attn_bf16_kernel(AttnArgs a) {
     for (int d = 0; d < DV / 32; ++d)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        f32x4 h4 = {o[d][4 * i] * inv, o[d][4 * i + 1] * inv, o[d][4 * i + 2] * inv, o[d][4 * i + 3] * inv};
+        const f32x4 h4 = {o[d][4 * i] * inv, o[d][4 * i + 1] * inv, o[d][4 * i + 2] * inv, o[d][4 * i + 3] * inv};
         *reinterpret_cast<f32x4*>(sH + qrow * (DV + 4) + d * 32 + 8 * i + 4 * hi) = h4;
       }
   }

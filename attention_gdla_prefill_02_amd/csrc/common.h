@@ -27,6 +27,13 @@ GDLA_DEV f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16 bytes global -> LDS without registers: lane i of the wave writes LDS bytes
+// [lds + 16 i, lds + 16 i + 16) (lds must be wave-uniform).  Completion is
+// tracked by vmcnt.
+__device__ __forceinline__ void g2lds16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
 GDLA_DEV float to_f32(bf16 v) { return (float)v; }
 GDLA_DEV float to_f32(float v) { return v; }
 template <class T> GDLA_DEV T from_f32(float v);

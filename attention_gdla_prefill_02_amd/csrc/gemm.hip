@@ -25,43 +25,76 @@ struct EpiMfma {
   OT* C; int64_t ldc; const OT* R; int64_t ldr; int M, N; int kind;
   const float* rope; int q_cols, d_qk, d_nope, d_rope;
   float* G; int64_t ldg;
+  int Npad;   // columns [N, Npad) are stored as zeros
+  bool vecC, vecG;   // row strides allow 4-element vector stores
 
-  // v0 belongs to (row, col), v1 to (row, col + 32); col0 is the first column
-  // of the 64-wide window that holds both.
-  GDLA_DEV void pair(int row, int col, int col0, float v0, float v1) const {
+  // v0[e] belongs to (row, n + e) and v1[e] to (row, n + 32 + e), e = 0..3; n0 is
+  // the first column of the 64-wide window holding both quads (n is 4-aligned).
+  GDLA_DEV void quads(int row, int n, int n0, f32x4 v0, f32x4 v1) const {
     if (row >= M) return;
     if (kind == EPI_QG) {
-      if (col0 < q_cols) {
-        if ((col0 % d_qk) == d_nope) {
-          const float2 cs = reinterpret_cast<const float2*>(rope)[(int64_t)row * (d_rope / 2) + (col - col0)];
-          const float a = v0 * cs.x - v1 * cs.y;
-          const float b = v1 * cs.x + v0 * cs.y;
-          v0 = a;
-          v1 = b;
+      if (n0 < q_cols) {
+        if ((n0 % d_qk) == d_nope) {
+          const float* cs = rope + ((int64_t)row * (d_rope / 2) + (n - n0)) * 2;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float c = cs[2 * e], sn = cs[2 * e + 1];
+            const float x1 = v0[e], x2 = v1[e];
+            v0[e] = x1 * c - x2 * sn;
+            v1[e] = x2 * c + x1 * sn;
+          }
         }
       } else {
         float* g = G + (int64_t)row * ldg - q_cols;
-        if (col < N) g[col] = sigmoidf_(v0);
-        if (col + 32 < N) g[col + 32] = sigmoidf_(v1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v0[e] = sigmoidf_(v0[e]);
+          v1[e] = sigmoidf_(v1[e]);
+        }
+        store4(g, n, v0, N, vecG);
+        store4(g, n + 32, v1, N, vecG);
         return;
       }
     }
     OT* c = C + (int64_t)row * ldc;
     if (R) {
       const OT* r = R + (int64_t)row * ldr;
-      if (col < N) v0 += to_f32(r[col]);
-      if (col + 32 < N) v1 += to_f32(r[col + 32]);
+      add4(r, n, v0);
+      add4(r, n + 32, v1);
     }
-    if (col < N) c[col] = from_f32<OT>(v0);
-    if (col + 32 < N) c[col + 32] = from_f32<OT>(v1);
+    store4(c, n, v0, Npad, vecC);
+    store4(c, n + 32, v1, Npad, vecC);
+  }
+  template <class T>
+  GDLA_DEV void store4(T* p, int n, f32x4 v, int lim, bool vec) const {
+    if (vec && n + 3 < N) {
+      if constexpr (sizeof(T) == 2) {
+        bf16x4 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+        *reinterpret_cast<bf16x4*>(p + n) = b;
+      } else {
+        *reinterpret_cast<f32x4*>(p + n) = v;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < lim) p[n + e] = from_f32<T>(n + e < N ? v[e] : 0.f);
+    }
+  }
+  GDLA_DEV void add4(const OT* r, int n, f32x4& v) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < N) v[e] += to_f32(r[n + e]);
   }
 };
 
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64, PAD = 8, LDR = BK + PAD, NT = 512;
-constexpr int CPR = BK / 8;                 // 16-byte chunks per tile row
-constexpr int LD_PER_THREAD = BM * CPR / NT;  // chunks of A (and of B) per thread
+constexpr int ROW_CH = LDR / 8;                   // 9 chunks of 16 B per padded row (1 pad)
+constexpr int OP_CH = BM * ROW_CH;                // 2304 chunks per operand tile
+constexpr int OP_KB = OP_CH / 64;                 // 36 one-KB blocks per operand tile
+constexpr int STAGE_BYTES = 2 * OP_CH * 16;       // A and B tiles of one K step (72 KB)
+static_assert(OP_CH % 64 == 0, "operand tiles must be whole 1 KB blocks");
 
 // blockIdx.x -> (tile_m, tile_n): XCD-contiguous bands, then groups of 8 tile
 // rows walked column by column so concurrent tiles share A rows and B columns.
@@ -76,13 +109,19 @@ __device__ __forceinline__ void tile_of(int id, int nt, int tiles_m, int tiles_n
   *bn = r / gm;
 }
 
+// C = A B^T.  The weight tile feeds the MFMA A operand and the activation tile
+// the B operand, so each lane's accumulator holds 4 consecutive output
+// columns of one row (vector stores) and columns n and n+32 of a 64-wide
+// window sit in the same lane (the RoPE pairs).  Tiles move global -> LDS with
+// global_load_lds (no staging registers), double buffered: the loads of step
+// k+1 are in flight while step k's 32 MFMAs per wave run.
 template <class OT>
 __global__ void __launch_bounds__(NT, 1)
 gemm_bf16_kernel(const bf16* __restrict__ A, int64_t lda, int64_t sA,
                  const bf16* __restrict__ B, int64_t ldb, int64_t sB,
                  const bf16* __restrict__ B2, int nb2, const bf16* __restrict__ B3, int nb3,
                  int M, int N, int K, int kwA, int kwB, int64_t sC, int64_t sR, EpiMfma<OT> epi) {
-  __shared__ __attribute__((aligned(16))) bf16 sm[2][(BM + BN) * LDR];
+  extern __shared__ __attribute__((aligned(1024))) unsigned char gsm[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -96,80 +135,84 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int64_t lda, int64_t sA,
   epi.C += bz * sC;
   if (epi.R) epi.R += bz * sR;
 
-  bf16x8 ra[LD_PER_THREAD], rb[LD_PER_THREAD];
-  const bf16x8 zero8 = {};
-  // B row pointer of each row this thread loads (segments resolved once)
-  const bf16* brow[LD_PER_THREAD];
+  // Each wave loads 1 KB blocks wave + 8i (i < 9) of the stage: blocks 0..35
+  // are the activation tile, 36..71 the weight tile.  The per-lane source of
+  // each block is fixed for the whole tile except for the K offset, so it is
+  // computed once (rows past M / N are clamped to a valid row: their results
+  // are never stored; the pad chunk of each row re-reads chunk 7).
+  constexpr int NLB = 2 * OP_KB / (NT / 64);   // 9 blocks per wave per stage
+  static_assert(2 * OP_KB % (NT / 64) == 0, "blocks must divide evenly over waves");
+  const bf16* lsrc[NLB];
 #pragma unroll
-  for (int c = 0; c < LD_PER_THREAD; ++c) {
-    const int gn = n0 + (tid + c * NT) / CPR;
-    brow[c] = gn >= nb3 ? B3 + (int64_t)(gn - nb3) * ldb
-            : gn >= nb2 ? B2 + (int64_t)(gn - nb2) * ldb
-                        : B + (int64_t)gn * ldb;
+  for (int i = 0; i < NLB; ++i) {
+    const int blk = wave + (NT / 64) * i;
+    const bool isB = blk >= OP_KB;
+    const int pos = (isB ? blk - OP_KB : blk) * 64 + lane;
+    const int r = pos / ROW_CH, c = min(pos % ROW_CH, ROW_CH - 2);
+    if (!isB) {
+      lsrc[i] = A + (int64_t)min(m0 + r, M - 1) * lda + c * 8;
+    } else {
+      const int gn = min(n0 + r, N - 1);
+      const bf16* row = gn >= nb3 ? B3 + (int64_t)(gn - nb3) * ldb
+                      : gn >= nb2 ? B2 + (int64_t)(gn - nb2) * ldb
+                                  : B + (int64_t)gn * ldb;
+      lsrc[i] = row + c * 8;
+    }
   }
-
-  auto gload = [&](int k0) {
+  auto load_stage = [&](int k0, int buf) {
+    unsigned char* base = gsm + buf * STAGE_BYTES;
     const int ka = kwA ? k0 % kwA : k0, kb = kwB ? k0 % kwB : k0;
 #pragma unroll
-    for (int c = 0; c < LD_PER_THREAD; ++c) {
-      const int idx = tid + c * NT, r = idx / CPR, cc = idx % CPR;
-      const int gm = m0 + r, gn = n0 + r;
-      ra[c] = gm < M ? *reinterpret_cast<const bf16x8*>(A + (int64_t)gm * lda + ka + cc * 8) : zero8;
-      rb[c] = gn < N ? *reinterpret_cast<const bf16x8*>(brow[c] + kb + cc * 8) : zero8;
-    }
-  };
-  auto sstore = [&](int buf) {
-    bf16* As = sm[buf];
-    bf16* Bs = sm[buf] + BM * LDR;
-#pragma unroll
-    for (int c = 0; c < LD_PER_THREAD; ++c) {
-      const int idx = tid + c * NT, r = idx / CPR, cc = idx % CPR;
-      *reinterpret_cast<bf16x8*>(As + r * LDR + cc * 8) = ra[c];
-      *reinterpret_cast<bf16x8*>(Bs + r * LDR + cc * 8) = rb[c];
+    for (int i = 0; i < NLB; ++i) {
+      const int blk = wave + (NT / 64) * i;
+      g2lds16(lsrc[i] + (blk >= OP_KB ? kb : ka), base + blk * 1024);
     }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[2][4];   // [n sub-tile][m sub-tile]
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
   const int KT = K / BK;
-  gload(0);
-  sstore(0);
+  load_stage(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const bf16* As = sm[cur] + (wm * 128 + l32) * LDR + hi * 8;
-    const bf16* Bs = sm[cur] + BM * LDR + (wn * 64 + l32) * LDR + hi * 8;
+    if (kt + 1 < KT) load_stage((kt + 1) * BK, cur ^ 1);
+    const bf16* As = reinterpret_cast<const bf16*>(gsm + cur * STAGE_BYTES) + (wm * 128 + l32) * LDR + hi * 8;
+    const bf16* Bs = reinterpret_cast<const bf16*>(gsm + cur * STAGE_BYTES + OP_CH * 16) + (wn * 64 + l32) * LDR + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[4], bfr[2];
+      bf16x8 wf[2], af[4];
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn) wf[tn] = *reinterpret_cast<const bf16x8*>(Bs + tn * 32 * LDR + ks * 16);
 #pragma unroll
       for (int tm = 0; tm < 4; ++tm) af[tm] = *reinterpret_cast<const bf16x8*>(As + tm * 32 * LDR + ks * 16);
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn) bfr[tn] = *reinterpret_cast<const bf16x8*>(Bs + tn * 32 * LDR + ks * 16);
+      for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
-      for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 2; ++tn) acc[tm][tn] = mfma32(af[tm], bfr[tn], acc[tm][tn]);
+        for (int tm = 0; tm < 4; ++tm) acc[tn][tm] = mfma32(wf[tn], af[tm], acc[tn][tm]);
     }
-    if (kt + 1 < KT) sstore(cur ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
-  const int col0 = n0 + wn * 64;
+  // D[n][m]: lane holds column m = 32*tm + l32, rows n = 32*tn + 8i + 4hi + j
+  const int nw0 = n0 + wn * 64;
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm)
+  for (int tm = 0; tm < 4; ++tm) {
+    const int row = m0 + wm * 128 + tm * 32 + l32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = m0 + wm * 128 + tm * 32 + 8 * i + 4 * hi + j;
-        epi.pair(row, col0 + l32, col0, acc[tm][0][4 * i + j], acc[tm][1][4 * i + j]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int n = nw0 + 8 * i + 4 * hi;
+      const f32x4 v0 = {acc[0][tm][4 * i], acc[0][tm][4 * i + 1], acc[0][tm][4 * i + 2], acc[0][tm][4 * i + 3]};
+      const f32x4 v1 = {acc[1][tm][4 * i], acc[1][tm][4 * i + 1], acc[1][tm][4 * i + 2], acc[1][tm][4 * i + 3]};
+      epi.quads(row, n, nw0, v0, v1);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -237,23 +280,37 @@ __global__ void qg_finish_f32(float* q, int64_t ldq, float* g, int64_t ldg, int6
   for (int c = threadIdx.x; c < gate_cols; c += blockDim.x) g[t * ldg + c] = sigmoidf_(g[t * ldg + c]);
 }
 
+template <class OT>
+hipError_t set_gemm_lds() {
+  static bool done = false;
+  if (done) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<OT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     2 * STAGE_BYTES);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
 }  // namespace
 
 hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;
   const int nb2 = a.B2 ? a.nb2 : a.N, nb3 = a.B3 ? a.nb3 : a.N;
+  hipError_t err = a.epi == EPI_F32 ? set_gemm_lds<float>() : set_gemm_lds<bf16>();
+  if (err != hipSuccess) return err;
   const int tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
   dim3 grid(tiles, a.batch), block(NT);
   if (a.epi == EPI_F32) {
     EpiMfma<float> e{(float*)a.C, a.ldc, (const float*)a.R, a.ldr, a.M, a.N, a.epi, a.rope, a.q_cols, a.d_qk,
-                     a.d_nope, a.d_rope, a.G, a.ldg};
-    hipLaunchKernelGGL(gemm_bf16_kernel<float>, grid, block, 0, s, (const bf16*)a.A, a.lda, a.strideA,
+                     a.d_nope, a.d_rope, a.G, a.ldg, a.Npad > a.N ? a.Npad : a.N, a.ldc % 4 == 0,
+                     a.ldg % 4 == 0};
+    hipLaunchKernelGGL(gemm_bf16_kernel<float>, grid, block, 2 * STAGE_BYTES, s, (const bf16*)a.A, a.lda, a.strideA,
                        (const bf16*)a.B, a.ldb, a.strideB, (const bf16*)a.B2, nb2, (const bf16*)a.B3, nb3,
                        a.M, a.N, a.K, a.kwrapA, a.kwrapB, a.strideC, a.strideC, e);
   } else {
     EpiMfma<bf16> e{(bf16*)a.C, a.ldc, (const bf16*)a.R, a.ldr, a.M, a.N, a.epi, a.rope, a.q_cols, a.d_qk,
-                    a.d_nope, a.d_rope, a.G, a.ldg};
-    hipLaunchKernelGGL(gemm_bf16_kernel<bf16>, grid, block, 0, s, (const bf16*)a.A, a.lda, a.strideA,
+                    a.d_nope, a.d_rope, a.G, a.ldg, a.Npad > a.N ? a.Npad : a.N, a.ldc % 4 == 0,
+                    a.ldg % 4 == 0};
+    hipLaunchKernelGGL(gemm_bf16_kernel<bf16>, grid, block, 2 * STAGE_BYTES, s, (const bf16*)a.A, a.lda, a.strideA,
                        (const bf16*)a.B, a.ldb, a.strideB, (const bf16*)a.B2, nb2, (const bf16*)a.B3, nb3,
                        a.M, a.N, a.K, a.kwrapA, a.kwrapB, a.strideC, a.strideC, e);
   }

@@ -26,6 +26,7 @@ struct GemmArgs {
   // [hi | lo] split of one operand (K = 2 * kwrap) meet the other unsplit
   int kwrapA, kwrapB;
   int M, N, K, batch;
+  int Npad;               // EPI_STORE: columns [N, Npad) are written as zeros (0 = none)
   int epi;
   // EPI_QG
   const float* rope;      // [rows][d_rope/2] (cos, sin) pairs
