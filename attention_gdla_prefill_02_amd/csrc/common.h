@@ -34,6 +34,22 @@ __device__ __forceinline__ void g2lds16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// The same copy issued from inline assembly: the compiler does not know that it
+// writes LDS, so it adds no waits for it before later LDS reads.  The caller
+// orders it with explicit s_waitcnt vmcnt counts and barriers.  `lds` must be
+// wave-uniform (it goes to M0); the instruction has no register results.
+__device__ __forceinline__ void g2lds16_explicit(const void* src, void* lds) {
+  const unsigned m0v = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(__attribute__((address_space(3))) char*)lds);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(m0v)
+      : "memory", "m0");
+}
+
 GDLA_DEV float to_f32(bf16 v) { return (float)v; }
 GDLA_DEV float to_f32(float v) { return v; }
 template <class T> GDLA_DEV T from_f32(float v);

@@ -13,23 +13,23 @@
 // running the prefill equations for the one query.
 //
 // Kernels, in launch order:
-//   skinny_gemm   x [B, d] -> fused down-projection partials (weight-streaming,
-//                 MFMA; each lane reads 64 contiguous bytes of a weight row
-//                 per 64-wide K block: element e of MFMA k-step s of lane half
-//                 hi is column 32*hi + 8*s + e for both operands)
+//   skinny_gemm   x [B, d] -> fused down-projection partials, split over K
+//                 (weights streamed from HBM into registers, activations
+//                 shared through LDS, MFMA)
 //   rowprep       norms, RoPE at position cache_lens[b], lambda; appends the
-//                 new row [c_KVn | RoPE(k_R)] to the cache
+//                 new row [c_KVn | RoPE(k_R)] to the cache (one block per row)
 //   skinny_gemm   c_Qn -> q (RoPE) and gate (sigmoid, fp32)
 //   absorb        q~ for every head (W_UK read transposed from LDS with the
 //                 gfx950 transpose read), packed with q^R into 576-wide rows
-//   plan          per-sequence attended range and a chunk size chosen from the
-//                 actual contexts so ~512 chunks cover all sequences
-//   dec_attn      one workgroup per (sequence, chunk), all heads: cache tile of
-//                 32 rows in LDS (double buffered); scores on the 16x16x32
-//                 MFMA with the cache rows as A operand; P V with the same LDS
-//                 tile read transposed (ds_read_b64_tr_b16) as A operand;
-//                 online softmax per head; writes (m, l, O) per chunk
-//   combine       merges the chunks of each sequence (log-sum-exp weights),
+//   plan          per-sequence attended range; the 32-row tiles of all
+//                 sequences are split evenly over up to 512 workgroups
+//   dec_attn      one workgroup per tile range, all heads: cache tiles go
+//                 HBM -> LDS directly (double buffered); scores on the
+//                 16x16x32 MFMA with the cache rows as A operand; P V with the
+//                 same LDS tile read transposed (ds_read_b64_tr_b16) as A
+//                 operand; online softmax per head; writes (m, l, O) per
+//                 segment (the part of one sequence that one workgroup covers)
+//   combine       merges the segments of each sequence (log-sum-exp weights),
 //                 forms D_lat = O_S - lambda * O_N and splits it into bf16 hi/lo
 //   skinny_gemm   W_UV per KV head over [hi | lo], times the gate -> Z
 //   skinny_gemm   Z W_O^T split over K, then wo_reduce -> y (bf16)
@@ -43,7 +43,7 @@ namespace gdla {
 namespace {
 
 constexpr int DN = 128, DR = 64, DQK = DN + DR, DV = 128;
-constexpr int MAX_SPLIT = 8, CHUNK_TARGET = 512;
+constexpr int MAX_SPLIT = 8;
 
 // largest split count in {8, 4, 2, 1} that cuts K into whole 64-wide blocks
 int ksplit(int K) {
@@ -64,13 +64,50 @@ __device__ __forceinline__ bf16x8 tr_pair(const bf16* p0, const bf16* p1) {
 }
 
 // ------------------------------------------------------------ skinny GEMM
+// C[m][n] = sum_k A[m][k] W[n][k] for a few tokens m (the decode batch) and
+// many weight rows n: bound by streaming W once from HBM, so what matters is
+// the number of bytes in flight.
+// Workgroup tile: 64 weight rows (wave w owns rows 16w .. 16w + 15) x 64 tokens,
+// K in stages of SK_KC columns, four stages in LDS: three are in flight while
+// one is multiplied.  Both operands go global -> LDS (the compiler does not
+// track these loads, so its own waits never drain the pipeline; the waits here
+// are explicit counts).  LDS tiles are [64 rows][SK_KC columns] in 16-byte
+// slots, chunk c of row r in slot SK_CH r + (c ^ (r & 7)); the MFMA k index is
+// permuted so that element e of k-step s of lane group q4 is column
+// (SK_KC / 4) q4 + 8 s + e for both operands, which makes every fragment read
+// conflict-free.  64 KB of LDS: two workgroups per CU.
 enum SkinnyMode { SK_PARTIAL = 0, SK_QG = 1, SK_ZGATE = 2 };
+constexpr int SK_KC = 64, SK_NSTG = 4;
+constexpr int SK_CH = SK_KC / 8;          // 16-byte chunks per tile row
+constexpr int SK_RPB = 64 / SK_CH;        // tile rows per 1 KB block
+constexpr int SK_BPW = SK_CH / 4;         // blocks per wave per operand (16 rows)
+constexpr int SK_KS = SK_KC / 32;         // MFMA k-steps per stage
+constexpr int SK_VM_PER_STAGE = 2 * SK_BPW;   // global-to-LDS loads per wave per stage
+
+// s_waitcnt vmcnt(N) through the builtin, so that the compiler's own wait
+// tracking sees it (expcnt and lgkmcnt fields left at "no wait")
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier without the release fence of __syncthreads (which waits for
+// every outstanding load and would drain the pipeline).  Used where each wave
+// has already waited for its own global-to-LDS loads of the stage to be read,
+// and where all LDS reads of a stage about to be overwritten were consumed by
+// instructions issued before the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 struct SkinnyArgs {
   const bf16* A; int64_t lda; int64_t sA;      // activations [M, K] (per-batch stride sA)
   const bf16* B; int64_t ldb; int64_t sB;      // weights [N, K]
   const bf16* B2; int nb2;                     // rows >= nb2 come from B2 (its own row 0)
-  int M, N, K, kwrapB, kper;                   // kper: K range per split (SK_PARTIAL)
+  const bf16* B3; int nb3;                     // rows >= nb3 (> nb2) come from B3
+  int M, N, K, kwrapB, kper;                   // kper: K range per split (SK_PARTIAL); kwrapB % SK_KC == 0
   int mode;
   float* Cf; int64_t ldcf; int64_t sCf;        // SK_PARTIAL: fp32 partial [z][M][N]
   // SK_QG
@@ -81,9 +118,13 @@ struct SkinnyArgs {
 
 __global__ void __launch_bounds__(256, 2)
 skinny_gemm_kernel(SkinnyArgs a) {
-  __shared__ float red[4][64][65];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 31, hi = lane >> 5;
+  // one LDS object per stage and operand: distinct objects let the compiler see
+  // that reads of one stage do not depend on the loads still in flight to others
+  __shared__ __attribute__((aligned(1024))) bf16 w_0[64 * SK_KC], w_1[64 * SK_KC], w_2[64 * SK_KC], w_3[64 * SK_KC];
+  __shared__ __attribute__((aligned(1024))) bf16 x_0[64 * SK_KC], x_1[64 * SK_KC], x_2[64 * SK_KC], x_3[64 * SK_KC];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, q4 = lane >> 4;
   const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64, z = blockIdx.z;
   const bf16* A = a.A;
   const bf16* B = a.B;
@@ -95,54 +136,113 @@ skinny_gemm_kernel(SkinnyArgs a) {
     A += z * a.sA;
     B += z * a.sB;
   }
-  const bf16* wrow[2];
-  const bf16* xrow[2];
-  bool wok[2], xok[2];
+  // LDS block SK_BPW wave + i (1 KB) of a stage holds tile rows
+  // SK_RPB (SK_BPW wave + i) + lane / SK_CH: the weight rows a wave loads are
+  // the ones it multiplies
+  const int lr = lane / SK_CH, lc = lane % SK_CH;
+  const bf16* wsrc[SK_BPW];
+  const bf16* xsrc[SK_BPW];
+  int sw[SK_BPW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int n = n0 + 32 * t + r;
-    wok[t] = n < a.N;
-    const int nn = wok[t] ? n : 0;
-    wrow[t] = (a.B2 && nn >= a.nb2) ? a.B2 + (int64_t)(nn - a.nb2) * a.ldb : B + (int64_t)nn * a.ldb;
-    const int m = m0 + 32 * t + r;
-    xok[t] = m < a.M;
-    xrow[t] = A + (int64_t)(xok[t] ? m : 0) * a.lda;
+  for (int i = 0; i < SK_BPW; ++i) {
+    const int row = SK_RPB * (SK_BPW * wave + i) + lr;
+    sw[i] = 8 * (lc ^ (row & 7));                      // source column of this lane's slot
+    const int nn = min(n0 + row, a.N - 1);             // rows past N repeat row N - 1 (results dropped)
+    wsrc[i] = (a.B3 && nn >= a.nb3) ? a.B3 + (int64_t)(nn - a.nb3) * a.ldb
+              : (a.B2 && nn >= a.nb2) ? a.B2 + (int64_t)(nn - a.nb2) * a.ldb
+                                      : B + (int64_t)nn * a.ldb;
+    xsrc[i] = A + (int64_t)min(m0 + row, a.M - 1) * a.lda;
   }
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  const bf16x8 zero8 = {};
-  for (int kb = kbeg + 64 * wave; kb < kend; kb += 256) {
+  // issue the loads of stage c; columns past the range read in-range data (the
+  // weights there are zeroed at use), so that every wave issues exactly
+  // SK_VM_PER_STAGE loads per stage
+  auto issue = [&](int c, bf16* wd, bf16* xd) {
+    const int kb = kbeg + c * SK_KC;
     const int kw = a.kwrapB ? kb % a.kwrapB : kb;
-    bf16x8 wf[2][4], xf[2][4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int i = 0; i < SK_BPW; ++i) {
+      const int off = kb + sw[i] < kend ? sw[i] : 0;
+      g2lds16_explicit(wsrc[i] + kw + off, wd + (SK_BPW * wave + i) * 512);
+      g2lds16_explicit(xsrc[i] + kb + off, xd + (SK_BPW * wave + i) * 512);
+    }
+  };
+  f32x4 acc[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        wf[t][s] = wok[t] ? *reinterpret_cast<const bf16x8*>(wrow[t] + kw + 32 * hi + 8 * s) : zero8;
-        xf[t][s] = xok[t] ? *reinterpret_cast<const bf16x8*>(xrow[t] + kb + 32 * hi + 8 * s) : zero8;
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4{};
+  const bf16x8 zero8 = {};
+  auto mma = [&](int c, const bf16* wt, const bf16* xt) {
+    const int kb = kbeg + c * SK_KC;
+    const bf16* wb = wt + (16 * wave + r16) * SK_KC;
+    const bf16* xb = xt + r16 * SK_KC;
+    bf16x8 wf[SK_KS];
+#pragma unroll
+    for (int s = 0; s < SK_KS; ++s)
+      wf[s] = *reinterpret_cast<const bf16x8*>(wb + 8 * (((SK_CH / 4) * q4 + s) ^ (r16 & 7)));
+    if (kb + SK_KC > kend) {   // partial stage (uniform): column groups past the range contribute nothing
+      const bool ok = kb + (SK_KC / 4) * q4 < kend;
+#pragma unroll
+      for (int s = 0; s < SK_KS; ++s) wf[s] = ok ? wf[s] : zero8;
+    }
+#pragma unroll
+    for (int s = 0; s < SK_KS; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8 xf =
+            *reinterpret_cast<const bf16x8*>(xb + 16 * t * SK_KC + 8 * (((SK_CH / 4) * q4 + s) ^ (r16 & 7)));
+        acc[t] = mfma16(wf[s], xf, acc[t]);
       }
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-        for (int tm = 0; tm < 2; ++tm) acc[tn][tm] = mfma32(wf[tn][s], xf[tm][s], acc[tn][tm]);
+  };
+  const int nsteps = (kend - kbeg + SK_KC - 1) / SK_KC;
+  // Stage c is multiplied while stages c + 1 .. c + 3 are in flight.  Past the
+  // last stage the loads repeat the last stage (cache hits, never used), which
+  // keeps the wait counts fixed and the loop free of branches around them.
+  auto issue_c = [&](int c, bf16* wd, bf16* xd) { issue(min(c, nsteps - 1), wd, xd); };
+  auto step = [&](int c, const bf16* wt, const bf16* xt, bf16* wn, bf16* xn) {
+    issue_c(c + 3, wn, xn);            // buffers of stage c - 1: every wave passed the barrier after it
+    mma(c, wt, xt);
+    vm_wait<2 * SK_VM_PER_STAGE>();    // this wave's part of stage c + 1 has landed
+    stage_barrier();                   // ... and every wave's; stage c is no longer read
+  };
+  if (nsteps > 0) {
+    issue_c(0, w_0, x_0);
+    issue_c(1, w_1, x_1);
+    issue_c(2, w_2, x_2);
+    vm_wait<2 * SK_VM_PER_STAGE>();
+    stage_barrier();
+    for (int c = 0; c < nsteps; c += 4) {
+      step(c, w_0, x_0, w_3, x_3);
+      if (c + 1 >= nsteps) break;
+      step(c + 1, w_1, x_1, w_0, x_0);
+      if (c + 2 >= nsteps) break;
+      step(c + 2, w_2, x_2, w_1, x_1);
+      if (c + 3 >= nsteps) break;
+      step(c + 3, w_3, x_3, w_2, x_2);
+    }
+    vm_wait<0>();
   }
-  // D[n][m]: lane holds column m = 32*tm + r, rows n = 32*tn + 8i + 4hi + j
+  __syncthreads();   // every wave is done with the LDS stages before they hold the output tile
+  // D[n][m]: lane holds token m = 16 t + r16, weight rows n = 16 wave + 4 q4 + j.
+  // The 64 x 64 fp32 tile goes through LDS: rows 0..31 in w_0, rows 32..63 in
+  // x_0 (8 KB each), element (r, m) of a half at r * 64 + (m ^ r)
+  float* rlo = reinterpret_cast<float*>(w_0);
+  float* rhi = reinterpret_cast<float*>(x_0);
+  static_assert(32 * 64 * sizeof(float) <= 64 * SK_KC * sizeof(bf16), "output half tile must fit one stage buffer");
+  {
+    float* half = wave < 2 ? rlo : rhi;
 #pragma unroll
-  for (int tn = 0; tn < 2; ++tn)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) red[wave][32 * tn + 8 * (e >> 2) + 4 * hi + (e & 3)][32 * tm + r] = acc[tn][tm][e];
+      for (int j = 0; j < 4; ++j) {
+        const int r = (16 * wave + 4 * q4 + j) & 31, m = 16 * t + r16;
+        half[r * 64 + (m ^ r)] = acc[t][j];
+      }
+  }
   __syncthreads();
+  // output columns vary fastest across lanes, so that stores are contiguous runs
   for (int idx = tid; idx < 32 * 64; idx += 256) {
-    const int nl = idx >> 6, ml = idx & 63;
-    float v0 = red[0][nl][ml] + red[1][nl][ml] + red[2][nl][ml] + red[3][nl][ml];
-    float v1 = red[0][nl + 32][ml] + red[1][nl + 32][ml] + red[2][nl + 32][ml] + red[3][nl + 32][ml];
+    const int nl = idx & 31, ml = idx >> 5;
+    float v0 = rlo[nl * 64 + (ml ^ nl)];
+    float v1 = rhi[nl * 64 + (ml ^ nl)];
     const int m = m0 + ml, n = n0 + nl;
     if (m >= a.M) continue;
     if (a.mode == SK_PARTIAL) {
@@ -283,36 +383,109 @@ absorb_kernel(AbsorbArgs a) {
 }
 
 // ------------------------------------------------------------ plan
-// plan[0] = keys per chunk, plan[1] = number of chunks, then lo[B], len[B], coff[B+1]
-__global__ void plan_kernel(const int32_t* lens, int B, int cap, int window, int target, int* plan) {
-  extern __shared__ int pl[];   // [2B]
-  for (int b = threadIdx.x; b < B; b += blockDim.x) {
-    const int p = lens[b];
-    const bool ok = p >= 0 && p < cap;
-    const int lo = (window > 0) ? max(0, p - window + 1) : 0;
-    pl[b] = ok ? lo : 0;
-    pl[B + b] = ok ? p + 1 - lo : 0;
-  }
+// The attended rows of every sequence are cut into 32-row tiles; the tiles of
+// all sequences, in sequence order, are split evenly over at most DEC_WGS
+// workgroups (see tile_owner).  The
+// part of one sequence that one workgroup covers is a segment; each segment
+// leaves one partial (m, l, O) that the combine step merges.
+// Plan layout (int32): [0] T, [1] number of segments, tstart[B + 1] (first
+// tile of each sequence), lo[B] (first attended row), len[B] (attended rows),
+// coff[B + 1] (first segment of each sequence), kf[B] (workgroup of the
+// sequence's first tile).
+constexpr int DEC_WGS = 512, DEC_TK = 32;
+
+size_t plan_ints(int B) { return 5 * (size_t)B + 4; }
+
+struct PlanView {
+  const int *tstart, *lo, *len, *coff, *kf;
+};
+__device__ __forceinline__ PlanView plan_view(const int* P, int B) {
+  PlanView v;
+  v.tstart = P + 2;
+  v.lo = v.tstart + B + 1;
+  v.len = v.lo + B;
+  v.coff = v.len + B;
+  v.kf = v.coff + B + 1;
+  return v;
+}
+
+// Workgroups in use: W = min(DEC_WGS, T), so that no range is empty and the
+// workgroups covering one sequence are consecutive.  Workgroup k < W takes
+// tiles [k T / W, (k + 1) T / W); tile t belongs to the largest k with k T / W <= t.
+__device__ __forceinline__ int dec_wgs(int T) { return min(DEC_WGS, T); }
+__device__ __forceinline__ int tile_owner(int t, int T) {
+  return (int)((((int64_t)t + 1) * dec_wgs(T) - 1) / T);
+}
+
+// inclusive prefix sum over the 256 threads of a block; *total gets the sum
+__device__ int block_incl_scan(int v, int* sc, int* total) {
+  const int tid = threadIdx.x;
+  sc[tid] = v;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t total = 0;
-    for (int b = 0; b < B; ++b) total += pl[B + b];
-    int64_t ck = (total + target - 1) / target;
-    ck = (ck + 31) / 32 * 32;
-    if (ck < 32) ck = 32;
-    int* lo = plan + 2;
-    int* len = lo + B;
-    int* coff = len + B;
-    int c = 0;
-    for (int b = 0; b < B; ++b) {
-      lo[b] = pl[b];
-      len[b] = pl[B + b];
-      coff[b] = c;
-      c += (int)((pl[B + b] + ck - 1) / ck);
+  for (int off = 1; off < 256; off <<= 1) {
+    const int t = tid >= off ? sc[tid - off] : 0;
+    __syncthreads();
+    sc[tid] += t;
+    __syncthreads();
+  }
+  const int r = sc[tid];
+  *total = sc[255];
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(256)
+plan_kernel(const int32_t* lens, int B, int cap, int window, int* plan) {
+  __shared__ int sc[256];
+  int* tstart = plan + 2;
+  int* lo = tstart + B + 1;
+  int* len = lo + B;
+  int* coff = len + B;
+  int* kf = coff + B + 1;
+  const int tid = threadIdx.x;
+  // pass 1: attended range and tile count of each sequence, prefix sum of tiles
+  int carry = 0;
+  for (int base = 0; base < B; base += 256) {
+    const int b = base + tid;
+    int nt = 0;
+    if (b < B) {
+      const int p = lens[b];
+      const bool ok = p >= 0 && p < cap;
+      const int l0 = (window > 0) ? max(0, p - window + 1) : 0;
+      lo[b] = ok ? l0 : 0;
+      len[b] = ok ? p + 1 - l0 : 0;
+      nt = ok ? (p + 1 - l0 + DEC_TK - 1) / DEC_TK : 0;
     }
-    coff[B] = c;
-    plan[0] = (int)ck;
-    plan[1] = c;
+    int tot;
+    const int incl = block_incl_scan(nt, sc, &tot);
+    if (b < B) tstart[b] = carry + incl - nt;
+    carry += tot;
+  }
+  const int T = carry;
+  // pass 2: segments per sequence (each thread revisits the sequences it wrote)
+  int scarry = 0;
+  for (int base = 0; base < B; base += 256) {
+    const int b = base + tid;
+    int segs = 0;
+    if (b < B) {
+      const int t0 = tstart[b], nt = (len[b] + DEC_TK - 1) / DEC_TK;
+      int k0 = 0;
+      if (nt > 0) {
+        k0 = tile_owner(t0, T);
+        segs = tile_owner(t0 + nt - 1, T) - k0 + 1;
+      }
+      kf[b] = k0;
+    }
+    int tot;
+    const int incl = block_incl_scan(segs, sc, &tot);
+    if (b < B) coff[b] = scarry + incl - segs;
+    scarry += tot;
+  }
+  if (tid == 0) {
+    tstart[B] = T;
+    coff[B] = scarry;
+    plan[0] = T;
+    plan[1] = scarry;
   }
 }
 
@@ -322,101 +495,120 @@ struct DecAttnArgs {
   const bf16* cache;       // [B, cap, RL]
   int cap, B, H;
   const int* plan;
-  float* part_ml;          // [chunks][H][2]: running max (exp2 domain) and sum
-  float* part_o;           // [chunks][H][KVR]: sum of p * c (relative to the max)
+  float* part_ml;          // [segments][H][2]: running max (exp2 domain) and sum
+  float* part_o;           // [segments][H][KVR]: sum of p * c (relative to the max)
   float scale_log2;
 };
 
+// One workgroup per tile range (see the plan), all heads: wave w owns heads
+// 16w .. 16w + 15.  32-row cache tiles go straight from HBM to LDS (global
+// load to LDS, two buffers: the next tile streams in while the current one is
+// used); scores on the 16x16x32 MFMA with the cache rows as A operand, P V with
+// the same LDS tile read transposed as A operand, online softmax per head.
+// LDS tile layout: the 16-byte chunk c of row r sits in slot 32 c + (r ^ 4 (c & 1)),
+// so one 1 KB global-to-LDS block is two chunk columns of all 32 rows, and both
+// the score reads (8 rows of one chunk) and the transposed reads (4 rows of two
+// neighbouring chunks) hit distinct banks.
 template <int KVR, int NW>
-__global__ void __launch_bounds__(64 * NW, 1)
+__global__ void __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1)
 dec_attn_kernel(DecAttnArgs a) {
-  constexpr int RL = KVR + DR, LDR = RL + 8, KS = RL / 32, DT = KVR / 16, TK = 32;
-  constexpr int NT = 64 * NW, CH = (TK * RL / 8 + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) bf16 tile[2][TK * LDR];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int RL = KVR + DR, KS = RL / 32, DT = KVR / 16, TK = DEC_TK;
+  constexpr int RCH = RL / 8;                         // 16-byte chunks per cache row
+  constexpr int TBLK = RCH / 2, NB = (TBLK + NW - 1) / NW;
+  static_assert(TK == 32 && RCH % 2 == 0, "tile layout assumes 32 rows and whole chunk pairs");
+  __shared__ __attribute__((aligned(1024))) bf16 tile[2][TBLK * 512];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q4 = lane >> 4;
-  const int gid = blockIdx.x;
-  const int* plan = a.plan;
-  const int nchunks = plan[1];
-  if (gid >= nchunks) return;
-  const int CK = plan[0], B = a.B;
-  const int* lo = plan + 2;
-  const int* len = lo + B;
-  const int* coff = len + B;
-  int bl = 0, bh = B - 1;   // last b with coff[b] <= gid
-  while (bl < bh) {
-    const int mid = (bl + bh + 1) >> 1;
-    if (coff[mid] <= gid) bl = mid; else bh = mid - 1;
-  }
-  const int b = bl;
-  const int c = gid - coff[b];
-  const int k_start = lo[b] + c * CK;
-  const int k_end = min(k_start + CK, lo[b] + len[b]);
+  const int B = a.B;
+  const PlanView pv = plan_view(a.plan, B);
+  const int T = __builtin_amdgcn_readfirstlane(a.plan[0]);
+  const int k = blockIdx.x;
+  const int nw = dec_wgs(T);
+  if (k >= nw) return;
+  const int tb = (int)((int64_t)k * T / nw), te = (int)((int64_t)(k + 1) * T / nw);
   const int h = wave * 16 + r16;
   const bool hok = h < a.H;
-
+  const int lrow = (lane & 31) ^ ((lane >> 5) << 2);  // row this lane fetches (chunk parity lane >> 5)
+  struct Seq {
+    int b, tend, row0, rend;   // tiles < tend; tile t starts at row row0 + TK t; rows < rend attended
+    const bf16* base;
+  };
+  auto seq_at = [&](int b) {   // all fields are wave-uniform
+    Seq q;
+    q.b = b;
+    q.tend = __builtin_amdgcn_readfirstlane(pv.tstart[b + 1]);
+    q.row0 = __builtin_amdgcn_readfirstlane(pv.lo[b] - TK * pv.tstart[b]);
+    q.rend = __builtin_amdgcn_readfirstlane(pv.lo[b] + pv.len[b]);
+    q.base = a.cache + (int64_t)b * a.cap * RL;
+    return q;
+  };
+  auto seq_for = [&](Seq q, int t) {   // advance past sequences that end at or before tile t
+    while (t >= q.tend) q = seq_at(q.b + 1);
+    return q;
+  };
+  auto load_tile = [&](const Seq& q, int t, int buf) {
+    const int key = min(q.row0 + TK * t + lrow, q.rend - 1);   // rows past the end repeat a valid row (masked)
+    const bf16* src = q.base + (int64_t)key * RL + 8 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int blk = wave + NW * i;
+      if (blk < TBLK) g2lds16(src + 16 * blk, &tile[buf][blk * 512]);
+    }
+  };
   bf16x8 qf[KS];
-  {
+  auto load_q = [&](int b) {
     const bf16* qp = a.qlat + ((int64_t)b * a.H + (hok ? h : 0)) * RL + 8 * q4;
     const bf16x8 zero8 = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = hok ? *reinterpret_cast<const bf16x8*>(qp + 32 * s) : zero8;
-  }
-  const bf16* crow = a.cache + (int64_t)b * a.cap * RL;
-  bf16x8 stg[CH];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int idx = tid + i * NT;
-      if (idx < TK * RL / 8) {
-        const int rr = idx / (RL / 8), cc = idx % (RL / 8);
-        const int key = min(kt + rr, k_end - 1);   // rows past the chunk repeat a valid row (masked below)
-        stg[i] = *reinterpret_cast<const bf16x8*>(crow + (int64_t)key * RL + cc * 8);
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int idx = tid + i * NT;
-      if (idx < TK * RL / 8) {
-        const int rr = idx / (RL / 8), cc = idx % (RL / 8);
-        *reinterpret_cast<bf16x8*>(&tile[buf][rr * LDR + cc * 8]) = stg[i];
-      }
-    }
   };
 
+  // first sequence: the last b with tstart[b] <= tb
+  int bl = 0, bh = B - 1;
+  while (bl < bh) {
+    const int mid = (bl + bh + 1) >> 1;
+    if (pv.tstart[mid] <= tb) bl = mid; else bh = mid - 1;
+  }
+  bl = __builtin_amdgcn_readfirstlane(bl);
+  Seq ls = seq_at(bl), cs = ls;
+  load_q(cs.b);
   f32x4 o[DT];
 #pragma unroll
   for (int d = 0; d < DT; ++d) o[d] = f32x4{};
   float m = NEG_INIT, lsum = 0.f;
   const float sc = a.scale_log2;
 
-  gload(k_start);
-  sstore(0);
+  load_tile(ls, tb, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int buf = 0;
-  for (int kt = k_start; kt < k_end; kt += TK) {
-    const bool more = kt + TK < k_end;
-    if (more) gload(kt + TK);
-    const bf16* T = tile[buf];
-    // scores S^T: lane holds head r16, keys 16*t + 4*q4 + j
+  for (int t = tb; t < te; ++t) {
+    if (t + 1 < te) {
+      ls = seq_for(ls, t + 1);
+      load_tile(ls, t + 1, buf ^ 1);
+    }
+    const bf16* Tl = tile[buf];
+    const int r0 = cs.row0 + TK * t;
+    // scores S^T: lane holds head r16, tile rows 16 u + 4 q4 + j
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
+    const bf16* kbase = Tl + (32 * q4 + (r16 ^ (4 * (q4 & 1)))) * 8;   // chunk 4 s + q4, row 16 u + r16
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(T + (16 * t + r16) * LDR + 32 * s + 8 * q4);
-        sacc[t] = mfma16(kf, qf[s], sacc[t]);
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbase + (128 * s + 16 * u) * 8);
+        sacc[u] = mfma16(kf, qf[s], sacc[u]);
       }
+      if (s % 6 == 5) __builtin_amdgcn_sched_barrier(0);   // bounds the LDS reads in flight (registers)
+    }
     float mt = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int key = kt + 16 * t + 4 * q4 + j;
-        if (key >= k_end) sacc[t][j] = -INFINITY;
-        mt = fmaxf(mt, sacc[t][j]);
+        if (r0 + 16 * u + 4 * q4 + j >= cs.rend) sacc[u][j] = -INFINITY;
+        mt = fmaxf(mt, sacc[u][j]);
       }
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sc;
@@ -431,33 +623,49 @@ dec_attn_kernel(DecAttnArgs a) {
     }
     bf16x8 pf;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p = fast_exp2(fmaf(sacc[t][j], sc, -m));
+        const float p = fast_exp2(fmaf(sacc[u][j], sc, -m));
         lsum += p;
-        pf[4 * t + j] = (bf16)p;
+        pf[4 * u + j] = (bf16)p;
       }
-    // O^T += C^T P: A operand = cache tile read transposed (dims x keys)
-    const bf16* base = T + (4 * q4 + (r16 >> 2)) * LDR + 4 * (r16 & 3);
+    // O^T += C^T P: A operand = cache tile read transposed (dims x rows); lane
+    // reads 4 values of row 4 q4 + (r16 >> 2) (and that + 16), columns 16 d + 4 (r16 & 3)
+    const int pc = (r16 >> 1) & 1;
+    const bf16* pbase = Tl + (32 * pc + ((4 * q4 + (r16 >> 2)) ^ (4 * pc))) * 8 + 4 * (r16 & 1);
 #pragma unroll
     for (int d = 0; d < DT; ++d) {
-      const bf16* p0 = base + 16 * d;
-      o[d] = mfma16(tr_pair(p0, p0 + 16 * LDR), pf, o[d]);
+      const bf16* p0 = pbase + 512 * d;
+      o[d] = mfma16(tr_pair(p0, p0 + 128), pf, o[d]);
+      if (d % 8 == 7) __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) sstore(buf ^ 1);
+    if (t + 1 == te || t + 1 >= cs.tend) {
+      // end of a segment: write its partial
+      float lt = lsum + __shfl_xor(lsum, 16, 64);
+      lt += __shfl_xor(lt, 32, 64);
+      const int seg = __builtin_amdgcn_readfirstlane(pv.coff[cs.b] + k - pv.kf[cs.b]);
+      if (hok) {
+        float* po = a.part_o + ((int64_t)seg * a.H + h) * KVR;
+#pragma unroll
+        for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(po + 16 * d + 4 * q4) = o[d];
+        if (q4 == 0) {
+          a.part_ml[((int64_t)seg * a.H + h) * 2] = m;
+          a.part_ml[((int64_t)seg * a.H + h) * 2 + 1] = lt;
+        }
+      }
+      if (t + 1 < te) {
+        cs = seq_for(cs, t + 1);
+        load_q(cs.b);
+#pragma unroll
+        for (int d = 0; d < DT; ++d) o[d] = f32x4{};
+        m = NEG_INIT;
+        lsum = 0.f;
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     buf ^= 1;
-  }
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  if (!hok) return;
-  float* po = a.part_o + ((int64_t)gid * a.H + h) * KVR;
-#pragma unroll
-  for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(po + 16 * d + 4 * q4) = o[d];
-  if (q4 == 0) {
-    a.part_ml[((int64_t)gid * a.H + h) * 2] = m;
-    a.part_ml[((int64_t)gid * a.H + h) * 2 + 1] = lsum;
   }
 }
 
@@ -469,39 +677,85 @@ struct CombineArgs {
   bf16* dlat;                // [nN][B][g][2*kv_rank]: hi | lo of O_j - lambda_j O_noise
 };
 
-// one workgroup per (sequence, KV head): merge the chunks of the group's g+1 heads
+// one workgroup per (sequence, KV head): merge the segments of the group's g+1
+// heads with log-sum-exp weights (computed once per segment into LDS), then
+// form the latent-space difference of each signal head with the noise head.
+// A sequence has at most DEC_WGS segments.
 __global__ void __launch_bounds__(256)
 combine_kernel(CombineArgs a) {
-  extern __shared__ float cmb[];   // [kv_rank] noise head output
+  __shared__ float wts[5][DEC_WGS];   // per head slot (g + 1 <= 5), per segment
   const int b = blockIdx.x, n = blockIdx.y;
-  const int* lo = a.plan + 2;
-  const int* coff = lo + 2 * a.B;
-  const int c0 = coff[b], c1 = coff[b + 1];
-  for (int slot = a.g; slot >= 0; --slot) {
+  const PlanView pv = plan_view(a.plan, a.B);
+  const int c0 = pv.coff[b], nch = min(pv.coff[b + 1] - c0, DEC_WGS);
+  for (int slot = 0; slot <= a.g; ++slot) {
     const int h = slot == a.g ? a.nS + n : n * a.g + slot;
-    float M = -INFINITY;
-    for (int c = c0; c < c1; ++c) M = fmaxf(M, a.part_ml[((int64_t)c * a.H + h) * 2]);
-    float Lsum = 0.f;
-    for (int c = c0; c < c1; ++c)
-      Lsum += a.part_ml[((int64_t)c * a.H + h) * 2 + 1] * fast_exp2(a.part_ml[((int64_t)c * a.H + h) * 2] - M);
-    const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
-    for (int d = threadIdx.x; d < a.kv_rank; d += blockDim.x) {
-      float v = 0.f;
-      for (int c = c0; c < c1; ++c)
-        v += a.part_o[((int64_t)c * a.H + h) * a.kv_rank + d] * fast_exp2(a.part_ml[((int64_t)c * a.H + h) * 2] - M);
-      v *= inv;
-      if (slot == a.g) {
-        cmb[d] = v;
-      } else {
-        const float lam = a.lam[(int64_t)b * a.nS + h];
-        const float dl = v - lam * cmb[d];
-        const bf16 hi = (bf16)dl;
-        bf16* out = a.dlat + (((int64_t)n * a.B + b) * a.g + slot) * 2 * a.kv_rank;
-        out[d] = hi;
-        out[a.kv_rank + d] = (bf16)(dl - (float)hi);
+    if ((int)(threadIdx.x >> 6) == (slot & 3)) {   // one wave per head slot
+      float M = -INFINITY;
+      for (int c = threadIdx.x & 63; c < nch; c += 64) M = fmaxf(M, a.part_ml[((int64_t)(c0 + c) * a.H + h) * 2]);
+      M = wave_max(M);
+      float Ls = 0.f;
+      for (int c = threadIdx.x & 63; c < nch; c += 64) {
+        const float* ml = a.part_ml + ((int64_t)(c0 + c) * a.H + h) * 2;
+        const float wv = fast_exp2(ml[0] - M);
+        wts[slot][c] = wv;
+        Ls += ml[1] * wv;
       }
+      Ls = wave_sum(Ls);
+      const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
+      for (int c = threadIdx.x & 63; c < nch; c += 64) wts[slot][c] *= inv;
     }
-    __syncthreads();
+    if ((slot & 3) == 3 || slot == a.g) __syncthreads();
+  }
+  // weighted sums: thread t owns latent dims 2t, 2t + 1 of every head slot; the
+  // loads of two segments x all slots are issued before any is consumed
+  const int d = 2 * threadIdx.x;
+  float2 acc[5] = {};
+  int hs[5];
+#pragma unroll
+  for (int slot = 0; slot < 5; ++slot) hs[slot] = slot == a.g ? a.nS + n : n * a.g + min(slot, a.g);
+  if (d < a.kv_rank) {
+    auto seg_row = [&](int c, int slot) {
+      return reinterpret_cast<const float2*>(a.part_o + ((int64_t)(c0 + c) * a.H + hs[slot]) * a.kv_rank + d);
+    };
+    int c = 0;
+    for (; c + 2 <= nch; c += 2) {
+      float2 p0[5], p1[5];
+#pragma unroll
+      for (int slot = 0; slot < 5; ++slot)
+        if (slot <= a.g) {
+          p0[slot] = *seg_row(c, slot);
+          p1[slot] = *seg_row(c + 1, slot);
+        }
+#pragma unroll
+      for (int slot = 0; slot < 5; ++slot)
+        if (slot <= a.g) {
+          const float w0 = wts[slot][c], w1 = wts[slot][c + 1];
+          acc[slot].x += w0 * p0[slot].x + w1 * p1[slot].x;
+          acc[slot].y += w0 * p0[slot].y + w1 * p1[slot].y;
+        }
+    }
+    if (c < nch) {
+#pragma unroll
+      for (int slot = 0; slot < 5; ++slot)
+        if (slot <= a.g) {
+          const float2 p = *seg_row(c, slot);
+          acc[slot].x += wts[slot][c] * p.x;
+          acc[slot].y += wts[slot][c] * p.y;
+        }
+    }
+#pragma unroll
+    for (int slot = 0; slot < 4; ++slot) {
+      if (slot >= a.g) break;
+      const float2 no = a.g == 1 ? acc[1] : a.g == 2 ? acc[2] : a.g == 3 ? acc[3] : acc[4];
+      const float lam = a.lam[(int64_t)b * a.nS + n * a.g + slot];
+      bf16* out = a.dlat + (((int64_t)n * a.B + b) * a.g + slot) * 2 * a.kv_rank;
+      const float dx = acc[slot].x - lam * no.x, dy = acc[slot].y - lam * no.y;
+      const bf16 hx = (bf16)dx, hy = (bf16)dy;
+      out[d] = hx;
+      out[d + 1] = hy;
+      out[a.kv_rank + d] = (bf16)(dx - (float)hx);
+      out[a.kv_rank + d + 1] = (bf16)(dy - (float)hy);
+    }
   }
 }
 
@@ -533,7 +787,7 @@ DecLayout dec_layout(const gdla_config* c, int B) {
   const int64_t nS = (int64_t)c->group * c->n_noise, H = nS + c->n_noise;
   const int64_t ndown = c->q_rank + c->kv_rank + c->d_rope + nS;
   const int64_t RL = c->kv_rank + c->d_rope;
-  const int64_t maxch = CHUNK_TARGET + B;
+  const int64_t maxch = DEC_WGS + B;
   DecLayout L;
   size_t o = 0;
   L.down = o; o = a256(o + (size_t)MAX_SPLIT * B * ndown * 4);
@@ -545,7 +799,7 @@ DecLayout dec_layout(const gdla_config* c, int B) {
   L.q = o;    o = a256(o + (size_t)B * H * DQK * 2);
   L.gate = o; o = a256(o + (size_t)B * nS * DV * 4);
   L.qlat = o; o = a256(o + (size_t)B * H * RL * 2);
-  L.plan = o; o = a256(o + (size_t)(3 * B + 4) * 4);
+  L.plan = o; o = a256(o + plan_ints(B) * 4);
   L.ml = o;   o = a256(o + (size_t)maxch * H * 2 * 4);
   L.po = o;   o = a256(o + (size_t)maxch * H * c->kv_rank * 4);
   L.dlat = o; o = a256(o + (size_t)c->n_noise * B * c->group * 2 * c->kv_rank * 2);
@@ -580,14 +834,10 @@ hipError_t decode_step(const gdla_config* c, const gdla_weights* w, int B, const
     k.B = (const bf16*)w->w_dq; k.ldb = d;
     k.M = B; k.N = ndown; k.K = d; k.kper = d / sp_down; k.mode = SK_PARTIAL;
     k.Cf = (float*)(ws + Lw.down); k.ldcf = ndown; k.sCf = (int64_t)B * ndown;
-    // rows rq.. come from W_DKV then W_lambda: expressed as two launches over row ranges
-    SkinnyArgs k1 = k;
-    k1.N = rq;
-    if ((err = skinny(k1, sp_down, s)) != hipSuccess) return err;
-    SkinnyArgs k2 = k;
-    k2.B = (const bf16*)w->w_dkv; k2.N = rkv + DR + nS; k2.B2 = (const bf16*)w->w_lambda; k2.nb2 = rkv + DR;
-    k2.Cf = k.Cf + rq;
-    if ((err = skinny(k2, sp_down, s)) != hipSuccess) return err;
+    // rows rq .. rq + rkv + d_rope - 1 come from W_DKV, the last nS from W_lambda
+    k.B2 = (const bf16*)w->w_dkv; k.nb2 = rq;
+    k.B3 = (const bf16*)w->w_lambda; k.nb3 = rq + rkv + DR;
+    if ((err = skinny(k, sp_down, s)) != hipSuccess) return err;
   }
   // 2. per-token prep at each sequence's position, cache append
   {
@@ -618,13 +868,12 @@ hipError_t decode_step(const gdla_config* c, const gdla_weights* w, int B, const
   }
   // 5. plan and latent attention
   int* plan = (int*)(ws + Lw.plan);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 2 * B * sizeof(int), s, cache_lens, B, capacity, c->window,
-                     CHUNK_TARGET, plan);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, cache_lens, B, capacity, c->window, plan);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   {
     DecAttnArgs k{(const bf16*)(ws + Lw.qlat), (const bf16*)cache, capacity, B, H, plan, (float*)(ws + Lw.ml),
                   (float*)(ws + Lw.po), (float)(1.4426950408889634 / std::sqrt((double)DQK))};
-    const int grid = CHUNK_TARGET + B;
+    const int grid = DEC_WGS;
     switch (rkv) {
       case 128: err = dec_attn_kvr<128>(k, grid, s); break;
       case 256: err = dec_attn_kvr<256>(k, grid, s); break;
@@ -636,7 +885,7 @@ hipError_t decode_step(const gdla_config* c, const gdla_weights* w, int B, const
   {
     CombineArgs k{plan, B, H, nN, g, nS, rkv, (const float*)(ws + Lw.ml), (const float*)(ws + Lw.po),
                   (const float*)(ws + Lw.lam), (bf16*)(ws + Lw.dlat)};
-    hipLaunchKernelGGL(combine_kernel, dim3(B, nN), dim3(256), rkv * sizeof(float), s, k);
+    hipLaunchKernelGGL(combine_kernel, dim3(B, nN), dim3(256), 0, s, k);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // 7. value up-projection per KV head, times the gate -> Z

@@ -106,6 +106,102 @@ rowprep_kernel(RowPrepArgs a) {
   for (int i = lane; i < a.nS; i += 64) a.lam[t * a.nS + i] = sigmoidf_(ll[i]);
 }
 
+// Block-per-row variant for small batches (decode): 256 threads share one
+// row, sum its split-K partials into LDS and reduce across the block.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+template <class T>
+__global__ void __launch_bounds__(256)
+rowprep_block_kernel(RowPrepArgs a) {
+  extern __shared__ float brow[];                   // [ld_down] + 4 reduction slots
+  float* red = brow + a.ld_down;
+  const int64_t t = blockIdx.x;
+  const float* src = a.down + t * a.ld_down;
+  // sum the split-K partials: all loads of a thread's elements are issued
+  // before any is consumed (up to 8 splits; more are summed in further rounds)
+  const int nsp = max(a.nsplit, 1);
+  for (int i = threadIdx.x; i < a.ld_down; i += blockDim.x) brow[i] = 0.f;
+  for (int sp0 = 0; sp0 < nsp; sp0 += 8) {
+    for (int i0 = 0; i0 < a.ld_down; i0 += 4 * blockDim.x) {
+      float v[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * blockDim.x + threadIdx.x;
+#pragma unroll
+        for (int sp = 0; sp < 8; ++sp)
+          v[u][sp] = (i < a.ld_down && sp0 + sp < nsp) ? src[(int64_t)(sp0 + sp) * a.split_stride + i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * blockDim.x + threadIdx.x;
+        if (i < a.ld_down)
+          brow[i] += ((v[u][0] + v[u][1]) + (v[u][2] + v[u][3])) + ((v[u][4] + v[u][5]) + (v[u][6] + v[u][7]));
+      }
+    }
+  }
+  __syncthreads();
+  const T* gq = (const T*)a.g_q;
+  const T* gkv = (const T*)a.g_kv;
+  int64_t seq, p;
+  bool write_cache = a.cache != nullptr;
+  if (a.pos_dev) {
+    seq = t;
+    p = a.pos_dev[t];
+    if (p < 0 || p >= a.cache_cap) {   // outside the cache: nothing is written there
+      write_cache = false;
+      p = p < 0 ? 0 : p;
+    }
+  } else {
+    seq = t / a.L;
+    p = a.pos_offset + (t - seq * a.L);
+  }
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < a.q_rank; i += blockDim.x) ss += brow[i] * brow[i];
+  float r = 1.0f / sqrtf(block_sum(ss, red) / a.q_rank + a.eps);
+  T* cqn = (T*)a.cqn + t * a.q_rank;
+  for (int i = threadIdx.x; i < a.q_rank; i += blockDim.x) cqn[i] = from_f32<T>(brow[i] * r * to_f32(gq[i]));
+  const float* ckv = brow + a.q_rank;
+  ss = 0.f;
+  for (int i = threadIdx.x; i < a.kv_rank; i += blockDim.x) ss += ckv[i] * ckv[i];
+  r = 1.0f / sqrtf(block_sum(ss, red) / a.kv_rank + a.eps);
+  T* ckvn = (T*)a.ckvn + t * (a.split_kv ? 2 * a.kv_rank : a.kv_rank);
+  T* crow = write_cache ? (T*)a.cache + (seq * a.cache_cap + p) * (int64_t)(a.kv_rank + a.d_rope) : nullptr;
+  for (int i = threadIdx.x; i < a.kv_rank; i += blockDim.x) {
+    const float f = ckv[i] * r * to_f32(gkv[i]);
+    const T v = from_f32<T>(f);
+    ckvn[i] = v;
+    if (a.split_kv) ckvn[a.kv_rank + i] = from_f32<T>(f - to_f32(v));
+    if (crow) crow[i] = v;
+  }
+  const float* kr = ckv + a.kv_rank;
+  const int half = a.d_rope / 2;
+  T* krow = (T*)a.kr + t * a.d_rope;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const double theta = pow(a.rope_base, -2.0 * (double)i / (double)a.d_rope);
+    double sd, cd;
+    sincos((double)p * theta, &sd, &cd);
+    const float c = (float)cd, s = (float)sd;
+    a.rope[(t * half + i) * 2] = c;
+    a.rope[(t * half + i) * 2 + 1] = s;
+    const float x1 = kr[i], x2 = kr[i + half];
+    const T o1 = from_f32<T>(x1 * c - x2 * s), o2 = from_f32<T>(x2 * c + x1 * s);
+    krow[i] = o1;
+    krow[i + half] = o2;
+    if (crow) {
+      crow[a.kv_rank + i] = o1;
+      crow[a.kv_rank + i + half] = o2;
+    }
+  }
+  const float* ll = kr + a.d_rope;
+  for (int i = threadIdx.x; i < a.nS; i += blockDim.x) a.lam[t * a.nS + i] = sigmoidf_(ll[i]);
+}
+
 template <class T>
 __global__ void __launch_bounds__(256)
 latent_norm_kernel(LatentNormArgs a) {
@@ -134,6 +230,14 @@ latent_norm_kernel(LatentNormArgs a) {
 
 hipError_t rowprep(const RowPrepArgs& a, bool bf16, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
+  if (a.T <= 1024) {
+    const size_t lds = ((size_t)a.ld_down + 4) * sizeof(float);
+    if (bf16)
+      hipLaunchKernelGGL(rowprep_block_kernel<__bf16>, dim3((unsigned)a.T), dim3(256), lds, s, a);
+    else
+      hipLaunchKernelGGL(rowprep_block_kernel<float>, dim3((unsigned)a.T), dim3(256), lds, s, a);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)cdiv(a.T, 4)), block(256);
   const size_t lds = a.nsplit > 1 ? 4 * (size_t)a.ld_down * sizeof(float) : 0;
   if (bf16)
