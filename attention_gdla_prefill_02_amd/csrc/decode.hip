@@ -92,11 +92,13 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 // Workgroup barrier without the release fence of __syncthreads (which waits for
-// every outstanding load and would drain the pipeline).  Used where each wave
-// has already waited for its own global-to-LDS loads of the stage to be read,
-// and where all LDS reads of a stage about to be overwritten were consumed by
-// instructions issued before the barrier.
+// every outstanding global load and would drain the pipeline).  Used where each
+// wave has already waited for its own global-to-LDS loads of the next stage.
+// It first waits for this wave's LDS reads (lgkmcnt(0); vmcnt and expcnt fields
+// at "no wait"): an MFMA may be scheduled after the barrier, but the LDS read
+// feeding it must be complete before another wave refills the slot.
 __device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -392,7 +394,7 @@ absorb_kernel(AbsorbArgs a) {
 // tile of each sequence), lo[B] (first attended row), len[B] (attended rows),
 // coff[B + 1] (first segment of each sequence), kf[B] (workgroup of the
 // sequence's first tile).
-constexpr int DEC_WGS = 512, DEC_TK = 32;
+constexpr int DEC_WGS = 512, DEC_TK = 32;   // two latent-attention workgroups per CU
 
 size_t plan_ints(int B) { return 5 * (size_t)B + 4; }
 

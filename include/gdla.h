@@ -189,7 +189,9 @@ size_t gdla_decode_workspace_size(const gdla_config* cfg, int32_t B);
  *   cache_lens  device int32 [B]: tokens already cached per sequence; the new
  *               token's position.  Read on the device (never on the host); it
  *               must be in [0, capacity - 1].  The caller advances it.
- * bf16 only.  All pointers 16-byte aligned. */
+ * bf16 only, kv_rank in {128, 256, 512}, at most 80 query heads
+ * (n_noise * (group + 1)); otherwise GDLA_ERR_UNSUPPORTED.  All pointers
+ * 16-byte aligned. */
 gdla_status gdla_decode(const gdla_config* cfg, const gdla_weights* w, int32_t B,
                         const void* x, void* y, void* cache, const int32_t* cache_lens,
                         int32_t capacity, void* workspace, size_t workspace_bytes,
