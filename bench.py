@@ -32,6 +32,31 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0                # MI355X HBM3E
 
+# HBM bytes per launch of the prefill attention kernel, from two rocprofv3
+# hardware-counter passes over this benchmark (FETCH_SIZE, then WRITE_SIZE, per
+# dispatch, averaged over the block's four attention launches), each scaled by
+# the ratio of bytes to counter reading of a device copy of known size timed in
+# the same pass (--copy-probe-mib).  Tied to the kernel source it was measured
+# on: reported as null once that source changes.
+ATTN_TRAFFIC = {"source_sha256": "b00cecf40b4533c7e2243a65a3165e44eaa4912cd027d8fe86a3a32699b0ab8d",
+                "fetch_bytes": 4107731687, "write_bytes": 402653184}
+ATTN_SOURCES = ("attention_gdla_prefill_02_amd/csrc/attn.hip", "attention_gdla_prefill_02_amd/csrc/common.h")
+
+
+def attn_source_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def attn_traffic():
+    if ATTN_TRAFFIC["source_sha256"] is None or ATTN_TRAFFIC["source_sha256"] != attn_source_sha():
+        return None
+    return ATTN_TRAFFIC["fetch_bytes"] + ATTN_TRAFFIC["write_bytes"]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -220,7 +245,13 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-only", action="store_true", help="time only the decode steps (for profiling)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (hardware-counter calibration)")
+    ap.add_argument("--print-attn-sha", action="store_true", help="print the attention source hash and exit")
     args = ap.parse_args()
+    if args.print_attn_sha:
+        print(attn_source_sha())
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the GDLA path here is built and timed on a single MI355X; "
@@ -235,6 +266,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     gdla.load()
+
+    if args.copy_probe_mib > 0:
+        src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {args.copy_probe_mib} MiB device-to-device")
+        del src, dst
 
     if args.decode_only:
         print(json.dumps({"decode": bench_decode(torch, gdla, configs, inputs)}), flush=True)
@@ -269,7 +309,7 @@ def main():
                    "global_batch": 1, "seq_len": 32768, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<3>",
                      "achieved": round(pf["attn_tflops"], 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(pf["attn_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(pf["attn_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": attn_traffic(),
                      "launches_per_step": n_attn_launch,
                      "flop_per_launch_avg": pf["attn_flop"] / n_attn_launch},
         "prefill": {"block_tflops": round(pf["tflops"], 2), "frac_of_peak": round(pf["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
