@@ -184,18 +184,33 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int64_t lda, int64_t sA,
     if (kt + 1 < KT) load_stage((kt + 1) * BK, cur ^ 1);
     const bf16* As = reinterpret_cast<const bf16*>(gsm + cur * STAGE_BYTES) + (wm * 128 + l32) * LDR + hi * 8;
     const bf16* Bs = reinterpret_cast<const bf16*>(gsm + cur * STAGE_BYTES + OP_CH * 16) + (wn * 64 + l32) * LDR + hi * 8;
+    bf16x8 wf[BK / 16][2], af[BK / 16][4];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 wf[2], af[4];
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn) wf[tn] = *reinterpret_cast<const bf16x8*>(Bs + tn * 32 * LDR + ks * 16);
+      for (int tn = 0; tn < 2; ++tn) wf[ks][tn] = *reinterpret_cast<const bf16x8*>(Bs + tn * 32 * LDR + ks * 16);
 #pragma unroll
-      for (int tm = 0; tm < 4; ++tm) af[tm] = *reinterpret_cast<const bf16x8*>(As + tm * 32 * LDR + ks * 16);
+      for (int tm = 0; tm < 4; ++tm) af[ks][tm] = *reinterpret_cast<const bf16x8*>(As + tm * 32 * LDR + ks * 16);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
       for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) acc[tn][tm] = mfma32(wf[tn], af[tm], acc[tn][tm]);
+        for (int tm = 0; tm < 4; ++tm) acc[tn][tm] = mfma32(wf[ks][tn], af[ks][tm], acc[tn][tm]);
+    // schedule: the 6 fragment reads of sub-step 0, then each sub-step's 8
+    // MFMAs with the 6 reads of the next sub-step interleaved
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16 - 1; ++ks) {
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
