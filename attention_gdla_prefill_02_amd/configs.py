@@ -1,4 +1,4 @@
-"""The five synthetic GDLA workloads (shapes, dtypes, masks and seeds only).
+"""The synthetic GDLA workloads (shapes, dtypes, masks and seeds only).
 
 Shapes follow the layer described in "Motif 3: Technical Report" (the
 model-configuration paragraph: 16 KV heads, 192-dim query-key heads with a
@@ -17,6 +17,11 @@ MOTIF_SHAPES = dict(d_model=4096, q_rank=1536, kv_rank=512, n_noise=16, group=3,
                     d_nope=128, d_rope=64, d_v=128)
 TINY_SHAPES = dict(d_model=256, q_rank=96, kv_rank=64, n_noise=2, group=2,
                    d_nope=32, d_rope=16, d_v=32)
+# The report's own layer configuration (model-configuration paragraph of the
+# report): group size 4 (64 signal + 16 noise = 80 query heads) and query rank
+# 1024; its sliding-window layers use W = 128.
+REPORT_SHAPES = dict(d_model=4096, q_rank=1024, kv_rank=512, n_noise=16, group=4,
+                     d_nope=128, d_rope=64, d_v=128)
 
 
 @dataclass(frozen=True)
@@ -55,6 +60,14 @@ WORKLOADS = {
         name="decode_b64", kind="decode", shapes=MOTIF_SHAPES, dtype="bf16", B=64,
         windows=(0, 4096), seed=3, ctx_range=(1024, 32768), capacity=32768,
         note="GDLA decode, bf16, batch 64, contexts U{1024..32768}"),
+    "report_hybrid_l32k": Workload(
+        name="report_hybrid_l32k", kind="block", shapes=REPORT_SHAPES, dtype="bf16", B=1, L=32768,
+        windows=(0, 128, 128, 128), seed=5, sampled_rows=256,
+        note="hybrid GDLA block at the report's shapes (g=4, q_rank 1024; 1 full + 3 x W=128), bf16, B=1 L=32768"),
+    "report_decode_b64": Workload(
+        name="report_decode_b64", kind="decode", shapes=REPORT_SHAPES, dtype="bf16", B=64,
+        windows=(0, 128), seed=6, ctx_range=(1024, 32768), capacity=32768,
+        note="GDLA decode at the report's shapes (g=4, 80 query heads), bf16, batch 64, contexts U{1024..32768}"),
     "hybrid_l256k": Workload(
         name="hybrid_l256k", kind="block", shapes=MOTIF_SHAPES, dtype="bf16", B=1,
         L=262144, windows=(0, 4096, 4096, 4096), seed=4, sampled_rows=256,
