@@ -9,7 +9,8 @@
 // with A(t) = {s <= t} (full) or {t - W < s <= t} (window W).
 //
 // bf16 kernel (d_nope = 128, d_rope = 64, d_v = 128), one workgroup per
-// (sequence, KV head n, 64-query block):
+// (sequence, KV head n, 64-query block; 32-query block when g = 4, with one
+// wave per head -- see halves() below):
 //  * 2(g+1) waves: wave w handles query head slot w/2 (g signal heads, then
 //    the noise head) for 32 consecutive queries.  All g+1 heads of the group
 //    read the same content key, rotary key and value, so each 64-key tile of
@@ -105,15 +106,21 @@ constexpr int K_BYTES = K_CHUNKS * 16;            // 12.5 KB
 constexpr int TILE_BYTES = T_CHUNKS * 16;         // 22.5 KB
 constexpr int TILE_KB = (T_CHUNKS + 63) / 64;     // 23 load instructions per tile
 
+// HV query halves of 32 per workgroup: 2 for g <= 3 (2(g+1) <= 8 waves, two
+// per SIMD within the 256-register budget); 1 for g = 4, whose 10 waves would
+// put three on a SIMD and cut the budget to 168 registers.
+template <int G> constexpr int halves() { return G <= 3 ? 2 : 1; }
+
 template <int G>
-__global__ void __launch_bounds__(128 * (G + 1), 1)
+__global__ void __launch_bounds__(64 * halves<G>() * (G + 1), 1)
 attn_bf16_kernel(AttnArgs a) {
-  constexpr int NW = 2 * (G + 1), NT = 64 * NW;
+  constexpr int HV = halves<G>(), BQ = 32 * HV;
+  constexpr int NW = HV * (G + 1), NT = 64 * NW;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   // wave w: query head slot w % (G+1), query half w / (G+1); waves w and w+4 share a SIMD
-  const int hs = w % (G + 1), half = w / (G + 1);
+  const int hs = w % (G + 1), half = HV == 2 ? w / (G + 1) : 0;
   const int l32 = lane & 31, hi = lane >> 5;
   const int L = a.L, nN = a.nN, nS = G * nN, W = a.window;
 
@@ -416,8 +423,8 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int blocks = a.B * a.nN * cdiv(a.L, BQ);
-  hipLaunchKernelGGL(attn_bf16_kernel<G>, dim3(blocks), dim3(128 * (G + 1)), lds, s, a);
+  const int blocks = a.B * a.nN * cdiv(a.L, 32 * halves<G>());
+  hipLaunchKernelGGL(attn_bf16_kernel<G>, dim3(blocks), dim3(64 * halves<G>() * (G + 1)), lds, s, a);
   return hipGetLastError();
 }
 

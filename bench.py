@@ -13,8 +13,9 @@ TFLOP/s over algorithmic work: 2 x MACs of every projection plus 640 FLOP per
 Prints one JSON line with the roofline of the dominant kernel (attention,
 timed with HIP events on its stream inside the timed steps), the decode
 throughput of a batch-64 step against the compressed latent cache (full and
-W = 4096 layers), and the fp64 CPU oracle timed on a bounded sample of the
-same workload.
+W = 4096 layers), the same prefill block and decode at the report's own layer
+shapes (group size 4, query rank 1024, W = 128), and the fp64 CPU oracle timed
+on a bounded sample of the headline workload.
 """
 
 from __future__ import annotations
@@ -106,8 +107,10 @@ def cpu_baseline(w, Wc0, x_cpu, sample_L: int):
                       f"{flop / 1e9:.1f} GFLOP in {dt:.1f} s on {len(os.sched_getaffinity(0))} host cores"}
 
 
-def bench_prefill(args, torch, gdla, configs, inputs):
-    w = configs.WORKLOADS["hybrid_l32k"]
+def bench_prefill(args, torch, gdla, configs, inputs, name="hybrid_l32k", steps=None, warmup=None):
+    w = configs.WORKLOADS[name]
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     s = w.shapes
     B, L = w.B, w.L
     log(f"[bench] building inputs: {w.note}")
@@ -123,7 +126,7 @@ def bench_prefill(args, torch, gdla, configs, inputs):
     pre = gdla.STAGE_DOWN | gdla.STAGE_PREP | gdla.STAGE_EXPAND | gdla.STAGE_QG
     n_layers = len(w.windows)
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_layers)]
-           for _ in range(args.steps)]
+           for _ in range(steps)]
 
     def step(ev):
         record = ev is not None
@@ -144,31 +147,31 @@ def bench_prefill(args, torch, gdla, configs, inputs):
             if record:
                 e[3].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = [sum(evs[k][l][1].elapsed_time(evs[k][l][2]) for k in range(args.steps)) for l in range(n_layers)]
-    pre_ms = [sum(evs[k][l][0].elapsed_time(evs[k][l][1]) for k in range(args.steps)) for l in range(n_layers)]
-    out_ms = [sum(evs[k][l][2].elapsed_time(evs[k][l][3]) for k in range(args.steps)) for l in range(n_layers)]
-    ms_step = wall * 1e3 / args.steps
+    attn_ms = [sum(evs[k][l][1].elapsed_time(evs[k][l][2]) for k in range(steps)) for l in range(n_layers)]
+    pre_ms = [sum(evs[k][l][0].elapsed_time(evs[k][l][1]) for k in range(steps)) for l in range(n_layers)]
+    out_ms = [sum(evs[k][l][2].elapsed_time(evs[k][l][3]) for k in range(steps)) for l in range(n_layers)]
+    ms_step = wall * 1e3 / steps
 
     proj = proj_flop_per_token(s) * B * L * n_layers
     pairs = [B * attended_pairs(L, win) for win in w.windows]
     attn_flop = attn_flop_per_pair(s) * sum(pairs)
     total = proj + attn_flop
-    attn_time = sum(attn_ms) / args.steps / 1e3
+    attn_time = sum(attn_ms) / steps / 1e3
     kern = {
-        "pre_ms": [round(v / args.steps, 3) for v in pre_ms],
-        "attn_ms": [round(v / args.steps, 3) for v in attn_ms],
-        "out_ms": [round(v / args.steps, 3) for v in out_ms],
+        "pre_ms": [round(v / steps, 3) for v in pre_ms],
+        "attn_ms": [round(v / steps, 3) for v in attn_ms],
+        "out_ms": [round(v / steps, 3) for v in out_ms],
     }
     attn_tflops = attn_flop / attn_time / 1e12
-    gemm_time = (sum(pre_ms) + sum(out_ms)) / args.steps / 1e3
+    gemm_time = (sum(pre_ms) + sum(out_ms)) / steps / 1e3
     res = dict(total_flop=total, proj_flop=proj, attn_flop=attn_flop, ms_step=ms_step,
                tflops=total / (ms_step / 1e3) / 1e12, attn_tflops=attn_tflops,
                other_tflops=proj / gemm_time / 1e12, kern=kern,
@@ -191,11 +194,11 @@ def decode_bytes(s: dict, lens, window: int) -> int:
     return rows * RL * 2 + params * 2 + B * RL * 2 + B * s["d_model"] * 2 * 2
 
 
-def bench_decode(torch, gdla, configs, inputs, reps: int = 20):
+def bench_decode(torch, gdla, configs, inputs, reps: int = 20, name="decode_b64", fixed_ctx=True):
     """Batch-64 decode step against a 32768-row latent cache (contexts
-    U{1024..32768}), full-causal and W = 4096 layers, plus all contexts at
-    32768.  The 256 MB MALL is flushed (512 MB write) before every timed rep."""
-    w = configs.WORKLOADS["decode_b64"]
+    U{1024..32768}), full-causal and sliding-window layers, plus all contexts
+    at 32768.  The 256 MB MALL is flushed (512 MB write) before every timed rep."""
+    w = configs.WORKLOADS[name]
     s = w.shapes
     log(f"[bench] building decode state: {w.note}")
     cache_c, lens = inputs.make_decode_state(w.B, w.capacity, s["kv_rank"], s["d_rope"], w.ctx_range, w.seed, "bf16")
@@ -206,8 +209,10 @@ def bench_decode(torch, gdla, configs, inputs, reps: int = 20):
     y = torch.empty_like(x)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     out = {}
-    cases = [("full", 0, lens), ("swa4096", 4096, lens),
-             ("full_ctx32768", 0, torch.full_like(lens, w.capacity - 1))]
+    win = w.windows[1]
+    cases = [("full", 0, lens), (f"swa{win}", win, lens)]
+    if fixed_ctx:
+        cases.append(("full_ctx32768", 0, torch.full_like(lens, w.capacity - 1)))
     for name, window, ln in cases:
         cfg = gdla.make_config(s, window, "bf16")
         ws = gdla.alloc_workspace(gdla.decode_workspace_size(cfg, w.B))
@@ -230,9 +235,10 @@ def bench_decode(torch, gdla, configs, inputs, reps: int = 20):
                      "tokens_per_s": round(w.B / t, 1), "GB": round(nbytes / 1e9, 4),
                      "GB_per_s": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"[bench] decode {name}: {out[name]}")
-    out["block_tokens_per_s"] = round(w.B / (out["full"]["us_per_step"] + 3 * out["swa4096"]["us_per_step"]) * 1e6, 1)
+    out["block_tokens_per_s"] = round(w.B / (out["full"]["us_per_step"] + 3 * out[f"swa{win}"]["us_per_step"]) * 1e6, 1)
     out["batch"] = w.B
-    out["contexts"] = "U{1024..32768} seeded (full, swa4096); all 32768 (full_ctx32768)"
+    out["contexts"] = (f"U{{{w.ctx_range[0]}..{w.ctx_range[1]}}} seeded (full, swa{win})"
+                       + ("; all 32768 (full_ctx32768)" if fixed_ctx else ""))
     return out
 
 
@@ -244,6 +250,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-report-shapes", action="store_true", help="skip the report-shape (g=4, W=128) workloads")
     ap.add_argument("--decode-only", action="store_true", help="time only the decode steps (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (hardware-counter calibration)")
@@ -285,6 +292,20 @@ def main():
 
     decode = None if args.no_decode else bench_decode(torch, gdla, configs, inputs)
 
+    report = None
+    if not args.no_report_shapes:
+        rp, _, _, _ = bench_prefill(args, torch, gdla, configs, inputs, name="report_hybrid_l32k", steps=3, warmup=1)
+        log(f"[bench] report-shape prefill: {rp['ms_step']:.2f} ms/step, {rp['tflops']:.1f} TFLOP/s, attention "
+            f"{rp['attn_tflops']:.1f} TFLOP/s, GEMMs+prep {rp['other_tflops']:.1f} TFLOP/s, stages {rp['kern']}")
+        rd = None if args.no_decode else bench_decode(torch, gdla, configs, inputs, reps=10,
+                                                      name="report_decode_b64", fixed_ctx=False)
+        report = {"workload": "report_hybrid_l32k + report_decode_b64: group size 4 (80 query heads), q_rank 1024, "
+                              "windows 128",
+                  "prefill": {"block_tflops": round(rp["tflops"], 2), "ms_per_step": round(rp["ms_step"], 3),
+                              "attn_tflops": round(rp["attn_tflops"], 2), "gemm_prep_tflops": round(rp["other_tflops"], 2),
+                              "algorithmic_tflop_per_step": round(rp["total_flop"] / 1e12, 3), "stage_ms": rp["kern"]},
+                  "decode": rd}
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens")
@@ -317,6 +338,7 @@ def main():
                     "algorithmic_tflop_per_step": round(pf["total_flop"] / 1e12, 3), "stage_ms": pf["kern"],
                     "output_finite": pf["finite"]},
         "decode": decode,
+        "report_shapes": report,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
