@@ -72,10 +72,15 @@ __device__ __forceinline__ bf16x8 tr_pair(const bf16* p0, const bf16* p1) {
 // one is multiplied.  Both operands go global -> LDS (the compiler does not
 // track these loads, so its own waits never drain the pipeline; the waits here
 // are explicit counts).  LDS tiles are [64 rows][SK_KC columns] in 16-byte
-// slots, chunk c of row r in slot SK_CH r + (c ^ (r & 7)); the MFMA k index is
-// permuted so that element e of k-step s of lane group q4 is column
-// (SK_KC / 4) q4 + 8 s + e for both operands, which makes every fragment read
-// conflict-free.  64 KB of LDS: two workgroups per CU.
+// slots, chunk c of row r in slot SK_CH r + (c ^ sk_swz(r)); the MFMA k index
+// is permuted so that element e of k-step s of lane group q4 is column
+// (SK_KC / 4) q4 + 8 s + e for both operands.  gfx950 serves a 16-byte LDS
+// read in four passes of 16 lanes: lanes 32 h + 4 j + i (i < 4) with the
+// parity of j (three bits) fixed.  A pass therefore holds lane groups q4 = 2h
+// and 2h + 1, with complementary parities of row bits 2 and 3; sk_swz puts that
+// parity into bit 2 of the chunk so the two halves of a pass fall on disjoint
+// bank quads and every fragment read is conflict-free.  64 KB of LDS: two
+// workgroups per CU.
 enum SkinnyMode { SK_PARTIAL = 0, SK_QG = 1, SK_ZGATE = 2 };
 constexpr int SK_KC = 64, SK_NSTG = 4;
 constexpr int SK_CH = SK_KC / 8;          // 16-byte chunks per tile row
@@ -83,6 +88,10 @@ constexpr int SK_RPB = 64 / SK_CH;        // tile rows per 1 KB block
 constexpr int SK_BPW = SK_CH / 4;         // blocks per wave per operand (16 rows)
 constexpr int SK_KS = SK_KC / 32;         // MFMA k-steps per stage
 constexpr int SK_VM_PER_STAGE = 2 * SK_BPW;   // global-to-LDS loads per wave per stage
+// chunk swizzle of tile row r (only bits 1..3 of r matter)
+__device__ __forceinline__ int sk_swz(int r) {
+  return ((r >> 1) & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
+}
 
 // s_waitcnt vmcnt(N) through the builtin, so that the compiler's own wait
 // tracking sees it (expcnt and lgkmcnt fields left at "no wait")
@@ -148,7 +157,7 @@ skinny_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
   for (int i = 0; i < SK_BPW; ++i) {
     const int row = SK_RPB * (SK_BPW * wave + i) + lr;
-    sw[i] = 8 * (lc ^ (row & 7));                      // source column of this lane's slot
+    sw[i] = 8 * (lc ^ sk_swz(row));               // source column of this lane's slot
     const int nn = min(n0 + row, a.N - 1);             // rows past N repeat row N - 1 (results dropped)
     wsrc[i] = (a.B3 && nn >= a.nb3) ? a.B3 + (int64_t)(nn - a.nb3) * a.ldb
               : (a.B2 && nn >= a.nb2) ? a.B2 + (int64_t)(nn - a.nb2) * a.ldb
@@ -179,7 +188,7 @@ skinny_gemm_kernel(SkinnyArgs a) {
     bf16x8 wf[SK_KS];
 #pragma unroll
     for (int s = 0; s < SK_KS; ++s)
-      wf[s] = *reinterpret_cast<const bf16x8*>(wb + 8 * (((SK_CH / 4) * q4 + s) ^ (r16 & 7)));
+      wf[s] = *reinterpret_cast<const bf16x8*>(wb + 8 * (((SK_CH / 4) * q4 + s) ^ sk_swz(r16)));
     if (kb + SK_KC > kend) {   // partial stage (uniform): column groups past the range contribute nothing
       const bool ok = kb + (SK_KC / 4) * q4 < kend;
 #pragma unroll
@@ -190,7 +199,7 @@ skinny_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const bf16x8 xf =
-            *reinterpret_cast<const bf16x8*>(xb + 16 * t * SK_KC + 8 * (((SK_CH / 4) * q4 + s) ^ (r16 & 7)));
+            *reinterpret_cast<const bf16x8*>(xb + 16 * t * SK_KC + 8 * (((SK_CH / 4) * q4 + s) ^ sk_swz(r16)));
         acc[t] = mfma16(wf[s], xf, acc[t]);
       }
   };
@@ -302,7 +311,9 @@ struct AbsorbArgs {
   bf16* qlat;                          // [B, H, kv_rank + 64]
 };
 
-constexpr int AB_LD = 64 + 8;
+// row stride 192 B: the four rows a 32-lane transposed read pass touches
+// (64 B each) fall on disjoint quarters of the 64 four-byte LDS banks
+constexpr int AB_LD = 96;
 
 // grid (kv_rank/64, nN, cdiv(B*(g+1), 256)); C[(b,h), r] = sum_i q^C[b,h,i] W_UK,n[i, r]
 __global__ void __launch_bounds__(256)
@@ -507,10 +518,16 @@ struct DecAttnArgs {
 // load to LDS, two buffers: the next tile streams in while the current one is
 // used); scores on the 16x16x32 MFMA with the cache rows as A operand, P V with
 // the same LDS tile read transposed as A operand, online softmax per head.
-// LDS tile layout: the 16-byte chunk c of row r sits in slot 32 c + (r ^ 4 (c & 1)),
-// so one 1 KB global-to-LDS block is two chunk columns of all 32 rows, and both
-// the score reads (8 rows of one chunk) and the transposed reads (4 rows of two
-// neighbouring chunks) hit distinct banks.
+// LDS tile layout: the 16-byte chunk c of row r sits in slot 32 c + (r ^ 8 (c & 1)),
+// so one 1 KB global-to-LDS block is two chunk columns of all 32 rows.  With
+// the 64 four-byte banks of gfx950's LDS, the transposed 8-byte reads of a
+// 32-lane pass (rows R..R+7, even chunk -> banks 0..31 via slot mod 16 = R,
+// odd chunk -> banks 32..63 via R ^ 8) touch every bank once.  A 16-byte read
+// is served in four passes of 16 lanes (lanes 32 h + 4 j + i, i < 4, with the
+// parity of j fixed): lane groups q4 = 2h and 2h + 1 with complementary
+// parities of row bits 2 and 3.  The score reads give both groups of a pass
+// chunks of one parity (the qc order below), so their 16 rows map to 16
+// distinct slots mod 16.
 template <int KVR, int NW>
 __global__ void __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1)
 dec_attn_kernel(DecAttnArgs a) {
@@ -522,6 +539,10 @@ dec_attn_kernel(DecAttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q4 = lane >> 4;
+  // k chunk of lane group q4 within a 32-wide k step: 0, 2, 1, 3, so that the
+  // two lane groups of one 16-byte LDS read pass (q4 = 2h, 2h + 1) read chunks
+  // of the same parity
+  const int qc = ((q4 & 1) << 1) | (q4 >> 1);
   const int B = a.B;
   const PlanView pv = plan_view(a.plan, B);
   const int T = __builtin_amdgcn_readfirstlane(a.plan[0]);
@@ -531,7 +552,7 @@ dec_attn_kernel(DecAttnArgs a) {
   const int tb = (int)((int64_t)k * T / nw), te = (int)((int64_t)(k + 1) * T / nw);
   const int h = wave * 16 + r16;
   const bool hok = h < a.H;
-  const int lrow = (lane & 31) ^ ((lane >> 5) << 2);  // row this lane fetches (chunk parity lane >> 5)
+  const int lrow = (lane & 31) ^ ((lane >> 5) << 3);  // row this lane fetches (chunk parity lane >> 5)
   struct Seq {
     int b, tend, row0, rend;   // tiles < tend; tile t starts at row row0 + TK t; rows < rend attended
     const bf16* base;
@@ -560,7 +581,7 @@ dec_attn_kernel(DecAttnArgs a) {
   };
   bf16x8 qf[KS];
   auto load_q = [&](int b) {
-    const bf16* qp = a.qlat + ((int64_t)b * a.H + (hok ? h : 0)) * RL + 8 * q4;
+    const bf16* qp = a.qlat + ((int64_t)b * a.H + (hok ? h : 0)) * RL + 8 * qc;
     const bf16x8 zero8 = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = hok ? *reinterpret_cast<const bf16x8*>(qp + 32 * s) : zero8;
@@ -594,7 +615,7 @@ dec_attn_kernel(DecAttnArgs a) {
     const int r0 = cs.row0 + TK * t;
     // scores S^T: lane holds head r16, tile rows 16 u + 4 q4 + j
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
-    const bf16* kbase = Tl + (32 * q4 + (r16 ^ (4 * (q4 & 1)))) * 8;   // chunk 4 s + q4, row 16 u + r16
+    const bf16* kbase = Tl + (32 * qc + (r16 ^ (8 * (qc & 1)))) * 8;   // chunk 4 s + qc, row 16 u + r16
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
@@ -635,7 +656,7 @@ dec_attn_kernel(DecAttnArgs a) {
     // O^T += C^T P: A operand = cache tile read transposed (dims x rows); lane
     // reads 4 values of row 4 q4 + (r16 >> 2) (and that + 16), columns 16 d + 4 (r16 & 3)
     const int pc = (r16 >> 1) & 1;
-    const bf16* pbase = Tl + (32 * pc + ((4 * q4 + (r16 >> 2)) ^ (4 * pc))) * 8 + 4 * (r16 & 1);
+    const bf16* pbase = Tl + (32 * pc + ((4 * q4 + (r16 >> 2)) ^ (8 * pc))) * 8 + 4 * (r16 & 1);
 #pragma unroll
     for (int d = 0; d < DT; ++d) {
       const bf16* p0 = pbase + 512 * d;
