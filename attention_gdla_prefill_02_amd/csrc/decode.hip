@@ -576,7 +576,7 @@ dec_attn_kernel(DecAttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int blk = wave + NW * i;
-      if (blk < TBLK) g2lds16(src + 16 * blk, &tile[buf][blk * 512]);
+      if (blk < TBLK) g2lds16_explicit(src + 16 * blk, &tile[buf][blk * 512]);
     }
   };
   bf16x8 qf[KS];
@@ -585,6 +585,10 @@ dec_attn_kernel(DecAttnArgs a) {
     const bf16x8 zero8 = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = hok ? *reinterpret_cast<const bf16x8*>(qp + 32 * s) : zero8;
+    // wait here, through the builtin, so the compiler knows qf is complete and
+    // adds no vmcnt waits before the score MFMAs (those would also wait for
+    // the next tile, which its wait tracking does not see)
+    vm_wait<0>();
   };
 
   // first sequence: the last b with tstart[b] <= tb
@@ -603,7 +607,7 @@ dec_attn_kernel(DecAttnArgs a) {
   const float sc = a.scale_log2;
 
   load_tile(ls, tb, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vm_wait<0>();
   __syncthreads();
   int buf = 0;
   for (int t = tb; t < te; ++t) {
@@ -686,7 +690,7 @@ dec_attn_kernel(DecAttnArgs a) {
         lsum = 0.f;
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    vm_wait<0>();   // this wave's part of tile t + 1
     __syncthreads();
     buf ^= 1;
   }

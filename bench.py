@@ -197,7 +197,9 @@ def decode_bytes(s: dict, lens, window: int) -> int:
 def bench_decode(torch, gdla, configs, inputs, reps: int = 20, name="decode_b64", fixed_ctx=True):
     """Batch-64 decode step against a 32768-row latent cache (contexts
     U{1024..32768}), full-causal and sliding-window layers, plus all contexts
-    at 32768.  The 256 MB MALL is flushed (512 MB write) before every timed rep."""
+    at 32768.  Before every timed rep the 256 MB MALL is flushed by reading a
+    512 MB buffer (a read leaves clean lines; a 512 MB write would leave 256 MB
+    of dirty lines whose write-back would land inside the timed step)."""
     w = configs.WORKLOADS[name]
     s = w.shapes
     log(f"[bench] building decode state: {w.note}")
@@ -207,7 +209,7 @@ def bench_decode(torch, gdla, configs, inputs, reps: int = 20, name="decode_b64"
     W = {k: v.to("cuda") for k, v in inputs.make_weights(s, configs.layer_seed(w, 0), "bf16").items()}
     x = inputs.make_x(w.B, 1, s["d_model"], w.seed, "bf16")[:, 0].contiguous().to("cuda")
     y = torch.empty_like(x)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.zeros((512 << 20) // 4, dtype=torch.float32, device="cuda")
     out = {}
     win = w.windows[1]
     cases = [("full", 0, lens), (f"swa{win}", win, lens)]
@@ -221,7 +223,7 @@ def bench_decode(torch, gdla, configs, inputs, reps: int = 20, name="decode_b64"
             gdla.decode(cfg, W, x, cache, ln_d, y=y, workspace=ws)
         times = []
         for _ in range(reps):
-            flush.zero_()
+            flush.sum()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             gdla.decode(cfg, W, x, cache, ln_d, y=y, workspace=ws)
