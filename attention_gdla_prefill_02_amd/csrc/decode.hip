@@ -120,6 +120,7 @@ struct SkinnyArgs {
   const bf16* B3; int nb3;                     // rows >= nb3 (> nb2) come from B3
   int M, N, K, kwrapB, kper;                   // kper: K range per split (SK_PARTIAL); kwrapB % SK_KC == 0
   int mode;
+  int stream_w;                                // weights read once (one M tile, no wrap): non-temporal loads
   float* Cf; int64_t ldcf; int64_t sCf;        // SK_PARTIAL: fp32 partial [z][M][N]
   // SK_QG
   bf16* Q; int64_t ldq; float* G; int64_t ldg; int q_cols; const float* rope;
@@ -173,7 +174,8 @@ skinny_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
     for (int i = 0; i < SK_BPW; ++i) {
       const int off = kb + sw[i] < kend ? sw[i] : 0;
-      g2lds16_explicit(wsrc[i] + kw + off, wd + (SK_BPW * wave + i) * 512);
+      if (a.stream_w) g2lds16_stream(wsrc[i] + kw + off, wd + (SK_BPW * wave + i) * 512);
+      else g2lds16_explicit(wsrc[i] + kw + off, wd + (SK_BPW * wave + i) * 512);
       g2lds16_explicit(xsrc[i] + kb + off, xd + (SK_BPW * wave + i) * 512);
     }
   };
@@ -290,7 +292,9 @@ skinny_gemm_kernel(SkinnyArgs a) {
 
 hipError_t skinny(const SkinnyArgs& a, int zdim, hipStream_t s) {
   dim3 grid(cdiv(a.N, 64), cdiv(a.M, 64), zdim);
-  hipLaunchKernelGGL(skinny_gemm_kernel, grid, dim3(256), 0, s, a);
+  SkinnyArgs k = a;
+  k.stream_w = a.M <= 64 && a.kwrapB == 0;   // each weight row is read by one workgroup, once
+  hipLaunchKernelGGL(skinny_gemm_kernel, grid, dim3(256), 0, s, k);
   return hipGetLastError();
 }
 
@@ -518,31 +522,28 @@ struct DecAttnArgs {
 // load to LDS, two buffers: the next tile streams in while the current one is
 // used); scores on the 16x16x32 MFMA with the cache rows as A operand, P V with
 // the same LDS tile read transposed as A operand, online softmax per head.
-// LDS tile layout: the 16-byte chunk c of row r sits in slot 32 c + (r ^ 8 (c & 1)),
-// so one 1 KB global-to-LDS block is two chunk columns of all 32 rows.  With
-// the 64 four-byte banks of gfx950's LDS, the transposed 8-byte reads of a
-// 32-lane pass (rows R..R+7, even chunk -> banks 0..31 via slot mod 16 = R,
-// odd chunk -> banks 32..63 via R ^ 8) touch every bank once.  A 16-byte read
-// is served in four passes of 16 lanes (lanes 32 h + 4 j + i, i < 4, with the
-// parity of j fixed): lane groups q4 = 2h and 2h + 1 with complementary
-// parities of row bits 2 and 3.  The score reads give both groups of a pass
-// chunks of one parity (the qc order below), so their 16 rows map to 16
-// distinct slots mod 16.
+// LDS tile layout: 1 KB blocks of 8 rows x 8 chunks (16 bytes each), block
+// 4 cg + rg holding rows 8 rg .. 8 rg + 7 and chunks 8 cg .. 8 cg + 7; inside a
+// block, chunk c of row x sits in slot 8 x + (c ^ (x & 6)).  A global-to-LDS
+// block load therefore fetches eight whole 128-byte lines, which lets it use
+// the non-temporal policy (a line requested piecewise by several loads would
+// be fetched from HBM more than once).  gfx950 serves a 16-byte LDS read in
+// four passes of 16 lanes (lanes 32 h + 4 j + i, i < 4, with the parity of j
+// fixed): in the score reads the two lane groups of a pass read chunks of
+// different parity, which the swizzle sends to disjoint bank quads; the
+// transposed 8-byte reads of a 32-lane pass cover eight rows and a chunk pair,
+// 32 distinct bank pairs.
 template <int KVR, int NW>
 __global__ void __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1)
 dec_attn_kernel(DecAttnArgs a) {
   constexpr int RL = KVR + DR, KS = RL / 32, DT = KVR / 16, TK = DEC_TK;
   constexpr int RCH = RL / 8;                         // 16-byte chunks per cache row
   constexpr int TBLK = RCH / 2, NB = (TBLK + NW - 1) / NW;
-  static_assert(TK == 32 && RCH % 2 == 0, "tile layout assumes 32 rows and whole chunk pairs");
+  static_assert(TK == 32 && RCH % 8 == 0, "tile layout assumes 32 rows and whole 128-byte lines");
   __shared__ __attribute__((aligned(1024))) bf16 tile[2][TBLK * 512];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q4 = lane >> 4;
-  // k chunk of lane group q4 within a 32-wide k step: 0, 2, 1, 3, so that the
-  // two lane groups of one 16-byte LDS read pass (q4 = 2h, 2h + 1) read chunks
-  // of the same parity
-  const int qc = ((q4 & 1) << 1) | (q4 >> 1);
   const int B = a.B;
   const PlanView pv = plan_view(a.plan, B);
   const int T = __builtin_amdgcn_readfirstlane(a.plan[0]);
@@ -552,7 +553,9 @@ dec_attn_kernel(DecAttnArgs a) {
   const int tb = (int)((int64_t)k * T / nw), te = (int)((int64_t)(k + 1) * T / nw);
   const int h = wave * 16 + r16;
   const bool hok = h < a.H;
-  const int lrow = (lane & 31) ^ ((lane >> 5) << 3);  // row this lane fetches (chunk parity lane >> 5)
+  // in a block load, lane l fetches row l >> 3 of the block and chunk
+  // (l & 7) ^ ((l >> 3) & 6) of its line, which lands in slot l
+  const int lrow = lane >> 3, lch = (lane & 7) ^ ((lane >> 3) & 6);
   struct Seq {
     int b, tend, row0, rend;   // tiles < tend; tile t starts at row row0 + TK t; rows < rend attended
     const bf16* base;
@@ -571,17 +574,34 @@ dec_attn_kernel(DecAttnArgs a) {
     return q;
   };
   auto load_tile = [&](const Seq& q, int t, int buf) {
-    const int key = min(q.row0 + TK * t + lrow, q.rend - 1);   // rows past the end repeat a valid row (masked)
-    const bf16* src = q.base + (int64_t)key * RL + 8 * (lane >> 5);
+    const bf16* src[4];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {   // rows past the end repeat a valid row (masked)
+      const int key = min(q.row0 + TK * t + 8 * rg + lrow, q.rend - 1);
+      src[rg] = q.base + (int64_t)key * RL + 8 * lch;
+    }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int blk = wave + NW * i;
-      if (blk < TBLK) g2lds16_explicit(src + 16 * blk, &tile[buf][blk * 512]);
+      const int blk = wave + NW * i;   // compile-time row group and line of each block
+      if (blk < TBLK) g2lds16_stream(src[blk & 3] + 64 * (blk >> 2), &tile[buf][blk * 512]);
     }
   };
+  // per-lane LDS slots of the fragment reads (16-byte units, block offsets added per read)
+  int kslot[2], pslot[4];
+  {
+    const int x = r16 & 7;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) kslot[p] = 64 * (r16 >> 3) + 8 * x + ((4 * p + q4) ^ (x & 6));
+    const int R = 4 * q4 + (r16 >> 2), xr = R & 7, pc = (r16 >> 1) & 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pslot[j] = 64 * (R >> 3) + 8 * xr + ((2 * j + pc) ^ (xr & 6));
+    // the transposed reads take the 8-byte half r16 & 1 of the slot
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pslot[j] = 2 * pslot[j] + (r16 & 1);
+  }
   bf16x8 qf[KS];
   auto load_q = [&](int b) {
-    const bf16* qp = a.qlat + ((int64_t)b * a.H + (hok ? h : 0)) * RL + 8 * qc;
+    const bf16* qp = a.qlat + ((int64_t)b * a.H + (hok ? h : 0)) * RL + 8 * q4;
     const bf16x8 zero8 = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = hok ? *reinterpret_cast<const bf16x8*>(qp + 32 * s) : zero8;
@@ -619,12 +639,15 @@ dec_attn_kernel(DecAttnArgs a) {
     const int r0 = cs.row0 + TK * t;
     // scores S^T: lane holds head r16, tile rows 16 u + 4 q4 + j
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
-    const bf16* kbase = Tl + (32 * qc + (r16 ^ (8 * (qc & 1)))) * 8;   // chunk 4 s + qc, row 16 u + r16
+    // lane reads chunk 4 s + q4 of row 16 u + r16: block 4 (s >> 1) + 2 u + (r16 >> 3),
+    // slot 8 x + ((4 (s & 1) + q4) ^ (x & 6)) with x = r16 & 7
+    const bf16* kb0 = Tl + kslot[0] * 8;
+    const bf16* kb1 = Tl + kslot[1] * 8;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kbase + (128 * s + 16 * u) * 8);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>((s & 1 ? kb1 : kb0) + (256 * (s >> 1) + 128 * u) * 8);
         sacc[u] = mfma16(kf, qf[s], sacc[u]);
       }
       if (s % 6 == 5) __builtin_amdgcn_sched_barrier(0);   // bounds the LDS reads in flight (registers)
@@ -658,13 +681,12 @@ dec_attn_kernel(DecAttnArgs a) {
         pf[4 * u + j] = (bf16)p;
       }
     // O^T += C^T P: A operand = cache tile read transposed (dims x rows); lane
-    // reads 4 values of row 4 q4 + (r16 >> 2) (and that + 16), columns 16 d + 4 (r16 & 3)
-    const int pc = (r16 >> 1) & 1;
-    const bf16* pbase = Tl + (32 * pc + ((4 * q4 + (r16 >> 2)) ^ (8 * pc))) * 8 + 4 * (r16 & 1);
+    // reads 4 values of row 4 q4 + (r16 >> 2) (and that + 16), columns 16 d + 4 (r16 & 3),
+    // i.e. half r16 & 1 of chunk 2 d + ((r16 >> 1) & 1)
 #pragma unroll
     for (int d = 0; d < DT; ++d) {
-      const bf16* p0 = pbase + 512 * d;
-      o[d] = mfma16(tr_pair(p0, p0 + 128), pf, o[d]);
+      const bf16* p0 = Tl + pslot[d & 3] * 4 + 2048 * (d >> 2);
+      o[d] = mfma16(tr_pair(p0, p0 + 1024), pf, o[d]);
       if (d % 8 == 7) __builtin_amdgcn_sched_barrier(0);
     }
     if (t + 1 == te || t + 1 >= cs.tend) {
