@@ -408,13 +408,14 @@ absorb_kernel(AbsorbArgs a) {
 // Plan layout (int32): [0] T, [1] number of segments, tstart[B + 1] (first
 // tile of each sequence), lo[B] (first attended row), len[B] (attended rows),
 // coff[B + 1] (first segment of each sequence), kf[B] (workgroup of the
-// sequence's first tile).
+// sequence's first tile), wgb[DEC_WGS] (sequence of each workgroup's first
+// tile, so that a workgroup finds it with one load).
 constexpr int DEC_WGS = 512, DEC_TK = 32;   // two latent-attention workgroups per CU
 
-size_t plan_ints(int B) { return 5 * (size_t)B + 4; }
+size_t plan_ints(int B) { return 5 * (size_t)B + 4 + DEC_WGS; }
 
 struct PlanView {
-  const int *tstart, *lo, *len, *coff, *kf;
+  const int *tstart, *lo, *len, *coff, *kf, *wgb;
 };
 __device__ __forceinline__ PlanView plan_view(const int* P, int B) {
   PlanView v;
@@ -423,6 +424,7 @@ __device__ __forceinline__ PlanView plan_view(const int* P, int B) {
   v.len = v.lo + B;
   v.coff = v.len + B;
   v.kf = v.coff + B + 1;
+  v.wgb = v.kf + B;
   return v;
 }
 
@@ -503,6 +505,24 @@ plan_kernel(const int32_t* lens, int B, int cap, int window, int* plan) {
     coff[B] = scarry;
     plan[0] = T;
     plan[1] = scarry;
+  }
+  // pass 3: the sequence of each workgroup's first tile: the last b with
+  // tstart[b] <= that tile (sequences without tiles share the next one's start)
+  __syncthreads();
+  int* wgb = kf + B;
+  const int W = dec_wgs(T);
+  for (int w = tid; w < DEC_WGS; w += 256) {
+    int bsel = 0;
+    if (w < W) {
+      const int t0 = (int)((int64_t)w * T / W);
+      int lo_b = 0, hi_b = B - 1;
+      while (lo_b < hi_b) {
+        const int mid = (lo_b + hi_b + 1) >> 1;
+        if (tstart[mid] <= t0) lo_b = mid; else hi_b = mid - 1;
+      }
+      bsel = lo_b;
+    }
+    wgb[w] = bsel;
   }
 }
 
@@ -611,14 +631,11 @@ dec_attn_kernel(DecAttnArgs a) {
     vm_wait<0>();
   };
 
-  // first sequence: the last b with tstart[b] <= tb
-  int bl = 0, bh = B - 1;
-  while (bl < bh) {
-    const int mid = (bl + bh + 1) >> 1;
-    if (pv.tstart[mid] <= tb) bl = mid; else bh = mid - 1;
-  }
-  bl = __builtin_amdgcn_readfirstlane(bl);
+  // first sequence (the plan's pass 3)
+  const int bl = __builtin_amdgcn_readfirstlane(pv.wgb[k]);
   Seq ls = seq_at(bl), cs = ls;
+  // the first tile and the query fragment are in flight together (load_q waits for both)
+  load_tile(ls, tb, 0);
   load_q(cs.b);
   f32x4 o[DT];
 #pragma unroll
@@ -626,8 +643,6 @@ dec_attn_kernel(DecAttnArgs a) {
   float m = NEG_INIT, lsum = 0.f;
   const float sc = a.scale_log2;
 
-  load_tile(ls, tb, 0);
-  vm_wait<0>();
   __syncthreads();
   int buf = 0;
   for (int t = tb; t < te; ++t) {
