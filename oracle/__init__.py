@@ -5,9 +5,9 @@ import it; the HIP library never does."""
 from .gdla_ref import (Cfg, attention_heads, attended_keys, differential_gate_out, gdla_block,
                        gdla_decode, gdla_layer, hybrid_windows, kv_head_of, latent_expand,
                        kv_tokens, latent_expand_from_norm, linear, project_tokens, query_tokens, rms_norm, rope,
-                       rope_inv_freq, sigmoid)
+                       rope_inv_freq, rope_params, sigmoid, yarn_inv_freq, yarn_mscale)
 
 __all__ = ["Cfg", "attention_heads", "attended_keys", "differential_gate_out", "gdla_block",
            "gdla_decode", "gdla_layer", "hybrid_windows", "kv_head_of", "latent_expand",
            "kv_tokens", "latent_expand_from_norm", "linear", "project_tokens", "query_tokens", "rms_norm", "rope",
-           "rope_inv_freq", "sigmoid"]
+           "rope_inv_freq", "rope_params", "sigmoid", "yarn_inv_freq", "yarn_mscale"]

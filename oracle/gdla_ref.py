@@ -37,6 +37,14 @@ report has no headings, so its paragraphs are named by topic):
   [OSM-impl] same page, implementation section: frequencies duplicated as
              cat(freqs, freqs) and the rotate-half application
              x*cos + rotate_half(x)*sin.
+  [OSM-yarn] same page, section 2 and the implementation section: YaRN
+             scales each rotary frequency by 1, 1/s or a ramp between them,
+             chosen by its wavelength against the native context length over
+             beta_fast and beta_slow, and corrects the softmax temperature by
+             m = 1 + 0.1 ln s, which the listing multiplies into cos and sin.
+  [M3-ctx]   "Motif 3: Technical Report", long-context paragraph: the
+             full-attention layers extend the native 4K context by a factor of
+             64 with YaRN; the sliding-window layers keep plain RoPE.
 
 Readings where the pages are silent (each listed in the design notes):
 RMSNorm with a learned gain for both latents; eps = cfg rms_eps; rotate-half
@@ -47,7 +55,11 @@ one rotary key per token shared by every head; softmax scale
 signal head j and noise head j//g both use KV head j//g; window W means keys
 s with t - W < s <= t (W <= 0 or W >= L: full causal); no biases; weights are
 [out, in] (y = x W^T); W_UKV rows are all content-key heads then all value
-heads.
+heads.  YaRN (when cfg.yarn_factor > 1, full-causal layers only): the
+frequency table and the cos/sin multiplier m of the listing in [OSM-yarn],
+applied to the rotary parts, so the rotary part of every logit scales by m^2
+(the page's prose writes the temperature as sqrt(1 + 0.1 ln s) on the logits;
+the listing is the executable statement and is the reading taken).
 
 Every function works in float64 on whatever it is given (inputs are widened
 with np.asarray(..., float64)); nothing is rounded to bf16 here.
@@ -76,6 +88,10 @@ class Cfg:
     window: int = 0   # <= 0: full causal
     rope_base: float = 10000.0
     rms_eps: float = 1e-6
+    yarn_factor: float = 0.0     # s; <= 1: plain RoPE
+    yarn_orig_len: int = 4096    # native context length
+    yarn_beta_fast: float = 32.0
+    yarn_beta_slow: float = 1.0
 
     @property
     def n_signal(self) -> int:
@@ -132,18 +148,54 @@ def rope_inv_freq(d_rope, base):
     return np.power(float(base), -2.0 * i / d_rope)
 
 
-def rope(u, pos, base):
+def yarn_inv_freq(d_rope, base, s, orig_len, beta_fast, beta_slow):
+    """YaRN frequencies ([OSM-yarn]).  With lambda_i = 2 pi / theta_i the
+    wavelength of pair i, the short-wavelength bound orig_len / beta_fast and
+    the long one orig_len / beta_slow, ramp_i is lambda_i's position between
+    the two bounds clamped to [0, 1], and the frequency becomes
+    (1 - ramp_i) theta_i + ramp_i theta_i / s: unchanged below the short
+    bound, divided by s above the long one."""
+    theta = rope_inv_freq(d_rope, base)
+    wavelength = 2.0 * math.pi / theta
+    short, long_ = orig_len / beta_fast, orig_len / beta_slow
+    ramp = np.clip((wavelength - short) / (long_ - short), 0.0, 1.0)
+    return (1.0 - ramp) * theta + ramp * theta / s
+
+
+def yarn_mscale(s):
+    """The listing's temperature correction m = 1 + 0.1 ln s ([OSM-yarn])."""
+    return 1.0 + 0.1 * math.log(s)
+
+
+def rope_params(cfg: Cfg):
+    """(base, yarn) for rope(): yarn is None for plain RoPE, else
+    (s, orig_len, beta_fast, beta_slow).  YaRN only on full-causal layers
+    ([M3-ctx])."""
+    if cfg.yarn_factor > 1.0 and cfg.window <= 0:
+        return cfg.rope_base, (float(cfg.yarn_factor), float(cfg.yarn_orig_len),
+                               float(cfg.yarn_beta_fast), float(cfg.yarn_beta_slow))
+    return cfg.rope_base, None
+
+
+def rope(u, pos, base, yarn=None):
     """Rotate-half RoPE ([OSM-impl]) of u[..., T, d_rope] at positions pos[T].
 
     For each i < d_rope/2 the pair (u_i, u_{i+d/2}) is rotated by angle
     pos * theta_i:  u_i' = u_i cos - u_{i+d/2} sin,
                     u_{i+d/2}' = u_{i+d/2} cos + u_i sin.
+    With yarn = (s, orig_len, beta_fast, beta_slow) the frequencies are YaRN's
+    and cos, sin carry the factor m = 1 + 0.1 ln s ([OSM-yarn]).
     """
     u = _f64(u)
     d = u.shape[-1]
     half = d // 2
-    ang = _f64(pos)[:, None] * rope_inv_freq(d, base)[None, :]      # [T, d/2]
-    cos, sin = np.cos(ang), np.sin(ang)
+    if yarn is None:
+        inv, m = rope_inv_freq(d, base), 1.0
+    else:
+        s_, orig, bf, bs = yarn
+        inv, m = yarn_inv_freq(d, base, s_, orig, bf, bs), yarn_mscale(s_)
+    ang = _f64(pos)[:, None] * inv[None, :]      # [T, d/2]
+    cos, sin = m * np.cos(ang), m * np.sin(ang)
     u1, u2 = u[..., :half], u[..., half:]
     return np.concatenate([u1 * cos - u2 * sin, u2 * cos + u1 * sin], axis=-1)
 
@@ -189,7 +241,7 @@ def kv_tokens(x, W, cfg: Cfg, pos):
     x [T, d_model], pos [T].  Returns (ckvn [T, kv_rank], kr [T, d_rope])."""
     ckv_kr = linear(x, W["w_dkv"])
     ckvn = rms_norm(ckv_kr[:, :cfg.kv_rank], W["g_kv"], cfg.rms_eps)
-    kr = rope(ckv_kr[:, cfg.kv_rank:], pos, cfg.rope_base)
+    kr = rope(ckv_kr[:, cfg.kv_rank:], pos, *rope_params(cfg))
     return ckvn, kr
 
 
@@ -201,7 +253,7 @@ def query_tokens(x, W, cfg: Cfg, pos):
     T = x.shape[0]
     cqn = rms_norm(linear(x, W["w_dq"]), W["g_q"], cfg.rms_eps)
     q = linear(cqn, W["w_uq"]).reshape(T, cfg.n_heads, cfg.d_qk)
-    q_rot = rope(np.transpose(q[:, :, cfg.d_nope:], (1, 0, 2)), pos, cfg.rope_base)
+    q_rot = rope(np.transpose(q[:, :, cfg.d_nope:], (1, 0, 2)), pos, *rope_params(cfg))
     q = np.concatenate([q[:, :, :cfg.d_nope], np.transpose(q_rot, (1, 0, 2))], axis=-1)
     lam = sigmoid(linear(x, W["w_lambda"]))
     gate = sigmoid(linear(cqn, W["w_gate"]))

@@ -419,4 +419,76 @@ def pin_hybrid_schedule():
     assert R.hybrid_windows(8, 128) == [0, 128, 128, 128, 0, 128, 128, 128]
 
 
+# YaRN ([OSM-yarn]) with the long-context settings of [M3-ctx]: factor 64 over
+# a native 4096, beta_fast 32, beta_slow 1, on a 64-wide rotary part, base 1e4.
+YARN = (64.0, 4096.0, 32.0, 1.0)
+
+
+def pin_yarn_identity_at_factor_one():
+    """s = 1 is plain RoPE: no frequency moves and m = 1 + 0.1 ln 1 = 1."""
+    th = R.rope_inv_freq(64, 1e4)
+    assert np.max(np.abs(R.yarn_inv_freq(64, 1e4, 1.0, 4096.0, 32.0, 1.0) / th - 1.0)) < 1e-15
+    assert R.yarn_mscale(1.0) == 1.0
+    u = np.random.Generator(np.random.PCG64(3)).standard_normal((5, 64))
+    pos = np.array([0.0, 1.0, 17.0, 4095.0, 70000.0])
+    close(R.rope(u, pos, 1e4, (1.0, 4096.0, 32.0, 1.0)), R.rope(u, pos, 1e4), 1e-12)
+
+
+def pin_yarn_bands_and_values():
+    """Pair i has wavelength 2 pi 10^(i/8).  It is below 4096/32 = 128 exactly
+    for i <= 10 (10^(10/8) = 17.8 < 20.37 < 10^(11/8) = 23.7), so those
+    frequencies are unchanged; it is above 4096 exactly for i >= 23
+    (10^(22/8) = 562 < 651.9 < 10^(23/8) = 750), so those are divided by 64.
+    Pair 16 (wavelength 200 pi = 628.32) sits at (628.32 - 128) / 3968 =
+    0.126088 of the ramp: 0.01 (0.873912 + 0.126088 / 64) = 0.0087588179.
+    m = 1 + 0.1 ln 64 = 1.4158883083."""
+    th = R.rope_inv_freq(64, 1e4)
+    y = R.yarn_inv_freq(64, 1e4, *YARN)
+    assert [i for i in range(32) if y[i] == th[i]] == list(range(11))
+    assert [i for i in range(32) if abs(y[i] * 64.0 / th[i] - 1.0) < 1e-12] == list(range(23, 32))
+    assert abs(y[16] - 0.0087588179) < 1e-10, y[16]
+    assert abs(R.yarn_mscale(64.0) - 1.4158883083) < 1e-10
+    assert np.all(np.diff(y) < 0)
+
+
+def pin_yarn_is_rope_at_scaled_positions():
+    """Each rotary pair turns on its own, so a vector living in the high band
+    (pairs <= 10) rotates like plain RoPE at position p and one in the low
+    band (pairs >= 23) like plain RoPE at p / 64, both times m."""
+    rng = np.random.Generator(np.random.PCG64(4))
+    pos = np.array([0.0, 5.0, 4096.0, 100000.0, 262143.0])
+    m = 1.0 + 0.1 * math.log(64.0)
+    for pairs, scale in ((range(0, 11), 1.0), (range(23, 32), 1.0 / 64.0)):
+        u = np.zeros((5, 64))
+        for i in pairs:
+            u[:, i] = rng.standard_normal(5)
+            u[:, 32 + i] = rng.standard_normal(5)
+        close(R.rope(u, pos, 1e4, YARN), m * R.rope(u, pos * scale, 1e4), 1e-9)
+
+
+def pin_yarn_relative_and_norm():
+    """Fixed frequencies keep <rope(q, a), rope(k, b)> a function of a - b;
+    the rotated vectors are m times as long."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    q, k = rng.standard_normal((1, 64)), rng.standard_normal((1, 64))
+    a = float((R.rope(q, np.array([9000.0]), 1e4, YARN) @ R.rope(k, np.array([1000.0]), 1e4, YARN).T)[0, 0])
+    b = float((R.rope(q, np.array([8000.0]), 1e4, YARN) @ R.rope(k, np.array([0.0]), 1e4, YARN).T)[0, 0])
+    assert abs(a - b) < 1e-9 * max(1.0, abs(a))
+    m = 1.0 + 0.1 * math.log(64.0)
+    r = R.rope(q, np.array([123456.0]), 1e4, YARN)
+    assert abs(np.linalg.norm(r) - m * np.linalg.norm(q)) < 1e-12 * np.linalg.norm(q) * 10
+
+
+def pin_yarn_full_layers_only():
+    """[M3-ctx]: YaRN on the full-causal layers; a windowed layer with the
+    same settings equals the plain-RoPE layer, a full one does not."""
+    W = tiny_weights()
+    x = tiny_x(B=1, L=7)
+    yarn_cfg = replace(TINY, yarn_factor=64.0, yarn_orig_len=4, yarn_beta_fast=2.0, yarn_beta_slow=0.5)
+    win = R.gdla_layer(x, W, replace(yarn_cfg, window=3))["y"]
+    close(win, R.gdla_layer(x, W, replace(TINY, window=3))["y"], 1e-12)
+    full = R.gdla_layer(x, W, yarn_cfg)["y"]
+    assert np.max(np.abs(full - R.gdla_layer(x, W, TINY)["y"])) > 1e-6
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

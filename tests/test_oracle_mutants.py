@@ -11,7 +11,7 @@ import oracle.gdla_ref as R
 from tests import oracle_pins as P
 
 
-def _rope_wrong_sign(u, pos, base):
+def _rope_wrong_sign(u, pos, base, yarn=None):
     u = np.asarray(u, np.float64)
     half = u.shape[-1] // 2
     ang = np.asarray(pos, np.float64)[:, None] * R.rope_inv_freq(u.shape[-1], base)[None, :]
@@ -20,7 +20,7 @@ def _rope_wrong_sign(u, pos, base):
     return np.concatenate([u1 * c + u2 * s, u2 * c - u1 * s * 0.5], axis=-1)
 
 
-def _rope_adjacent_pairs(u, pos, base):
+def _rope_adjacent_pairs(u, pos, base, yarn=None):
     u = np.asarray(u, np.float64)
     d = u.shape[-1]
     ang = np.asarray(pos, np.float64)[:, None] * R.rope_inv_freq(d, base)[None, :]
@@ -160,6 +160,34 @@ def _hybrid_last_full(n, w):
     return [0 if (l % 4) == 3 else int(w) for l in range(n)]
 
 
+_orig_yif = R.yarn_inv_freq
+
+
+def _yarn_ramp_reversed(d, base, s, orig, bf, bs):
+    # interpolate the short wavelengths instead of the long ones
+    th = R.rope_inv_freq(d, base)
+    y = _orig_yif(d, base, s, orig, bf, bs)
+    ramp = (th - y) / (th - th / s)
+    return ramp * th + (1.0 - ramp) * th / s
+
+
+def _yarn_times_s(d, base, s, orig, bf, bs):
+    th = R.rope_inv_freq(d, base)
+    ramp = (th - _orig_yif(d, base, s, orig, bf, bs)) / (th - th / s)
+    return (1.0 - ramp) * th + ramp * th * s
+
+
+def _yarn_mscale_sqrt(s):
+    return math.sqrt(1.0 + 0.1 * math.log(s))
+
+
+def _rope_params_every_layer(cfg):
+    if cfg.yarn_factor > 1.0:
+        return cfg.rope_base, (float(cfg.yarn_factor), float(cfg.yarn_orig_len),
+                               float(cfg.yarn_beta_fast), float(cfg.yarn_beta_slow))
+    return cfg.rope_base, None
+
+
 MUTANTS = {
     "rope_wrong_sign": ("rope", _rope_wrong_sign),
     "rope_adjacent_pairs": ("rope", _rope_adjacent_pairs),
@@ -182,6 +210,10 @@ MUTANTS = {
     "linear_transposed": ("linear", _linear_transposed),
     "latent_expand_swapped": ("latent_expand", _latent_expand_swapped),
     "hybrid_last_full": ("hybrid_windows", _hybrid_last_full),
+    "yarn_ramp_reversed": ("yarn_inv_freq", _yarn_ramp_reversed),
+    "yarn_times_s": ("yarn_inv_freq", _yarn_times_s),
+    "yarn_mscale_sqrt": ("yarn_mscale", _yarn_mscale_sqrt),
+    "yarn_on_window_layers": ("rope_params", _rope_params_every_layer),
 }
 
 
