@@ -60,6 +60,11 @@ gdla_status check_config(const gdla_config* c) {
   if (c->d_rope % 2) return fail(GDLA_ERR_INVALID_ARG, "d_rope must be even (got %d)", c->d_rope);
   if (!(c->rope_base > 0.f) || !std::isfinite(c->rope_base)) return fail(GDLA_ERR_INVALID_ARG, "rope_base must be positive");
   if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps)) return fail(GDLA_ERR_INVALID_ARG, "rms_eps must be >= 0");
+  if (std::isnan(c->yarn_factor)) return fail(GDLA_ERR_INVALID_ARG, "yarn_factor is NaN");
+  if (c->yarn_factor > 1.f &&
+      !(std::isfinite(c->yarn_factor) && c->yarn_orig_len > 0 && std::isfinite(c->yarn_beta_fast) &&
+        c->yarn_beta_slow > 0.f && c->yarn_beta_fast > c->yarn_beta_slow))
+    return fail(GDLA_ERR_INVALID_ARG, "YaRN needs a finite factor, yarn_orig_len > 0 and beta_fast > beta_slow > 0");
   const int64_t H = (int64_t)c->group * c->n_noise + c->n_noise;
   if (H * (c->d_nope + c->d_rope) > (1 << 24)) return fail(GDLA_ERR_INVALID_ARG, "too many query heads");
   if (c->dtype == GDLA_BF16) {
@@ -132,7 +137,7 @@ const char* gdla_status_string(gdla_status s) {
 
 const char* gdla_last_error(void) { return g_err; }
 
-int32_t gdla_version(void) { return 100; }
+int32_t gdla_version(void) { return 101; }   // 1.01: YaRN fields in gdla_config
 
 size_t gdla_prefill_workspace_size(const gdla_config* cfg, int32_t B, int32_t L) {
   if (check_config(cfg) != GDLA_OK || B < 0 || L < 0) return 0;
@@ -212,7 +217,9 @@ gdla_status gdla_prefill_stages(const gdla_config* cfg, const gdla_weights* w, i
     r.down = (const float*)(ws + P.down); r.ld_down = D.ndown;
     r.T = T; r.L = L; r.pos_offset = pos_offset;
     r.q_rank = (int)D.rq; r.kv_rank = (int)D.rkv; r.d_rope = (int)D.dr; r.nS = (int)D.nS;
-    r.g_q = w->g_q; r.g_kv = w->g_kv; r.eps = cfg->rms_eps; r.rope_base = cfg->rope_base;
+    r.g_q = w->g_q; r.g_kv = w->g_kv; r.eps = cfg->rms_eps;
+    set_rope(r, cfg->rope_base, cfg->window, cfg->yarn_factor, cfg->yarn_orig_len, cfg->yarn_beta_fast,
+             cfg->yarn_beta_slow);
     r.cqn = ws + P.cqn; r.ckvn = ws + P.ckvn; r.kr = ws + P.kr; r.lam = (float*)(ws + P.lam);
     r.rope = (float*)(ws + P.rope); r.cache = cache; r.cache_cap = cache_capacity;
     r.split_kv = bf;

@@ -908,7 +908,8 @@ hipError_t decode_step(const gdla_config* c, const gdla_weights* w, int B, const
     RowPrepArgs r{};
     r.down = (const float*)(ws + Lw.down); r.ld_down = ndown; r.nsplit = sp_down; r.split_stride = (int64_t)B * ndown;
     r.T = B; r.L = 1; r.q_rank = rq; r.kv_rank = rkv; r.d_rope = DR; r.nS = nS;
-    r.g_q = w->g_q; r.g_kv = w->g_kv; r.eps = c->rms_eps; r.rope_base = c->rope_base;
+    r.g_q = w->g_q; r.g_kv = w->g_kv; r.eps = c->rms_eps;
+    set_rope(r, c->rope_base, c->window, c->yarn_factor, c->yarn_orig_len, c->yarn_beta_fast, c->yarn_beta_slow);
     r.cqn = ws + Lw.cqn; r.ckvn = ws + Lw.ckvn; r.kr = ws + Lw.kr; r.lam = (float*)(ws + Lw.lam);
     r.rope = (float*)(ws + Lw.rope); r.cache = cache; r.cache_cap = capacity; r.pos_dev = cache_lens;
     if ((err = rowprep(r, true, s)) != hipSuccess) return err;

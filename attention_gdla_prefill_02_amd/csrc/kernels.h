@@ -49,6 +49,7 @@ struct RowPrepArgs {
   int q_rank, kv_rank, d_rope, nS;
   const void* g_q; const void* g_kv;
   float eps; double rope_base;
+  double yarn_s, yarn_short, yarn_long, yarn_m;   // YaRN (yarn_s > 1): wavelength bounds and cos/sin factor
   void* cqn; void* ckvn; void* kr; float* lam; float* rope;
   bool split_kv;                         // ckvn rows are [hi | lo] (2*kv_rank wide)
   void* cache; int cache_cap;            // nullable
@@ -57,6 +58,9 @@ struct RowPrepArgs {
   int nsplit; int64_t split_stride;      // down holds nsplit partial sums (elements apart); 0/1 = one
 };
 hipError_t rowprep(const RowPrepArgs& a, bool bf16, hipStream_t s);
+// RoPE fields of the row prep: base, and YaRN when factor > 1 on a full-causal layer
+void set_rope(RowPrepArgs& r, double base, int window, float yarn_factor, int yarn_orig_len, float beta_fast,
+              float beta_slow);
 
 struct LatentNormArgs {
   const void* c; int64_t ldc; int64_t T; int kv_rank;

@@ -16,6 +16,25 @@
 #include "kernels.h"
 
 namespace gdla {
+
+// cos and sin of pair i at position p (fp64 angle): theta_i = base^(-2i/d_rope),
+// or its YaRN form (wavelength ramp between yarn_short and yarn_long, factor
+// yarn_m on cos and sin; "Open-Source Frontier Models: Architecture and
+// Benchmarks of Rnj-1 and Motif-2", YaRN section)
+__device__ __forceinline__ void rope_cos_sin(const RowPrepArgs& a, int i, int64_t p, float* c, float* s) {
+  double theta = pow(a.rope_base, -2.0 * (double)i / (double)a.d_rope);
+  double mul = 1.0;
+  if (a.yarn_s > 1.0) {
+    const double wavelength = 6.283185307179586 / theta;
+    const double ramp = fmin(fmax((wavelength - a.yarn_short) / (a.yarn_long - a.yarn_short), 0.0), 1.0);
+    theta = (1.0 - ramp) * theta + ramp * theta / a.yarn_s;
+    mul = a.yarn_m;
+  }
+  double sd, cd;
+  sincos((double)p * theta, &sd, &cd);
+  *c = (float)(cd * mul);
+  *s = (float)(sd * mul);
+}
 namespace {
 
 template <class T>
@@ -85,10 +104,8 @@ rowprep_kernel(RowPrepArgs a) {
   const int half = a.d_rope / 2;
   T* krow = (T*)a.kr + t * a.d_rope;
   for (int i = lane; i < half; i += 64) {
-    const double theta = pow(a.rope_base, -2.0 * (double)i / (double)a.d_rope);
-    double sd, cd;
-    sincos((double)p * theta, &sd, &cd);
-    const float c = (float)cd, s = (float)sd;
+    float c, s;
+    rope_cos_sin(a, i, p, &c, &s);
     a.rope[(t * half + i) * 2] = c;
     a.rope[(t * half + i) * 2 + 1] = s;
     const float x1 = kr[i], x2 = kr[i + half];
@@ -183,10 +200,8 @@ rowprep_block_kernel(RowPrepArgs a) {
   const int half = a.d_rope / 2;
   T* krow = (T*)a.kr + t * a.d_rope;
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    const double theta = pow(a.rope_base, -2.0 * (double)i / (double)a.d_rope);
-    double sd, cd;
-    sincos((double)p * theta, &sd, &cd);
-    const float c = (float)cd, s = (float)sd;
+    float c, s;
+    rope_cos_sin(a, i, p, &c, &s);
     a.rope[(t * half + i) * 2] = c;
     a.rope[(t * half + i) * 2 + 1] = s;
     const float x1 = kr[i], x2 = kr[i + half];
@@ -255,6 +270,18 @@ hipError_t latent_norm(const LatentNormArgs& a, bool bf16, hipStream_t s) {
   else
     hipLaunchKernelGGL(latent_norm_kernel<float>, grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+void set_rope(RowPrepArgs& r, double base, int window, float yarn_factor, int yarn_orig_len, float beta_fast,
+              float beta_slow) {
+  r.rope_base = base;
+  r.yarn_s = 0.0;
+  if (yarn_factor > 1.f && window <= 0) {   // full-causal layers only
+    r.yarn_s = yarn_factor;
+    r.yarn_short = (double)yarn_orig_len / beta_fast;
+    r.yarn_long = (double)yarn_orig_len / beta_slow;
+    r.yarn_m = 1.0 + 0.1 * std::log((double)yarn_factor);
+  }
 }
 
 }  // namespace gdla

@@ -35,7 +35,9 @@ class Config(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("q_rank", ctypes.c_int32), ("kv_rank", ctypes.c_int32),
                 ("n_noise", ctypes.c_int32), ("group", ctypes.c_int32), ("d_nope", ctypes.c_int32),
                 ("d_rope", ctypes.c_int32), ("d_v", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int)]
+                ("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int),
+                ("yarn_factor", ctypes.c_float), ("yarn_orig_len", ctypes.c_int32),
+                ("yarn_beta_fast", ctypes.c_float), ("yarn_beta_slow", ctypes.c_float)]
 
 
 WEIGHT_FIELDS = ("w_dq", "g_q", "w_dkv", "g_kv", "w_lambda", "w_uq", "w_ukv", "w_gate", "w_o")
@@ -103,10 +105,14 @@ def _stream(stream=None):
 
 
 def make_config(shapes: dict, window: int = 0, dtype: str = "bf16", rope_base: float = 10000.0,
-                rms_eps: float = 1e-6) -> Config:
+                rms_eps: float = 1e-6, yarn=None) -> Config:
+    """yarn: None, or (factor, orig_len, beta_fast, beta_slow); the library
+    applies it on full-causal layers (window <= 0) only."""
+    yf, yl, ybf, ybs = (0.0, 0, 0.0, 0.0) if not yarn else yarn
     return Config(shapes["d_model"], shapes["q_rank"], shapes["kv_rank"], shapes["n_noise"], shapes["group"],
                   shapes["d_nope"], shapes["d_rope"], shapes["d_v"], int(window), float(rope_base),
-                  float(rms_eps), GDLA_BF16 if dtype == "bf16" else GDLA_FP32)
+                  float(rms_eps), GDLA_BF16 if dtype == "bf16" else GDLA_FP32,
+                  float(yf), int(yl), float(ybf), float(ybs))
 
 
 def weights_struct(W: dict) -> Weights:

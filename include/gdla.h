@@ -85,6 +85,21 @@ typedef struct {
   float rope_base;   /* RoPE base, e.g. 10000 */
   float rms_eps;     /* RMSNorm epsilon, e.g. 1e-6 */
   gdla_dtype dtype;  /* one dtype for x, y, weights, gains and cache */
+  /* YaRN extension of the rotary frequencies ("Open-Source Frontier Models:
+   * Architecture and Benchmarks of Rnj-1 and Motif-2", YaRN section and its
+   * listing; the Motif 3 report's long-context paragraph uses it, factor 64
+   * over a native 4K, on its full-attention layers).  Applied when
+   * yarn_factor > 1 and window <= 0 (full-causal layers only); zero-filled
+   * fields mean plain RoPE.  Pair i of wavelength l_i = 2 pi / theta_i keeps
+   * theta_i below yarn_orig_len / yarn_beta_fast, becomes theta_i / s above
+   * yarn_orig_len / yarn_beta_slow and is interpolated linearly in l_i in
+   * between; cos and sin are multiplied by m = 1 + 0.1 ln s, so the rotary
+   * part of every logit scales by m^2.  Invalid when yarn_factor > 1 unless
+   * yarn_orig_len > 0 and yarn_beta_fast > yarn_beta_slow > 0. */
+  float yarn_factor;       /* s */
+  int32_t yarn_orig_len;   /* native context length */
+  float yarn_beta_fast;
+  float yarn_beta_slow;
 } gdla_config;
 
 typedef struct {          /* device pointers, all [out, in] row-major, dtype of the config */

@@ -50,7 +50,7 @@ def test_status_strings_and_version():
     L = lib()
     assert L.gdla_status_string(0) == b"GDLA_OK"
     assert L.gdla_status_string(3) == b"GDLA_ERR_WORKSPACE"
-    assert L.gdla_version() >= 100
+    assert L.gdla_version() >= 101
 
 
 def _cfg(**kw):
@@ -108,6 +108,25 @@ def test_prefill_rejects_bad_arguments():
     assert call_prefill(bad, w)[0] == gdla.GDLA_ERR_INVALID_ARG
     st = lib().gdla_prefill(None, ctypes.byref(w), 1, 1, 0, 0x100000, 0x200000, None, None, 0, 0x300000, 1 << 30, None)
     assert st == gdla.GDLA_ERR_INVALID_ARG
+
+
+def test_yarn_settings_validated():
+    w = FakeW().struct()
+    ok = _cfg()
+    ok.yarn_factor, ok.yarn_orig_len, ok.yarn_beta_fast, ok.yarn_beta_slow = 64.0, 4096, 32.0, 1.0
+    assert call_prefill(ok, w, B=0, x=0, y=0, ws=0)[0] == gdla.GDLA_OK
+    assert lib().gdla_prefill_workspace_size(ctypes.byref(ok), 1, 16) > 0
+    for field, value in (("yarn_orig_len", 0), ("yarn_beta_slow", 0.0), ("yarn_beta_fast", 0.5),
+                         ("yarn_factor", float("nan")), ("yarn_factor", float("inf"))):
+        bad = _cfg()
+        bad.yarn_factor, bad.yarn_orig_len, bad.yarn_beta_fast, bad.yarn_beta_slow = 64.0, 4096, 32.0, 1.0
+        setattr(bad, field, value)
+        st, msg = call_prefill(bad, w)
+        assert st == gdla.GDLA_ERR_INVALID_ARG, (field, value, st)
+        assert "yarn" in msg.lower() or "YaRN" in msg, msg
+    off = _cfg()
+    off.yarn_factor, off.yarn_orig_len = 1.0, 0    # factor <= 1: plain RoPE, other fields ignored
+    assert lib().gdla_prefill_workspace_size(ctypes.byref(off), 1, 16) > 0
 
 
 def test_empty_inputs_are_noops():
