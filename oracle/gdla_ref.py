@@ -45,6 +45,14 @@ report has no headings, so its paragraphs are named by topic):
   [M3-ctx]   "Motif 3: Technical Report", long-context paragraph: the
              full-attention layers extend the native 4K context by a factor of
              64 with YaRN; the sliding-window layers keep plain RoPE.
+  [M3-pack]  same page, long-context training paragraph: training batches
+             hold complete sequences packed together, which are re-balanced
+             across data-parallel ranks by a longest-processing-time greedy
+             rule.
+  [OSM-page] "Open-Source Frontier Models: Architecture and Benchmarks of
+             Rnj-1 and Motif-2", section 2, prefill sequence diagram: the
+             attention step stores the normalized KV rows in the blocks of a
+             PagedAttention cache.
 
 Readings where the pages are silent (each listed in the design notes):
 RMSNorm with a learned gain for both latents; eps = cfg rms_eps; rotate-half
@@ -60,6 +68,13 @@ frequency table and the cos/sin multiplier m of the listing in [OSM-yarn],
 applied to the rotary parts, so the rotary part of every logit scales by m^2
 (the page's prose writes the temperature as sqrt(1 + 0.1 ln s) on the logits;
 the listing is the executable statement and is the reading taken).
+Packed sequences ([M3-pack]): sequence b of a packed stream holds rows
+cu[b] .. cu[b+1]-1, its positions restart at pos_offsets[b], and its tokens
+attend only to earlier tokens of the same sequence -- each sequence is the
+layer applied to it alone.  Paged cache ([OSM-page]): the rows of one sequence
+are cut into blocks of page_rows positions; block j of sequence b lives in
+pool page block_table[b][j], so position p is row p mod page_rows of page
+block_table[b][p div page_rows].
 
 Every function works in float64 on whatever it is given (inputs are widened
 with np.asarray(..., float64)); nothing is rounded to bf16 here.
@@ -422,6 +437,91 @@ def gdla_decode(x_new, W, cfg: Cfg, cache, cache_lens):
         Zs.append(Z[0])
         rows_out.append(new_row)
     return dict(y=np.stack(ys), Z=np.stack(Zs), new_rows=np.stack(rows_out))
+
+
+# --------------------------------------------------------------------------
+# Packed variable-length prefill ([M3-pack]) and the paged cache ([OSM-page])
+# --------------------------------------------------------------------------
+
+def packed_segments(cu_seqlens):
+    """[(start, end)] row ranges of the packed sequences: sequence b holds rows
+    cu_seqlens[b] .. cu_seqlens[b+1]-1 of the stream."""
+    cu = [int(c) for c in cu_seqlens]
+    return [(cu[b], cu[b + 1]) for b in range(len(cu) - 1)]
+
+
+def gdla_layer_packed(x, W, cfg: Cfg, cu_seqlens, pos_offsets=None):
+    """One GDLA layer over complete sequences packed end to end.
+
+    x            [T, d_model], the sequences one after another
+    cu_seqlens   [n+1] row offsets (cu[0] = 0, cu[n] = T)
+    pos_offsets  [n] position of each sequence's first token (default 0)
+
+    Each sequence is the layer applied to it alone: its rows attend only to
+    earlier rows of the same sequence, at positions pos_offsets[b] + i.
+    Returns dict y [T, d_model], Z [T, nS*d_v], cache [T, kv_rank + d_rope]
+    (the row each token would store) and lam [T, nS].
+    """
+    x = _f64(x)
+    T = x.shape[0]
+    segs = packed_segments(cu_seqlens)
+    if pos_offsets is None:
+        pos_offsets = [0] * len(segs)
+    RL = cfg.kv_rank + cfg.d_rope
+    y = np.zeros((T, cfg.d_model))
+    Z = np.zeros((T, cfg.n_signal * cfg.d_v))
+    cache = np.zeros((T, RL))
+    lam = np.zeros((T, cfg.n_signal))
+    for (s0, s1), p0 in zip(segs, pos_offsets):
+        if s1 <= s0:
+            continue
+        r = gdla_layer(x[None, s0:s1], W, cfg, pos_offset=int(p0))
+        y[s0:s1] = r["y"][0]
+        Z[s0:s1] = r["Z"][0]
+        cache[s0:s1] = r["cache"][0]
+        lam[s0:s1] = r["lam"][0]
+    return dict(y=y, Z=Z, cache=cache, lam=lam)
+
+
+def paged_slot(block_table, page_rows, b, p):
+    """(page, row) that holds position p of sequence b."""
+    return int(block_table[b][p // page_rows]), p % page_rows
+
+
+def paged_rows(pages, block_table, page_rows, b, n_rows):
+    """Rows 0 .. n_rows-1 of sequence b read out of a paged cache
+    pages [num_pages, page_rows, kv_rank + d_rope]."""
+    pages = _f64(pages)
+    out = np.zeros((n_rows, pages.shape[-1]))
+    for p in range(n_rows):
+        pg, r = paged_slot(block_table, page_rows, b, p)
+        out[p] = pages[pg, r]
+    return out
+
+
+def paged_write(pages, block_table, page_rows, b, positions, rows):
+    """Copy of the pool with rows stored at the given positions of sequence b."""
+    out = np.array(_f64(pages))
+    for p, row in zip(positions, _f64(rows)):
+        pg, r = paged_slot(block_table, page_rows, b, int(p))
+        out[pg, r] = row
+    return out
+
+
+def gdla_decode_paged(x_new, W, cfg: Cfg, pages, block_table, page_rows, cache_lens):
+    """One decode step against a paged cache: each sequence's cached rows are
+    read through its block table, then the step is gdla_decode's.  Returns
+    gdla_decode's dict plus `slots`, the (page, row) each new row goes to."""
+    B = len(cache_lens)
+    RL = cfg.kv_rank + cfg.d_rope
+    cap = int(max(cache_lens)) + 1
+    dense = np.zeros((B, cap, RL))
+    for b in range(B):
+        n = int(cache_lens[b])
+        dense[b, :n] = paged_rows(pages, block_table, page_rows, b, n)
+    out = gdla_decode(x_new, W, cfg, dense, cache_lens)
+    out["slots"] = [paged_slot(block_table, page_rows, b, int(cache_lens[b])) for b in range(B)]
+    return out
 
 
 # --------------------------------------------------------------------------

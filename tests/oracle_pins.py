@@ -491,4 +491,153 @@ def pin_yarn_full_layers_only():
     assert np.max(np.abs(full - R.gdla_layer(x, W, TINY)["y"])) > 1e-6
 
 
+# ------------------------------------------- packed sequences and the paged cache
+PACK_LENS = (3, 1, 5, 0, 2)
+PACK_POS = (0, 7, 2, 9, 4)
+
+
+def _pack(lens, seed=3):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(int)
+    x = np.random.Generator(np.random.PCG64(seed)).standard_normal((int(cu[-1]), TINY.d_model))
+    return cu, x
+
+
+def pin_packed_one_sequence_is_the_layer():
+    """A stream holding one sequence is the layer over that sequence, at the
+    sequence's position offset, full and windowed."""
+    W = tiny_weights()
+    x = tiny_x(B=1)
+    L = x.shape[1]
+    for window in (0, 3):
+        cfg = replace(TINY, window=window)
+        r = R.gdla_layer_packed(x[0], W, cfg, [0, L], [5])
+        ref = R.gdla_layer(x, W, cfg, pos_offset=5)
+        close(r["y"], ref["y"][0], 1e-13)
+        close(r["cache"], ref["cache"][0], 1e-13)
+
+
+def pin_packed_equal_lengths_is_the_batch():
+    """Sequences of one length packed end to end give the batched layer's rows."""
+    W = tiny_weights()
+    x = tiny_x(B=3, L=6)
+    r = R.gdla_layer_packed(x.reshape(18, -1), W, TINY, [0, 6, 12, 18])
+    ref = R.gdla_layer(x, W, TINY)
+    close(r["y"], ref["y"].reshape(18, -1), 1e-13)
+    close(r["cache"], ref["cache"].reshape(18, -1), 1e-13)
+
+
+def pin_packed_sequences_are_separate_layers():
+    """Every packed sequence (an empty one included) matches the layer run on
+    it alone at its own offset; row ranges come from the lengths here."""
+    W = tiny_weights()
+    cu, x = _pack(PACK_LENS)
+    starts = np.cumsum((0,) + PACK_LENS[:-1])
+    for window in (0, 2):
+        cfg = replace(TINY, window=window)
+        r = R.gdla_layer_packed(x, W, cfg, cu, PACK_POS)
+        assert r["y"].shape == (sum(PACK_LENS), TINY.d_model)
+        for b, n in enumerate(PACK_LENS):
+            if n == 0:
+                continue
+            s0 = int(starts[b])
+            ref = R.gdla_layer(x[None, s0:s0 + n], W, cfg, pos_offset=PACK_POS[b])
+            close(r["y"][s0:s0 + n], ref["y"][0], 1e-13)
+            close(r["lam"][s0:s0 + n], ref["lam"][0], 1e-13)
+
+
+def pin_packed_isolation():
+    """Changing one sequence leaves every other row bit for bit; dropping it
+    from the stream shifts the others' rows without changing their values
+    (positions restart per sequence, keys never cross a boundary)."""
+    W = tiny_weights()
+    cu, x = _pack(PACK_LENS)
+    for window in (0, 4):
+        cfg = replace(TINY, window=window)
+        base = R.gdla_layer_packed(x, W, cfg, cu, PACK_POS)
+        x2 = x.copy()
+        x2[0:3] += 1.0
+        r2 = R.gdla_layer_packed(x2, W, cfg, cu, PACK_POS)
+        assert np.array_equal(r2["y"][3:], base["y"][3:]), "a change in sequence 0 reached another sequence"
+        assert not np.allclose(r2["y"][:3], base["y"][:3])
+        r3 = R.gdla_layer_packed(x[3:], W, cfg, [0, 1, 6, 6, 8], PACK_POS[1:])
+        close(r3["y"], base["y"][3:], 1e-13)
+
+
+def pin_packed_order_invariance():
+    """Reordering the sequences in the stream reorders the output rows."""
+    W = tiny_weights()
+    cu, x = _pack(PACK_LENS)
+    base = R.gdla_layer_packed(x, W, TINY, cu, PACK_POS)
+    order = [2, 4, 0, 1, 3]
+    parts = [np.arange(cu[b], cu[b + 1]) for b in order]
+    idx = np.concatenate(parts)
+    cu2 = np.concatenate([[0], np.cumsum([len(q) for q in parts])])
+    r = R.gdla_layer_packed(x[idx], W, TINY, cu2, [PACK_POS[b] for b in order])
+    close(r["y"], base["y"][idx], 1e-13)
+
+
+def _dense_and_pages(seed=4, B=3, cap=12, page_rows=4):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    RL = TINY.kv_rank + TINY.d_rope
+    dense = rng.standard_normal((B, cap, RL))
+    k = cap // page_rows
+    return rng, dense, dense.reshape(B * k, page_rows, RL), [[b * k + j for j in range(k)] for b in range(B)]
+
+
+def pin_paged_identity_table_is_reshape():
+    """With the table that numbers the pages in order, the pool is the dense
+    cache reshaped: every sequence reads back its own rows."""
+    _, dense, pages, bt = _dense_and_pages()
+    for b in range(3):
+        close(R.paged_rows(pages, bt, 4, b, 11), dense[b, :11], 0.0)
+        assert R.paged_slot(bt, 4, b, 9) == (b * 3 + 2, 1)
+
+
+def pin_paged_pool_permutation():
+    """Moving the pages around the pool with the table updated to match leaves
+    every sequence's rows unchanged; a write then a read returns what was
+    written and changes no other sequence."""
+    rng, dense, pages, bt = _dense_and_pages()
+    perm = rng.permutation(9)
+    pages2 = np.zeros_like(pages)
+    pages2[perm] = pages
+    bt2 = [[int(perm[p]) for p in row] for row in bt]
+    for b in range(3):
+        close(R.paged_rows(pages2, bt2, 4, b, 12), dense[b], 0.0)
+    rows = rng.standard_normal((5, pages.shape[-1]))
+    positions = [0, 3, 4, 7, 11]
+    w = R.paged_write(pages2, bt2, 4, 1, positions, rows)
+    expect = dense[1].copy()
+    expect[positions] = rows
+    close(R.paged_rows(w, bt2, 4, 1, 12), expect, 0.0)
+    for b in (0, 2):
+        close(R.paged_rows(w, bt2, 4, b, 12), dense[b], 0.0)
+
+
+def pin_decode_paged_is_dense_decode():
+    """Decoding against a shuffled paged copy of a cache equals decoding
+    against the dense cache, and the new row goes to the slot the table names
+    for its position."""
+    W = tiny_weights()
+    rng = np.random.Generator(np.random.PCG64(6))
+    RL = TINY.kv_rank + TINY.d_rope
+    lens = np.array([9, 5])
+    dense = np.zeros((2, 12, RL))
+    dense[0, :9] = rng.standard_normal((9, RL))
+    dense[1, :5] = rng.standard_normal((5, RL))
+    bt = [[5, 2, 7], [0, 6, 3]]
+    pages = np.full((8, 4, RL), np.nan)      # pages and rows nobody owns stay NaN
+    for b in range(2):
+        for p in range(int(lens[b])):
+            pages[bt[b][p // 4], p % 4] = dense[b, p]
+    x_new = tiny_x(B=2, L=1)[:, 0]
+    for window in (0, 4):
+        cfg = replace(TINY, window=window)
+        dec = R.gdla_decode_paged(x_new, W, cfg, pages, bt, 4, lens)
+        ref = R.gdla_decode(x_new, W, cfg, dense, lens)
+        close(dec["y"], ref["y"], 1e-13)
+        close(dec["new_rows"], ref["new_rows"], 1e-13)
+        assert dec["slots"] == [(7, 1), (6, 1)], dec["slots"]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -188,6 +188,49 @@ def _rope_params_every_layer(cfg):
     return cfg.rope_base, None
 
 
+def _packed_global_positions(x, W, cfg, cu_seqlens, pos_offsets=None):
+    # positions run on through the stream instead of restarting per sequence
+    segs = R.packed_segments(cu_seqlens)
+    pos = pos_offsets if pos_offsets is not None else [0] * len(segs)
+    x = np.asarray(x, np.float64)
+    y = np.zeros((x.shape[0], cfg.d_model))
+    cache = np.zeros((x.shape[0], cfg.kv_rank + cfg.d_rope))
+    lam = np.zeros((x.shape[0], cfg.n_signal))
+    for (s0, s1), p0 in zip(segs, pos):
+        if s1 > s0:
+            r = R.gdla_layer(x[None, s0:s1], W, cfg, pos_offset=int(p0) + s0)
+            y[s0:s1], cache[s0:s1], lam[s0:s1] = r["y"][0], r["cache"][0], r["lam"][0]
+    return dict(y=y, Z=None, cache=cache, lam=lam)
+
+
+def _packed_leaky(x, W, cfg, cu_seqlens, pos_offsets=None):
+    # each sequence also sees the rows of the sequences before it
+    segs = R.packed_segments(cu_seqlens)
+    pos = pos_offsets if pos_offsets is not None else [0] * len(segs)
+    x = np.asarray(x, np.float64)
+    y = np.zeros((x.shape[0], cfg.d_model))
+    cache = np.zeros((x.shape[0], cfg.kv_rank + cfg.d_rope))
+    lam = np.zeros((x.shape[0], cfg.n_signal))
+    for (s0, s1), p0 in zip(segs, pos):
+        if s1 > s0:
+            r = R.gdla_layer(x[None, 0:s1], W, cfg, pos_offset=int(p0) - s0)
+            y[s0:s1], cache[s0:s1], lam[s0:s1] = r["y"][0, s0:], r["cache"][0, s0:], r["lam"][0, s0:]
+    return dict(y=y, Z=None, cache=cache, lam=lam)
+
+
+def _packed_segments_skip_first(cu):
+    cu = [int(c) for c in cu]
+    return [(min(cu[b] + 1, cu[b + 1]), cu[b + 1]) for b in range(len(cu) - 1)]
+
+
+def _paged_slot_swapped(block_table, page_rows, b, p):
+    return int(block_table[b][p % page_rows]), p // page_rows
+
+
+def _paged_slot_no_table(block_table, page_rows, b, p):
+    return b * len(block_table[b]) + p // page_rows, p % page_rows
+
+
 MUTANTS = {
     "rope_wrong_sign": ("rope", _rope_wrong_sign),
     "rope_adjacent_pairs": ("rope", _rope_adjacent_pairs),
@@ -214,6 +257,11 @@ MUTANTS = {
     "yarn_times_s": ("yarn_inv_freq", _yarn_times_s),
     "yarn_mscale_sqrt": ("yarn_mscale", _yarn_mscale_sqrt),
     "yarn_on_window_layers": ("rope_params", _rope_params_every_layer),
+    "packed_global_positions": ("gdla_layer_packed", _packed_global_positions),
+    "packed_leaky": ("gdla_layer_packed", _packed_leaky),
+    "packed_segments_skip_first": ("packed_segments", _packed_segments_skip_first),
+    "paged_slot_swapped": ("paged_slot", _paged_slot_swapped),
+    "paged_slot_no_table": ("paged_slot", _paged_slot_no_table),
 }
 
 
