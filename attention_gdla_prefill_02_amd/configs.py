@@ -27,7 +27,7 @@ REPORT_SHAPES = dict(d_model=4096, q_rank=1024, kv_rank=512, n_noise=16, group=4
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill" | "block" | "decode"
+    kind: str                 # "prefill" | "block" | "packed" | "decode"
     shapes: dict
     dtype: str                # "fp32" | "bf16"
     B: int
@@ -37,6 +37,8 @@ class Workload:
     seed: int = 0
     ctx_range: tuple = ()     # decode: context lengths c_b ~ U{lo..hi}
     capacity: int = 0         # decode: cache rows per sequence
+    len_range: tuple = ()     # packed: sequence lengths ~ U{lo..hi}, cut to sum to L
+    page_rows: int = 0        # paged cache: rows per page (0 = dense cache)
     sampled_rows: int = 0     # >0: score this many seeded rows per layer
     rope_base: float = 10000.0
     rms_eps: float = 1e-6
@@ -68,6 +70,16 @@ WORKLOADS = {
         name="report_decode_b64", kind="decode", shapes=REPORT_SHAPES, dtype="bf16", B=64,
         windows=(0, 128), seed=6, ctx_range=(1024, 32768), capacity=32768,
         note="GDLA decode at the report's shapes (g=4, 80 query heads), bf16, batch 64, contexts U{1024..32768}"),
+    "packed_hybrid_l32k": Workload(
+        name="packed_hybrid_l32k", kind="packed", shapes=MOTIF_SHAPES, dtype="bf16", B=1, L=32768,
+        windows=(0, 4096, 4096, 4096), seed=7, len_range=(256, 8192), sampled_rows=64,
+        note="hybrid GDLA block over complete sequences of U{256..8192} tokens packed into one "
+             "stream of 32768, bf16"),
+    "paged_decode_b64": Workload(
+        name="paged_decode_b64", kind="decode", shapes=MOTIF_SHAPES, dtype="bf16", B=64,
+        windows=(0, 4096), seed=8, ctx_range=(1024, 32768), capacity=32768, page_rows=64,
+        note="GDLA decode, bf16, batch 64, contexts U{1024..32768}, paged cache of 64-row pages in "
+             "shuffled pool order"),
     "hybrid_l256k": Workload(
         name="hybrid_l256k", kind="block", shapes=MOTIF_SHAPES, dtype="bf16", B=1,
         L=262144, windows=(0, 4096, 4096, 4096), seed=4, sampled_rows=256,

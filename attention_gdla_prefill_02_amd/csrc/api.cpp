@@ -81,18 +81,17 @@ gdla_status check_config(const gdla_config* c) {
   return GDLA_OK;
 }
 
-// Prefill workspace: every intermediate of the layer, each 256-byte aligned.
+// Prefill workspace: every intermediate of the layer, each 256-byte aligned,
+// for a stream of T tokens; plan_bytes for the packed attention's work list.
 struct PrefillLayout {
-  size_t down, cqn, ckvn, kr, lam, rope, q, gate, kc, vt, z, total;
-  int64_t vt_seq, vt_ld;
+  size_t down, cqn, ckvn, kr, lam, rope, q, gate, kc, vt, z, plan, total;
+  int64_t vt_ld;
 };
 
-PrefillLayout prefill_layout(const Dims& D, int64_t B, int64_t L) {
+PrefillLayout prefill_layout(const Dims& D, int64_t T, size_t plan_bytes) {
   PrefillLayout P;
-  const int64_t T = B * L;
   const int e = D.elt;
-  P.vt_seq = (L + 63) / 64 * 64;
-  P.vt_ld = B * P.vt_seq;
+  P.vt_ld = (T + 63) / 64 * 64;
   size_t o = 0;
   P.down = o; o = align256(o + (size_t)T * D.ndown * 4);
   P.cqn = o;  o = align256(o + (size_t)T * D.rq * e);
@@ -105,8 +104,17 @@ PrefillLayout prefill_layout(const Dims& D, int64_t B, int64_t L) {
   P.kc = o;   o = align256(o + (size_t)T * D.nN * D.dn * e);
   P.vt = o;   o = align256(o + (size_t)D.nN * D.dv * P.vt_ld * e);
   P.z = o;    o = align256(o + (size_t)T * D.nS * D.dv * e);
+  P.plan = o; o = align256(o + plan_bytes);
   P.total = o;
   return P;
+}
+
+constexpr int64_t PACKED_MAX_T = (int64_t)1 << 20;
+
+// Workspace of a packed call; 0 when the sizes are outside the supported range.
+size_t packed_plan_bytes(const gdla_config* c, int32_t n_seq, int64_t T) {
+  if (c->dtype != GDLA_BF16) return 0;
+  return gdla::attn_plan_bytes(n_seq, T, c->group);
 }
 
 gdla_status check_weights(const gdla_weights* w) {
@@ -120,82 +128,42 @@ gdla_status check_weights(const gdla_weights* w) {
   return GDLA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* gdla_status_string(gdla_status s) {
-  switch (s) {
-    case GDLA_OK: return "GDLA_OK";
-    case GDLA_ERR_INVALID_ARG: return "GDLA_ERR_INVALID_ARG";
-    case GDLA_ERR_UNSUPPORTED: return "GDLA_ERR_UNSUPPORTED";
-    case GDLA_ERR_WORKSPACE: return "GDLA_ERR_WORKSPACE";
-    case GDLA_ERR_HIP: return "GDLA_ERR_HIP";
-  }
-  return "GDLA_ERR_UNKNOWN";
-}
-
-const char* gdla_last_error(void) { return g_err; }
-
-int32_t gdla_version(void) { return 101; }   // 1.01: YaRN fields in gdla_config
-
-size_t gdla_prefill_workspace_size(const gdla_config* cfg, int32_t B, int32_t L) {
-  if (check_config(cfg) != GDLA_OK || B < 0 || L < 0) return 0;
-  return prefill_layout(dims_of(cfg), B, L).total;
-}
-
-gdla_status gdla_prefill_workspace_layout(const gdla_config* cfg, int32_t B, int32_t L, gdla_prefill_layout* out) {
-  gdla_status st = check_config(cfg);
-  if (st != GDLA_OK) return st;
-  if (!out) return fail(GDLA_ERR_INVALID_ARG, "out is NULL");
-  if (B < 0 || L < 0) return fail(GDLA_ERR_INVALID_ARG, "B and L must be >= 0");
-  const PrefillLayout P = prefill_layout(dims_of(cfg), B, L);
-  out->down = P.down; out->cqn = P.cqn; out->ckvn = P.ckvn; out->kr = P.kr; out->lam = P.lam;
-  out->rope = P.rope; out->q = P.q; out->gate = P.gate; out->kc = P.kc; out->vt = P.vt; out->z = P.z;
+gdla_status check_paged(const gdla_paged_cache* c) {
+  if (!c->pages || !c->block_table) return fail(GDLA_ERR_INVALID_ARG, "cache pages and block_table must be non-NULL");
+  if (!aligned16(c->pages) || ((uintptr_t)c->block_table & 3))
+    return fail(GDLA_ERR_INVALID_ARG, "cache pages must be 16-byte aligned, block_table 4-byte aligned");
+  if (c->page_rows <= 0 || c->page_rows % 32)
+    return fail(GDLA_ERR_INVALID_ARG, "page_rows must be a positive multiple of 32 (got %d)", c->page_rows);
+  if (c->max_pages <= 0 || c->num_pages <= 0)
+    return fail(GDLA_ERR_INVALID_ARG, "max_pages and num_pages must be positive");
+  if ((int64_t)c->page_rows * c->max_pages > ((int64_t)1 << 30))
+    return fail(GDLA_ERR_INVALID_ARG, "page_rows * max_pages beyond 2^30 positions");
   return GDLA_OK;
 }
 
-gdla_status gdla_prefill(const gdla_config* cfg, const gdla_weights* w, int32_t B, int32_t L, int64_t pos_offset,
-                         const void* x, void* y, const void* residual, void* cache, int32_t cache_capacity,
-                         void* workspace, size_t workspace_bytes, void* stream) {
-  return gdla_prefill_stages(cfg, w, B, L, pos_offset, x, y, residual, cache, cache_capacity, workspace,
-                             workspace_bytes, stream, GDLA_STAGE_ALL);
+gdla::CacheView paged_view(const gdla_paged_cache* c) {
+  return gdla::CacheView{c->pages, c->block_table, c->page_rows, c->max_pages, c->num_pages};
 }
 
-gdla_status gdla_prefill_stages(const gdla_config* cfg, const gdla_weights* w, int32_t B, int32_t L,
-                                int64_t pos_offset, const void* x, void* y, const void* residual, void* cache,
-                                int32_t cache_capacity, void* workspace, size_t workspace_bytes, void* stream,
-                                uint32_t stages) {
-  using namespace gdla;
-  gdla_status st = check_config(cfg);
-  if (st != GDLA_OK) return st;
-  if (B < 0 || L < 0) return fail(GDLA_ERR_INVALID_ARG, "B and L must be >= 0 (got %d, %d)", B, L);
-  if (pos_offset < 0) return fail(GDLA_ERR_INVALID_ARG, "pos_offset must be >= 0");
-  if (stages & ~(uint32_t)GDLA_STAGE_ALL) return fail(GDLA_ERR_INVALID_ARG, "unknown stage bits 0x%x", stages);
-  if (B == 0 || L == 0) return GDLA_OK;
-  const bool bf = cfg->dtype == GDLA_BF16;
-  if (!bf && L > 8192) return fail(GDLA_ERR_UNSUPPORTED, "fp32 path supports L <= 8192 (got %d)", L);
-  if ((int64_t)B * L > ((int64_t)1 << 31) / 8) return fail(GDLA_ERR_UNSUPPORTED, "B*L too large");
-  st = check_weights(w);
-  if (st != GDLA_OK) return st;
-  if (!x || !y) return fail(GDLA_ERR_INVALID_ARG, "x and y must be non-NULL");
-  if (!aligned16(x) || !aligned16(y) || (residual && !aligned16(residual)) || (cache && !aligned16(cache)))
-    return fail(GDLA_ERR_INVALID_ARG, "x, y, residual and cache must be 16-byte aligned");
-  if (x == y) return fail(GDLA_ERR_INVALID_ARG, "y must not alias x");
-  if (cache && (int64_t)cache_capacity < pos_offset + L)
-    return fail(GDLA_ERR_INVALID_ARG, "cache_capacity %d < pos_offset + L = %lld", cache_capacity,
-                (long long)(pos_offset + L));
-  if (pos_offset + L > (int64_t)1 << 30) return fail(GDLA_ERR_INVALID_ARG, "positions beyond 2^30");
-  const Dims D = dims_of(cfg);
-  const PrefillLayout P = prefill_layout(D, B, L);
-  if (!workspace) return fail(GDLA_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", P.total);
-  if (((uintptr_t)workspace & 255) != 0) return fail(GDLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (workspace_bytes < P.total)
-    return fail(GDLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, P.total);
+// The sequences of one prefill call: B of L rows each (cu == nullptr) or a
+// packed stream (cu, nseq, per-sequence first positions).
+struct Stream {
+  int64_t T;
+  int B, L;
+  int64_t pos_offset;
+  const int32_t* cu;
+  int nseq;
+  const int32_t* seq_pos;
+};
 
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  const int64_t T = (int64_t)B * L;
+// Launch sequence of one layer; every argument has been checked.
+gdla_status run_prefill(const gdla_config* cfg, const gdla_weights* w, const Stream& S, const void* x, void* y,
+                        const void* residual, const gdla::CacheView& cache, char* ws, const PrefillLayout& P,
+                        hipStream_t s, uint32_t stages) {
+  using namespace gdla;
+  const Dims D = dims_of(cfg);
+  const bool bf = cfg->dtype == GDLA_BF16;
+  const int64_t T = S.T;
   const int e = D.elt;
   auto gemm = bf ? gemm_bf16 : gemm_f32;
   hipError_t err;
@@ -215,19 +183,21 @@ gdla_status gdla_prefill_stages(const gdla_config* cfg, const gdla_weights* w, i
   if (stages & GDLA_STAGE_PREP) {
     RowPrepArgs r{};
     r.down = (const float*)(ws + P.down); r.ld_down = D.ndown;
-    r.T = T; r.L = L; r.pos_offset = pos_offset;
+    r.T = T; r.L = S.L; r.pos_offset = S.pos_offset;
+    r.cu = S.cu; r.nseq = S.nseq; r.seq_pos = S.seq_pos;
     r.q_rank = (int)D.rq; r.kv_rank = (int)D.rkv; r.d_rope = (int)D.dr; r.nS = (int)D.nS;
     r.g_q = w->g_q; r.g_kv = w->g_kv; r.eps = cfg->rms_eps;
     set_rope(r, cfg->rope_base, cfg->window, cfg->yarn_factor, cfg->yarn_orig_len, cfg->yarn_beta_fast,
              cfg->yarn_beta_slow);
     r.cqn = ws + P.cqn; r.ckvn = ws + P.ckvn; r.kr = ws + P.kr; r.lam = (float*)(ws + P.lam);
-    r.rope = (float*)(ws + P.rope); r.cache = cache; r.cache_cap = cache_capacity;
+    r.rope = (float*)(ws + P.rope); r.cache = cache;
     r.split_kv = bf;
     if ((err = rowprep(r, bf, s)) != hipSuccess) return hip_fail(err, "row prep");
   }
-  // 3. latent expansion: K^C = c_KVn W_UK^T (token-major), V^T = W_UV c_KVn^T (per
-  //    sequence).  bf16: c_KVn enters as [hi | lo] over K = 2*kv_rank against the
-  //    weight read twice (K wrap), so the expansion does not round the latent.
+  // 3. latent expansion: K^C = c_KVn W_UK^T (token-major), V^T = W_UV c_KVn^T
+  //    (token t in column t).  bf16: c_KVn enters as [hi | lo] over K =
+  //    2*kv_rank against the weight read twice (K wrap), so the expansion does
+  //    not round the latent.
   if (stages & GDLA_STAGE_EXPAND) {
     const int64_t kk = bf ? 2 * D.rkv : D.rkv;
     GemmArgs g{};
@@ -237,12 +207,12 @@ gdla_status gdla_prefill_stages(const gdla_config* cfg, const gdla_weights* w, i
     g.M = (int)T; g.N = (int)(D.nN * D.dn); g.K = (int)kk; g.batch = 1; g.epi = EPI_STORE;
     if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "latent expand (keys)");
     GemmArgs v{};
-    v.A = (const char*)w->w_ukv + (size_t)D.nN * D.dn * D.rkv * e; v.lda = D.rkv; v.strideA = 0;
+    v.A = (const char*)w->w_ukv + (size_t)D.nN * D.dn * D.rkv * e; v.lda = D.rkv;
     v.kwrapA = bf ? (int)D.rkv : 0;
-    v.B = ws + P.ckvn; v.ldb = kk; v.strideB = (int64_t)L * kk;
-    v.C = ws + P.vt; v.ldc = P.vt_ld; v.strideC = P.vt_seq;
-    v.M = (int)(D.nN * D.dv); v.N = L; v.K = (int)kk; v.batch = B; v.epi = EPI_STORE;
-    v.Npad = (int)P.vt_seq;   // the attention kernel reads whole 64-key tiles: pad with zeros
+    v.B = ws + P.ckvn; v.ldb = kk;
+    v.C = ws + P.vt; v.ldc = P.vt_ld;
+    v.M = (int)(D.nN * D.dv); v.N = (int)T; v.K = (int)kk; v.batch = 1; v.epi = EPI_STORE;
+    v.Npad = (int)P.vt_ld;   // the attention kernel reads whole 32-key tiles: pad with zeros
     if ((err = gemm(v, s)) != hipSuccess) return hip_fail(err, "latent expand (values)");
   }
   // 4. query up-projection with RoPE on the rotary parts, and the sigmoid gate
@@ -273,19 +243,28 @@ gdla_status gdla_prefill_stages(const gdla_config* cfg, const gdla_weights* w, i
         return hip_fail(err, "query/gate finish");
     }
   }
-  // 5. attention, signal + noise heads, fused differential and gate
+  // 5. attention, signal + noise heads, fused differential and gate (a packed
+  //    bf16 stream first builds its work list)
   if (stages & GDLA_STAGE_ATTN) {
     AttnArgs a{};
     a.q = ws + P.q; a.ld_q = D.nq;
     a.gate = (const float*)(ws + P.gate); a.ld_gate = D.ngate;
     a.kc = ws + P.kc; a.ld_kc = D.nN * D.dn;
     a.kr = ws + P.kr;
-    a.vt = ws + P.vt; a.ld_vt = P.vt_ld; a.vt_seq = P.vt_seq;
+    a.vt = ws + P.vt; a.ld_vt = P.vt_ld;
     a.lam = (const float*)(ws + P.lam);
     a.z = ws + P.z;
-    a.B = B; a.L = L; a.nN = (int)D.nN; a.g = (int)D.g; a.window = cfg->window;
+    a.T = T; a.B = S.B; a.L = S.L;
+    a.cu = S.cu; a.nseq = S.nseq;
+    a.nN = (int)D.nN; a.g = (int)D.g; a.window = cfg->window;
     a.d_nope = (int)D.dn; a.d_rope = (int)D.dr; a.d_v = (int)D.dv;
     a.scale = (float)(1.0 / std::sqrt((double)D.dqk));
+    if (bf && S.cu) {
+      int* plan = (int*)(ws + P.plan);
+      if ((err = attn_plan(S.cu, S.nseq, T, (int)D.g, plan, s)) != hipSuccess) return hip_fail(err, "attention plan");
+      a.plan = plan;
+      a.items_cap = attn_plan_items(S.nseq, T, (int)D.g);
+    }
     if ((err = bf ? attn_bf16(a, s) : attn_f32(a, s)) != hipSuccess) return hip_fail(err, "attention");
   }
   // 6. output projection (+ residual)
@@ -299,6 +278,123 @@ gdla_status gdla_prefill_stages(const gdla_config* cfg, const gdla_weights* w, i
     if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "output projection");
   }
   return GDLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdla_status_string(gdla_status s) {
+  switch (s) {
+    case GDLA_OK: return "GDLA_OK";
+    case GDLA_ERR_INVALID_ARG: return "GDLA_ERR_INVALID_ARG";
+    case GDLA_ERR_UNSUPPORTED: return "GDLA_ERR_UNSUPPORTED";
+    case GDLA_ERR_WORKSPACE: return "GDLA_ERR_WORKSPACE";
+    case GDLA_ERR_HIP: return "GDLA_ERR_HIP";
+  }
+  return "GDLA_ERR_UNKNOWN";
+}
+
+const char* gdla_last_error(void) { return g_err; }
+
+int32_t gdla_version(void) { return 102; }   // 1.02: packed prefill, paged cache
+
+size_t gdla_prefill_workspace_size(const gdla_config* cfg, int32_t B, int32_t L) {
+  if (check_config(cfg) != GDLA_OK || B < 0 || L < 0) return 0;
+  return prefill_layout(dims_of(cfg), (int64_t)B * L, 0).total;
+}
+
+gdla_status gdla_prefill_workspace_layout(const gdla_config* cfg, int32_t B, int32_t L, gdla_prefill_layout* out) {
+  gdla_status st = check_config(cfg);
+  if (st != GDLA_OK) return st;
+  if (!out) return fail(GDLA_ERR_INVALID_ARG, "out is NULL");
+  if (B < 0 || L < 0) return fail(GDLA_ERR_INVALID_ARG, "B and L must be >= 0");
+  const PrefillLayout P = prefill_layout(dims_of(cfg), (int64_t)B * L, 0);
+  out->down = P.down; out->cqn = P.cqn; out->ckvn = P.ckvn; out->kr = P.kr; out->lam = P.lam;
+  out->rope = P.rope; out->q = P.q; out->gate = P.gate; out->kc = P.kc; out->vt = P.vt; out->z = P.z;
+  return GDLA_OK;
+}
+
+gdla_status gdla_prefill(const gdla_config* cfg, const gdla_weights* w, int32_t B, int32_t L, int64_t pos_offset,
+                         const void* x, void* y, const void* residual, void* cache, int32_t cache_capacity,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return gdla_prefill_stages(cfg, w, B, L, pos_offset, x, y, residual, cache, cache_capacity, workspace,
+                             workspace_bytes, stream, GDLA_STAGE_ALL);
+}
+
+gdla_status gdla_prefill_stages(const gdla_config* cfg, const gdla_weights* w, int32_t B, int32_t L,
+                                int64_t pos_offset, const void* x, void* y, const void* residual, void* cache,
+                                int32_t cache_capacity, void* workspace, size_t workspace_bytes, void* stream,
+                                uint32_t stages) {
+  gdla_status st = check_config(cfg);
+  if (st != GDLA_OK) return st;
+  if (B < 0 || L < 0) return fail(GDLA_ERR_INVALID_ARG, "B and L must be >= 0 (got %d, %d)", B, L);
+  if (pos_offset < 0) return fail(GDLA_ERR_INVALID_ARG, "pos_offset must be >= 0");
+  if (stages & ~(uint32_t)GDLA_STAGE_ALL) return fail(GDLA_ERR_INVALID_ARG, "unknown stage bits 0x%x", stages);
+  if (B == 0 || L == 0) return GDLA_OK;
+  const bool bf = cfg->dtype == GDLA_BF16;
+  if (!bf && L > 8192) return fail(GDLA_ERR_UNSUPPORTED, "fp32 path supports L <= 8192 (got %d)", L);
+  if ((int64_t)B * L > ((int64_t)1 << 31) / 8) return fail(GDLA_ERR_UNSUPPORTED, "B*L too large");
+  st = check_weights(w);
+  if (st != GDLA_OK) return st;
+  if (!x || !y) return fail(GDLA_ERR_INVALID_ARG, "x and y must be non-NULL");
+  if (!aligned16(x) || !aligned16(y) || (residual && !aligned16(residual)) || (cache && !aligned16(cache)))
+    return fail(GDLA_ERR_INVALID_ARG, "x, y, residual and cache must be 16-byte aligned");
+  if (x == y) return fail(GDLA_ERR_INVALID_ARG, "y must not alias x");
+  if (cache && (int64_t)cache_capacity < pos_offset + L)
+    return fail(GDLA_ERR_INVALID_ARG, "cache_capacity %d < pos_offset + L = %lld", cache_capacity,
+                (long long)(pos_offset + L));
+  if (pos_offset + L > (int64_t)1 << 30) return fail(GDLA_ERR_INVALID_ARG, "positions beyond 2^30");
+  const PrefillLayout P = prefill_layout(dims_of(cfg), (int64_t)B * L, 0);
+  if (!workspace) return fail(GDLA_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", P.total);
+  if (((uintptr_t)workspace & 255) != 0) return fail(GDLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < P.total)
+    return fail(GDLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, P.total);
+  const Stream S{(int64_t)B * L, B, L, pos_offset, nullptr, 0, nullptr};
+  const gdla::CacheView view{cache, nullptr, cache_capacity, 1, B};
+  return run_prefill(cfg, w, S, x, y, residual, view, (char*)workspace, P, (hipStream_t)stream, stages);
+}
+
+size_t gdla_prefill_packed_workspace_size(const gdla_config* cfg, int32_t n_seq, int64_t T) {
+  if (check_config(cfg) != GDLA_OK || n_seq < 0 || T < 0) return 0;
+  const bool bf = cfg->dtype == GDLA_BF16;
+  if (T > (bf ? PACKED_MAX_T : 8192) || n_seq > PACKED_MAX_T) return 0;
+  const size_t plan = packed_plan_bytes(cfg, n_seq, T);
+  if (bf && plan == 0) return 0;
+  return prefill_layout(dims_of(cfg), T, plan).total;
+}
+
+gdla_status gdla_prefill_packed(const gdla_config* cfg, const gdla_weights* w, int32_t n_seq, int64_t T,
+                                const int32_t* cu_seqlens, const int32_t* pos_offsets, const void* x, void* y,
+                                const void* residual, const gdla_paged_cache* cache, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  gdla_status st = check_config(cfg);
+  if (st != GDLA_OK) return st;
+  if (n_seq < 0 || T < 0) return fail(GDLA_ERR_INVALID_ARG, "n_seq and T must be >= 0");
+  if (T == 0) return GDLA_OK;
+  if (n_seq == 0) return fail(GDLA_ERR_INVALID_ARG, "T = %lld tokens but no sequences", (long long)T);
+  const bool bf = cfg->dtype == GDLA_BF16;
+  if (T > (bf ? PACKED_MAX_T : 8192))
+    return fail(GDLA_ERR_UNSUPPORTED, "packed prefill supports T <= %lld (got %lld)", (long long)(bf ? PACKED_MAX_T : 8192),
+                (long long)T);
+  if (n_seq > PACKED_MAX_T) return fail(GDLA_ERR_UNSUPPORTED, "packed prefill supports n_seq <= 2^20");
+  st = check_weights(w);
+  if (st != GDLA_OK) return st;
+  if (!x || !y || !cu_seqlens) return fail(GDLA_ERR_INVALID_ARG, "x, y and cu_seqlens must be non-NULL");
+  if (!aligned16(x) || !aligned16(y) || (residual && !aligned16(residual)))
+    return fail(GDLA_ERR_INVALID_ARG, "x, y and residual must be 16-byte aligned");
+  if (((uintptr_t)cu_seqlens & 3) || ((uintptr_t)pos_offsets & 3))
+    return fail(GDLA_ERR_INVALID_ARG, "cu_seqlens and pos_offsets must be 4-byte aligned");
+  if (x == y) return fail(GDLA_ERR_INVALID_ARG, "y must not alias x");
+  if (cache && (st = check_paged(cache)) != GDLA_OK) return st;
+  const PrefillLayout P = prefill_layout(dims_of(cfg), T, packed_plan_bytes(cfg, n_seq, T));
+  if (!workspace) return fail(GDLA_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", P.total);
+  if (((uintptr_t)workspace & 255) != 0) return fail(GDLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < P.total)
+    return fail(GDLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, P.total);
+  const Stream S{T, 0, 0, 0, cu_seqlens, n_seq, pos_offsets};
+  const gdla::CacheView view = cache ? paged_view(cache) : gdla::CacheView{nullptr, nullptr, 1, 1, 0};
+  return run_prefill(cfg, w, S, x, y, residual, view, (char*)workspace, P, (hipStream_t)stream, GDLA_STAGE_ALL);
 }
 
 gdla_status gdla_latent_expand(const gdla_config* cfg, int64_t T, const void* c_kv, int64_t ld_c, const void* g_kv,
@@ -340,9 +436,11 @@ size_t gdla_decode_workspace_size(const gdla_config* cfg, int32_t B) {
   return gdla::decode_workspace_bytes(cfg, B);
 }
 
-gdla_status gdla_decode(const gdla_config* cfg, const gdla_weights* w, int32_t B, const void* x, void* y, void* cache,
-                        const int32_t* cache_lens, int32_t capacity, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+namespace {
+
+// Checks shared by the dense and paged decode entry points (everything but the cache).
+gdla_status check_decode(const gdla_config* cfg, const gdla_weights* w, int32_t B, const void* x, void* y,
+                         const int32_t* cache_lens, void* workspace, size_t workspace_bytes) {
   gdla_status st = check_config(cfg);
   if (st != GDLA_OK) return st;
   if (cfg->dtype != GDLA_BF16) return fail(GDLA_ERR_UNSUPPORTED, "decode is bf16 only");
@@ -350,17 +448,42 @@ gdla_status gdla_decode(const gdla_config* cfg, const gdla_weights* w, int32_t B
     return fail(GDLA_ERR_UNSUPPORTED, "decode needs kv_rank in {128, 256, 512} and at most 80 query heads");
   if (B < 0) return fail(GDLA_ERR_INVALID_ARG, "B must be >= 0");
   if (B == 0) return GDLA_OK;
-  if (capacity <= 0) return fail(GDLA_ERR_INVALID_ARG, "capacity must be positive");
   st = check_weights(w);
   if (st != GDLA_OK) return st;
-  if (!x || !y || !cache || !cache_lens) return fail(GDLA_ERR_INVALID_ARG, "x, y, cache and cache_lens must be non-NULL");
-  if (!aligned16(x) || !aligned16(y) || !aligned16(cache) || ((uintptr_t)cache_lens & 3))
-    return fail(GDLA_ERR_INVALID_ARG, "x, y, cache must be 16-byte aligned, cache_lens 4-byte aligned");
+  if (!x || !y || !cache_lens) return fail(GDLA_ERR_INVALID_ARG, "x, y and cache_lens must be non-NULL");
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)cache_lens & 3))
+    return fail(GDLA_ERR_INVALID_ARG, "x, y must be 16-byte aligned, cache_lens 4-byte aligned");
   const size_t need = gdla::decode_workspace_bytes(cfg, B);
   if (!workspace) return fail(GDLA_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", need);
   if (((uintptr_t)workspace & 255) != 0) return fail(GDLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (workspace_bytes < need) return fail(GDLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-  hipError_t err = gdla::decode_step(cfg, w, B, x, y, cache, cache_lens, capacity, workspace, (hipStream_t)stream);
+  return GDLA_OK;
+}
+
+}  // namespace
+
+gdla_status gdla_decode(const gdla_config* cfg, const gdla_weights* w, int32_t B, const void* x, void* y, void* cache,
+                        const int32_t* cache_lens, int32_t capacity, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  gdla_status st = check_decode(cfg, w, B, x, y, cache_lens, workspace, workspace_bytes);
+  if (st != GDLA_OK || B == 0) return st;
+  if (capacity <= 0) return fail(GDLA_ERR_INVALID_ARG, "capacity must be positive");
+  if (!cache) return fail(GDLA_ERR_INVALID_ARG, "cache must be non-NULL");
+  if (!aligned16(cache)) return fail(GDLA_ERR_INVALID_ARG, "cache must be 16-byte aligned");
+  const gdla::CacheView view{cache, nullptr, capacity, 1, B};
+  hipError_t err = gdla::decode_step(cfg, w, B, x, y, view, cache_lens, workspace, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "decode");
+  return GDLA_OK;
+}
+
+gdla_status gdla_decode_paged(const gdla_config* cfg, const gdla_weights* w, int32_t B, const void* x, void* y,
+                              const gdla_paged_cache* cache, const int32_t* cache_lens, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  gdla_status st = check_decode(cfg, w, B, x, y, cache_lens, workspace, workspace_bytes);
+  if (st != GDLA_OK || B == 0) return st;
+  if (!cache) return fail(GDLA_ERR_INVALID_ARG, "cache must be non-NULL");
+  if ((st = check_paged(cache)) != GDLA_OK) return st;
+  hipError_t err = gdla::decode_step(cfg, w, B, x, y, paged_view(cache), cache_lens, workspace, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "decode");
   return GDLA_OK;
 }

@@ -122,25 +122,37 @@ attn_bf16_kernel(AttnArgs a) {
   // wave w: query head slot w % (G+1), query half w / (G+1); waves w and w+4 share a SIMD
   const int hs = w % (G + 1), half = HV == 2 ? w / (G + 1) : 0;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int L = a.L, nN = a.nN, nS = G * nN, W = a.window;
 
-  // workgroup -> (sequence, KV head, query block)
-  const int HN = a.B * nN, nqb = cdiv(L, BQ);
-  int id = blockIdx.x, hn, qbi;
-  if ((HN & 7) == 0) {
-    const int hpx = HN >> 3, slot = id >> 3;
-    hn = (id & 7) + 8 * (slot % hpx);
-    qbi = slot / hpx;
+  // workgroup -> (KV head n, work slot); XCD x = blockIdx % 8 keeps whole KV heads
+  const int nN = a.nN, nS = G * nN, W = a.window;
+  int id = blockIdx.x, n, slot;
+  if ((nN & 7) == 0) {
+    const int hpx = nN >> 3, s8 = id >> 3;
+    n = (id & 7) + 8 * (s8 % hpx);
+    slot = s8 / hpx;
   } else {
-    hn = id % HN;
-    qbi = id / HN;
+    n = id % nN;
+    slot = id / nN;
   }
-  const int qb = nqb - 1 - qbi;
-  const int b = hn / nN, n = hn % nN;
-  const int q0 = qb * BQ;
-  const int64_t tb = (int64_t)b * L;
+  // work slot -> (first stream row tb of the sequence, its length L, query block q0),
+  // heaviest query blocks first
+  int64_t tb;
+  int L, q0;
+  if (a.plan) {
+    if (slot >= a.plan[0]) return;
+    const int4 it = reinterpret_cast<const int4*>(a.plan + 4)[slot];
+    tb = it.x;
+    L = it.y;
+    q0 = it.z;
+  } else {
+    const int nqb = cdiv(a.L, BQ), b = slot % a.B;
+    L = a.L;
+    q0 = (nqb - 1 - slot / a.B) * BQ;
+    tb = (int64_t)b * L;
+  }
+  const int64_t T = a.T;
   const int head = hs < G ? n * G + hs : nS + n;
-  const int qw0 = q0 + 32 * half;                 // first query of this wave
+  const int qw0 = q0 + 32 * half;                 // first query of this wave (within the sequence)
   const int qme = qw0 + l32;                       // this lane's query
   const int qlast = min(qw0 + 31, L - 1);
   const float sc = a.scale * 1.4426950408889634f;  // exp2 domain
@@ -153,18 +165,19 @@ attn_bf16_kernel(AttnArgs a) {
     for (int s = 0; s < DQK / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
   }
 
-  // key tiles this workgroup visits
+  // key tiles this workgroup visits: 32-row tiles of the stream (aligned to the
+  // stream, so a tile may begin in the previous sequence; those rows are masked)
   const int k_lo = W > 0 ? max(0, q0 - W + 1) : 0;
   const int k_hi = min(L, q0 + BQ);
-  const int t_lo = k_lo / BKV, t_hi = cdiv(k_hi, BKV);
+  const int t_lo = (int)((tb + k_lo) / BKV), t_hi = (int)cdiv(tb + k_hi, (int64_t)BKV);
 
-  const bf16* kc = (const bf16*)a.kc + tb * a.ld_kc + (int64_t)n * DN;
-  const bf16* kr = (const bf16*)a.kr + tb * DR;
-  const bf16* vt = (const bf16*)a.vt + (int64_t)n * DV * a.ld_vt + (int64_t)b * a.vt_seq;
+  const bf16* kc = (const bf16*)a.kc + (int64_t)n * DN;
+  const bf16* kr = (const bf16*)a.kr;
+  const bf16* vt = (const bf16*)a.vt + (int64_t)n * DV * a.ld_vt;
 
   // issue the loads of one tile into LDS buffer buf (1 KB blocks round-robin over waves)
   auto load_tile = [&](int tile, int buf) {
-    const int kb = tile * BKV;
+    const int64_t kb = (int64_t)tile * BKV;
     unsigned char* base = smem_raw + buf * TILE_BYTES;
 #pragma unroll
     for (int blk = w; blk < TILE_KB; blk += NW) {
@@ -173,13 +186,13 @@ attn_bf16_kernel(AttnArgs a) {
         const void* src;
         if (pos < K_CHUNKS) {
           const int r = pos / KROW_CH, c = pos % KROW_CH;   // c == 24: pad chunk
-          const int key = min(kb + r, L - 1);      // rows past L repeat a valid row; masked to -inf
+          const int64_t key = min(kb + r, T - 1);  // rows past the stream repeat a valid row (masked)
           src = c < DN / 8 ? (const void*)(kc + (int64_t)key * a.ld_kc + c * 8)
                            : (const void*)(kr + (int64_t)key * DR + min(c - DN / 8, DR / 8 - 1) * 8);
         } else {
           const int pv = pos - K_CHUNKS;
           const int d = pv / VROW_CH, c = min(pv % VROW_CH, VROW_CH - 2);   // pad chunk -> chunk 3
-          // value columns past L lie in the zero-filled padding of V^T
+          // value columns past T lie in the zero-filled padding of V^T
           src = vt + (int64_t)d * a.ld_vt + kb + c * 8;
         }
         g2lds16(src, base + blk * 1024);
@@ -208,10 +221,10 @@ attn_bf16_kernel(AttnArgs a) {
   };
   // softmax, first half: masks on boundary tiles, tile max, lazy rescale of O
   // (branches; rare after the first tiles)
-  auto softmax_max = [&](f32x16& s, int kb) {
-    const bool full = kb + BKV - 1 <= qw0 && kb + BKV <= L && (W <= 0 || kb > qlast - W);
+  auto softmax_max = [&](f32x16& s, int kb) {   // kb: first key of the tile, within the sequence
+    const bool full = kb >= 0 && kb + BKV - 1 <= qw0 && kb + BKV <= L && (W <= 0 || kb > qlast - W);
     if (!full) {
-      const int lo_ok = W > 0 ? qme - W + 1 : 0;   // keys in [lo_ok, min(qme, L-1)] are visible
+      const int lo_ok = W > 0 ? max(0, qme - W + 1) : 0;   // keys in [lo_ok, min(qme, L-1)] are visible
       const unsigned span = (unsigned)(min(qme, L - 1) - lo_ok);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -271,7 +284,7 @@ attn_bf16_kernel(AttnArgs a) {
   __syncthreads();
   qk(t_lo % 3, sA);
   auto step = [&](int tile, f32x16& cur, f32x16& nxt, bool has_next) {
-    const int kb = tile * BKV;
+    const int kb = (int)((int64_t)tile * BKV - tb);
     if (tile + 2 < t_hi) load_tile(tile + 2, (tile + 2) % 3);
     if (lead) {
       if (has_next) qk((tile + 1) % 3, nxt);
@@ -346,19 +359,31 @@ attn_bf16_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------ fp32 kernel
-// One workgroup per (query position, KV head, sequence).  Noise head first
-// (its H stays in LDS), then each signal head: scores into LDS, block max,
-// exp and sum, then H over value dims, then Z = gate * (H - lambda * H_N).
+// One workgroup per (stream row, KV head).  Noise head first (its H stays in
+// LDS), then each signal head: scores into LDS, block max, exp and sum, then H
+// over value dims, then Z = gate * (H - lambda * H_N).
 __global__ void __launch_bounds__(256)
 attn_f32_kernel(AttnArgs a) {
   extern __shared__ float fsm[];
-  const int L = a.L;
-  const int t = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
+  const int64_t row = blockIdx.x;
+  const int n = blockIdx.y;
+  // the sequence holding this row: [tb, tb + L)
+  int64_t tb;
+  int L;
+  if (a.cu) {
+    const int b = packed_seq_of(a.cu, a.nseq, row);
+    tb = min(max((int64_t)a.cu[b], (int64_t)0), a.T);
+    L = (int)(min(max((int64_t)a.cu[b + 1], tb), a.T) - tb);
+    if (row < tb || row >= tb + L) return;          // a row outside every sequence
+  } else {
+    tb = row / a.L * a.L;
+    L = a.L;
+  }
+  const int t = (int)(row - tb);
   const int nS = a.g * a.nN, dqk = a.d_nope + a.d_rope, dv = a.d_v;
   float* sc = fsm;             // [L]
   float* hN = fsm + L;         // [dv]
   float* red = hN + dv;        // [64]
-  const int64_t tb = (int64_t)b * L;
   const int lo = a.window > 0 ? max(0, t - a.window + 1) : 0;
   const float* qv = (const float*)a.q;
   const float* kc = (const float*)a.kc;
@@ -396,7 +421,7 @@ attn_f32_kernel(AttnArgs a) {
     sum = 0.f;
     for (int i = 0; i < (int)(blockDim.x >> 6); ++i) sum += red[i];
     for (int d = threadIdx.x; d < dv; d += blockDim.x) {
-      const float* v = vt + (int64_t)(n * dv + d) * a.ld_vt + (int64_t)b * a.vt_seq;
+      const float* v = vt + (int64_t)(n * dv + d) * a.ld_vt + tb;
       float acc = 0.f;
       for (int s = lo; s <= t; ++s) acc += sc[s - lo] * v[s];
       const float H = acc / sum;
@@ -423,9 +448,101 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int blocks = a.B * a.nN * cdiv(a.L, 32 * halves<G>());
-  hipLaunchKernelGGL(attn_bf16_kernel<G>, dim3(blocks), dim3(64 * halves<G>() * (G + 1)), lds, s, a);
+  const int64_t slots = a.plan ? a.items_cap : (int64_t)a.B * cdiv(a.L, 32 * halves<G>());
+  const int64_t blocks = slots * a.nN;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_bf16_kernel<G>, dim3((unsigned)blocks), dim3(64 * halves<G>() * (G + 1)), lds, s, a);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------ packed plan
+// Work items of the packed bf16 attention: item (sequence b, block level j)
+// covers queries j*BQ .. j*BQ + BQ - 1 of sequence b.  The cost of an item
+// (key tiles visited) grows with j for causal and window masks alike, so the
+// list is ordered by level, highest first: the hardware dispatcher, which
+// starts workgroups in index order as slots free up, then runs a
+// longest-processing-time-first schedule.  Level j holds the sequences with
+// more than j blocks; with the sequences sorted by block count (counting
+// sort, ties in any order) those are a prefix of the sorted list, so item i
+// is found by a binary search over the level starts.
+// Plan layout (int32): [0] item count, [1..3] unused, int4 items[cap] =
+// {first stream row, length, first query, 0}, then perm[nseq].
+constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_LDS_INTS = 40 * 1024;   // 160 KB: 2 * PLAN_THREADS for the 64-bit partials, then A
+
+// A[v] <- min(sum of A[m] over m > v, cap) for v < n, by the 1024 threads of
+// the block (64-bit sums: a malformed offset list cannot overflow them)
+__device__ void suffix_scan_excl(int* A, int n, long long* part, int cap) {
+  const int tid = threadIdx.x;
+  const int per = (n + PLAN_THREADS - 1) / PLAN_THREADS;
+  const int b0 = min(n, tid * per), b1 = min(n, b0 + per);
+  long long own = 0;
+  for (int i = b0; i < b1; ++i) own += A[i];
+  part[tid] = own;
+  __syncthreads();
+  for (int off = 1; off < PLAN_THREADS; off <<= 1) {   // inclusive suffix sums of the chunk totals
+    const long long v = tid + off < PLAN_THREADS ? part[tid + off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  long long run = part[tid] - own;   // everything after this thread's chunk
+  for (int i = b1 - 1; i >= b0; --i) {
+    const int v = A[i];
+    A[i] = (int)min(run, (long long)cap);
+    run += v;
+  }
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(PLAN_THREADS)
+attn_plan_kernel(const int32_t* cu, int nseq, int T, int bq, int nlev, int* plan) {
+  extern __shared__ long long psh[];   // part[PLAN_THREADS] (64-bit), then A[nlev + 1]
+  long long* part = psh;
+  int* A = reinterpret_cast<int*>(psh + PLAN_THREADS);
+  const int tid = threadIdx.x;
+  const int cap = nlev + nseq;
+  int4* items = reinterpret_cast<int4*>(plan + 4);
+  int* perm = plan + 4 + 4 * cap;
+  auto bounds = [&](int b, int& s0, int& len) {   // clamped into [0, T], nondecreasing
+    s0 = min(max(cu[b], 0), T);
+    len = min(max(cu[b + 1], s0), T) - s0;
+  };
+  for (int i = tid; i <= nlev; i += PLAN_THREADS) A[i] = 0;
+  __syncthreads();
+  for (int b = tid; b < nseq; b += PLAN_THREADS) {   // histogram of block counts
+    int s0, len;
+    bounds(b, s0, len);
+    atomicAdd(&A[(len + bq - 1) / bq], 1);
+  }
+  __syncthreads();
+  suffix_scan_excl(A, nlev + 1, part, INT32_MAX);   // A[v] = sequences with more than v blocks
+  for (int b = tid; b < nseq; b += PLAN_THREADS) {   // perm: sequences by block count, descending
+    int s0, len;
+    bounds(b, s0, len);
+    const int v = (len + bq - 1) / bq;
+    if (v > 0) perm[atomicAdd(&A[v], 1)] = b;
+  }
+  __syncthreads();
+  // now A[v] (v >= 1) = sequences with at least v blocks = items of level v - 1;
+  // after the next scan, level j occupies items [A[j + 1], A[j]).  Starts are
+  // capped at the grid's slot count: a well-formed list never reaches it, a
+  // malformed one (overlapping sequences) loses the items past it.
+  suffix_scan_excl(A, nlev + 1, part, cap);
+  const int total = A[0];
+  if (tid == 0) plan[0] = total;
+  for (int i = tid; i < total; i += PLAN_THREADS) {
+    int lo = 0, hi = nlev - 1;   // the smallest j with A[j + 1] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (A[mid + 1] <= i) hi = mid; else lo = mid + 1;
+    }
+    const int b = perm[i - A[lo + 1]];
+    int s0, len;
+    bounds(b, s0, len);
+    items[i] = make_int4(s0, len, lo * bq, 0);
+  }
 }
 
 }  // namespace
@@ -440,8 +557,36 @@ size_t attn_bf16_lds_bytes(int g) {
   }
 }
 
+int attn_block_q(int g) { return g <= 3 ? 64 : 32; }
+
+int attn_plan_items(int nseq, int64_t T, int g) {
+  return (int)((T + attn_block_q(g) - 1) / attn_block_q(g)) + nseq;
+}
+
+size_t attn_plan_bytes(int nseq, int64_t T, int g) {
+  const int64_t nlev = (T + attn_block_q(g) - 1) / attn_block_q(g);
+  if (nlev + 1 + 2 * PLAN_THREADS > PLAN_LDS_INTS) return 0;
+  return (4 + 4 * (size_t)attn_plan_items(nseq, T, g) + (size_t)nseq) * sizeof(int);
+}
+
+hipError_t attn_plan(const int32_t* cu, int nseq, int64_t T, int g, int* plan, hipStream_t s) {
+  const int bq = attn_block_q(g);
+  const int nlev = (int)((T + bq - 1) / bq);
+  if (nlev + 1 + 2 * PLAN_THREADS > PLAN_LDS_INTS) return hipErrorInvalidValue;
+  const size_t lds = ((size_t)nlev + 1 + 2 * PLAN_THREADS) * sizeof(int);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       PLAN_LDS_INTS * (int)sizeof(int));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(PLAN_THREADS), lds, s, cu, nseq, (int)T, bq, nlev, plan);
+  return hipGetLastError();
+}
+
 hipError_t attn_bf16(const AttnArgs& a, hipStream_t s) {
-  if (a.B <= 0 || a.L <= 0) return hipSuccess;
+  if (a.T <= 0) return hipSuccess;
   switch (a.g) {
     case 1: return launch_g<1>(a, s);
     case 2: return launch_g<2>(a, s);
@@ -452,14 +597,15 @@ hipError_t attn_bf16(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t attn_f32(const AttnArgs& a, hipStream_t s) {
-  if (a.B <= 0 || a.L <= 0) return hipSuccess;
-  const size_t lds = ((size_t)a.L + a.d_v + 64) * sizeof(float);
+  if (a.T <= 0) return hipSuccess;
+  const int64_t lmax = a.cu ? a.T : a.L;   // longest possible sequence
+  const size_t lds = ((size_t)lmax + a.d_v + 64) * sizeof(float);
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_f32_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(attn_f32_kernel, dim3(a.L, a.nN, a.B), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)a.T, a.nN), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 

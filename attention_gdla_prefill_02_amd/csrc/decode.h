@@ -6,13 +6,16 @@
 #include <stddef.h>
 
 #include "../../include/gdla.h"
+#include "kernels.h"
 
 namespace gdla {
 
 // Shapes the decode kernels cover (bf16; kv_rank 128, 256 or 512; at most 80 query heads).
 bool decode_supported(const gdla_config* cfg);
 size_t decode_workspace_bytes(const gdla_config* cfg, int B);
-hipError_t decode_step(const gdla_config* cfg, const gdla_weights* w, int B, const void* x, void* y, void* cache,
-                       const int32_t* cache_lens, int capacity, void* workspace, hipStream_t s);
+// One step: row cache_lens[b] of sequence b is written, then attended with its
+// predecessors (the window's part), all through `cache`.
+hipError_t decode_step(const gdla_config* cfg, const gdla_weights* w, int B, const void* x, void* y,
+                       const CacheView& cache, const int32_t* cache_lens, void* workspace, hipStream_t s);
 
 }  // namespace gdla

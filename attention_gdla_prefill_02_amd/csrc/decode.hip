@@ -428,6 +428,13 @@ __device__ __forceinline__ PlanView plan_view(const int* P, int B) {
   return v;
 }
 
+// 32-row tiles covering attended rows [lo, lo + len): tiles start at multiples
+// of 32 (a tile never straddles a page of a paged cache); rows before lo in
+// the first tile are masked.
+__device__ __forceinline__ int tiles_of(int lo, int len) {
+  return len > 0 ? ((lo + len - 1) >> 5) - (lo >> 5) + 1 : 0;
+}
+
 // Workgroups in use: W = min(DEC_WGS, T), so that no range is empty and the
 // workgroups covering one sequence are consecutive.  Workgroup k < W takes
 // tiles [k T / W, (k + 1) T / W); tile t belongs to the largest k with k T / W <= t.
@@ -454,7 +461,7 @@ __device__ int block_incl_scan(int v, int* sc, int* total) {
 }
 
 __global__ void __launch_bounds__(256)
-plan_kernel(const int32_t* lens, int B, int cap, int window, int* plan) {
+plan_kernel(const int32_t* lens, int B, int64_t cap, int window, int* plan) {
   __shared__ int sc[256];
   int* tstart = plan + 2;
   int* lo = tstart + B + 1;
@@ -473,7 +480,7 @@ plan_kernel(const int32_t* lens, int B, int cap, int window, int* plan) {
       const int l0 = (window > 0) ? max(0, p - window + 1) : 0;
       lo[b] = ok ? l0 : 0;
       len[b] = ok ? p + 1 - l0 : 0;
-      nt = ok ? (p + 1 - l0 + DEC_TK - 1) / DEC_TK : 0;
+      nt = ok ? tiles_of(l0, p + 1 - l0) : 0;
     }
     int tot;
     const int incl = block_incl_scan(nt, sc, &tot);
@@ -487,7 +494,7 @@ plan_kernel(const int32_t* lens, int B, int cap, int window, int* plan) {
     const int b = base + tid;
     int segs = 0;
     if (b < B) {
-      const int t0 = tstart[b], nt = (len[b] + DEC_TK - 1) / DEC_TK;
+      const int t0 = tstart[b], nt = tiles_of(lo[b], len[b]);
       int k0 = 0;
       if (nt > 0) {
         k0 = tile_owner(t0, T);
@@ -529,8 +536,8 @@ plan_kernel(const int32_t* lens, int B, int cap, int window, int* plan) {
 // ------------------------------------------------------------ latent attention
 struct DecAttnArgs {
   const bf16* qlat;        // [B, H, RL]
-  const bf16* cache;       // [B, cap, RL]
-  int cap, B, H;
+  CacheView cache;         // rows of RL elements
+  int B, H;
   const int* plan;
   float* part_ml;          // [segments][H][2]: running max (exp2 domain) and sum
   float* part_o;           // [segments][H][KVR]: sum of p * c (relative to the max)
@@ -577,34 +584,41 @@ dec_attn_kernel(DecAttnArgs a) {
   // (l & 7) ^ ((l >> 3) & 6) of its line, which lands in slot l
   const int lrow = lane >> 3, lch = (lane & 7) ^ ((lane >> 3) & 6);
   struct Seq {
-    int b, tend, row0, rend;   // tiles < tend; tile t starts at row row0 + TK t; rows < rend attended
-    const bf16* base;
+    // tiles < tend; tile t starts at position row0 + TK t; positions [rlo, rend) attended
+    int b, tend, row0, rlo, rend;
   };
   auto seq_at = [&](int b) {   // all fields are wave-uniform
     Seq q;
     q.b = b;
     q.tend = __builtin_amdgcn_readfirstlane(pv.tstart[b + 1]);
-    q.row0 = __builtin_amdgcn_readfirstlane(pv.lo[b] - TK * pv.tstart[b]);
-    q.rend = __builtin_amdgcn_readfirstlane(pv.lo[b] + pv.len[b]);
-    q.base = a.cache + (int64_t)b * a.cap * RL;
+    q.rlo = __builtin_amdgcn_readfirstlane(pv.lo[b]);
+    q.row0 = (q.rlo & ~(TK - 1)) - TK * __builtin_amdgcn_readfirstlane(pv.tstart[b]);
+    q.rend = q.rlo + __builtin_amdgcn_readfirstlane(pv.len[b]);
     return q;
   };
   auto seq_for = [&](Seq q, int t) {   // advance past sequences that end at or before tile t
     while (t >= q.tend) q = seq_at(q.b + 1);
     return q;
   };
+  // Issue the loads of tile t into buffer buf; returns false when the tile's
+  // page is missing from the table (the tile is then loaded from row 0 of the
+  // pool and not used).
   auto load_tile = [&](const Seq& q, int t, int buf) {
+    const int ts = q.row0 + TK * t;   // first position of the tile, a multiple of 32
+    const int64_t r0 = cache_row_index(a.cache, q.b, ts);
+    const bf16* tbase = (const bf16*)a.cache.base + (r0 < 0 ? 0 : r0) * RL;
     const bf16* src[4];
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {   // rows past the end repeat a valid row (masked)
-      const int key = min(q.row0 + TK * t + 8 * rg + lrow, q.rend - 1);
-      src[rg] = q.base + (int64_t)key * RL + 8 * lch;
+    for (int rg = 0; rg < 4; ++rg) {   // rows outside [rlo, rend) repeat an attended row of the tile (masked)
+      const int key = min(max(ts + 8 * rg + lrow, q.rlo), q.rend - 1) - ts;
+      src[rg] = tbase + (int64_t)key * RL + 8 * lch;
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int blk = wave + NW * i;   // compile-time row group and line of each block
       if (blk < TBLK) g2lds16_stream(src[blk & 3] + 64 * (blk >> 2), &tile[buf][blk * 512]);
     }
+    return r0 >= 0;
   };
   // per-lane LDS slots of the fragment reads (16-byte units, block offsets added per read)
   int kslot[2], pslot[4];
@@ -635,7 +649,7 @@ dec_attn_kernel(DecAttnArgs a) {
   const int bl = __builtin_amdgcn_readfirstlane(pv.wgb[k]);
   Seq ls = seq_at(bl), cs = ls;
   // the first tile and the query fragment are in flight together (load_q waits for both)
-  load_tile(ls, tb, 0);
+  bool cur_ok = load_tile(ls, tb, 0), nxt_ok = true;
   load_q(cs.b);
   f32x4 o[DT];
 #pragma unroll
@@ -648,10 +662,11 @@ dec_attn_kernel(DecAttnArgs a) {
   for (int t = tb; t < te; ++t) {
     if (t + 1 < te) {
       ls = seq_for(ls, t + 1);
-      load_tile(ls, t + 1, buf ^ 1);
+      nxt_ok = load_tile(ls, t + 1, buf ^ 1);
     }
     const bf16* Tl = tile[buf];
     const int r0 = cs.row0 + TK * t;
+    if (cur_ok) {
     // scores S^T: lane holds head r16, tile rows 16 u + 4 q4 + j
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
     // lane reads chunk 4 s + q4 of row 16 u + r16: block 4 (s >> 1) + 2 u + (r16 >> 3),
@@ -672,7 +687,7 @@ dec_attn_kernel(DecAttnArgs a) {
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (r0 + 16 * u + 4 * q4 + j >= cs.rend) sacc[u][j] = -INFINITY;
+        if ((unsigned)(r0 + 16 * u + 4 * q4 + j - cs.rlo) >= (unsigned)(cs.rend - cs.rlo)) sacc[u][j] = -INFINITY;
         mt = fmaxf(mt, sacc[u][j]);
       }
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
@@ -704,6 +719,7 @@ dec_attn_kernel(DecAttnArgs a) {
       o[d] = mfma16(tr_pair(p0, p0 + 1024), pf, o[d]);
       if (d % 8 == 7) __builtin_amdgcn_sched_barrier(0);
     }
+    }   // cur_ok
     if (t + 1 == te || t + 1 >= cs.tend) {
       // end of a segment: write its partial
       float lt = lsum + __shfl_xor(lsum, 16, 64);
@@ -730,6 +746,7 @@ dec_attn_kernel(DecAttnArgs a) {
     vm_wait<0>();   // this wave's part of tile t + 1
     __syncthreads();
     buf ^= 1;
+    cur_ok = nxt_ok;
   }
 }
 
@@ -882,8 +899,8 @@ bool decode_supported(const gdla_config* c) {
 
 size_t decode_workspace_bytes(const gdla_config* cfg, int B) { return dec_layout(cfg, B).total; }
 
-hipError_t decode_step(const gdla_config* c, const gdla_weights* w, int B, const void* x, void* y, void* cache,
-                       const int32_t* cache_lens, int capacity, void* workspace, hipStream_t s) {
+hipError_t decode_step(const gdla_config* c, const gdla_weights* w, int B, const void* x, void* y,
+                       const CacheView& cache, const int32_t* cache_lens, void* workspace, hipStream_t s) {
   const DecLayout Lw = dec_layout(c, B);
   char* ws = (char*)workspace;
   const int nN = c->n_noise, g = c->group, nS = g * nN, H = nS + nN, rkv = c->kv_rank, rq = c->q_rank;
@@ -911,7 +928,7 @@ hipError_t decode_step(const gdla_config* c, const gdla_weights* w, int B, const
     r.g_q = w->g_q; r.g_kv = w->g_kv; r.eps = c->rms_eps;
     set_rope(r, c->rope_base, c->window, c->yarn_factor, c->yarn_orig_len, c->yarn_beta_fast, c->yarn_beta_slow);
     r.cqn = ws + Lw.cqn; r.ckvn = ws + Lw.ckvn; r.kr = ws + Lw.kr; r.lam = (float*)(ws + Lw.lam);
-    r.rope = (float*)(ws + Lw.rope); r.cache = cache; r.cache_cap = capacity; r.pos_dev = cache_lens;
+    r.rope = (float*)(ws + Lw.rope); r.cache = cache; r.pos_dev = cache_lens;
     if ((err = rowprep(r, true, s)) != hipSuccess) return err;
   }
   // 3. query heads (RoPE) and gate
@@ -933,10 +950,11 @@ hipError_t decode_step(const gdla_config* c, const gdla_weights* w, int B, const
   }
   // 5. plan and latent attention
   int* plan = (int*)(ws + Lw.plan);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, cache_lens, B, capacity, c->window, plan);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, cache_lens, B,
+                     (int64_t)cache.page_rows * cache.max_pages, c->window, plan);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   {
-    DecAttnArgs k{(const bf16*)(ws + Lw.qlat), (const bf16*)cache, capacity, B, H, plan, (float*)(ws + Lw.ml),
+    DecAttnArgs k{(const bf16*)(ws + Lw.qlat), cache, B, H, plan, (float*)(ws + Lw.ml),
                   (float*)(ws + Lw.po), (float)(1.4426950408889634 / std::sqrt((double)DQK))};
     const int grid = DEC_WGS;
     switch (rkv) {

@@ -43,16 +43,48 @@ hipError_t gemm_f32(const GemmArgs& a, hipStream_t s);
 hipError_t qg_finish(float* q, int64_t ldq, float* g, int64_t ldg, int64_t T, int heads, int gate_cols, int d_qk,
                      int d_nope, int d_rope, const float* rope, hipStream_t s);
 
+// Where the cache rows of a sequence live: page p / page_rows of the sequence
+// (its block-table entry) holds position p at row p % page_rows.  A dense
+// cache [B, capacity, row] is the case bt == nullptr: sequence b is page b and
+// page_rows = capacity.  A position outside [0, page_rows * max_pages), or a
+// table entry outside [0, num_pages), names no row.
+struct CacheView {
+  void* base;            // [num_pages, page_rows, kv_rank + d_rope]
+  const int32_t* bt;     // [sequences, max_pages], or nullptr (dense)
+  int page_rows, max_pages, num_pages;
+};
+
+__device__ __forceinline__ int64_t cache_row_index(const CacheView& c, int64_t seq, int64_t p) {
+  if (p < 0 || p >= (int64_t)c.page_rows * c.max_pages) return -1;
+  const int64_t j = p / c.page_rows;
+  const int64_t page = c.bt ? (int64_t)c.bt[seq * c.max_pages + j] : seq;
+  if (page < 0 || page >= c.num_pages) return -1;
+  return page * c.page_rows + (p - j * c.page_rows);
+}
+
+// Sequence of stream row t in a packed stream with offsets cu[0..nseq]: the
+// last b whose clamped start is <= t (b = 0 if none).
+__device__ __forceinline__ int packed_seq_of(const int32_t* cu, int nseq, int64_t t) {
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 struct RowPrepArgs {
   const float* down; int64_t ld_down;   // [T, q_rank + kv_rank + d_rope + nS]
   int64_t T; int L; int64_t pos_offset;
+  const int32_t* cu; int nseq;           // packed stream: sequence offsets [nseq + 1] (else nullptr)
+  const int32_t* seq_pos;                // packed stream: first position of each sequence (nullable: 0)
   int q_rank, kv_rank, d_rope, nS;
   const void* g_q; const void* g_kv;
   float eps; double rope_base;
   double yarn_s, yarn_short, yarn_long, yarn_m;   // YaRN (yarn_s > 1): wavelength bounds and cos/sin factor
   void* cqn; void* ckvn; void* kr; float* lam; float* rope;
   bool split_kv;                         // ckvn rows are [hi | lo] (2*kv_rank wide)
-  void* cache; int cache_cap;            // nullable
+  CacheView cache;                       // base nullable: no cache rows written
   const int32_t* pos_dev;                // decode: per-row positions (device), else null;
                                          // row b is then sequence b at position pos_dev[b]
   int nsplit; int64_t split_stride;      // down holds nsplit partial sums (elements apart); 0/1 = one
@@ -69,20 +101,36 @@ struct LatentNormArgs {
 };
 hipError_t latent_norm(const LatentNormArgs& a, bool bf16, hipStream_t s);
 
+// Attention over a stream of T token rows holding whole sequences: either B
+// sequences of L rows each (items == nullptr), or a packed stream whose
+// sequences the plan (attn_plan) has cut into query-block work items.
 struct AttnArgs {
   const void* q; int64_t ld_q;                        // query heads, head h at column h*d_qk
   const float* gate; int64_t ld_gate;                 // fp32 gate, signal head j at column j*d_v
   const void* kc; int64_t ld_kc;                      // [T, nN*d_nope]
   const void* kr;                                     // [T, d_rope]
-  const void* vt; int64_t ld_vt; int64_t vt_seq;      // [nN*d_v][ld_vt], sequence b at column b*vt_seq
+  const void* vt; int64_t ld_vt;                      // [nN*d_v][ld_vt]: column t = row t; zeros from T to ld_vt
   const float* lam;                                   // [T, nS]
   void* z;                                            // [T, nS*d_v]
-  int B, L, nN, g, window;
+  int64_t T;
+  int B, L;                                           // uniform sequences (items == nullptr)
+  const int* plan;                                    // packed (bf16): attn_plan's output, else nullptr
+  int items_cap;                                      // packed (bf16): work-item slots in the grid
+  const int32_t* cu; int nseq;                        // packed (fp32): sequence offsets [nseq + 1]
+  int nN, g, window;
   int d_nope, d_rope, d_v;
   float scale;                                        // 1/sqrt(d_nope + d_rope)
 };
 hipError_t attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t attn_f32(const AttnArgs& a, hipStream_t s);
 size_t attn_bf16_lds_bytes(int g);
+
+// Work list of the packed bf16 attention: every (sequence, query block) of
+// the stream, heaviest block level first.  plan_bytes is 0 when T is too
+// large for the plan kernel.
+int attn_block_q(int g);
+size_t attn_plan_bytes(int nseq, int64_t T, int g);
+int attn_plan_items(int nseq, int64_t T, int g);
+hipError_t attn_plan(const int32_t* cu, int nseq, int64_t T, int g, int* plan, hipStream_t s);
 
 }  // namespace gdla

@@ -37,6 +37,30 @@ __device__ __forceinline__ void rope_cos_sin(const RowPrepArgs& a, int i, int64_
 }
 namespace {
 
+// Position of row t and the cache row it is stored in (nullptr: none):
+//   decode (pos_dev): row t is sequence t at position pos_dev[t];
+//   packed stream (cu): the sequence holding row t, position seq_pos[b] + t - cu[b];
+//   uniform: sequence t / L at position pos_offset + t mod L.
+// Negative positions take the angles of position 0 and store nothing.
+template <class T>
+__device__ __forceinline__ T* locate_row(const RowPrepArgs& a, int64_t t, int64_t* p_out) {
+  int64_t seq, p;
+  if (a.pos_dev) {
+    seq = t;
+    p = a.pos_dev[t];
+  } else if (a.cu) {
+    const int b = packed_seq_of(a.cu, a.nseq, t);
+    seq = b;
+    p = (a.seq_pos ? (int64_t)a.seq_pos[b] : 0) + (t - a.cu[b]);
+  } else {
+    seq = t / a.L;
+    p = a.pos_offset + (t - seq * a.L);
+  }
+  const int64_t row = a.cache.base ? cache_row_index(a.cache, seq, p) : -1;
+  *p_out = p < 0 ? 0 : p;
+  return row >= 0 ? (T*)a.cache.base + row * (int64_t)(a.kv_rank + a.d_rope) : nullptr;
+}
+
 template <class T>
 __global__ void __launch_bounds__(256)
 rowprep_kernel(RowPrepArgs a) {
@@ -61,19 +85,8 @@ rowprep_kernel(RowPrepArgs a) {
   }
   const T* gq = (const T*)a.g_q;
   const T* gkv = (const T*)a.g_kv;
-  int64_t seq, p;
-  bool write_cache = a.cache != nullptr;
-  if (a.pos_dev) {
-    seq = t;
-    p = a.pos_dev[t];
-    if (p < 0 || p >= a.cache_cap) {   // outside the cache: nothing is written there
-      write_cache = false;
-      p = p < 0 ? 0 : p;
-    }
-  } else {
-    seq = t / a.L;
-    p = a.pos_offset + (t - seq * a.L);
-  }
+  int64_t p;
+  T* crow = locate_row<T>(a, t, &p);
 
   // query latent
   float ss = 0.f;
@@ -90,7 +103,6 @@ rowprep_kernel(RowPrepArgs a) {
   // split rows: [hi | lo] with hi = round(c_KVn), lo = round(c_KVn - hi); the
   // expansion then sees c_KVn to ~16 bits while the cache keeps hi
   T* ckvn = (T*)a.ckvn + t * (a.split_kv ? 2 * a.kv_rank : a.kv_rank);
-  T* crow = write_cache ? (T*)a.cache + (seq * a.cache_cap + p) * (int64_t)(a.kv_rank + a.d_rope) : nullptr;
   for (int i = lane; i < a.kv_rank; i += 64) {
     const float f = ckv[i] * r * to_f32(gkv[i]);
     const T v = from_f32<T>(f);
@@ -165,19 +177,8 @@ rowprep_block_kernel(RowPrepArgs a) {
   __syncthreads();
   const T* gq = (const T*)a.g_q;
   const T* gkv = (const T*)a.g_kv;
-  int64_t seq, p;
-  bool write_cache = a.cache != nullptr;
-  if (a.pos_dev) {
-    seq = t;
-    p = a.pos_dev[t];
-    if (p < 0 || p >= a.cache_cap) {   // outside the cache: nothing is written there
-      write_cache = false;
-      p = p < 0 ? 0 : p;
-    }
-  } else {
-    seq = t / a.L;
-    p = a.pos_offset + (t - seq * a.L);
-  }
+  int64_t p;
+  T* crow = locate_row<T>(a, t, &p);
   float ss = 0.f;
   for (int i = threadIdx.x; i < a.q_rank; i += blockDim.x) ss += brow[i] * brow[i];
   float r = 1.0f / sqrtf(block_sum(ss, red) / a.q_rank + a.eps);
@@ -188,7 +189,6 @@ rowprep_block_kernel(RowPrepArgs a) {
   for (int i = threadIdx.x; i < a.kv_rank; i += blockDim.x) ss += ckv[i] * ckv[i];
   r = 1.0f / sqrtf(block_sum(ss, red) / a.kv_rank + a.eps);
   T* ckvn = (T*)a.ckvn + t * (a.split_kv ? 2 * a.kv_rank : a.kv_rank);
-  T* crow = write_cache ? (T*)a.cache + (seq * a.cache_cap + p) * (int64_t)(a.kv_rank + a.d_rope) : nullptr;
   for (int i = threadIdx.x; i < a.kv_rank; i += blockDim.x) {
     const float f = ckv[i] * r * to_f32(gkv[i]);
     const T v = from_f32<T>(f);

@@ -21,7 +21,8 @@ GDLA_BF16, GDLA_FP32 = 0, 1
 STAGE_DOWN, STAGE_PREP, STAGE_EXPAND, STAGE_QG, STAGE_ATTN, STAGE_OUT, STAGE_ALL = 1, 2, 4, 8, 16, 32, 63
 EXPORTED = ("gdla_prefill_workspace_size", "gdla_prefill", "gdla_prefill_stages", "gdla_prefill_workspace_layout",
             "gdla_decode_workspace_size", "gdla_decode", "gdla_latent_expand", "gdla_status_string",
-            "gdla_last_error", "gdla_version")
+            "gdla_last_error", "gdla_version", "gdla_prefill_packed_workspace_size", "gdla_prefill_packed",
+            "gdla_decode_paged")
 
 
 class GdlaError(RuntimeError):
@@ -51,6 +52,11 @@ class PrefillLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("down", "cqn", "ckvn", "kr", "lam", "rope", "q", "gate", "kc", "vt", "z")]
 
 
+class PagedCache(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("page_rows", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -77,6 +83,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdla_decode_workspace_size.restype = sz
     lib.gdla_decode.argtypes = [cfgp, wp, i32, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.gdla_decode.restype = ctypes.c_int
+    pcp = ctypes.POINTER(PagedCache)
+    lib.gdla_prefill_packed_workspace_size.argtypes = [cfgp, i32, i64]
+    lib.gdla_prefill_packed_workspace_size.restype = sz
+    lib.gdla_prefill_packed.argtypes = [cfgp, wp, i32, i64, vp, vp, vp, vp, vp, pcp, vp, sz, vp]
+    lib.gdla_prefill_packed.restype = ctypes.c_int
+    lib.gdla_decode_paged.argtypes = [cfgp, wp, i32, vp, vp, pcp, vp, vp, sz, vp]
+    lib.gdla_decode_paged.restype = ctypes.c_int
     lib.gdla_latent_expand.argtypes = [cfgp, i64, vp, i64, vp, vp, vp, vp, vp, vp]
     lib.gdla_latent_expand.restype = ctypes.c_int
     lib.gdla_status_string.argtypes = [ctypes.c_int]
@@ -168,6 +181,50 @@ def decode(cfg: Config, W: dict, x: torch.Tensor, cache: torch.Tensor, cache_len
         workspace = alloc_workspace(decode_workspace_size(cfg, B), x.device)
     _check(load().gdla_decode(ctypes.byref(cfg), ctypes.byref(weights_struct(W)), B, _ptr(x), _ptr(y), _ptr(cache),
                               _ptr(cache_lens), cache.shape[1], _ptr(workspace), workspace.numel(), _stream(stream)))
+    return y
+
+
+def paged_cache(pages: torch.Tensor, block_table: torch.Tensor) -> PagedCache:
+    """pages [num_pages, page_rows, kv_rank + d_rope]; block_table int32 [sequences, max_pages]."""
+    return PagedCache(pages.data_ptr(), block_table.data_ptr(), pages.shape[1], block_table.shape[1],
+                      pages.shape[0])
+
+
+def prefill_packed_workspace_size(cfg: Config, n_seq: int, T: int) -> int:
+    return int(load().gdla_prefill_packed_workspace_size(ctypes.byref(cfg), n_seq, T))
+
+
+def prefill_packed(cfg: Config, W: dict, x: torch.Tensor, cu_seqlens: torch.Tensor, *, pos_offsets=None,
+                   y=None, residual=None, pages=None, block_table=None, workspace=None, stream=None,
+                   wstruct=None) -> torch.Tensor:
+    """One GDLA layer over packed sequences: x [T, d_model] -> y [T, d_model].
+    cu_seqlens, pos_offsets: device int32; pages / block_table: optional paged cache."""
+    T = x.shape[0]
+    n = cu_seqlens.numel() - 1
+    if y is None:
+        y = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(prefill_packed_workspace_size(cfg, n, T), x.device)
+    pc = None if pages is None else ctypes.byref(paged_cache(pages, block_table))
+    ws = wstruct if wstruct is not None else weights_struct(W)
+    _check(load().gdla_prefill_packed(ctypes.byref(cfg), ctypes.byref(ws), n, T, _ptr(cu_seqlens),
+                                      _ptr(pos_offsets), _ptr(x), _ptr(y), _ptr(residual), pc, _ptr(workspace),
+                                      workspace.numel(), _stream(stream)))
+    return y
+
+
+def decode_paged(cfg: Config, W: dict, x: torch.Tensor, pages: torch.Tensor, block_table: torch.Tensor,
+                 cache_lens: torch.Tensor, *, y=None, workspace=None, stream=None) -> torch.Tensor:
+    """One decode step against a paged cache: x [B, d_model] -> y [B, d_model]."""
+    B = x.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(decode_workspace_size(cfg, B), x.device)
+    pc = paged_cache(pages, block_table)
+    _check(load().gdla_decode_paged(ctypes.byref(cfg), ctypes.byref(weights_struct(W)), B, _ptr(x), _ptr(y),
+                                    ctypes.byref(pc), _ptr(cache_lens), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)))
     return y
 
 

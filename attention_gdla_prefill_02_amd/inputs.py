@@ -115,3 +115,33 @@ def sampled_rows(L: int, window: int, count: int, seed: int) -> list:
         if 0 <= r < L:
             rows.add(r)
     return sorted(rows)
+
+
+def packed_lengths(T: int, lo: int, hi: int, seed: int) -> list:
+    """Sequence lengths ~ U{lo..hi} drawn until they cover T tokens; the last
+    one is cut so that the lengths sum to exactly T."""
+    rng = np.random.Generator(np.random.PCG64(seed + 32452843))
+    out, total = [], 0
+    while total < T:
+        n = int(min(rng.integers(lo, hi + 1), T - total))
+        out.append(n)
+        total += n
+    return out
+
+
+def page_table(rows_needed, page_rows: int, seed: int, spare: int = 3, max_pages: int = 0):
+    """A shuffled page pool for sequences that need rows_needed[b] rows each:
+    every sequence gets ceil(rows / page_rows) distinct pages in random pool
+    order, `spare` pages belong to nobody, and unused table entries are -1.
+    Returns (block_table int32 [B, max_pages], num_pages)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 49979687))
+    need = [(int(r) + page_rows - 1) // page_rows for r in rows_needed]
+    mp = max(max_pages, max(need) if need else 1, 1)
+    num_pages = sum(need) + spare
+    order = rng.permutation(num_pages)
+    bt = np.full((len(need), mp), -1, dtype=np.int32)
+    k = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = order[k:k + n]
+        k += n
+    return bt, num_pages

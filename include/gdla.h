@@ -181,8 +181,8 @@ gdla_status gdla_prefill_stages(const gdla_config* cfg, const gdla_weights* w, i
  *   q      [T, H*(d_nope+d_rope)] query heads, rotary parts RoPE'd
  *   gate   [T, nS*d_v] fp32       sigmoid gate
  *   kc     [T, nN*d_nope]         content keys
- *   vt     [nN*d_v, B*Lp]         values transposed; sequence b's tokens at
- *                                 columns b*Lp .. b*Lp+L-1, Lp = L rounded up to 64
+ *   vt     [nN*d_v, Tp]           values transposed: token t in column t;
+ *                                 Tp = T rounded up to 64, columns T.. zero
  *   z      [T, nS*d_v]            gate * D                                     */
 typedef struct {
   int64_t down, cqn, ckvn, kr, lam, rope, q, gate, kc, vt, z;
@@ -211,6 +211,75 @@ gdla_status gdla_decode(const gdla_config* cfg, const gdla_weights* w, int32_t B
                         const void* x, void* y, void* cache, const int32_t* cache_lens,
                         int32_t capacity, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* A paged latent cache ("Open-Source Frontier Models: Architecture and
+ * Benchmarks of Rnj-1 and Motif-2", section 2, prefill sequence diagram: the
+ * normalized KV rows are stored in the blocks of a PagedAttention cache).
+ * The positions of sequence b are cut into blocks of page_rows; block j lives
+ * in pool page block_table[b * max_pages + j], so position p is row
+ * p % page_rows of page block_table[b * max_pages + p / page_rows].
+ *   pages        device [num_pages, page_rows, kv_rank + d_rope], config
+ *                dtype, 16-byte aligned; rows hold [c_KVn | RoPE(k_R)]
+ *   block_table  device int32 [sequences, max_pages], 4-byte aligned; read
+ *                on the device only
+ *   page_rows    rows per page: a positive multiple of 32
+ *   max_pages    block-table columns (> 0); positions run up to
+ *                page_rows * max_pages - 1 (that product at most 2^30)
+ *   num_pages    pages in the pool (> 0)
+ * Table entries are not trusted: a position whose entry lies outside
+ * [0, num_pages), or beyond the table, is neither written nor read (decode
+ * leaves such rows out of the attention).  Pages may sit anywhere in the
+ * pool and in any order; calls that write one row from two places race. */
+typedef struct {
+  void* pages;
+  const int32_t* block_table;
+  int32_t page_rows;
+  int32_t max_pages;
+  int32_t num_pages;
+} gdla_paged_cache;
+
+/* Bytes of workspace gdla_prefill_packed needs for n_seq sequences holding T
+ * tokens in all (0 if the configuration or the sizes are not supported). */
+size_t gdla_prefill_packed_workspace_size(const gdla_config* cfg, int32_t n_seq, int64_t T);
+
+/* One GDLA layer over n_seq complete sequences packed end to end into one
+ * stream of T tokens (report, long-context training paragraph: complete
+ * packed sequences).  Each sequence is the layer applied to it alone: its
+ * tokens attend only to earlier tokens of the same sequence, at positions
+ * that restart at pos_offsets[b].
+ *   cu_seqlens   device int32 [n_seq + 1], read on the device only: sequence b
+ *                holds stream rows cu_seqlens[b] .. cu_seqlens[b+1] - 1.  It
+ *                must be nondecreasing from cu_seqlens[0] = 0 to
+ *                cu_seqlens[n_seq] = T (empty sequences allowed).  Other
+ *                values cause no access outside the buffers, but rows that
+ *                no sequence holds get unspecified outputs.
+ *   pos_offsets  nullable device int32 [n_seq]: position of each sequence's
+ *                first token (>= 0; NULL means 0 for all)
+ *   x, y, residual  [T, d_model], as in gdla_prefill
+ *   cache        nullable: every token's row [c_KVn | RoPE(k_R)] goes to its
+ *                position in the paged cache, sequence b through row b of
+ *                the block table (the layout gdla_decode_paged reads)
+ *   workspace    at least gdla_prefill_packed_workspace_size bytes, 256-byte
+ *                aligned
+ * The attention runs one work item per (sequence, query block), ordered by
+ * cost, heaviest first (the report's longest-processing-time rule, applied to
+ * the workgroups of one GPU).  Limits: n_seq >= 0, T >= 0 (T = 0 is a no-op),
+ * T <= 2^20 and n_seq <= 2^20 (bf16), T <= 8192 (fp32).  All pointers 16-byte
+ * aligned except cu_seqlens and pos_offsets (4-byte). */
+gdla_status gdla_prefill_packed(const gdla_config* cfg, const gdla_weights* w, int32_t n_seq, int64_t T,
+                                const int32_t* cu_seqlens, const int32_t* pos_offsets, const void* x,
+                                void* y, const void* residual, const gdla_paged_cache* cache,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* gdla_decode against a paged cache (same workspace size and limits): the new
+ * token of sequence b is written at position cache_lens[b] through row b of
+ * the block table, then attends positions 0 .. cache_lens[b] (the window's
+ * part of them) read through the same row.  cache_lens[b] must be below
+ * page_rows * max_pages; a sequence outside that gets y = 0 and writes
+ * nothing, as in gdla_decode. */
+gdla_status gdla_decode_paged(const gdla_config* cfg, const gdla_weights* w, int32_t B, const void* x,
+                              void* y, const gdla_paged_cache* cache, const int32_t* cache_lens,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Latent expansion alone (report, GDLA summary and definition paragraphs):
  * c_KVn = RMSNorm(c_KV) * g_kv, [K^C | V] = c_KVn W_UKV^T.

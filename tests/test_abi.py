@@ -50,7 +50,7 @@ def test_status_strings_and_version():
     L = lib()
     assert L.gdla_status_string(0) == b"GDLA_OK"
     assert L.gdla_status_string(3) == b"GDLA_ERR_WORKSPACE"
-    assert L.gdla_version() >= 101
+    assert L.gdla_version() >= 102
 
 
 def _cfg(**kw):
@@ -170,3 +170,74 @@ def test_decode_and_expand_reject_bad_arguments():
                                  0x600000, None) == gdla.GDLA_ERR_INVALID_ARG   # ld_c < kv_rank
     assert L_.gdla_latent_expand(ctypes.byref(c), 10, 0x100000, 512, 0x200000, 0x300000, 0x400000, 0x500000,
                                  None, None) == gdla.GDLA_ERR_INVALID_ARG   # c_norm required
+
+
+def call_packed(cfg, w, n=2, T=100, cu=0x700000, pos=None, x=0x100000, y=0x200000, res=None, cache=None,
+                ws=0x300000, wsb=None):
+    L_ = lib()
+    if wsb is None:
+        wsb = L_.gdla_prefill_packed_workspace_size(ctypes.byref(cfg), n, T)
+    pc = None if cache is None else ctypes.byref(cache)
+    st = L_.gdla_prefill_packed(ctypes.byref(cfg), ctypes.byref(w), n, T, cu, pos, x, y, res, pc, ws, wsb, None)
+    return st, L_.gdla_last_error().decode()
+
+
+def paged(pages=0x800000, bt=0x900000, page_rows=64, max_pages=8, num_pages=16):
+    return gdla.PagedCache(pages, bt, page_rows, max_pages, num_pages)
+
+
+def test_packed_prefill_rejects_bad_arguments():
+    w = FakeW().struct()
+    c = _cfg()
+    assert call_packed(c, w, T=0, cu=0, x=0, y=0, ws=0)[0] == gdla.GDLA_OK   # empty stream: no-op
+    assert call_packed(c, w, n=-1)[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_packed(c, w, n=0, wsb=1 << 40)[0] == gdla.GDLA_ERR_INVALID_ARG   # tokens but no sequences
+    st, msg = call_packed(c, w, cu=0)
+    assert st == gdla.GDLA_ERR_INVALID_ARG and "cu_seqlens" in msg
+    assert call_packed(c, w, cu=0x700002)[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_packed(c, w, pos=0x700001)[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_packed(c, w, y=0x100000)[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_packed(c, w, x=0x100008)[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_packed(c, FakeW().struct(null="w_gate"))[0] == gdla.GDLA_ERR_INVALID_ARG
+    assert call_packed(c, w, T=(1 << 20) + 1, wsb=1 << 45)[0] == gdla.GDLA_ERR_UNSUPPORTED
+    fp = _cfg(dtype="fp32", d_nope=32, d_rope=16, d_v=32)
+    assert call_packed(fp, w, T=9000, wsb=1 << 40)[0] == gdla.GDLA_ERR_UNSUPPORTED
+    st, msg = call_packed(c, w, wsb=1000)
+    assert st == gdla.GDLA_ERR_WORKSPACE and "needs" in msg
+    assert call_packed(c, w, ws=0x300040)[0] == gdla.GDLA_ERR_INVALID_ARG
+    for bad in (paged(page_rows=48), paged(page_rows=0), paged(bt=0), paged(pages=0), paged(pages=0x800008),
+                paged(bt=0x900002), paged(max_pages=0), paged(num_pages=0), paged(page_rows=1 << 16, max_pages=1 << 15)):
+        st, msg = call_packed(c, w, cache=bad)
+        assert st == gdla.GDLA_ERR_INVALID_ARG, (bad.page_rows, bad.max_pages, st, msg)
+
+
+def test_packed_workspace_size():
+    L_ = lib()
+    c = _cfg()
+    one = L_.gdla_prefill_packed_workspace_size(ctypes.byref(c), 1, 4096)
+    assert one > L_.gdla_prefill_workspace_size(ctypes.byref(c), 1, 4096)   # plus the work list
+    assert L_.gdla_prefill_packed_workspace_size(ctypes.byref(c), 1000, 4096) > one
+    assert L_.gdla_prefill_packed_workspace_size(ctypes.byref(c), 1, (1 << 20) + 1) == 0
+    assert L_.gdla_prefill_packed_workspace_size(ctypes.byref(c), -1, 10) == 0
+    fp = _cfg(dtype="fp32", d_nope=32, d_rope=16, d_v=32)
+    assert L_.gdla_prefill_packed_workspace_size(ctypes.byref(fp), 3, 8192) > 0
+    assert L_.gdla_prefill_packed_workspace_size(ctypes.byref(fp), 3, 8193) == 0
+
+
+def test_paged_decode_rejects_bad_arguments():
+    L_ = lib()
+    w = FakeW().struct()
+    c = _cfg()
+    ws = L_.gdla_decode_workspace_size(ctypes.byref(c), 4)
+
+    def call(cache, B=4, lens=0x500000, wsb=ws):
+        pc = None if cache is None else ctypes.byref(cache)
+        return L_.gdla_decode_paged(ctypes.byref(c), ctypes.byref(w), B, 0x100000, 0x200000, pc, lens, 0x300000,
+                                    wsb, None)
+
+    assert call(None, B=0, lens=0) == gdla.GDLA_OK
+    assert call(None) == gdla.GDLA_ERR_INVALID_ARG
+    assert call(paged(), lens=0) == gdla.GDLA_ERR_INVALID_ARG
+    assert call(paged(), wsb=ws - 1) == gdla.GDLA_ERR_WORKSPACE
+    for bad in (paged(page_rows=16), paged(bt=0), paged(num_pages=-1), paged(max_pages=0)):
+        assert call(bad) == gdla.GDLA_ERR_INVALID_ARG
