@@ -132,8 +132,8 @@ gdla_status check_paged(const gdla_paged_cache* c) {
   if (!c->pages || !c->block_table) return fail(GDLA_ERR_INVALID_ARG, "cache pages and block_table must be non-NULL");
   if (!aligned16(c->pages) || ((uintptr_t)c->block_table & 3))
     return fail(GDLA_ERR_INVALID_ARG, "cache pages must be 16-byte aligned, block_table 4-byte aligned");
-  if (c->page_rows <= 0 || c->page_rows % 32)
-    return fail(GDLA_ERR_INVALID_ARG, "page_rows must be a positive multiple of 32 (got %d)", c->page_rows);
+  if (c->page_rows < 32 || (c->page_rows & (c->page_rows - 1)))
+    return fail(GDLA_ERR_INVALID_ARG, "page_rows must be a power of two >= 32 (got %d)", c->page_rows);
   if (c->max_pages <= 0 || c->num_pages <= 0)
     return fail(GDLA_ERR_INVALID_ARG, "max_pages and num_pages must be positive");
   if ((int64_t)c->page_rows * c->max_pages > ((int64_t)1 << 30))
@@ -483,6 +483,8 @@ gdla_status gdla_decode_paged(const gdla_config* cfg, const gdla_weights* w, int
   if (st != GDLA_OK || B == 0) return st;
   if (!cache) return fail(GDLA_ERR_INVALID_ARG, "cache must be non-NULL");
   if ((st = check_paged(cache)) != GDLA_OK) return st;
+  if ((int64_t)B * cache->max_pages > ((int64_t)1 << 28))
+    return fail(GDLA_ERR_UNSUPPORTED, "B * max_pages beyond 2^28 block-table entries");
   hipError_t err = gdla::decode_step(cfg, w, B, x, y, paged_view(cache), cache_lens, workspace, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "decode");
   return GDLA_OK;

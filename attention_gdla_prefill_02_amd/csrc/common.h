@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -13,6 +15,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define GDLA_DEV __device__ __forceinline__
+
+// f(std::integral_constant<int, i>) for i = B .. E-1, unrolled at compile time
+template <int B, int E, class F>
+GDLA_DEV void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // gfx950 matrix cores, bf16 inputs, fp32 accumulation.
 //   32x32x16: A lane l supplies row l%32, k = 8*(l/32)+e (e = vector element);
@@ -62,6 +73,23 @@ __device__ __forceinline__ void g2lds16_stream(const void* src, void* lds) {
       "global_load_lds_dwordx4 %0, off nt"
       :
       : "v"(src), "s"(m0v)
+      : "memory", "m0");
+}
+
+// g2lds16_stream of src + OFF bytes, with OFF in the instruction's offset
+// field (saves a 64-bit address add per load; 0 <= OFF < 4096).  The
+// instruction adds its offset to the LDS address too, so M0 gets lds - OFF.
+template <int OFF>
+__device__ __forceinline__ void g2lds16_stream_off(const void* src, void* lds) {
+  static_assert(OFF >= 0 && OFF < 4096, "instruction offset is 13-bit signed");
+  const unsigned m0v = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(__attribute__((address_space(3))) char*)lds - (unsigned)OFF);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off offset:%2 nt"
+      :
+      : "v"(src), "s"(m0v), "i"(OFF)
       : "memory", "m0");
 }
 

@@ -537,6 +537,8 @@ plan_kernel(const int32_t* lens, int B, int64_t cap, int window, int* plan) {
 struct DecAttnArgs {
   const bf16* qlat;        // [B, H, RL]
   CacheView cache;         // rows of RL elements
+  int bt_bytes;            // bytes of the block table ([B, max_pages] int32; paged only)
+  int page_shift;          // log2(page_rows) (paged only)
   int B, H;
   const int* plan;
   float* part_ml;          // [segments][H][2]: running max (exp2 domain) and sum
@@ -560,7 +562,7 @@ struct DecAttnArgs {
 // different parity, which the swizzle sends to disjoint bank quads; the
 // transposed 8-byte reads of a 32-lane pass cover eight rows and a chunk pair,
 // 32 distinct bank pairs.
-template <int KVR, int NW>
+template <int KVR, int NW, bool PAGED>
 __global__ void __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1)
 dec_attn_kernel(DecAttnArgs a) {
   constexpr int RL = KVR + DR, KS = RL / 32, DT = KVR / 16, TK = DEC_TK;
@@ -572,7 +574,6 @@ dec_attn_kernel(DecAttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q4 = lane >> 4;
   const int B = a.B;
-  const PlanView pv = plan_view(a.plan, B);
   const int T = __builtin_amdgcn_readfirstlane(a.plan[0]);
   const int k = blockIdx.x;
   const int nw = dec_wgs(T);
@@ -590,35 +591,76 @@ dec_attn_kernel(DecAttnArgs a) {
   auto seq_at = [&](int b) {   // all fields are wave-uniform
     Seq q;
     q.b = b;
-    q.tend = __builtin_amdgcn_readfirstlane(pv.tstart[b + 1]);
-    q.rlo = __builtin_amdgcn_readfirstlane(pv.lo[b]);
-    q.row0 = (q.rlo & ~(TK - 1)) - TK * __builtin_amdgcn_readfirstlane(pv.tstart[b]);
-    q.rend = q.rlo + __builtin_amdgcn_readfirstlane(pv.len[b]);
+    // plan fields addressed from the plan base (fewer live scalar registers than a PlanView)
+    q.tend = __builtin_amdgcn_readfirstlane(a.plan[3 + b]);
+    q.rlo = __builtin_amdgcn_readfirstlane(a.plan[3 + B + b]);
+    q.row0 = (q.rlo & ~(TK - 1)) - TK * __builtin_amdgcn_readfirstlane(a.plan[2 + b]);
+    q.rend = q.rlo + __builtin_amdgcn_readfirstlane(a.plan[3 + 2 * B + b]);
     return q;
   };
   auto seq_for = [&](Seq q, int t) {   // advance past sequences that end at or before tile t
     while (t >= q.tend) q = seq_at(q.b + 1);
     return q;
   };
-  // Issue the loads of tile t into buffer buf; returns false when the tile's
-  // page is missing from the table (the tile is then loaded from row 0 of the
-  // pool and not used).
-  auto load_tile = [&](const Seq& q, int t, int buf) {
-    const int ts = q.row0 + TK * t;   // first position of the tile, a multiple of 32
-    const int64_t r0 = cache_row_index(a.cache, q.b, ts);
-    const bf16* tbase = (const bf16*)a.cache.base + (r0 < 0 ? 0 : r0) * RL;
-    const bf16* src[4];
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {   // rows outside [rlo, rend) repeat an attended row of the tile (masked)
+  // Cache addressing.  Tile t of a sequence covers positions ts .. ts + 31,
+  // ts = row0 + TK t, inside one page (pages are multiples of 32 rows): page
+  // pg (the block-table entry; the sequence itself for a dense cache) at row
+  // offset off.  For a paged cache the entry of tile t + 2 is fetched while
+  // tile t is computed, with a vector buffer load that the tile loads' wait
+  // covers (a scalar load would hold up every LDS wait until it returned).
+  auto page_of = [&](const Seq& q, int t, int& off) {   // entry index (paged) or page (dense)
+    const int ts = q.row0 + TK * t;
+    if (!PAGED) {
+      off = ts;
+      return q.b;
+    }
+    off = ts & (a.cache.page_rows - 1);   // page_rows is a power of two
+    return q.b * a.cache.max_pages + (ts >> a.page_shift);
+  };
+  auto fetch_page = [&](int e) {   // vector load of block-table entry e
+    const __amdgpu_buffer_rsrc_t bt_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.cache.bt, (short)0, a.bt_bytes, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, e * 4, 0, 0);
+  };
+  // Issue the loads of tile t into buffer buf; returns false when its page is
+  // not in the pool (the tile is then read from row 0 of the pool and unused).
+  auto load_tile = [&](const Seq& q, int t, int buf, int pg, int off) {
+    const int ts = q.row0 + TK * t;
+    const bool ok = !PAGED || (unsigned)pg < (unsigned)a.cache.num_pages;
+    const char* tbase = (const char*)a.cache.base +
+                        ((int64_t)(ok ? pg : 0) * a.cache.page_rows + (ok ? off : 0)) * (RL * 2);
+    // rows outside [rlo, rend) repeat an attended row of the tile (masked)
+    auto src_of = [&](int rg) {
       const int key = min(max(ts + 8 * rg + lrow, q.rlo), q.rend - 1) - ts;
-      src[rg] = tbase + (int64_t)key * RL + 8 * lch;
-    }
+      return tbase + (unsigned)(key * (RL * 2) + 16 * lch);
+    };
+    if constexpr (NW >= 4) {
+      // waves 0-3 load row group w of the first LINES - XW lines (one address,
+      // line offsets in the instruction); each extra wave loads one of the
+      // last XW lines, all four row groups
+      constexpr int LINES = TBLK / 4, XW = NW - 4;
+      static_assert(LINES > XW, "more extra waves than lines");
+      if (wave < 4) {
+        const char* src = src_of(wave);
+        static_for<0, LINES - XW>([&](auto l) {
+          g2lds16_stream_off<128 * decltype(l)::value>(src, &tile[buf][(4 * decltype(l)::value + wave) * 512]);
+        });
+      } else {
+        const int l = LINES - XW + (wave - 4);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int blk = wave + NW * i;   // compile-time row group and line of each block
-      if (blk < TBLK) g2lds16_stream(src[blk & 3] + 64 * (blk >> 2), &tile[buf][blk * 512]);
+        for (int rg = 0; rg < 4; ++rg) g2lds16_stream(src_of(rg) + 128 * l, &tile[buf][(4 * l + rg) * 512]);
+      }
+    } else {
+      const char* src[4];
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) src[rg] = src_of(rg);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int blk = wave + NW * i;
+        if (blk < TBLK) g2lds16_stream(src[blk & 3] + 128 * (blk >> 2), &tile[buf][blk * 512]);
+      }
     }
-    return r0 >= 0;
+    return ok;
   };
   // per-lane LDS slots of the fragment reads (16-byte units, block offsets added per read)
   int kslot[2], pslot[4];
@@ -646,10 +688,15 @@ dec_attn_kernel(DecAttnArgs a) {
   };
 
   // first sequence (the plan's pass 3)
-  const int bl = __builtin_amdgcn_readfirstlane(pv.wgb[k]);
+  const int bl = __builtin_amdgcn_readfirstlane(a.plan[4 + 5 * B + k]);
   Seq ls = seq_at(bl), cs = ls;
-  // the first tile and the query fragment are in flight together (load_q waits for both)
-  bool cur_ok = load_tile(ls, tb, 0), nxt_ok = true;
+  // the first tile and the query fragment are in flight together (load_q waits
+  // for both), and so is the page entry of the second tile
+  int off0, nx_off = 0, nx_pg = 0;
+  const int e0 = page_of(ls, tb, off0);
+  bool cur_ok = load_tile(ls, tb, 0, PAGED ? __builtin_amdgcn_readfirstlane(a.cache.bt[e0]) : e0, off0);
+  bool nxt_ok = true;
+  if (PAGED && tb + 1 < te) nx_pg = fetch_page(page_of(seq_for(ls, tb + 1), tb + 1, nx_off));
   load_q(cs.b);
   f32x4 o[DT];
 #pragma unroll
@@ -662,11 +709,18 @@ dec_attn_kernel(DecAttnArgs a) {
   for (int t = tb; t < te; ++t) {
     if (t + 1 < te) {
       ls = seq_for(ls, t + 1);
-      nxt_ok = load_tile(ls, t + 1, buf ^ 1);
+      if (PAGED) {
+        nxt_ok = load_tile(ls, t + 1, buf ^ 1, __builtin_amdgcn_readfirstlane(nx_pg), nx_off);
+        if (t + 2 < te) nx_pg = fetch_page(page_of(seq_for(ls, t + 2), t + 2, nx_off));
+      } else {
+        int off;
+        const int pg = page_of(ls, t + 1, off);
+        load_tile(ls, t + 1, buf ^ 1, pg, off);
+      }
     }
     const bf16* Tl = tile[buf];
     const int r0 = cs.row0 + TK * t;
-    if (cur_ok) {
+    if (!PAGED || cur_ok) {
     // scores S^T: lane holds head r16, tile rows 16 u + 4 q4 + j
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
     // lane reads chunk 4 s + q4 of row 16 u + r16: block 4 (s >> 1) + 2 u + (r16 >> 3),
@@ -682,14 +736,18 @@ dec_attn_kernel(DecAttnArgs a) {
       }
       if (s % 6 == 5) __builtin_amdgcn_sched_barrier(0);   // bounds the LDS reads in flight (registers)
     }
+    if (r0 < cs.rlo || r0 + TK > cs.rend) {   // a tile at either end of the attended rows
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if ((unsigned)(r0 + 16 * u + 4 * q4 + j - cs.rlo) >= (unsigned)(cs.rend - cs.rlo)) sacc[u][j] = -INFINITY;
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if ((unsigned)(r0 + 16 * u + 4 * q4 + j - cs.rlo) >= (unsigned)(cs.rend - cs.rlo)) sacc[u][j] = -INFINITY;
-        mt = fmaxf(mt, sacc[u][j]);
-      }
+      for (int j = 0; j < 4; ++j) mt = fmaxf(mt, sacc[u][j]);
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sc;
     const bool raise = mt > m + 8.0f;
@@ -724,7 +782,7 @@ dec_attn_kernel(DecAttnArgs a) {
       // end of a segment: write its partial
       float lt = lsum + __shfl_xor(lsum, 16, 64);
       lt += __shfl_xor(lt, 32, 64);
-      const int seg = __builtin_amdgcn_readfirstlane(pv.coff[cs.b] + k - pv.kf[cs.b]);
+      const int seg = __builtin_amdgcn_readfirstlane(a.plan[3 + 3 * B + cs.b] + k - a.plan[4 + 4 * B + cs.b]);
       if (hok) {
         float* po = a.part_o + ((int64_t)seg * a.H + h) * KVR;
 #pragma unroll
@@ -842,7 +900,10 @@ combine_kernel(CombineArgs a) {
 
 template <int KVR, int NW>
 hipError_t launch_dec_attn(const DecAttnArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((dec_attn_kernel<KVR, NW>), dim3(grid), dim3(64 * NW), 0, s, a);
+  if (a.cache.bt)
+    hipLaunchKernelGGL((dec_attn_kernel<KVR, NW, true>), dim3(grid), dim3(64 * NW), 0, s, a);
+  else
+    hipLaunchKernelGGL((dec_attn_kernel<KVR, NW, false>), dim3(grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -954,7 +1015,8 @@ hipError_t decode_step(const gdla_config* c, const gdla_weights* w, int B, const
                      (int64_t)cache.page_rows * cache.max_pages, c->window, plan);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   {
-    DecAttnArgs k{(const bf16*)(ws + Lw.qlat), cache, B, H, plan, (float*)(ws + Lw.ml),
+    DecAttnArgs k{(const bf16*)(ws + Lw.qlat), cache, (int)((int64_t)B * cache.max_pages * 4),
+                  cache.bt ? __builtin_ctz((unsigned)cache.page_rows) : 0, B, H, plan, (float*)(ws + Lw.ml),
                   (float*)(ws + Lw.po), (float)(1.4426950408889634 / std::sqrt((double)DQK))};
     const int grid = DEC_WGS;
     switch (rkv) {

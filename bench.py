@@ -14,8 +14,9 @@ Prints one JSON line with the roofline of the dominant kernel (attention,
 timed with HIP events on its stream inside the timed steps), the decode
 throughput of a batch-64 step against the compressed latent cache (full and
 W = 4096 layers), the same prefill block and decode at the report's own layer
-shapes (group size 4, query rank 1024, W = 128), and the fp64 CPU oracle timed
-on a bounded sample of the headline workload.
+shapes (group size 4, query rank 1024, W = 128), the block over a packed stream
+of complete sequences of mixed lengths and decode against a paged cache, and
+the fp64 CPU oracle timed on a bounded sample of the headline workload.
 """
 
 from __future__ import annotations
@@ -179,6 +180,68 @@ def bench_prefill(args, torch, gdla, configs, inputs, name="hybrid_l32k", steps=
     return res, w, Wc[0], x_cpu
 
 
+def bench_packed(args, torch, gdla, configs, inputs, name="packed_hybrid_l32k", steps=5, warmup=2):
+    """The hybrid block over a packed stream of complete sequences (one
+    gdla_prefill_packed call per layer), and the same sequences run as one
+    gdla_prefill call each, for comparison."""
+    w = configs.WORKLOADS[name]
+    s = w.shapes
+    T = w.L
+    lens = inputs.packed_lengths(T, *w.len_range, w.seed)
+    log(f"[bench] building inputs: {w.note} ({len(lens)} sequences)")
+    Wd = [{k: v.to("cuda") for k, v in inputs.make_weights(s, configs.layer_seed(w, l), "bf16").items()}
+          for l in range(len(w.windows))]
+    wstructs = [gdla.weights_struct(W) for W in Wd]
+    cfgs = [gdla.make_config(s, win, "bf16") for win in w.windows]
+    x0 = inputs.make_x(1, T, s["d_model"], w.seed, "bf16")[0].to("cuda")
+    xs = [x0] + [torch.empty_like(x0) for _ in w.windows]
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    ws = gdla.alloc_workspace(max(max(gdla.prefill_packed_workspace_size(c, len(lens), T),
+                                      gdla.prefill_workspace_size(c, 1, max(lens))) for c in cfgs))
+
+    def packed_step():
+        for l in range(len(cfgs)):
+            gdla.prefill_packed(cfgs[l], None, xs[l], cu_d, y=xs[l + 1], residual=xs[l], workspace=ws,
+                                wstruct=wstructs[l])
+
+    def per_sequence_step():
+        for l in range(len(cfgs)):
+            for b, n in enumerate(lens):
+                xa = xs[l][cu[b]:cu[b + 1]].unsqueeze(0)
+                gdla.prefill(cfgs[l], None, xa, y=xs[l + 1][cu[b]:cu[b + 1]].unsqueeze(0), residual=xa,
+                             workspace=ws, wstruct=wstructs[l])
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    t_seq = timed(per_sequence_step)
+    t_packed = timed(packed_step)
+    proj = proj_flop_per_token(s) * T * len(w.windows)
+    attn = attn_flop_per_pair(s) * sum(attended_pairs(n, win) for n in lens for win in w.windows)
+    total = proj + attn
+    out = {"workload": f"{name}: {w.note}", "sequences": len(lens), "tokens": T,
+           "lengths": f"U{{{w.len_range[0]}..{w.len_range[1]}}} seeded, min {min(lens)}, max {max(lens)}",
+           "ms_per_step": round(t_packed * 1e3, 3), "tokens_per_s": round(T / t_packed, 1),
+           "block_tflops": round(total / t_packed / 1e12, 2),
+           "frac_of_peak": round(total / t_packed / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "algorithmic_tflop_per_step": round(total / 1e12, 3), "attn_share_of_flop": round(attn / total, 4),
+           "per_sequence_calls_ms_per_step": round(t_seq * 1e3, 3),
+           "speedup_vs_per_sequence_calls": round(t_seq / t_packed, 3),
+           "output_finite": bool(torch.isfinite(xs[-1]).all().item())}
+    log(f"[bench] packed block: {out}")
+    return out
+
+
 def decode_bytes(s: dict, lens, window: int) -> int:
     """Algorithmic HBM bytes of one decode step: attended cache rows, every
     weight once, the appended rows, x and y."""
@@ -194,18 +257,30 @@ def decode_bytes(s: dict, lens, window: int) -> int:
     return rows * RL * 2 + params * 2 + B * RL * 2 + B * s["d_model"] * 2 * 2
 
 
-def bench_decode(torch, gdla, configs, inputs, reps: int = 20, name="decode_b64", fixed_ctx=True):
+def bench_decode(torch, gdla, configs, inputs, reps: int = 20, name="decode_b64", fixed_ctx=True, paged=False):
     """Batch-64 decode step against a 32768-row latent cache (contexts
     U{1024..32768}), full-causal and sliding-window layers, plus all contexts
     at 32768.  Before every timed rep the 256 MB MALL is flushed by reading a
     512 MB buffer (a read leaves clean lines; a 512 MB write would leave 256 MB
-    of dirty lines whose write-back would land inside the timed step)."""
+    of dirty lines whose write-back would land inside the timed step).  With
+    paged=True the same rows live in a pool of page_rows-row pages in shuffled
+    order and the step is gdla_decode_paged."""
     w = configs.WORKLOADS[name]
     s = w.shapes
     log(f"[bench] building decode state: {w.note}")
     cache_c, lens = inputs.make_decode_state(w.B, w.capacity, s["kv_rank"], s["d_rope"], w.ctx_range, w.seed, "bf16")
     cache = cache_c.to("cuda")
     del cache_c
+    run = lambda cfg, ln_d, ws: gdla.decode(cfg, W, x, cache, ln_d, y=y, workspace=ws)   # noqa: E731
+    if paged:
+        pr = w.page_rows
+        bt, npages = inputs.page_table([w.capacity] * w.B, pr, w.seed)
+        pool = torch.empty((npages, pr, cache.shape[-1]), dtype=cache.dtype, device="cuda")
+        bt_d = torch.from_numpy(bt).to("cuda")
+        kpp = w.capacity // pr
+        pool[bt_d[:, :kpp].reshape(-1).long()] = cache.reshape(w.B * kpp, pr, -1)
+        cache = None
+        run = lambda cfg, ln_d, ws: gdla.decode_paged(cfg, W, x, pool, bt_d, ln_d, y=y, workspace=ws)   # noqa: E731
     W = {k: v.to("cuda") for k, v in inputs.make_weights(s, configs.layer_seed(w, 0), "bf16").items()}
     x = inputs.make_x(w.B, 1, s["d_model"], w.seed, "bf16")[:, 0].contiguous().to("cuda")
     y = torch.empty_like(x)
@@ -220,13 +295,13 @@ def bench_decode(torch, gdla, configs, inputs, reps: int = 20, name="decode_b64"
         ws = gdla.alloc_workspace(gdla.decode_workspace_size(cfg, w.B))
         ln_d = ln.to("cuda")
         for _ in range(3):
-            gdla.decode(cfg, W, x, cache, ln_d, y=y, workspace=ws)
+            run(cfg, ln_d, ws)
         times = []
         for _ in range(reps):
             flush.sum()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            gdla.decode(cfg, W, x, cache, ln_d, y=y, workspace=ws)
+            run(cfg, ln_d, ws)
             e1.record()
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1) / 1e3)
@@ -241,6 +316,8 @@ def bench_decode(torch, gdla, configs, inputs, reps: int = 20, name="decode_b64"
     out["batch"] = w.B
     out["contexts"] = (f"U{{{w.ctx_range[0]}..{w.ctx_range[1]}}} seeded (full, swa{win})"
                        + ("; all 32768 (full_ctx32768)" if fixed_ctx else ""))
+    if paged:
+        out["cache"] = f"paged: {w.page_rows}-row pages, shuffled pool order"
     return out
 
 
@@ -254,6 +331,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-report-shapes", action="store_true", help="skip the report-shape (g=4, W=128) workloads")
     ap.add_argument("--decode-only", action="store_true", help="time only the decode steps (for profiling)")
+    ap.add_argument("--no-packed", action="store_true", help="skip the packed-stream and paged-cache workloads")
+    ap.add_argument("--packed-only", action="store_true", help="time only the packed-stream block (for profiling)")
+    ap.add_argument("--paged-only", action="store_true", help="time only the paged-cache decode (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (hardware-counter calibration)")
     ap.add_argument("--print-attn-sha", action="store_true", help="print the attention source hash and exit")
@@ -288,6 +368,13 @@ def main():
     if args.decode_only:
         print(json.dumps({"decode": bench_decode(torch, gdla, configs, inputs)}), flush=True)
         return
+    if args.packed_only:
+        print(json.dumps({"packed": bench_packed(args, torch, gdla, configs, inputs)}), flush=True)
+        return
+    if args.paged_only:
+        print(json.dumps({"paged_decode": bench_decode(torch, gdla, configs, inputs, name="paged_decode_b64",
+                                                       fixed_ctx=False, paged=True)}), flush=True)
+        return
     pf, w, Wc0, x_cpu = bench_prefill(args, torch, gdla, configs, inputs)
     log(f"[bench] prefill: {pf['ms_step']:.2f} ms/step, {pf['tflops']:.1f} TFLOP/s, attention "
         f"{pf['attn_tflops']:.1f} TFLOP/s, GEMMs+prep {pf['other_tflops']:.1f} TFLOP/s, stages {pf['kern']}")
@@ -307,6 +394,12 @@ def main():
                               "attn_tflops": round(rp["attn_tflops"], 2), "gemm_prep_tflops": round(rp["other_tflops"], 2),
                               "algorithmic_tflop_per_step": round(rp["total_flop"] / 1e12, 3), "stage_ms": rp["kern"]},
                   "decode": rd}
+
+    packed = None
+    if not args.no_packed:
+        packed = {"prefill": bench_packed(args, torch, gdla, configs, inputs),
+                  "paged_decode": None if args.no_decode else bench_decode(
+                      torch, gdla, configs, inputs, reps=10, name="paged_decode_b64", fixed_ctx=False, paged=True)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -341,6 +434,7 @@ def main():
                     "output_finite": pf["finite"]},
         "decode": decode,
         "report_shapes": report,
+        "packed_and_paged": packed,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

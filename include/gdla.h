@@ -222,7 +222,7 @@ gdla_status gdla_decode(const gdla_config* cfg, const gdla_weights* w, int32_t B
  *                dtype, 16-byte aligned; rows hold [c_KVn | RoPE(k_R)]
  *   block_table  device int32 [sequences, max_pages], 4-byte aligned; read
  *                on the device only
- *   page_rows    rows per page: a positive multiple of 32
+ *   page_rows    rows per page: a power of two, at least 32
  *   max_pages    block-table columns (> 0); positions run up to
  *                page_rows * max_pages - 1 (that product at most 2^30)
  *   num_pages    pages in the pool (> 0)
@@ -276,7 +276,8 @@ gdla_status gdla_prefill_packed(const gdla_config* cfg, const gdla_weights* w, i
  * the block table, then attends positions 0 .. cache_lens[b] (the window's
  * part of them) read through the same row.  cache_lens[b] must be below
  * page_rows * max_pages; a sequence outside that gets y = 0 and writes
- * nothing, as in gdla_decode. */
+ * nothing, as in gdla_decode.  B * max_pages at most 2^28
+ * (GDLA_ERR_UNSUPPORTED beyond). */
 gdla_status gdla_decode_paged(const gdla_config* cfg, const gdla_weights* w, int32_t B, const void* x,
                               void* y, const gdla_paged_cache* cache, const int32_t* cache_lens,
                               void* workspace, size_t workspace_bytes, void* stream);

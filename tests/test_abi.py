@@ -205,7 +205,7 @@ def test_packed_prefill_rejects_bad_arguments():
     st, msg = call_packed(c, w, wsb=1000)
     assert st == gdla.GDLA_ERR_WORKSPACE and "needs" in msg
     assert call_packed(c, w, ws=0x300040)[0] == gdla.GDLA_ERR_INVALID_ARG
-    for bad in (paged(page_rows=48), paged(page_rows=0), paged(bt=0), paged(pages=0), paged(pages=0x800008),
+    for bad in (paged(page_rows=48), paged(page_rows=0), paged(page_rows=96), paged(page_rows=16), paged(bt=0), paged(pages=0), paged(pages=0x800008),
                 paged(bt=0x900002), paged(max_pages=0), paged(num_pages=0), paged(page_rows=1 << 16, max_pages=1 << 15)):
         st, msg = call_packed(c, w, cache=bad)
         assert st == gdla.GDLA_ERR_INVALID_ARG, (bad.page_rows, bad.max_pages, st, msg)

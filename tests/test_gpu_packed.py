@@ -145,7 +145,7 @@ def _decode_state(shapes, lens, seed, page_rows, extra_pages=0):
     return inputs.to_storage(pool, "bf16"), bt
 
 
-@pytest.mark.parametrize("window,page_rows", [(0, 32), (64, 32), (0, 96), (100, 64)])
+@pytest.mark.parametrize("window,page_rows", [(0, 32), (64, 32), (0, 128), (100, 64)])
 def test_paged_decode(window, page_rows):
     s = SMALL
     lens = [0, 1, 31, 32, 33, 100, 1000, 2047]
