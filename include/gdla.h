@@ -243,8 +243,8 @@ typedef struct {
 size_t gdla_prefill_packed_workspace_size(const gdla_config* cfg, int32_t n_seq, int64_t T);
 
 /* One GDLA layer over n_seq complete sequences packed end to end into one
- * stream of T tokens (report, long-context training paragraph: complete
- * packed sequences).  Each sequence is the layer applied to it alone: its
+ * stream of T tokens (report, long-context training paragraph: whole
+ * sequences packed together).  Each sequence is the layer applied to it alone: its
  * tokens attend only to earlier tokens of the same sequence, at positions
  * that restart at pos_offsets[b].
  *   cu_seqlens   device int32 [n_seq + 1], read on the device only: sequence b
