@@ -49,6 +49,9 @@ report has no headings, so its paragraphs are named by topic):
              hold complete sequences packed together, which are re-balanced
              across data-parallel ranks by a longest-processing-time greedy
              rule.
+  [M3-train] "Motif 3: Technical Report", training-infrastructure paragraph:
+             activations are recomputed for the backward pass (selective
+             recomputation, full recomputation at the longest lengths).
   [OSM-page] "Open-Source Frontier Models: Architecture and Benchmarks of
              Rnj-1 and Motif-2", section 2, prefill sequence diagram: the
              attention step stores the normalized KV rows in the blocks of a
@@ -522,6 +525,152 @@ def gdla_decode_paged(x_new, W, cfg: Cfg, pages, block_table, page_rows, cache_l
     out = gdla_decode(x_new, W, cfg, dense, cache_lens)
     out["slots"] = [paged_slot(block_table, page_rows, b, int(cache_lens[b])) for b in range(B)]
     return out
+
+
+# --------------------------------------------------------------------------
+# Backward of one layer ([M3-train]: training recomputes the forward's
+# activations; the gradient is the chain rule of the steps above, taken in
+# reverse order)
+# --------------------------------------------------------------------------
+
+def rms_norm_backward(c, gamma, eps, g):
+    """Gradients of y = c r gamma, r = (mean(c^2) + eps)^(-1/2), for upstream
+    g = dL/dy: dc = r (g gamma) - c r^3 mean((g gamma) c), dgamma = sum over
+    rows of g c r."""
+    c, g = _f64(c), _f64(g)
+    n = c.shape[-1]
+    r = 1.0 / np.sqrt(np.mean(c * c, axis=-1, keepdims=True) + eps)
+    u = g * _f64(gamma)
+    dc = r * u - c * r ** 3 * np.sum(u * c, axis=-1, keepdims=True) / n
+    dgamma = np.sum((g * c * r).reshape(-1, n), axis=0)
+    return dc, dgamma
+
+
+def rope_backward(g, pos, base, yarn=None):
+    """Gradient through rope(): the transpose of the pairwise rotation (scaled
+    by m with YaRN), i.e. rotation by the opposite angle."""
+    g = _f64(g)
+    d = g.shape[-1]
+    half = d // 2
+    if yarn is None:
+        inv, m = rope_inv_freq(d, base), 1.0
+    else:
+        s_, orig, bf, bs = yarn
+        inv, m = yarn_inv_freq(d, base, s_, orig, bf, bs), yarn_mscale(s_)
+    ang = _f64(pos)[:, None] * inv[None, :]
+    cos, sin = m * np.cos(ang), m * np.sin(ang)
+    g1, g2 = g[..., :half], g[..., half:]
+    return np.concatenate([g1 * cos + g2 * sin, g2 * cos - g1 * sin], axis=-1)
+
+
+def attention_heads_backward(q, kc, kr, v, dH, cfg: Cfg):
+    """Gradients of attention_heads over all rows 0..L-1 for upstream dH
+    [L, H, d_v]: per head, P = softmax(S) with S = q k^T / sqrt(d_qk) masked,
+    O = P v; dv += P^T dO, dP = dO v^T, dS = P (dP - rowsum(dP P)),
+    dq = dS k / sqrt(d_qk), dk += dS^T q / sqrt(d_qk).  k = [k^C_n | k_R]: the
+    content part of dk goes to KV head n, the rotary part (one k_R per token)
+    collects every head.  Returns dq [L, H, d_qk], dkc [L, nN, d_nope],
+    dkr [L, d_rope], dv [L, nN, d_v]."""
+    L = q.shape[0]
+    scale = 1.0 / math.sqrt(cfg.d_qk)
+    dq = np.zeros_like(_f64(q))
+    dkc = np.zeros((L, cfg.n_noise, cfg.d_nope))
+    dkr = np.zeros((L, cfg.d_rope))
+    dv = np.zeros((L, cfg.n_noise, cfg.d_v))
+    t = np.arange(L)
+    lo = np.array([attended_keys(i, cfg.window)[0] for i in range(L)])
+    allowed = (t[None, :] <= t[:, None]) & (t[None, :] >= lo[:, None])
+    for h in range(cfg.n_heads):
+        n = kv_head_of(h, cfg)
+        k = np.concatenate([kc[:, n, :], kr], axis=-1)
+        s = np.where(allowed, (q[:, h, :] @ k.T) * scale, -np.inf)
+        s = s - s.max(axis=-1, keepdims=True)
+        P = np.exp(s)
+        P /= P.sum(axis=-1, keepdims=True)
+        dO = dH[:, h, :]
+        dv[:, n, :] += P.T @ dO
+        dP = dO @ v[:, n, :].T
+        dS = P * (dP - np.sum(dP * P, axis=-1, keepdims=True))
+        dq[:, h, :] = (dS @ k) * scale
+        dk = (dS.T @ q[:, h, :]) * scale
+        dkc[:, n, :] += dk[:, :cfg.d_nope]
+        dkr += dk[:, cfg.d_nope:]
+    return dq, dkc, dkr, dv
+
+
+def gdla_layer_backward(x, W, cfg: Cfg, dy, pos_offset=0):
+    """Gradients of one GDLA layer's output y (gdla_layer) with respect to its
+    input and every weight, for upstream dy [B, L, d_model].  The forward's
+    activations are recomputed from x, then the steps are differentiated in
+    reverse: output projection, gate and differential, attention, query
+    up-projection with RoPE, latent expansion, the two RMSNorms, RoPE of the
+    rotary key, and the fused down-projection.  Returns dict dx [B, L, d_model]
+    and one entry per weight name (same shapes as the weights)."""
+    x, dy = _f64(x), _f64(dy)
+    B, L, _ = x.shape
+    nS, nN, g = cfg.n_signal, cfg.n_noise, cfg.group
+    grads = {k: np.zeros_like(_f64(v)) for k, v in W.items()}
+    dx = np.zeros_like(x)
+    base, yarn = rope_params(cfg)
+    for b in range(B):
+        xb, dyb = x[b], dy[b]
+        pos = pos_offset + np.arange(L, dtype=np.float64)
+        # recompute the forward
+        ckv_kr = linear(xb, W["w_dkv"])
+        c_kv, kr_raw = ckv_kr[:, :cfg.kv_rank], ckv_kr[:, cfg.kv_rank:]
+        ckvn = rms_norm(c_kv, W["g_kv"], cfg.rms_eps)
+        kr = rope(kr_raw, pos, base, yarn)
+        kc, v, _ = latent_expand_from_norm(ckvn, W["w_ukv"], cfg)
+        cq = linear(xb, W["w_dq"])
+        cqn = rms_norm(cq, W["g_q"], cfg.rms_eps)
+        qf = linear(cqn, W["w_uq"]).reshape(L, cfg.n_heads, cfg.d_qk)
+        q_rot = rope(np.transpose(qf[:, :, cfg.d_nope:], (1, 0, 2)), pos, base, yarn)
+        q = np.concatenate([qf[:, :, :cfg.d_nope], np.transpose(q_rot, (1, 0, 2))], axis=-1)
+        lam = sigmoid(linear(xb, W["w_lambda"]))
+        gate = sigmoid(linear(cqn, W["w_gate"]))
+        Hh = attention_heads(q, kc, kr, v, list(range(L)), cfg)
+        Hs, Hn = Hh[:, :nS], Hh[:, nS:]
+        D = Hs - lam[:, :, None] * np.repeat(Hn, g, axis=1)
+        Z = gate * D.reshape(L, -1)
+        # output projection
+        grads["w_o"] += dyb.T @ Z
+        dZ = dyb @ _f64(W["w_o"])
+        # gate and differential
+        dgate = dZ * D.reshape(L, -1)
+        dD = (dZ * gate).reshape(L, nS, cfg.d_v)
+        dlam = -np.sum(dD * np.repeat(Hn, g, axis=1), axis=-1)
+        dHn = -np.sum((lam[:, :, None] * dD).reshape(L, nN, g, cfg.d_v), axis=2)
+        dH = np.concatenate([dD, dHn], axis=1)
+        # attention
+        dq, dkc, dkr, dv = attention_heads_backward(q, kc, kr, v, dH, cfg)
+        # query side: RoPE on the rotary parts, W_UQ, the gate, RMSNorm, W_DQ
+        dq_rot = rope_backward(np.transpose(dq[:, :, cfg.d_nope:], (1, 0, 2)), pos, base, yarn)
+        dqf = np.concatenate([dq[:, :, :cfg.d_nope], np.transpose(dq_rot, (1, 0, 2))], axis=-1).reshape(L, -1)
+        grads["w_uq"] += dqf.T @ cqn
+        dcqn = dqf @ _f64(W["w_uq"])
+        dglogit = dgate * gate * (1.0 - gate)
+        grads["w_gate"] += dglogit.T @ cqn
+        dcqn += dglogit @ _f64(W["w_gate"])
+        dcq, dgq = rms_norm_backward(cq, W["g_q"], cfg.rms_eps, dcqn)
+        grads["g_q"] += dgq
+        grads["w_dq"] += dcq.T @ xb
+        dxb = dcq @ _f64(W["w_dq"])
+        # lambda
+        dllogit = dlam * lam * (1.0 - lam)
+        grads["w_lambda"] += dllogit.T @ xb
+        dxb += dllogit @ _f64(W["w_lambda"])
+        # KV side: expansion, RMSNorm, RoPE of the rotary key, W_DKV
+        dkv = np.concatenate([dkc.reshape(L, -1), dv.reshape(L, -1)], axis=-1)
+        grads["w_ukv"] += dkv.T @ ckvn
+        dckvn = dkv @ _f64(W["w_ukv"])
+        dckv, dgkv = rms_norm_backward(c_kv, W["g_kv"], cfg.rms_eps, dckvn)
+        grads["g_kv"] += dgkv
+        dkr_raw = rope_backward(dkr, pos, base, yarn)
+        dckv_kr = np.concatenate([dckv, dkr_raw], axis=-1)
+        grads["w_dkv"] += dckv_kr.T @ xb
+        dxb += dckv_kr @ _f64(W["w_dkv"])
+        dx[b] = dxb
+    return dict(dx=dx, **grads)
 
 
 # --------------------------------------------------------------------------

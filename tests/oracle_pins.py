@@ -640,4 +640,88 @@ def pin_decode_paged_is_dense_decode():
         assert dec["slots"] == [(7, 1), (6, 1)], dec["slots"]
 
 
+# ------------------------------------------------------------------ backward
+def _fd_check(cfg, pos_offset=0, B=1, L=7, seed=11, per_tensor=6, tol=2e-6):
+    """Central differences of the loss sum(dy * y) against the analytic
+    gradients of gdla_layer_backward, on sampled elements of x and of every
+    weight (fp64, h = 1e-5: truncation error ~1e-10 relative)."""
+    W = tiny_weights(cfg, seed=seed)
+    x = tiny_x(B=B, L=L, cfg=cfg, seed=seed + 1)
+    rng = np.random.Generator(np.random.PCG64(seed + 2))
+    dy = rng.standard_normal((B, L, cfg.d_model))
+    grads = R.gdla_layer_backward(x, W, cfg, dy, pos_offset=pos_offset)
+
+    def loss(x_, W_):
+        return float(np.sum(dy * R.gdla_layer(x_, W_, cfg, pos_offset=pos_offset)["y"]))
+
+    h = 1e-5
+    checks = [("dx", x, None)] + [(k, W[k], k) for k in sorted(W)]
+    for name, arr, key in checks:
+        flat = np.arange(arr.size)
+        for idx in rng.choice(flat, size=min(per_tensor, arr.size), replace=False):
+            i = np.unravel_index(idx, arr.shape)
+            plus, minus = arr.copy(), arr.copy()
+            plus[i] += h
+            minus[i] -= h
+            if key is None:
+                fd = (loss(plus, W) - loss(minus, W)) / (2 * h)
+            else:
+                fd = (loss(x, dict(W, **{key: plus})) - loss(x, dict(W, **{key: minus}))) / (2 * h)
+            got = grads["dx" if key is None else key][i]
+            scale = max(1.0, float(np.max(np.abs(grads["dx" if key is None else key]))))
+            assert abs(got - fd) <= tol * scale, f"{name}{i}: analytic {got:.9e} vs finite difference {fd:.9e}"
+
+
+def pin_backward_finite_differences_full():
+    """Every gradient of a full-causal layer (x and all nine weights) matches
+    central finite differences of sum(dy * y)."""
+    _fd_check(TINY, pos_offset=0)
+
+
+def pin_backward_finite_differences_window_batch():
+    """The same for a windowed layer over two sequences at a position offset."""
+    _fd_check(replace(TINY, window=3), pos_offset=5, B=2, L=6, seed=21)
+
+
+def pin_backward_finite_differences_yarn():
+    """The same with YaRN frequencies and the cos/sin factor on a full layer."""
+    cfg = replace(TINY, yarn_factor=8.0, yarn_orig_len=8, yarn_beta_fast=32.0, yarn_beta_slow=1.0)
+    _fd_check(cfg, pos_offset=3, seed=31)
+
+
+def pin_rope_backward_is_adjoint():
+    """<rope(u), g> = <u, rope_backward(g)> for plain and YaRN frequencies."""
+    rng = np.random.Generator(np.random.PCG64(41))
+    u = rng.standard_normal((3, 9, 8))
+    g = rng.standard_normal((3, 9, 8))
+    pos = np.arange(9) * 3.0 + 1.0
+    for yarn in (None, (16.0, 4.0, 32.0, 1.0)):
+        a = float(np.sum(R.rope(u, pos, 100.0, yarn) * g))
+        b = float(np.sum(u * R.rope_backward(g, pos, 100.0, yarn)))
+        assert abs(a - b) <= 1e-12 * max(1.0, abs(a)), (a, b)
+
+
+def pin_rms_norm_backward_finite_differences():
+    """RMSNorm's input and gain gradients against central differences."""
+    rng = np.random.Generator(np.random.PCG64(43))
+    c = rng.standard_normal((4, 10))
+    gamma = 1.0 + 0.3 * rng.standard_normal(10)
+    g = rng.standard_normal((4, 10))
+    dc, dgamma = R.rms_norm_backward(c, gamma, 1e-3, g)
+    h = 1e-6
+    for i in range(4):
+        for j in range(10):
+            p, m = c.copy(), c.copy()
+            p[i, j] += h
+            m[i, j] -= h
+            fd = (np.sum(g * R.rms_norm(p, gamma, 1e-3)) - np.sum(g * R.rms_norm(m, gamma, 1e-3))) / (2 * h)
+            assert abs(fd - dc[i, j]) < 1e-8, (i, j, fd, dc[i, j])
+    for j in range(10):
+        p, m = gamma.copy(), gamma.copy()
+        p[j] += h
+        m[j] -= h
+        fd = (np.sum(g * R.rms_norm(c, p, 1e-3)) - np.sum(g * R.rms_norm(c, m, 1e-3))) / (2 * h)
+        assert abs(fd - dgamma[j]) < 1e-8, (j, fd, dgamma[j])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

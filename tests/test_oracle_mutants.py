@@ -10,6 +10,9 @@ import pytest
 import oracle.gdla_ref as R
 from tests import oracle_pins as P
 
+# unpatched oracle functions, for mutants built on top of them
+_ORIG = {name: getattr(R, name) for name in ("rope", "attention_heads_backward")}
+
 
 def _rope_wrong_sign(u, pos, base, yarn=None):
     u = np.asarray(u, np.float64)
@@ -231,6 +234,53 @@ def _paged_slot_no_table(block_table, page_rows, b, p):
     return b * len(block_table[b]) + p // page_rows, p % page_rows
 
 
+def _rope_backward_forward_rotation(g, pos, base, yarn=None):
+    # applies the forward rotation instead of its transpose
+    return _ORIG["rope"](g, pos, base, yarn)
+
+
+def _rms_backward_no_projection(c, gamma, eps, g):
+    c, g = np.asarray(c, np.float64), np.asarray(g, np.float64)
+    r = 1.0 / np.sqrt(np.mean(c * c, axis=-1, keepdims=True) + eps)
+    return r * g * np.asarray(gamma, np.float64), np.sum((g * c * r).reshape(-1, c.shape[-1]), axis=0)
+
+
+def _attn_backward_no_rowsum(q, kc, kr, v, dH, cfg):
+    # dS = P * dP, the softmax's rowsum term dropped
+    import math as _m
+    L = q.shape[0]
+    scale = 1.0 / _m.sqrt(cfg.d_qk)
+    dq = np.zeros_like(q)
+    dkc = np.zeros((L, cfg.n_noise, cfg.d_nope))
+    dkr = np.zeros((L, cfg.d_rope))
+    dv = np.zeros((L, cfg.n_noise, cfg.d_v))
+    t = np.arange(L)
+    lo = np.array([R.attended_keys(i, cfg.window)[0] for i in range(L)])
+    allowed = (t[None, :] <= t[:, None]) & (t[None, :] >= lo[:, None])
+    for h in range(cfg.n_heads):
+        n = R.kv_head_of(h, cfg)
+        k = np.concatenate([kc[:, n, :], kr], axis=-1)
+        s = np.where(allowed, (q[:, h, :] @ k.T) * scale, -np.inf)
+        P = np.exp(s - s.max(axis=-1, keepdims=True))
+        P /= P.sum(axis=-1, keepdims=True)
+        dv[:, n, :] += P.T @ dH[:, h, :]
+        dS = P * (dH[:, h, :] @ v[:, n, :].T)
+        dq[:, h, :] = (dS @ k) * scale
+        dk = (dS.T @ q[:, h, :]) * scale
+        dkc[:, n, :] += dk[:, :cfg.d_nope]
+        dkr += dk[:, cfg.d_nope:]
+    return dq, dkc, dkr, dv
+
+
+def _attn_backward_rotary_key_per_group(q, kc, kr, v, dH, cfg):
+    # the rotary key's gradient kept from the noise heads only (not every head)
+    dq, dkc, dkr, dv = _ORIG["attention_heads_backward"](q, kc, kr, v, dH, cfg)
+    dH2 = np.array(dH)
+    dH2[:, :cfg.n_signal] = 0.0
+    _, _, dkr_noise, _ = _ORIG["attention_heads_backward"](q, kc, kr, v, dH2, cfg)
+    return dq, dkc, dkr_noise, dv
+
+
 MUTANTS = {
     "rope_wrong_sign": ("rope", _rope_wrong_sign),
     "rope_adjacent_pairs": ("rope", _rope_adjacent_pairs),
@@ -262,6 +312,10 @@ MUTANTS = {
     "packed_segments_skip_first": ("packed_segments", _packed_segments_skip_first),
     "paged_slot_swapped": ("paged_slot", _paged_slot_swapped),
     "paged_slot_no_table": ("paged_slot", _paged_slot_no_table),
+    "rope_backward_forward_rotation": ("rope_backward", _rope_backward_forward_rotation),
+    "rms_backward_no_projection": ("rms_norm_backward", _rms_backward_no_projection),
+    "attn_backward_no_rowsum": ("attention_heads_backward", _attn_backward_no_rowsum),
+    "attn_backward_rotary_key_per_group": ("attention_heads_backward", _attn_backward_rotary_key_per_group),
 }
 
 
