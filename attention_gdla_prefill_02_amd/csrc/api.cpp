@@ -10,6 +10,7 @@
 #include <cstring>
 
 #include "../../include/gdla.h"
+#include "backward.h"
 #include "decode.h"
 #include "kernels.h"
 
@@ -297,7 +298,7 @@ const char* gdla_status_string(gdla_status s) {
 
 const char* gdla_last_error(void) { return g_err; }
 
-int32_t gdla_version(void) { return 102; }   // 1.02: packed prefill, paged cache
+int32_t gdla_version(void) { return 103; }   // 1.03: layer backward
 
 size_t gdla_prefill_workspace_size(const gdla_config* cfg, int32_t B, int32_t L) {
   if (check_config(cfg) != GDLA_OK || B < 0 || L < 0) return 0;
@@ -487,6 +488,62 @@ gdla_status gdla_decode_paged(const gdla_config* cfg, const gdla_weights* w, int
     return fail(GDLA_ERR_UNSUPPORTED, "B * max_pages beyond 2^28 block-table entries");
   hipError_t err = gdla::decode_step(cfg, w, B, x, y, paged_view(cache), cache_lens, workspace, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "decode");
+  return GDLA_OK;
+}
+
+namespace {
+
+gdla::BwdDims bwd_dims(const gdla_config* c) {
+  const Dims D = dims_of(c);
+  return gdla::BwdDims{D.d, D.rq, D.rkv, D.nN, D.g, D.dn, D.dr, D.dv, D.nS, D.H, D.dqk, D.ndown, D.nq, D.ngate};
+}
+
+gdla_status check_backward_shape(const gdla_config* cfg, int32_t B, int32_t L) {
+  gdla_status st = check_config(cfg);
+  if (st != GDLA_OK) return st;
+  if (cfg->dtype != GDLA_BF16) return fail(GDLA_ERR_UNSUPPORTED, "backward is bf16 only");
+  if (cfg->q_rank + cfg->kv_rank > 2048) return fail(GDLA_ERR_UNSUPPORTED, "backward needs q_rank + kv_rank <= 2048");
+  if (B < 0 || L < 0) return fail(GDLA_ERR_INVALID_ARG, "B and L must be >= 0 (got %d, %d)", B, L);
+  if ((int64_t)B * L > ((int64_t)1 << 22)) return fail(GDLA_ERR_UNSUPPORTED, "backward supports B*L <= 2^22");
+  return GDLA_OK;
+}
+
+}  // namespace
+
+size_t gdla_backward_workspace_size(const gdla_config* cfg, int32_t B, int32_t L) {
+  if (check_backward_shape(cfg, B, L) != GDLA_OK) return 0;
+  return gdla::backward_layout(bwd_dims(cfg), (int64_t)B * L).total;
+}
+
+gdla_status gdla_backward(const gdla_config* cfg, const gdla_weights* w, int32_t B, int32_t L, int64_t pos_offset,
+                          const void* x, const void* dy, void* dx, const gdla_grads* grads, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  gdla_status st = check_backward_shape(cfg, B, L);
+  if (st != GDLA_OK) return st;
+  if (pos_offset < 0) return fail(GDLA_ERR_INVALID_ARG, "pos_offset must be >= 0");
+  if (B == 0 || L == 0) return GDLA_OK;
+  if (pos_offset + L > (int64_t)1 << 30) return fail(GDLA_ERR_INVALID_ARG, "positions beyond 2^30");
+  st = check_weights(w);
+  if (st != GDLA_OK) return st;
+  if (!x || !dy || !dx || !grads) return fail(GDLA_ERR_INVALID_ARG, "x, dy, dx and grads must be non-NULL");
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dx))
+    return fail(GDLA_ERR_INVALID_ARG, "x, dy and dx must be 16-byte aligned");
+  if (dx == x || dx == dy) return fail(GDLA_ERR_INVALID_ARG, "dx must not alias x or dy");
+  const float* gp[] = {grads->w_dq, grads->g_q, grads->w_dkv, grads->g_kv, grads->w_lambda,
+                       grads->w_uq, grads->w_ukv, grads->w_gate, grads->w_o};
+  for (const float* p : gp) {
+    if (!p) return fail(GDLA_ERR_INVALID_ARG, "every gradient pointer must be non-NULL");
+    if (!aligned16(p)) return fail(GDLA_ERR_INVALID_ARG, "gradient buffers must be 16-byte aligned");
+  }
+  const gdla::BwdDims D = bwd_dims(cfg);
+  const gdla::BackwardLayout P = gdla::backward_layout(D, (int64_t)B * L);
+  if (!workspace) return fail(GDLA_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", P.total);
+  if (((uintptr_t)workspace & 255) != 0) return fail(GDLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < P.total)
+    return fail(GDLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, P.total);
+  const gdla::BwdCall c{cfg, w, grads, B, L, (int64_t)B * L, pos_offset, x, dy, dx, workspace};
+  hipError_t err = gdla::backward_step(D, P, c, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "backward");
   return GDLA_OK;
 }
 

@@ -313,7 +313,23 @@ attn_bf16_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: H = O / l, Z = gate * (H_S - lambda * H_N)
-  const float inv = 1.0f / (lsum + xor32(lsum));
+  const float ltot = lsum + xor32(lsum);
+  const float inv = 1.0f / ltot;
+  if (a.h_out && qme < L) {
+    // training forward: this head's H row (bf16) and the log-sum-exp of its
+    // scores in the exp2 domain, m + log2(l), which the backward re-uses
+    bf16* hrow = (bf16*)a.h_out + ((tb + qme) * (int64_t)(nS + nN) + head) * DV;
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bf16x4 h4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h4[e] = (bf16)(o[d][4 * i + e] * inv);
+        *reinterpret_cast<bf16x4*>(hrow + d * 32 + 8 * i + 4 * hi) = h4;
+      }
+    if (hi == 0) a.lse_out[(tb + qme) * (int64_t)(nS + nN) + head] = m + log2f(ltot);
+  }
   float* sH = reinterpret_cast<float*>(smem_raw);                          // [BQ][DV + 4]
   bf16* sZ = reinterpret_cast<bf16*>(smem_raw + (size_t)BQ * (DV + 4) * 4);  // [BQ][g*DV + 8]
   const int qrow = 32 * half + l32;

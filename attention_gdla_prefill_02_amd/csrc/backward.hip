@@ -1,0 +1,901 @@
+// Backward of one GDLA layer (bf16), with the forward's activations
+// recomputed from x ("Motif 3: Technical Report", training-infrastructure
+// paragraph: activations are recomputed for the backward pass).  The steps of
+// the GDLA definition paragraph are differentiated in reverse:
+//
+//   y = Z W_O^T                 dZ = dy W_O, dW_O = dy^T Z
+//   Z = G * D, G = sigmoid(.)   dG_logit = dZ D G (1 - G), dD = dZ G
+//   D_j = H_j - lambda_j H_N    dH_j = dD_j, dH_N = -sum_j lambda_j dD_j,
+//                               dlambda_j = -<dD_j, H_N>
+//   H = softmax(S) V            per head: dV = P^T dH, dP = dH V^T,
+//                               dS = P (dP - rowsum(dH * H)), dQ = c dS K,
+//                               dK = c dS^T Q  (c = 1/sqrt(d_qk))
+//   RoPE, RMSNorm, the up- and down-projections: transposed rotations,
+//   the RMSNorm Jacobian, and GEMMs against the transposed weights.
+//
+// Attention backward on the 16x16x32 bf16 MFMA, in two kernels so that no
+// gradient needs atomics: attn_bwd_dq_kernel owns a 32-query block of one KV
+// group (its g+1 heads share every staged key tile, as in the forward) and
+// sweeps the key tiles; attn_bwd_dkv_kernel owns a 128-key block (16 keys per
+// wave) and sweeps (query tile, head) pairs, so dK and dV of the group's
+// shared keys accumulate in registers across all g+1 heads.  Products whose
+// reduction runs over keys (dQ) or queries (dK, dV) take their A operand from
+// a transposed copy of K, Q or dH staged in LDS, read as two 8-byte halves
+// at keys/queries 4q..4q+3 and 16+4q..16+4q+3, the order in which the
+// score-shaped registers (rows 4q+j of two 16-row tiles) become a B operand.
+#include <cmath>
+
+#include "backward.h"
+#include "common.h"
+
+namespace gdla {
+namespace {
+
+constexpr int DN = 128, DR = 64, DQK = DN + DR, DV = 128;
+constexpr int TR = 32;                    // rows of a streamed tile (keys or queries)
+constexpr int QK_LD = DQK + 8;            // LDS row of a [row][d_qk] tile (elements)
+constexpr int V_LD = DV + 8;              // LDS row of a [row][d_v] tile
+constexpr int T_LD = TR + 8;              // LDS row of a transposed [dim][32 rows] tile
+
+// 8 bf16 of a transposed tile row: columns 4q..4q+3 and 16+4q..16+4q+3
+GDLA_DEV bf16x8 tr_cols(const bf16* row, int q4) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(row + 4 * q4);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(row + 16 + 4 * q4);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Stage R rows of C 16-byte chunks into LDS rows of C + 1 chunks (the last is
+// padding), 1 KB per load instruction: lane i of a block writes LDS bytes
+// 16i.. of that block, so each lane fetches the chunk that belongs there.
+// src(r, c) returns the global address of chunk c of row r; pad chunks fetch
+// chunk 0 of their row.  Called by all waves; wave w issues blocks w, w+NW..
+template <int R, int C, int NW, class Src>
+GDLA_DEV void stage_rows(unsigned char* lds, int wave, int lane, Src src) {
+  constexpr int CH = R * (C + 1), BLK = (CH + 63) / 64;
+#pragma unroll
+  for (int i = 0; i < (BLK + NW - 1) / NW; ++i) {
+    const int blk = wave + NW * i;
+    const int pos = blk * 64 + lane;
+    if (blk < BLK && pos < CH) {
+      const int r = pos / (C + 1), c = pos % (C + 1);
+      g2lds16(src(r, c < C ? c : 0), lds + blk * 1024);
+    }
+  }
+}
+
+// ------------------------------------------------------------ transpose
+// dst[c][r] = src[r][c] (r < R, c < C); dst[c][r] = 0 for R <= r < Rpad.
+// 64 x 64 tiles through LDS; rows 16-byte aligned (ld multiples of 8).
+__global__ void __launch_bounds__(256)
+transpose_kernel(const bf16* src, int64_t lds_, bf16* dst, int64_t ldd, int R, int C, int Rpad) {
+  __shared__ bf16 t[64][72];
+  const int tid = threadIdx.x;
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  {
+    const int rr = tid >> 2, cc = 16 * (tid & 3);
+    const int r = r0 + rr;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = c0 + cc + 8 * h;
+      bf16x8 v = {};
+      if (r < R) {
+        if (c + 8 <= C) {
+          v = *reinterpret_cast<const bf16x8*>(src + (int64_t)r * lds_ + c);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (c + e < C) v[e] = src[(int64_t)r * lds_ + c + e];
+        }
+      }
+      *reinterpret_cast<bf16x8*>(&t[rr][cc + 8 * h]) = v;
+    }
+  }
+  __syncthreads();
+  {
+    const int cc = tid >> 2, rr = 16 * (tid & 3);
+    const int c = c0 + cc;
+    if (c < C) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = r0 + rr + 8 * h;
+        if (r < Rpad) {
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = t[rr + 8 * h + e][cc];
+          *reinterpret_cast<bf16x8*>(dst + (int64_t)c * ldd + r) = v;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ gate and differential
+struct EpiBwdArgs {
+  const float* dz;        // [T, nS*d_v] fp32: dy W_O
+  const float* gate;      // [T, nS*d_v] fp32
+  const bf16* h;          // [T, H, d_v]: the forward's per-head outputs
+  const float* lam;       // [T, nS]
+  bf16* dglogit; int64_t ld_dg;   // gate-logit gradient, row t at dglogit + t*ld_dg
+  bf16* dh;               // [T, H, d_v]
+  float* dvec;            // [T, H]: rowsum(dH * H)
+  bf16* dllogit; int64_t ld_dl;   // lambda-logit gradient, [T] rows of nS
+  int64_t T; int nN, g;
+};
+
+// One wave per token; lane l holds value dims 2l, 2l+1 of every head.
+__global__ void __launch_bounds__(256)
+epi_bwd_kernel(EpiBwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int nS = a.g * a.nN, H = nS + a.nN, d = 2 * lane;
+  const bf16* hrow = a.h + t * H * DV;
+  for (int n = 0; n < a.nN; ++n) {
+    const bf16x2 hn2 = *reinterpret_cast<const bf16x2*>(hrow + (nS + n) * DV + d);
+    const float hn0 = (float)hn2[0], hn1 = (float)hn2[1];
+    float dhn0 = 0.f, dhn1 = 0.f;
+    for (int jj = 0; jj < a.g; ++jj) {
+      const int j = n * a.g + jj;
+      const bf16x2 hs2 = *reinterpret_cast<const bf16x2*>(hrow + j * DV + d);
+      const float2 dz = *reinterpret_cast<const float2*>(a.dz + t * nS * DV + j * DV + d);
+      const float2 gt = *reinterpret_cast<const float2*>(a.gate + t * nS * DV + j * DV + d);
+      const float lam = a.lam[t * nS + j];
+      const float D0 = (float)hs2[0] - lam * hn0, D1 = (float)hs2[1] - lam * hn1;
+      bf16x2 dg;
+      dg[0] = (bf16)(dz.x * D0 * gt.x * (1.f - gt.x));
+      dg[1] = (bf16)(dz.y * D1 * gt.y * (1.f - gt.y));
+      *reinterpret_cast<bf16x2*>(a.dglogit + t * a.ld_dg + j * DV + d) = dg;
+      const float dD0 = dz.x * gt.x, dD1 = dz.y * gt.y;
+      bf16x2 dd;
+      dd[0] = (bf16)dD0;
+      dd[1] = (bf16)dD1;
+      *reinterpret_cast<bf16x2*>(a.dh + t * H * DV + j * DV + d) = dd;
+      const float dv = wave_sum((float)dd[0] * (float)hs2[0] + (float)dd[1] * (float)hs2[1]);
+      const float dl = wave_sum(-(dD0 * hn0 + dD1 * hn1));
+      if (lane == 0) {
+        a.dvec[t * H + j] = dv;
+        a.dllogit[t * a.ld_dl + j] = (bf16)(dl * lam * (1.f - lam));
+      }
+      dhn0 -= lam * dD0;
+      dhn1 -= lam * dD1;
+    }
+    bf16x2 dn;
+    dn[0] = (bf16)dhn0;
+    dn[1] = (bf16)dhn1;
+    *reinterpret_cast<bf16x2*>(a.dh + t * H * DV + (nS + n) * DV + d) = dn;
+    const float dv = wave_sum((float)dn[0] * hn0 + (float)dn[1] * hn1);
+    if (lane == 0) a.dvec[t * H + nS + n] = dv;
+  }
+}
+
+// ------------------------------------------------------------ attention backward
+struct AttnBwdArgs {
+  const bf16* q; int64_t ld_q;          // [T, H*d_qk], rotary parts RoPE'd
+  const bf16* kv; int64_t ld_kv;        // [T, nN*d_nope | nN*d_v]: K^C, then V
+  const bf16* kr;                       // [T, d_rope]
+  const bf16* kvT; const bf16* krT; const bf16* qT; const bf16* dhT; int64_t ld_t;   // transposed, [dim][Tp]
+  const bf16* dh;                       // [T, H*d_v]
+  const float* lse; const float* dvec;  // [T, H]
+  const float* rope;                    // [T, d_rope/2, 2]
+  bf16* dq; int64_t ld_dq;              // out: dQ with RoPE's backward applied, [T] rows
+  bf16* dkv;                            // out: [T, nN*d_nope | nN*d_v]
+  float* dkr_part;                      // out: [nN, T, d_rope], one slice per KV group
+  int64_t T; int B, L, nN, window;
+  float scale, sc;                      // 1/sqrt(d_qk), and times log2(e)
+};
+
+GDLA_DEV bool visible(int ql, int kl, int L, int W) {
+  return (unsigned)ql < (unsigned)L && kl <= ql && kl >= 0 && (W <= 0 || ql - kl < W);
+}
+
+// dQ: workgroup = (sequence, KV group n, 32 queries); wave = (head slot, 16
+// queries).  Key tiles of 32 stream rows through LDS: K rows (score A
+// operand), V rows (dP A operand) and K^T (dQ A operand).
+template <int G>
+__global__ void __launch_bounds__(128 * (G + 1), 1)
+attn_bwd_dq_kernel(AttnBwdArgs a) {
+  constexpr int NW = 2 * (G + 1);
+  constexpr int K_BYTES = TR * QK_LD * 2, V_BYTES = TR * V_LD * 2, KT_BYTES = DQK * T_LD * 2;
+  constexpr int BUF = K_BYTES + V_BYTES + KT_BYTES;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int hs = w % (G + 1), qg = w / (G + 1);
+  const int nN = a.nN, nS = G * nN, H = nS + nN, L = a.L, W = a.window;
+  const int nqb = cdiv(L, 32);
+  const int qb = blockIdx.x % nqb, rest = blockIdx.x / nqb, n = rest % nN, b = rest / nN;
+  const int64_t tb = (int64_t)b * L, T = a.T;
+  const int head = hs < G ? n * G + hs : nS + n;
+  const int q0 = qb * 32, ql = q0 + 16 * qg + r16;        // this lane's query (score column)
+  const int64_t qrow = tb + min(ql, L - 1);
+
+  bf16x8 qf[DQK / 32], dhf[DV / 32];
+#pragma unroll
+  for (int s = 0; s < DQK / 32; ++s)
+    qf[s] = *reinterpret_cast<const bf16x8*>(a.q + qrow * a.ld_q + head * DQK + 32 * s + 8 * q4);
+#pragma unroll
+  for (int s = 0; s < DV / 32; ++s)
+    dhf[s] = *reinterpret_cast<const bf16x8*>(a.dh + qrow * H * DV + head * DV + 32 * s + 8 * q4);
+  const float lse = a.lse[qrow * H + head], dvec = a.dvec[qrow * H + head];
+
+  // key tiles (32 stream rows, aligned to the stream) that hold keys of this block
+  const int k_lo = W > 0 ? max(0, q0 - W + 1) : 0, k_hi = min(L, q0 + 32);
+  const int t_lo = (int)((tb + k_lo) / TR), t_hi = (int)cdiv(tb + k_hi, (int64_t)TR);
+  const int koff = n * DN, voff = nN * DN + n * DV;
+
+  auto load = [&](int tile, int buf) {
+    unsigned char* base = smem + buf * BUF;
+    const int64_t r0 = (int64_t)tile * TR;
+    stage_rows<TR, DQK / 8, NW>(base, w, lane, [&](int r, int c) -> const void* {
+      const int64_t row = min(r0 + r, T - 1);
+      return c < DN / 8 ? (const void*)(a.kv + row * a.ld_kv + koff + 8 * c)
+                        : (const void*)(a.kr + row * DR + 8 * (c - DN / 8));
+    });
+    stage_rows<TR, DV / 8, NW>(base + K_BYTES, w, lane, [&](int r, int c) -> const void* {
+      const int64_t row = min(r0 + r, T - 1);
+      return a.kv + row * a.ld_kv + voff + 8 * c;
+    });
+    stage_rows<DQK, TR / 8, NW>(base + K_BYTES + V_BYTES, w, lane, [&](int r, int c) -> const void* {
+      return r < DN ? (const void*)(a.kvT + (int64_t)(koff + r) * a.ld_t + r0 + 8 * c)
+                    : (const void*)(a.krT + (int64_t)(r - DN) * a.ld_t + r0 + 8 * c);
+    });
+  };
+
+  f32x4 dq[DQK / 16];
+#pragma unroll
+  for (int i = 0; i < DQK / 16; ++i) dq[i] = f32x4{};
+
+  load(t_lo, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int tile = t_lo; tile < t_hi; ++tile) {
+    const int buf = (tile - t_lo) & 1;
+    if (tile + 1 < t_hi) load(tile + 1, buf ^ 1);
+    const unsigned char* base = smem + buf * BUF;
+    const bf16* Kt = reinterpret_cast<const bf16*>(base);
+    const bf16* Vt = reinterpret_cast<const bf16*>(base + K_BYTES);
+    const bf16* KT = reinterpret_cast<const bf16*>(base + K_BYTES + V_BYTES);
+    const int kb = (int)((int64_t)tile * TR - tb);   // first key of the tile, within the sequence
+    // S^T (keys x this wave's queries) and dP^T = V dH^T
+    f32x4 st[2], dp[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      st[u] = f32x4{};
+      dp[u] = f32x4{};
+#pragma unroll
+      for (int s = 0; s < DQK / 32; ++s)
+        st[u] = mfma16(*reinterpret_cast<const bf16x8*>(Kt + (16 * u + r16) * QK_LD + 32 * s + 8 * q4), qf[s], st[u]);
+#pragma unroll
+      for (int s = 0; s < DV / 32; ++s)
+        dp[u] = mfma16(*reinterpret_cast<const bf16x8*>(Vt + (16 * u + r16) * V_LD + 32 * s + 8 * q4), dhf[s], dp[u]);
+    }
+    // dS^T = P^T (dP^T - rowsum(dH H)), as the B operand of dQ^T += K^T dS^T
+    bf16x8 dsb;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kl = kb + 16 * u + 4 * q4 + j;
+        const float p = visible(ql, kl, L, W) ? fast_exp2(st[u][j] * a.sc - lse) : 0.f;
+        dsb[4 * u + j] = (bf16)(p * (dp[u][j] - dvec));
+      }
+#pragma unroll
+    for (int rt = 0; rt < DQK / 16; ++rt) dq[rt] = mfma16(tr_cols(KT + (16 * rt + r16) * T_LD, q4), dsb, dq[rt]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // dQ = c dS K; RoPE's backward on the rotary dims (pairs i, i + 32 of the
+  // rotary block sit in tiles rt and rt + 2 of the same lane)
+  if ((unsigned)ql < (unsigned)L) {
+    const int64_t row = tb + ql;
+#pragma unroll
+    for (int rt = 0; rt < DQK / 16; ++rt) dq[rt] *= a.scale;
+#pragma unroll
+    for (int rt = DN / 16; rt < DN / 16 + 2; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 16 * (rt - DN / 16) + 4 * q4 + j;
+        const float c = a.rope[(row * (DR / 2) + i) * 2], s = a.rope[(row * (DR / 2) + i) * 2 + 1];
+        const float g1 = dq[rt][j], g2 = dq[rt + 2][j];
+        dq[rt][j] = g1 * c + g2 * s;
+        dq[rt + 2][j] = g2 * c - g1 * s;
+      }
+    bf16* out = a.dq + row * a.ld_dq + head * DQK;
+#pragma unroll
+    for (int rt = 0; rt < DQK / 16; ++rt) {
+      bf16x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = (bf16)dq[rt][j];
+      *reinterpret_cast<bf16x4*>(out + 16 * rt + 4 * q4) = v;
+    }
+  }
+}
+
+// dK, dV: workgroup = (sequence, KV group n, 128 keys), wave = 16 keys; the
+// workgroup sweeps (query tile, head) pairs, staging per pair the head's Q and
+// dH rows (score and dP A operands), Q^T and dH^T (dK and dV A operands),
+// and the rows' log-sum-exp and rowsum(dH H).
+constexpr int DKV_KEYS = 128, DKV_NW = DKV_KEYS / 16;
+
+template <int G>
+__global__ void __launch_bounds__(64 * DKV_NW, 1)
+attn_bwd_dkv_kernel(AttnBwdArgs a) {
+  constexpr int NW = DKV_NW;
+  constexpr int Q_BYTES = TR * QK_LD * 2, DH_BYTES = TR * V_LD * 2, QT_BYTES = DQK * T_LD * 2,
+                DHT_BYTES = DV * T_LD * 2, ST_BYTES = 2 * TR * 4;
+  constexpr int BUF = Q_BYTES + DH_BYTES + QT_BYTES + DHT_BYTES + ST_BYTES;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int nN = a.nN, nS = G * nN, H = nS + nN, L = a.L, W = a.window;
+  const int nkb = cdiv(L, DKV_KEYS);
+  const int kbk = blockIdx.x % nkb, rest = blockIdx.x / nkb, n = rest % nN, b = rest / nN;
+  const int64_t tb = (int64_t)b * L, T = a.T;
+  const int k0 = kbk * DKV_KEYS, kw = k0 + 16 * w, kl = kw + r16;   // this lane's key (score column)
+  const int64_t krow = tb + min(kl, L - 1);
+  const int koff = n * DN, voff = nN * DN + n * DV;
+
+  bf16x8 kf[DQK / 32], vf[DV / 32];
+#pragma unroll
+  for (int s = 0; s < DQK / 32; ++s)
+    kf[s] = s < DN / 32 ? *reinterpret_cast<const bf16x8*>(a.kv + krow * a.ld_kv + koff + 32 * s + 8 * q4)
+                        : *reinterpret_cast<const bf16x8*>(a.kr + krow * DR + 32 * (s - DN / 32) + 8 * q4);
+#pragma unroll
+  for (int s = 0; s < DV / 32; ++s)
+    vf[s] = *reinterpret_cast<const bf16x8*>(a.kv + krow * a.ld_kv + voff + 32 * s + 8 * q4);
+
+  // query tiles (stream-aligned) that see keys of this block
+  const int kend = min(L, k0 + DKV_KEYS);
+  const int q_hi = W > 0 ? min(L, kend - 1 + W) : L;
+  const int t_lo = (int)((tb + k0) / TR), t_hi = (int)cdiv(tb + q_hi, (int64_t)TR);
+  const int steps = (t_hi - t_lo) * (G + 1);
+
+  auto load = [&](int step, int buf) {
+    const int tile = t_lo + step / (G + 1), hs = step % (G + 1);
+    const int head = hs < G ? n * G + hs : nS + n;
+    unsigned char* base = smem + buf * BUF;
+    const int64_t r0 = (int64_t)tile * TR;
+    stage_rows<TR, DQK / 8, NW>(base, w, lane, [&](int r, int c) -> const void* {
+      return a.q + min(r0 + r, T - 1) * a.ld_q + head * DQK + 8 * c;
+    });
+    stage_rows<TR, DV / 8, NW>(base + Q_BYTES, w, lane, [&](int r, int c) -> const void* {
+      return a.dh + min(r0 + r, T - 1) * H * DV + head * DV + 8 * c;
+    });
+    stage_rows<DQK, TR / 8, NW>(base + Q_BYTES + DH_BYTES, w, lane, [&](int r, int c) -> const void* {
+      return a.qT + (int64_t)(head * DQK + r) * a.ld_t + r0 + 8 * c;
+    });
+    stage_rows<DV, TR / 8, NW>(base + Q_BYTES + DH_BYTES + QT_BYTES, w, lane, [&](int r, int c) -> const void* {
+      return a.dhT + (int64_t)(head * DV + r) * a.ld_t + r0 + 8 * c;
+    });
+  };
+  // the rows' log-sum-exp and rowsum(dH H) go through registers (strided in HBM)
+  float st_lse = 0.f, st_dv = 0.f;
+  auto fetch_stats = [&](int step) {
+    const int tile = t_lo + step / (G + 1), hs = step % (G + 1);
+    const int head = hs < G ? n * G + hs : nS + n;
+    if (tid < TR) {
+      const int64_t row = min((int64_t)tile * TR + tid, T - 1);
+      st_lse = a.lse[row * H + head];
+      st_dv = a.dvec[row * H + head];
+    }
+  };
+  auto store_stats = [&](int buf) {
+    float* st = reinterpret_cast<float*>(smem + buf * BUF + Q_BYTES + DH_BYTES + QT_BYTES + DHT_BYTES);
+    if (tid < TR) {
+      st[tid] = st_lse;
+      st[TR + tid] = st_dv;
+    }
+  };
+
+  f32x4 dk[DQK / 16], dv[DV / 16];
+#pragma unroll
+  for (int i = 0; i < DQK / 16; ++i) dk[i] = f32x4{};
+#pragma unroll
+  for (int i = 0; i < DV / 16; ++i) dv[i] = f32x4{};
+
+  if (steps > 0) {
+    load(0, 0);
+    fetch_stats(0);
+    store_stats(0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int step = 0; step < steps; ++step) {
+    const int buf = step & 1;
+    if (step + 1 < steps) {
+      load(step + 1, buf ^ 1);
+      fetch_stats(step + 1);
+    }
+    const int tile = t_lo + step / (G + 1);
+    const int qb = (int)((int64_t)tile * TR - tb);   // first query of the tile, within the sequence
+    // skip pairs this wave cannot see (wave-uniform)
+    const bool any = qb + TR - 1 >= kw && qb < L && (W <= 0 || qb - (kw + 15) < W);
+    if (any) {
+      const unsigned char* base = smem + buf * BUF;
+      const bf16* Qt = reinterpret_cast<const bf16*>(base);
+      const bf16* Dt = reinterpret_cast<const bf16*>(base + Q_BYTES);
+      const bf16* QT = reinterpret_cast<const bf16*>(base + Q_BYTES + DH_BYTES);
+      const bf16* DT = reinterpret_cast<const bf16*>(base + Q_BYTES + DH_BYTES + QT_BYTES);
+      const float* st = reinterpret_cast<const float*>(base + Q_BYTES + DH_BYTES + QT_BYTES + DHT_BYTES);
+      // S (queries x this wave's keys) and dP = dH V^T
+      f32x4 s_[2], dp[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        s_[u] = f32x4{};
+        dp[u] = f32x4{};
+#pragma unroll
+        for (int s = 0; s < DQK / 32; ++s)
+          s_[u] = mfma16(*reinterpret_cast<const bf16x8*>(Qt + (16 * u + r16) * QK_LD + 32 * s + 8 * q4), kf[s], s_[u]);
+#pragma unroll
+        for (int s = 0; s < DV / 32; ++s)
+          dp[u] = mfma16(*reinterpret_cast<const bf16x8*>(Dt + (16 * u + r16) * V_LD + 32 * s + 8 * q4), vf[s], dp[u]);
+      }
+      bf16x8 pb, dsb;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(st + 16 * u + 4 * q4);
+        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(st + TR + 16 * u + 4 * q4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int qlq = qb + 16 * u + 4 * q4 + j;
+          const float p = visible(qlq, kl, L, W) ? fast_exp2(s_[u][j] * a.sc - lse4[j]) : 0.f;
+          pb[4 * u + j] = (bf16)p;
+          dsb[4 * u + j] = (bf16)(p * (dp[u][j] - dv4[j]));
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < DV / 16; ++rt) dv[rt] = mfma16(tr_cols(DT + (16 * rt + r16) * T_LD, q4), pb, dv[rt]);
+#pragma unroll
+      for (int rt = 0; rt < DQK / 16; ++rt) dk[rt] = mfma16(tr_cols(QT + (16 * rt + r16) * T_LD, q4), dsb, dk[rt]);
+    }
+    if (step + 1 < steps) store_stats(buf ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // dK = c dS^T Q (content dims to dkv, rotary dims to this group's slice of
+  // dkr_part), dV = P^T dH; lane holds key kl, dims 16 rt + 4 q4 + j
+  if ((unsigned)kl < (unsigned)L) {
+    const int64_t row = tb + kl;
+    bf16* krow_out = a.dkv + row * a.ld_kv;
+#pragma unroll
+    for (int rt = 0; rt < DN / 16; ++rt) {
+      bf16x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = (bf16)(dk[rt][j] * a.scale);
+      *reinterpret_cast<bf16x4*>(krow_out + koff + 16 * rt + 4 * q4) = v;
+    }
+    float* rp = a.dkr_part + ((int64_t)n * T + row) * DR;
+#pragma unroll
+    for (int rt = DN / 16; rt < DQK / 16; ++rt)
+      *reinterpret_cast<f32x4*>(rp + 16 * (rt - DN / 16) + 4 * q4) = dk[rt] * a.scale;
+#pragma unroll
+    for (int rt = 0; rt < DV / 16; ++rt) {
+      bf16x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = (bf16)dv[rt][j];
+      *reinterpret_cast<bf16x4*>(krow_out + voff + 16 * rt + 4 * q4) = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------ RMSNorm, RoPE, gains
+struct PrepBwdArgs {
+  const float* down; int64_t ld_down;   // [T, ...]: raw c_Q | c_KV (the forward's fp32 down-projection)
+  const float* dcqn; const float* dckvn;                // [T, q_rank], [T, kv_rank] fp32
+  const float* dkr_part; int nN;                        // [nN, T, d_rope]
+  const float* rope;                                    // [T, d_rope/2, 2]
+  const bf16* g_q; const bf16* g_kv; float eps;
+  bf16* ddown; int64_t ld_dd;   // out: [T, ld_dd]: dc_Q | dc_KV | dk_R (before RoPE) | (lambda) | zero pad
+  int pad_from;                 // first pad column (q_rank + kv_rank + d_rope + nS)
+  float* gpart;                 // out: [blocks, q_rank + kv_rank] per-block gain-gradient sums
+  int64_t T; int q_rank, kv_rank;
+};
+constexpr int PREP_TOK = 32;    // tokens per workgroup
+constexpr int PREP_MAXC = 32;   // columns per lane of each latent (q_rank, kv_rank <= 2048)
+
+// One wave per token, four waves per workgroup; the gain gradients of the
+// workgroup's tokens are summed in registers (lane l owns columns l + 64 i)
+// and written as one partial row per workgroup.
+__global__ void __launch_bounds__(256)
+prep_bwd_kernel(PrepBwdArgs a) {
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float accq[PREP_MAXC], acck[PREP_MAXC];
+#pragma unroll
+  for (int i = 0; i < PREP_MAXC; ++i) accq[i] = acck[i] = 0.f;
+  const int nq = a.q_rank / 64, nk = a.kv_rank / 64;
+  // RMSNorm backward of one latent: dc = r u - c r^3 mean(u c), u = g gamma;
+  // gain gradient g c r
+  auto rms_bwd = [&](const float* c, const float* g, const bf16* gamma, int nc, bf16* out, float (&acc)[PREP_MAXC]) {
+    float ss = 0.f, uc = 0.f;
+#pragma unroll
+    for (int i = 0; i < PREP_MAXC; ++i)
+      if (i < nc) {
+        const int col = lane + 64 * i;
+        const float cv = c[col], u = g[col] * (float)gamma[col];
+        ss += cv * cv;
+        uc += u * cv;
+      }
+    const float ncol = (float)(nc * 64);
+    const float r = 1.0f / sqrtf(wave_sum(ss) / ncol + a.eps);
+    const float m = wave_sum(uc) / ncol;
+#pragma unroll
+    for (int i = 0; i < PREP_MAXC; ++i)
+      if (i < nc) {
+        const int col = lane + 64 * i;
+        const float cv = c[col], u = g[col] * (float)gamma[col];
+        out[col] = (bf16)(r * u - cv * r * r * r * m);
+        acc[i] += g[col] * cv * r;
+      }
+  };
+  for (int k = w; k < PREP_TOK; k += 4) {
+    const int64_t t = (int64_t)blockIdx.x * PREP_TOK + k;
+    if (t >= a.T) break;
+    const float* row = a.down + t * a.ld_down;
+    bf16* out = a.ddown + t * a.ld_dd;
+    rms_bwd(row, a.dcqn + t * a.q_rank, a.g_q, nq, out, accq);
+    rms_bwd(row + a.q_rank, a.dckvn + t * a.kv_rank, a.g_kv, nk, out + a.q_rank, acck);
+    // rotary key: sum over KV groups, then the transposed rotation
+    if (lane < DR / 2) {
+      float g1 = 0.f, g2 = 0.f;
+      for (int n = 0; n < a.nN; ++n) {
+        const float* p = a.dkr_part + ((int64_t)n * a.T + t) * DR;
+        g1 += p[lane];
+        g2 += p[lane + DR / 2];
+      }
+      const float c = a.rope[(t * (DR / 2) + lane) * 2], s = a.rope[(t * (DR / 2) + lane) * 2 + 1];
+      out[a.q_rank + a.kv_rank + lane] = (bf16)(g1 * c + g2 * s);
+      out[a.q_rank + a.kv_rank + DR / 2 + lane] = (bf16)(g2 * c - g1 * s);
+    }
+    for (int col = a.pad_from + lane; col < a.ld_dd; col += 64) out[col] = (bf16)0.f;
+  }
+  // the four waves' partial gain sums, one column per lane at a time
+  float* gp = a.gpart + (int64_t)blockIdx.x * (a.q_rank + a.kv_rank);
+  auto flush = [&](float (&acc)[PREP_MAXC], int nc, int off) {
+#pragma unroll
+    for (int i = 0; i < PREP_MAXC; ++i) {
+      if (i < nc) {
+        red[w][lane] = acc[i];
+        __syncthreads();
+        if (w == 0) gp[off + lane + 64 * i] = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+        __syncthreads();
+      }
+    }
+  };
+  flush(accq, nq, 0);
+  flush(acck, nk, a.q_rank);
+}
+
+// gain gradients: column sums of the per-block partials
+__global__ void __launch_bounds__(256)
+gain_reduce_kernel(const float* gpart, int blocks, int q_rank, int kv_rank, float* dg_q, float* dg_kv) {
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  const int ncol = q_rank + kv_rank;
+  if (col >= ncol) return;
+  float s = 0.f;
+  for (int b = 0; b < blocks; ++b) s += gpart[(int64_t)b * ncol + col];
+  if (col < q_rank) dg_q[col] = s;
+  else dg_kv[col - q_rank] = s;
+}
+
+template <class K>
+hipError_t set_lds(K kernel, size_t bytes) {
+  return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int G>
+hipError_t attn_bwd_g(const AttnBwdArgs& a, hipStream_t s) {
+  constexpr size_t dq_lds = 2 * (size_t)(TR * QK_LD * 2 + TR * V_LD * 2 + DQK * T_LD * 2);
+  constexpr size_t dkv_lds = 2 * (size_t)(TR * QK_LD * 2 + TR * V_LD * 2 + DQK * T_LD * 2 + DV * T_LD * 2 + 2 * TR * 4);
+  static bool attr = false;
+  hipError_t e;
+  if (!attr) {
+    if ((e = set_lds(attn_bwd_dq_kernel<G>, dq_lds)) != hipSuccess) return e;
+    if ((e = set_lds(attn_bwd_dkv_kernel<G>, dkv_lds)) != hipSuccess) return e;
+    attr = true;
+  }
+  const int64_t gq = (int64_t)a.B * a.nN * cdiv(a.L, 32), gk = (int64_t)a.B * a.nN * cdiv(a.L, DKV_KEYS);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<G>, dim3((unsigned)gq), dim3(128 * (G + 1)), dq_lds, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dkv_kernel<G>, dim3((unsigned)gk), dim3(64 * DKV_NW), dkv_lds, s, a);
+  return hipGetLastError();
+}
+
+size_t a256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+hipError_t transpose_bf16(const void* src, int64_t ld_src, void* dst, int64_t ld_dst, int R, int C, int Rpad,
+                          hipStream_t s) {
+  if (R <= 0 && Rpad <= 0) return hipSuccess;
+  if (C <= 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv(Rpad, 64), (unsigned)cdiv(C, 64));
+  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, (const bf16*)src, ld_src, (bf16*)dst, ld_dst, R, C,
+                     Rpad);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ the backward step
+BackwardLayout backward_layout(const BwdDims& D, int64_t T) {
+  BackwardLayout P;
+  const int64_t Tp = (T + 63) / 64 * 64;
+  const int64_t nkv = D.nN * (D.dn + D.dv), nqg = D.nq + D.ngate;
+  P.Tp = Tp;
+  P.ndp = (D.ndown + 63) / 64 * 64;
+  P.prep_blocks = (T + PREP_TOK - 1) / PREP_TOK;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t r = o; o = a256(o + bytes); return r; };
+  P.down = take((size_t)T * D.ndown * 4);
+  P.cqn = take((size_t)T * D.rq * 2);
+  P.ckvn = take((size_t)T * D.rkv * 2 * 2);
+  P.kr = take((size_t)T * DR * 2);
+  P.lam = take((size_t)T * D.nS * 4);
+  P.rope = take((size_t)T * DR * 4);
+  P.q = take((size_t)T * D.nq * 2);
+  P.gate = take((size_t)T * D.ngate * 4);
+  P.kv = take((size_t)T * nkv * 2);
+  P.kvT = take((size_t)nkv * Tp * 2);
+  P.z = take((size_t)T * D.ngate * 2);
+  P.hall = take((size_t)T * D.H * DV * 2);
+  P.lse = take((size_t)T * D.H * 4);
+  P.woT = take((size_t)D.ngate * D.d * 2);
+  P.wuqgT = take((size_t)D.rq * nqg * 2);
+  P.wukvT = take((size_t)D.rkv * nkv * 2);
+  P.wdownT = take((size_t)D.d * P.ndp * 2);
+  P.dz = take((size_t)T * D.ngate * 4);
+  P.dyT = take((size_t)D.d * Tp * 2);
+  P.zT = take((size_t)D.ngate * Tp * 2);
+  P.dh = take((size_t)T * D.H * DV * 2);
+  P.dhT = take((size_t)D.H * DV * Tp * 2);
+  P.dvec = take((size_t)T * D.H * 4);
+  P.qT = take((size_t)D.nq * Tp * 2);
+  P.krT = take((size_t)DR * Tp * 2);
+  P.dqg = take((size_t)T * nqg * 2);
+  P.dkv = take((size_t)T * nkv * 2);
+  P.dkrp = take((size_t)D.nN * T * DR * 4);
+  P.dcqn = take((size_t)T * D.rq * 4);
+  P.dckvn = take((size_t)T * D.rkv * 4);
+  P.dqgT = take((size_t)nqg * Tp * 2);
+  P.cqnT = take((size_t)D.rq * Tp * 2);
+  P.dkvT = take((size_t)nkv * Tp * 2);
+  P.ckvnT = take((size_t)D.rkv * Tp * 2);
+  P.ddown = take((size_t)T * P.ndp * 2);
+  P.ddownT = take((size_t)P.ndp * Tp * 2);
+  P.xT = take((size_t)D.d * Tp * 2);
+  P.gpart = take((size_t)P.prep_blocks * (D.rq + D.rkv) * 4);
+  P.total = o;
+  return P;
+}
+
+hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCall& c, hipStream_t s) {
+  char* ws = (char*)c.workspace;
+  const int64_t T = c.T, Tp = P.Tp;
+  const int64_t nkv = D.nN * (D.dn + D.dv), nqg = D.nq + D.ngate;
+  const int rq = (int)D.rq, rkv = (int)D.rkv, d = (int)D.d, nS = (int)D.nS;
+  hipError_t e;
+  // 1. recompute the forward: down-projection, row prep, expansion (token-major
+  //    and transposed), query/gate, attention with per-head outputs
+  {
+    GemmArgs g{};
+    g.A = c.x; g.lda = d;
+    g.B = c.w->w_dq; g.ldb = d;
+    g.B2 = c.w->w_dkv; g.nb2 = rq;
+    g.B3 = c.w->w_lambda; g.nb3 = rq + rkv + DR;
+    g.C = ws + P.down; g.ldc = D.ndown;
+    g.M = (int)T; g.N = (int)D.ndown; g.K = d; g.batch = 1; g.epi = EPI_F32;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+  }
+  {
+    RowPrepArgs r{};
+    r.down = (const float*)(ws + P.down); r.ld_down = D.ndown;
+    r.T = T; r.L = c.L; r.pos_offset = c.pos_offset;
+    r.q_rank = rq; r.kv_rank = rkv; r.d_rope = DR; r.nS = nS;
+    r.g_q = c.w->g_q; r.g_kv = c.w->g_kv; r.eps = c.cfg->rms_eps;
+    set_rope(r, c.cfg->rope_base, c.cfg->window, c.cfg->yarn_factor, c.cfg->yarn_orig_len, c.cfg->yarn_beta_fast,
+             c.cfg->yarn_beta_slow);
+    r.cqn = ws + P.cqn; r.ckvn = ws + P.ckvn; r.kr = ws + P.kr; r.lam = (float*)(ws + P.lam);
+    r.rope = (float*)(ws + P.rope); r.split_kv = true;
+    if ((e = rowprep(r, true, s)) != hipSuccess) return e;
+  }
+  {
+    GemmArgs g{};   // [K^C | V] token-major
+    g.A = ws + P.ckvn; g.lda = 2 * rkv;
+    g.B = c.w->w_ukv; g.ldb = rkv; g.kwrapB = rkv;
+    g.C = ws + P.kv; g.ldc = nkv;
+    g.M = (int)T; g.N = (int)nkv; g.K = 2 * rkv; g.batch = 1; g.epi = EPI_STORE;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    GemmArgs v{};   // [K^C | V]^T, columns padded to Tp with zeros
+    v.A = c.w->w_ukv; v.lda = rkv; v.kwrapA = rkv;
+    v.B = ws + P.ckvn; v.ldb = 2 * rkv;
+    v.C = ws + P.kvT; v.ldc = Tp;
+    v.M = (int)nkv; v.N = (int)T; v.K = 2 * rkv; v.batch = 1; v.epi = EPI_STORE; v.Npad = (int)Tp;
+    if ((e = gemm_bf16(v, s)) != hipSuccess) return e;
+  }
+  {
+    GemmArgs g{};
+    g.A = ws + P.cqn; g.lda = rq;
+    g.B = c.w->w_uq; g.ldb = rq;
+    g.B2 = c.w->w_gate; g.nb2 = (int)D.nq;
+    g.C = ws + P.q; g.ldc = D.nq;
+    g.G = (float*)(ws + P.gate); g.ldg = D.ngate;
+    g.M = (int)T; g.N = (int)(D.nq + D.ngate); g.K = rq; g.batch = 1; g.epi = EPI_QG;
+    g.rope = (const float*)(ws + P.rope); g.q_cols = (int)D.nq;
+    g.d_qk = DQK; g.d_nope = DN; g.d_rope = DR;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+  }
+  {
+    AttnArgs a{};
+    a.q = ws + P.q; a.ld_q = D.nq;
+    a.gate = (const float*)(ws + P.gate); a.ld_gate = D.ngate;
+    a.kc = ws + P.kv; a.ld_kc = nkv;
+    a.kr = ws + P.kr;
+    a.vt = ws + P.kvT + (size_t)D.nN * DN * Tp * 2; a.ld_vt = Tp;
+    a.lam = (const float*)(ws + P.lam);
+    a.z = ws + P.z;
+    a.T = T; a.B = c.B; a.L = c.L;
+    a.nN = (int)D.nN; a.g = (int)D.g; a.window = c.cfg->window;
+    a.d_nope = DN; a.d_rope = DR; a.d_v = DV;
+    a.scale = (float)(1.0 / std::sqrt((double)DQK));
+    a.h_out = ws + P.hall; a.lse_out = (float*)(ws + P.lse);
+    if ((e = attn_bf16(a, s)) != hipSuccess) return e;
+  }
+  // 2. transposed weights: W_O^T, [W_UQ; W_G]^T, W_UKV^T, [W_DQ; W_DKV; W_lambda]^T (zero-padded)
+  if ((e = transpose_bf16(c.w->w_o, D.ngate, ws + P.woT, d, d, (int)D.ngate, d, s)) != hipSuccess) return e;
+  if ((e = transpose_bf16(c.w->w_uq, rq, ws + P.wuqgT, nqg, (int)D.nq, rq, (int)D.nq, s)) != hipSuccess) return e;
+  if ((e = transpose_bf16(c.w->w_gate, rq, ws + P.wuqgT + D.nq * 2, nqg, (int)D.ngate, rq, (int)D.ngate, s)) !=
+      hipSuccess)
+    return e;
+  if ((e = transpose_bf16(c.w->w_ukv, rkv, ws + P.wukvT, nkv, (int)nkv, rkv, (int)nkv, s)) != hipSuccess) return e;
+  if ((e = transpose_bf16(c.w->w_dq, d, ws + P.wdownT, P.ndp, rq, d, rq, s)) != hipSuccess) return e;
+  if ((e = transpose_bf16(c.w->w_dkv, d, ws + P.wdownT + (size_t)rq * 2, P.ndp, rkv + DR, d, rkv + DR, s)) !=
+      hipSuccess)
+    return e;
+  if ((e = transpose_bf16(c.w->w_lambda, d, ws + P.wdownT + (size_t)(rq + rkv + DR) * 2, P.ndp, nS, d,
+                          (int)(P.ndp - (rq + rkv + DR)), s)) != hipSuccess)
+    return e;
+  // 3. output projection: dZ = dy W_O (fp32), dW_O = dy^T Z
+  {
+    GemmArgs g{};
+    g.A = c.dy; g.lda = d;
+    g.B = ws + P.woT; g.ldb = d;
+    g.C = ws + P.dz; g.ldc = D.ngate;
+    g.M = (int)T; g.N = (int)D.ngate; g.K = d; g.batch = 1; g.epi = EPI_F32;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+  }
+  if ((e = transpose_bf16(c.dy, d, ws + P.dyT, Tp, (int)T, d, (int)Tp, s)) != hipSuccess) return e;
+  if ((e = transpose_bf16(ws + P.z, D.ngate, ws + P.zT, Tp, (int)T, (int)D.ngate, (int)Tp, s)) != hipSuccess) return e;
+  {
+    GemmArgs g{};
+    g.A = ws + P.dyT; g.lda = Tp;
+    g.B = ws + P.zT; g.ldb = Tp;
+    g.C = c.grads->w_o; g.ldc = D.ngate;
+    g.M = d; g.N = (int)D.ngate; g.K = (int)Tp; g.batch = 1; g.epi = EPI_F32;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+  }
+  // 4. gate and differential
+  {
+    EpiBwdArgs k{(const float*)(ws + P.dz), (const float*)(ws + P.gate), (const bf16*)(ws + P.hall),
+                 (const float*)(ws + P.lam), (bf16*)(ws + P.dqg) + D.nq, nqg, (bf16*)(ws + P.dh),
+                 (float*)(ws + P.dvec), (bf16*)(ws + P.ddown) + rq + rkv + DR, P.ndp, T, (int)D.nN, (int)D.g};
+    hipLaunchKernelGGL(epi_bwd_kernel, dim3((unsigned)cdiv(T, 4)), dim3(256), 0, s, k);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // 5. attention backward (transposed Q, dH and k_R staged first)
+  if ((e = transpose_bf16(ws + P.q, D.nq, ws + P.qT, Tp, (int)T, (int)D.nq, (int)Tp, s)) != hipSuccess) return e;
+  if ((e = transpose_bf16(ws + P.dh, D.H * DV, ws + P.dhT, Tp, (int)T, (int)(D.H * DV), (int)Tp, s)) != hipSuccess)
+    return e;
+  if ((e = transpose_bf16(ws + P.kr, DR, ws + P.krT, Tp, (int)T, DR, (int)Tp, s)) != hipSuccess) return e;
+  {
+    AttnBwdArgs a{};
+    a.q = (const bf16*)(ws + P.q); a.ld_q = D.nq;
+    a.kv = (const bf16*)(ws + P.kv); a.ld_kv = nkv;
+    a.kr = (const bf16*)(ws + P.kr);
+    a.kvT = (const bf16*)(ws + P.kvT); a.krT = (const bf16*)(ws + P.krT); a.qT = (const bf16*)(ws + P.qT);
+    a.dhT = (const bf16*)(ws + P.dhT); a.ld_t = Tp;
+    a.dh = (const bf16*)(ws + P.dh);
+    a.lse = (const float*)(ws + P.lse); a.dvec = (const float*)(ws + P.dvec);
+    a.rope = (const float*)(ws + P.rope);
+    a.dq = (bf16*)(ws + P.dqg); a.ld_dq = nqg;
+    a.dkv = (bf16*)(ws + P.dkv);
+    a.dkr_part = (float*)(ws + P.dkrp);
+    a.T = T; a.B = c.B; a.L = c.L; a.nN = (int)D.nN; a.window = c.cfg->window;
+    a.scale = (float)(1.0 / std::sqrt((double)DQK));
+    a.sc = (float)(1.4426950408889634 / std::sqrt((double)DQK));
+    switch (D.g) {
+      case 1: e = attn_bwd_g<1>(a, s); break;
+      case 2: e = attn_bwd_g<2>(a, s); break;
+      case 3: e = attn_bwd_g<3>(a, s); break;
+      case 4: e = attn_bwd_g<4>(a, s); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+  }
+  // 6. query side: dc_Qn = [dQ | dG_logit] [W_UQ; W_G]; dW_UQ, dW_G = [dQ | dG]^T c_Qn
+  {
+    GemmArgs g{};
+    g.A = ws + P.dqg; g.lda = nqg;
+    g.B = ws + P.wuqgT; g.ldb = nqg;
+    g.C = ws + P.dcqn; g.ldc = rq;
+    g.M = (int)T; g.N = rq; g.K = (int)nqg; g.batch = 1; g.epi = EPI_F32;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+  }
+  if ((e = transpose_bf16(ws + P.dqg, nqg, ws + P.dqgT, Tp, (int)T, (int)nqg, (int)Tp, s)) != hipSuccess) return e;
+  if ((e = transpose_bf16(ws + P.cqn, rq, ws + P.cqnT, Tp, (int)T, rq, (int)Tp, s)) != hipSuccess) return e;
+  {
+    GemmArgs g{};
+    g.A = ws + P.dqgT; g.lda = Tp;
+    g.B = ws + P.cqnT; g.ldb = Tp;
+    g.C = c.grads->w_uq; g.ldc = rq;
+    g.M = (int)D.nq; g.N = rq; g.K = (int)Tp; g.batch = 1; g.epi = EPI_F32;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    g.A = ws + P.dqgT + (size_t)D.nq * Tp * 2;
+    g.C = c.grads->w_gate; g.M = (int)D.ngate;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+  }
+  // 7. KV side: dc_KVn = [dK^C | dV] W_UKV; dW_UKV = [dK^C | dV]^T c_KVn
+  {
+    GemmArgs g{};
+    g.A = ws + P.dkv; g.lda = nkv;
+    g.B = ws + P.wukvT; g.ldb = nkv;
+    g.C = ws + P.dckvn; g.ldc = rkv;
+    g.M = (int)T; g.N = rkv; g.K = (int)nkv; g.batch = 1; g.epi = EPI_F32;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+  }
+  if ((e = transpose_bf16(ws + P.dkv, nkv, ws + P.dkvT, Tp, (int)T, (int)nkv, (int)Tp, s)) != hipSuccess) return e;
+  if ((e = transpose_bf16(ws + P.ckvn, 2 * rkv, ws + P.ckvnT, Tp, (int)T, rkv, (int)Tp, s)) != hipSuccess) return e;
+  {
+    GemmArgs g{};
+    g.A = ws + P.dkvT; g.lda = Tp;
+    g.B = ws + P.ckvnT; g.ldb = Tp;
+    g.C = c.grads->w_ukv; g.ldc = rkv;
+    g.M = (int)nkv; g.N = rkv; g.K = (int)Tp; g.batch = 1; g.epi = EPI_F32;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+  }
+  // 8. RMSNorms, the rotary key's RoPE, gains
+  {
+    PrepBwdArgs k{};
+    k.down = (const float*)(ws + P.down); k.ld_down = D.ndown;
+    k.dcqn = (const float*)(ws + P.dcqn); k.dckvn = (const float*)(ws + P.dckvn);
+    k.dkr_part = (const float*)(ws + P.dkrp); k.nN = (int)D.nN;
+    k.rope = (const float*)(ws + P.rope);
+    k.g_q = (const bf16*)c.w->g_q; k.g_kv = (const bf16*)c.w->g_kv; k.eps = c.cfg->rms_eps;
+    k.ddown = (bf16*)(ws + P.ddown); k.ld_dd = P.ndp; k.pad_from = (int)D.ndown;
+    k.gpart = (float*)(ws + P.gpart);
+    k.T = T; k.q_rank = rq; k.kv_rank = rkv;
+    hipLaunchKernelGGL(prep_bwd_kernel, dim3((unsigned)P.prep_blocks), dim3(256), 0, s, k);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(gain_reduce_kernel, dim3((unsigned)cdiv(rq + rkv, 256)), dim3(256), 0, s,
+                       (const float*)(ws + P.gpart), (int)P.prep_blocks, rq, rkv, c.grads->g_q, c.grads->g_kv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // 9. down-projections: dx = d[c_Q | c_KV k_R | lambda] [W_DQ; W_DKV; W_lambda];
+  //    their weight gradients d^T x
+  {
+    GemmArgs g{};
+    g.A = ws + P.ddown; g.lda = P.ndp;
+    g.B = ws + P.wdownT; g.ldb = P.ndp;
+    g.C = c.dx; g.ldc = d;
+    g.M = (int)T; g.N = d; g.K = (int)P.ndp; g.batch = 1; g.epi = EPI_STORE;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+  }
+  if ((e = transpose_bf16(ws + P.ddown, P.ndp, ws + P.ddownT, Tp, (int)T, (int)P.ndp, (int)Tp, s)) != hipSuccess)
+    return e;
+  if ((e = transpose_bf16(c.x, d, ws + P.xT, Tp, (int)T, d, (int)Tp, s)) != hipSuccess) return e;
+  {
+    GemmArgs g{};
+    g.A = ws + P.ddownT; g.lda = Tp;
+    g.B = ws + P.xT; g.ldb = Tp;
+    g.C = c.grads->w_dq; g.ldc = d;
+    g.M = rq; g.N = d; g.K = (int)Tp; g.batch = 1; g.epi = EPI_F32;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    g.A = ws + P.ddownT + (size_t)rq * Tp * 2; g.C = c.grads->w_dkv; g.M = rkv + DR;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    g.A = ws + P.ddownT + (size_t)(rq + rkv + DR) * Tp * 2; g.C = c.grads->w_lambda; g.M = nS;
+    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace gdla

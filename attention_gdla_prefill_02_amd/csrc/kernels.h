@@ -120,6 +120,9 @@ struct AttnArgs {
   int nN, g, window;
   int d_nope, d_rope, d_v;
   float scale;                                        // 1/sqrt(d_nope + d_rope)
+  // training forward (bf16, nullable): per-head outputs H [T, H, d_v] bf16 and
+  // the exp2-domain log-sum-exp of each (row, head) [T, H] fp32
+  void* h_out; float* lse_out;
 };
 hipError_t attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t attn_f32(const AttnArgs& a, hipStream_t s);

@@ -22,7 +22,7 @@ STAGE_DOWN, STAGE_PREP, STAGE_EXPAND, STAGE_QG, STAGE_ATTN, STAGE_OUT, STAGE_ALL
 EXPORTED = ("gdla_prefill_workspace_size", "gdla_prefill", "gdla_prefill_stages", "gdla_prefill_workspace_layout",
             "gdla_decode_workspace_size", "gdla_decode", "gdla_latent_expand", "gdla_status_string",
             "gdla_last_error", "gdla_version", "gdla_prefill_packed_workspace_size", "gdla_prefill_packed",
-            "gdla_decode_paged")
+            "gdla_decode_paged", "gdla_backward_workspace_size", "gdla_backward")
 
 
 class GdlaError(RuntimeError):
@@ -50,6 +50,10 @@ class Weights(ctypes.Structure):
 
 class PrefillLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("down", "cqn", "ckvn", "kr", "lam", "rope", "q", "gate", "kc", "vt", "z")]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
 
 
 class PagedCache(ctypes.Structure):
@@ -90,6 +94,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdla_prefill_packed.restype = ctypes.c_int
     lib.gdla_decode_paged.argtypes = [cfgp, wp, i32, vp, vp, pcp, vp, vp, sz, vp]
     lib.gdla_decode_paged.restype = ctypes.c_int
+    lib.gdla_backward_workspace_size.argtypes = [cfgp, i32, i32]
+    lib.gdla_backward_workspace_size.restype = sz
+    lib.gdla_backward.argtypes = [cfgp, wp, i32, i32, i64, vp, vp, vp, ctypes.POINTER(Grads), vp, sz, vp]
+    lib.gdla_backward.restype = ctypes.c_int
     lib.gdla_latent_expand.argtypes = [cfgp, i64, vp, i64, vp, vp, vp, vp, vp, vp]
     lib.gdla_latent_expand.restype = ctypes.c_int
     lib.gdla_status_string.argtypes = [ctypes.c_int]
@@ -226,6 +234,27 @@ def decode_paged(cfg: Config, W: dict, x: torch.Tensor, pages: torch.Tensor, blo
                                     ctypes.byref(pc), _ptr(cache_lens), _ptr(workspace), workspace.numel(),
                                     _stream(stream)))
     return y
+
+
+def backward_workspace_size(cfg: Config, B: int, L: int) -> int:
+    return int(load().gdla_backward_workspace_size(ctypes.byref(cfg), B, L))
+
+
+def backward(cfg: Config, W: dict, x: torch.Tensor, dy: torch.Tensor, *, pos_offset=0, dx=None, grads=None,
+             workspace=None, stream=None, wstruct=None):
+    """Backward of one layer: returns (dx [B, L, d_model], dict of fp32 weight gradients)."""
+    B, L, _ = x.shape
+    if dx is None:
+        dx = torch.empty_like(x)
+    if grads is None:
+        grads = {n: torch.empty(W[n].shape, dtype=torch.float32, device=x.device) for n in WEIGHT_FIELDS}
+    if workspace is None:
+        workspace = alloc_workspace(backward_workspace_size(cfg, B, L), x.device)
+    gs = Grads(*[grads[n].data_ptr() for n in WEIGHT_FIELDS])
+    ws = wstruct if wstruct is not None else weights_struct(W)
+    _check(load().gdla_backward(ctypes.byref(cfg), ctypes.byref(ws), B, L, int(pos_offset), _ptr(x), _ptr(dy),
+                                _ptr(dx), ctypes.byref(gs), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dx, grads
 
 
 def latent_expand(cfg: Config, c_kv: torch.Tensor, g_kv: torch.Tensor, w_ukv: torch.Tensor, stream=None):

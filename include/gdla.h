@@ -282,6 +282,34 @@ gdla_status gdla_decode_paged(const gdla_config* cfg, const gdla_weights* w, int
                               void* y, const gdla_paged_cache* cache, const int32_t* cache_lens,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Weight gradients of one layer: fp32 device buffers with the shapes of the
+ * matching gdla_weights fields (gains [q_rank] and [kv_rank]), overwritten. */
+typedef struct {
+  float* w_dq; float* g_q; float* w_dkv; float* g_kv; float* w_lambda;
+  float* w_uq; float* w_ukv; float* w_gate; float* w_o;
+} gdla_grads;
+
+/* Bytes of workspace gdla_backward needs for B sequences of L tokens (0 if
+ * the configuration or sizes are not supported). */
+size_t gdla_backward_workspace_size(const gdla_config* cfg, int32_t B, int32_t L);
+
+/* Backward of one GDLA layer (gdla_prefill's layer, without residual): given
+ * its input x and the gradient dy of its output, the gradient dx and every
+ * weight gradient.  The forward's activations are recomputed from x inside
+ * the call (report, training-infrastructure paragraph: activations are
+ * recomputed for the backward pass), so the caller keeps only x.
+ *   x, dy      [B, L, d_model], config dtype
+ *   dx         [B, L, d_model] out, config dtype; must not alias x or dy
+ *   grads      every pointer non-NULL, fp32, overwritten (not accumulated)
+ *   workspace  at least gdla_backward_workspace_size bytes, 256-byte aligned
+ * bf16 only (GDLA_ERR_UNSUPPORTED otherwise); the bf16 shape limits of
+ * gdla_prefill, q_rank + kv_rank <= 2048, B*L <= 2^22 and positions below
+ * 2^30.  All pointers 16-byte aligned. */
+gdla_status gdla_backward(const gdla_config* cfg, const gdla_weights* w, int32_t B, int32_t L,
+                          int64_t pos_offset, const void* x, const void* dy, void* dx,
+                          const gdla_grads* grads, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Latent expansion alone (report, GDLA summary and definition paragraphs):
  * c_KVn = RMSNorm(c_KV) * g_kv, [K^C | V] = c_KVn W_UKV^T.
  *   c_kv    [T, ld_c] raw latent (first kv_rank columns used), ld_c >= kv_rank

@@ -1,0 +1,69 @@
+"""Backward parity: the HIP layer backward (forward recomputed from x) through
+the C ABI against the oracle's fp64 gradients on the same bits, for dx and
+every weight gradient, over several query and key tiles with ragged tails,
+full and windowed masks, position offsets, YaRN, and the report's g = 4
+shapes.  Tolerance: the bf16 path rounds dZ-derived products, dH, dS and the
+transposed operands to bf16 before each MFMA; each rounding adds ~2e-3 of
+relative error, so gradient tensors are held to rel-L2 <= 1.5e-2 and max-abs
+<= 3e-2 of the tensor's largest magnitude (floored at 1e-3, for gradients
+that are exactly zero in the reference, such as dQ with a window of 1)."""
+
+import numpy as np
+import pytest
+import torch
+
+from attention_gdla_prefill_02_amd import configs, gdla, inputs
+from oracle import gdla_ref as R
+from tests.helpers import SMALL, errors, host64, make_layer, oracle_cfg
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = dict(rel_l2=1.5e-2, max_rel=3e-2)
+
+
+def check(got, ref, what):
+    ma, rl = errors(got, ref)
+    scale = max(float(np.max(np.abs(ref))) if ref.size else 1.0, 1e-3)   # floor: exactly-zero references
+    print(f"[grad] {what}: rel_l2={rl:.3e} max_abs={ma:.3e} (|ref| max {scale:.3e})", flush=True)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    assert rl <= GRAD_TOL["rel_l2"], f"{what}: rel_l2 {rl:.3e}"
+    assert ma <= GRAD_TOL["max_rel"] * scale, f"{what}: max_abs {ma:.3e} > {GRAD_TOL['max_rel']} x {scale:.3e}"
+
+
+def run(shapes, B, L, window, seed, pos_offset=0, yarn=None):
+    print(f"[case] backward shapes={shapes['d_model']}/{shapes['group']} B={B} L={L} W={window} "
+          f"pos={pos_offset} yarn={yarn}", flush=True)
+    Wd, W64 = make_layer(shapes, seed, "bf16", gamma="random")
+    xc = inputs.make_x(B, L, shapes["d_model"], seed, "bf16")
+    dyc = inputs.make_x(B, L, shapes["d_model"], seed + 1000, "bf16")
+    cfg = gdla.make_config(shapes, window, "bf16", yarn=yarn)
+    dx, grads = gdla.backward(cfg, Wd, xc.to("cuda"), dyc.to("cuda"), pos_offset=pos_offset)
+    torch.cuda.synchronize()
+    ocfg = oracle_cfg(shapes, window)
+    if yarn:
+        from dataclasses import replace
+        ocfg = replace(ocfg, yarn_factor=yarn[0], yarn_orig_len=yarn[1], yarn_beta_fast=yarn[2],
+                       yarn_beta_slow=yarn[3])
+    ref = R.gdla_layer_backward(inputs.widen(xc), W64, ocfg, inputs.widen(dyc), pos_offset=pos_offset)
+    check(host64(dx), ref["dx"], "dx")
+    for n in inputs.WEIGHT_NAMES:
+        check(host64(grads[n]), ref[n], n)
+
+
+@pytest.mark.parametrize("B,L,window", [(1, 64, 0), (2, 100, 0), (1, 300, 0), (2, 150, 40), (1, 257, 1)])
+def test_backward_small(B, L, window):
+    run(SMALL, B, L, window, seed=81 + L)
+
+
+def test_backward_position_offset_and_yarn():
+    run(SMALL, 2, 130, 0, seed=82, pos_offset=70000, yarn=(64.0, 4096, 32.0, 1.0))
+
+
+@pytest.mark.parametrize("window", [0, 64])
+def test_backward_report_shapes_g4(window):
+    s = dict(configs.REPORT_SHAPES, d_model=512, q_rank=256)
+    run(s, 1, 160, window, seed=83)
+
+
+def test_backward_motif_shapes():
+    run(configs.MOTIF_SHAPES, 1, 200, 0, seed=84)
