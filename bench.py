@@ -15,8 +15,9 @@ timed with HIP events on its stream inside the timed steps), the decode
 throughput of a batch-64 step against the compressed latent cache (full and
 W = 4096 layers), the same prefill block and decode at the report's own layer
 shapes (group size 4, query rank 1024, W = 128), the block over a packed stream
-of complete sequences of mixed lengths and decode against a paged cache, and
-the fp64 CPU oracle timed on a bounded sample of the headline workload.
+of complete sequences of mixed lengths and decode against a paged cache, the
+block's backward (forward recomputed per layer), and the fp64 CPU oracle
+timed on a bounded sample of the headline workload.
 """
 
 from __future__ import annotations
@@ -242,6 +243,63 @@ def bench_packed(args, torch, gdla, configs, inputs, name="packed_hybrid_l32k", 
     return out
 
 
+def bench_backward(args, torch, gdla, configs, inputs, name="hybrid_l32k", steps=3, warmup=1):
+    """Backward of the hybrid block (each layer's gdla_backward recomputes its
+    forward from the layer input), timed per layer with HIP events on the
+    library's stream.  Algorithmic work: the recomputed forward (projections
+    and 640 FLOP per attended pair) plus the backward (2 x the projection
+    FLOPs, 1664 FLOP per attended pair: S, dP, dV, dK, dQ)."""
+    w = configs.WORKLOADS[name]
+    s = w.shapes
+    B, L = w.B, w.L
+    log(f"[bench] building backward inputs: {w.note}")
+    Wd = [{k: v.to("cuda") for k, v in inputs.make_weights(s, configs.layer_seed(w, l), "bf16").items()}
+          for l in range(len(w.windows))]
+    wstructs = [gdla.weights_struct(W) for W in Wd]
+    cfgs = [gdla.make_config(s, win, "bf16") for win in w.windows]
+    x = inputs.make_x(B, L, s["d_model"], w.seed, "bf16").to("cuda")
+    dy = inputs.make_x(B, L, s["d_model"], w.seed + 1000, "bf16").to("cuda")
+    dx = torch.empty_like(x)
+    grads = {n: torch.empty(Wd[0][n].shape, dtype=torch.float32, device="cuda") for n in gdla.WEIGHT_FIELDS}
+    ws = gdla.alloc_workspace(max(gdla.backward_workspace_size(c, B, L) for c in cfgs))
+    stream = torch.cuda.current_stream()
+    n_layers = len(w.windows)
+
+    def step(ev):
+        for l in range(n_layers):
+            if ev is not None:
+                ev[l][0].record(stream)
+            gdla.backward(cfgs[l], None, x, dy, dx=dx, grads=grads, workspace=ws, wstruct=wstructs[l])
+            if ev is not None:
+                ev[l][1].record(stream)
+
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_layers)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    layer_ms = [sum(evs[k][l][0].elapsed_time(evs[k][l][1]) for k in range(steps)) / steps for l in range(n_layers)]
+    proj = proj_flop_per_token(s) * B * L
+    pairs = [B * attended_pairs(L, win) for win in w.windows]
+    hs = s["n_noise"] * (s["group"] + 1)
+    # per head: S, dK, dQ (2 d_qk each) and dP, dV (2 d_v each)
+    fwd_pair, bwd_pair = attn_flop_per_pair(s), hs * (6 * (s["d_nope"] + s["d_rope"]) + 4 * s["d_v"])
+    total = sum(3 * proj + (fwd_pair + bwd_pair) * p for p in pairs)
+    out = {"workload": f"{name}: backward of every layer of the block, forward recomputed inside each call",
+           "ms_per_step": round(wall * 1e3, 3), "layer_ms": [round(v, 3) for v in layer_ms],
+           "algorithmic_tflop_per_step": round(total / 1e12, 3),
+           "tflops": round(total / wall / 1e12, 2), "frac_of_peak": round(total / wall / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "flop_per_pair": {"recomputed_forward": fwd_pair, "backward": bwd_pair},
+           "finite": bool(torch.isfinite(dx).all().item()) and all(bool(torch.isfinite(g).all().item())
+                                                                   for g in grads.values())}
+    log(f"[bench] backward: {out}")
+    return out
+
+
 def decode_bytes(s: dict, lens, window: int) -> int:
     """Algorithmic HBM bytes of one decode step: attended cache rows, every
     weight once, the appended rows, x and y."""
@@ -332,6 +390,8 @@ def main():
     ap.add_argument("--no-report-shapes", action="store_true", help="skip the report-shape (g=4, W=128) workloads")
     ap.add_argument("--decode-only", action="store_true", help="time only the decode steps (for profiling)")
     ap.add_argument("--no-packed", action="store_true", help="skip the packed-stream and paged-cache workloads")
+    ap.add_argument("--no-backward", action="store_true", help="skip the layer backward")
+    ap.add_argument("--backward-only", action="store_true", help="time only the block backward (for profiling)")
     ap.add_argument("--packed-only", action="store_true", help="time only the packed-stream block (for profiling)")
     ap.add_argument("--paged-only", action="store_true", help="time only the paged-cache decode (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -368,6 +428,9 @@ def main():
     if args.decode_only:
         print(json.dumps({"decode": bench_decode(torch, gdla, configs, inputs)}), flush=True)
         return
+    if args.backward_only:
+        print(json.dumps({"backward": bench_backward(args, torch, gdla, configs, inputs)}), flush=True)
+        return
     if args.packed_only:
         print(json.dumps({"packed": bench_packed(args, torch, gdla, configs, inputs)}), flush=True)
         return
@@ -400,6 +463,8 @@ def main():
         packed = {"prefill": bench_packed(args, torch, gdla, configs, inputs),
                   "paged_decode": None if args.no_decode else bench_decode(
                       torch, gdla, configs, inputs, reps=10, name="paged_decode_b64", fixed_ctx=False, paged=True)}
+
+    backward = None if args.no_backward else bench_backward(args, torch, gdla, configs, inputs)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -435,6 +500,7 @@ def main():
         "decode": decode,
         "report_shapes": report,
         "packed_and_paged": packed,
+        "backward": backward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -563,23 +563,25 @@ def rope_backward(g, pos, base, yarn=None):
     return np.concatenate([g1 * cos + g2 * sin, g2 * cos - g1 * sin], axis=-1)
 
 
-def attention_heads_backward(q, kc, kr, v, dH, cfg: Cfg):
-    """Gradients of attention_heads over all rows 0..L-1 for upstream dH
-    [L, H, d_v]: per head, P = softmax(S) with S = q k^T / sqrt(d_qk) masked,
-    O = P v; dv += P^T dO, dP = dO v^T, dS = P (dP - rowsum(dP P)),
-    dq = dS k / sqrt(d_qk), dk += dS^T q / sqrt(d_qk).  k = [k^C_n | k_R]: the
-    content part of dk goes to KV head n, the rotary part (one k_R per token)
-    collects every head.  Returns dq [L, H, d_qk], dkc [L, nN, d_nope],
-    dkr [L, d_rope], dv [L, nN, d_v]."""
-    L = q.shape[0]
+def attention_heads_backward(q, kc, kr, v, dH, cfg: Cfg, rows=None):
+    """Gradients of attention_heads for upstream dH [R, H, d_v] on the query
+    rows `rows` (default: every row 0..L-1; q holds those rows' queries):
+    per head, P = softmax(S) with S = q k^T / sqrt(d_qk) masked, O = P v;
+    dv += P^T dO, dP = dO v^T, dS = P (dP - rowsum(dP P)), dq = dS k / sqrt(d_qk),
+    dk += dS^T q / sqrt(d_qk).  k = [k^C_n | k_R]: the content part of dk goes
+    to KV head n, the rotary part (one k_R per token) collects every head.
+    Rows outside `rows` have zero upstream gradient.  Returns dq [R, H, d_qk],
+    dkc [L, nN, d_nope], dkr [L, d_rope], dv [L, nN, d_v]."""
+    L = kc.shape[0]
+    R = np.arange(L) if rows is None else np.asarray(rows)
     scale = 1.0 / math.sqrt(cfg.d_qk)
     dq = np.zeros_like(_f64(q))
     dkc = np.zeros((L, cfg.n_noise, cfg.d_nope))
     dkr = np.zeros((L, cfg.d_rope))
     dv = np.zeros((L, cfg.n_noise, cfg.d_v))
     t = np.arange(L)
-    lo = np.array([attended_keys(i, cfg.window)[0] for i in range(L)])
-    allowed = (t[None, :] <= t[:, None]) & (t[None, :] >= lo[:, None])
+    lo = np.array([attended_keys(int(i), cfg.window)[0] for i in R])
+    allowed = (t[None, :] <= R[:, None]) & (t[None, :] >= lo[:, None])
     for h in range(cfg.n_heads):
         n = kv_head_of(h, cfg)
         k = np.concatenate([kc[:, n, :], kr], axis=-1)
@@ -598,54 +600,61 @@ def attention_heads_backward(q, kc, kr, v, dH, cfg: Cfg):
     return dq, dkc, dkr, dv
 
 
-def gdla_layer_backward(x, W, cfg: Cfg, dy, pos_offset=0):
+def gdla_layer_backward(x, W, cfg: Cfg, dy, pos_offset=0, rows=None):
     """Gradients of one GDLA layer's output y (gdla_layer) with respect to its
-    input and every weight, for upstream dy [B, L, d_model].  The forward's
+    input and every weight, for upstream dy [B, L, d_model] -- or, with
+    `rows` (a sorted list of positions, the same for every sequence), dy
+    [B, R, d_model] on those rows and zero elsewhere.  The forward's
     activations are recomputed from x, then the steps are differentiated in
     reverse: output projection, gate and differential, attention, query
     up-projection with RoPE, latent expansion, the two RMSNorms, RoPE of the
-    rotary key, and the fused down-projection.  Returns dict dx [B, L, d_model]
+    rotary key, and the fused down-projection.  The query path is evaluated
+    only on the rows with a gradient (every other row's query-side gradient is
+    zero); the key/value path on every row.  Returns dict dx [B, L, d_model]
     and one entry per weight name (same shapes as the weights)."""
     x, dy = _f64(x), _f64(dy)
     B, L, _ = x.shape
+    R = list(range(L)) if rows is None else sorted(int(r) for r in rows)
+    nR = len(R)
     nS, nN, g = cfg.n_signal, cfg.n_noise, cfg.group
     grads = {k: np.zeros_like(_f64(v)) for k, v in W.items()}
     dx = np.zeros_like(x)
     base, yarn = rope_params(cfg)
     for b in range(B):
         xb, dyb = x[b], dy[b]
+        xr = xb[R]
         pos = pos_offset + np.arange(L, dtype=np.float64)
-        # recompute the forward
+        # recompute the forward: keys and values on every row, queries on rows R
         ckv_kr = linear(xb, W["w_dkv"])
         c_kv, kr_raw = ckv_kr[:, :cfg.kv_rank], ckv_kr[:, cfg.kv_rank:]
         ckvn = rms_norm(c_kv, W["g_kv"], cfg.rms_eps)
         kr = rope(kr_raw, pos, base, yarn)
         kc, v, _ = latent_expand_from_norm(ckvn, W["w_ukv"], cfg)
-        cq = linear(xb, W["w_dq"])
+        cq = linear(xr, W["w_dq"])
         cqn = rms_norm(cq, W["g_q"], cfg.rms_eps)
-        qf = linear(cqn, W["w_uq"]).reshape(L, cfg.n_heads, cfg.d_qk)
-        q_rot = rope(np.transpose(qf[:, :, cfg.d_nope:], (1, 0, 2)), pos, base, yarn)
+        qf = linear(cqn, W["w_uq"]).reshape(nR, cfg.n_heads, cfg.d_qk)
+        q_rot = rope(np.transpose(qf[:, :, cfg.d_nope:], (1, 0, 2)), pos[R], base, yarn)
         q = np.concatenate([qf[:, :, :cfg.d_nope], np.transpose(q_rot, (1, 0, 2))], axis=-1)
-        lam = sigmoid(linear(xb, W["w_lambda"]))
+        lam = sigmoid(linear(xr, W["w_lambda"]))
         gate = sigmoid(linear(cqn, W["w_gate"]))
-        Hh = attention_heads(q, kc, kr, v, list(range(L)), cfg)
+        Hh = attention_heads(q, kc, kr, v, R, cfg)
         Hs, Hn = Hh[:, :nS], Hh[:, nS:]
         D = Hs - lam[:, :, None] * np.repeat(Hn, g, axis=1)
-        Z = gate * D.reshape(L, -1)
+        Z = gate * D.reshape(nR, -1)
         # output projection
         grads["w_o"] += dyb.T @ Z
         dZ = dyb @ _f64(W["w_o"])
         # gate and differential
-        dgate = dZ * D.reshape(L, -1)
-        dD = (dZ * gate).reshape(L, nS, cfg.d_v)
+        dgate = dZ * D.reshape(nR, -1)
+        dD = (dZ * gate).reshape(nR, nS, cfg.d_v)
         dlam = -np.sum(dD * np.repeat(Hn, g, axis=1), axis=-1)
-        dHn = -np.sum((lam[:, :, None] * dD).reshape(L, nN, g, cfg.d_v), axis=2)
+        dHn = -np.sum((lam[:, :, None] * dD).reshape(nR, nN, g, cfg.d_v), axis=2)
         dH = np.concatenate([dD, dHn], axis=1)
         # attention
-        dq, dkc, dkr, dv = attention_heads_backward(q, kc, kr, v, dH, cfg)
+        dq, dkc, dkr, dv = attention_heads_backward(q, kc, kr, v, dH, cfg, rows=R)
         # query side: RoPE on the rotary parts, W_UQ, the gate, RMSNorm, W_DQ
-        dq_rot = rope_backward(np.transpose(dq[:, :, cfg.d_nope:], (1, 0, 2)), pos, base, yarn)
-        dqf = np.concatenate([dq[:, :, :cfg.d_nope], np.transpose(dq_rot, (1, 0, 2))], axis=-1).reshape(L, -1)
+        dq_rot = rope_backward(np.transpose(dq[:, :, cfg.d_nope:], (1, 0, 2)), pos[R], base, yarn)
+        dqf = np.concatenate([dq[:, :, :cfg.d_nope], np.transpose(dq_rot, (1, 0, 2))], axis=-1).reshape(nR, -1)
         grads["w_uq"] += dqf.T @ cqn
         dcqn = dqf @ _f64(W["w_uq"])
         dglogit = dgate * gate * (1.0 - gate)
@@ -653,12 +662,12 @@ def gdla_layer_backward(x, W, cfg: Cfg, dy, pos_offset=0):
         dcqn += dglogit @ _f64(W["w_gate"])
         dcq, dgq = rms_norm_backward(cq, W["g_q"], cfg.rms_eps, dcqn)
         grads["g_q"] += dgq
-        grads["w_dq"] += dcq.T @ xb
-        dxb = dcq @ _f64(W["w_dq"])
+        grads["w_dq"] += dcq.T @ xr
+        dxr = dcq @ _f64(W["w_dq"])
         # lambda
         dllogit = dlam * lam * (1.0 - lam)
-        grads["w_lambda"] += dllogit.T @ xb
-        dxb += dllogit @ _f64(W["w_lambda"])
+        grads["w_lambda"] += dllogit.T @ xr
+        dxr += dllogit @ _f64(W["w_lambda"])
         # KV side: expansion, RMSNorm, RoPE of the rotary key, W_DKV
         dkv = np.concatenate([dkc.reshape(L, -1), dv.reshape(L, -1)], axis=-1)
         grads["w_ukv"] += dkv.T @ ckvn
@@ -668,7 +677,8 @@ def gdla_layer_backward(x, W, cfg: Cfg, dy, pos_offset=0):
         dkr_raw = rope_backward(dkr, pos, base, yarn)
         dckv_kr = np.concatenate([dckv, dkr_raw], axis=-1)
         grads["w_dkv"] += dckv_kr.T @ xb
-        dxb += dckv_kr @ _f64(W["w_dkv"])
+        dxb = dckv_kr @ _f64(W["w_dkv"])
+        dxb[R] += dxr
         dx[b] = dxb
     return dict(dx=dx, **grads)
 

@@ -724,4 +724,22 @@ def pin_rms_norm_backward_finite_differences():
         assert abs(fd - dgamma[j]) < 1e-8, (j, fd, dgamma[j])
 
 
+def pin_backward_rows_equals_sparse_dy():
+    """The row-restricted backward (upstream gradient on a few rows) equals
+    the full backward with dy zero on every other row."""
+    W = tiny_weights(seed=51)
+    x = tiny_x(B=2, L=9, seed=52)
+    rng = np.random.Generator(np.random.PCG64(53))
+    rows = [0, 4, 5, 8]
+    dy_rows = rng.standard_normal((2, len(rows), TINY.d_model))
+    dy = np.zeros((2, 9, TINY.d_model))
+    dy[:, rows] = dy_rows
+    for window in (0, 3):
+        cfg = replace(TINY, window=window)
+        full = R.gdla_layer_backward(x, W, cfg, dy, pos_offset=2)
+        part = R.gdla_layer_backward(x, W, cfg, dy_rows, pos_offset=2, rows=rows)
+        for k in full:
+            close(part[k], full[k], 1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -67,3 +67,34 @@ def test_backward_report_shapes_g4(window):
 
 def test_backward_motif_shapes():
     run(configs.MOTIF_SHAPES, 1, 200, 0, seed=84)
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_backward_hybrid_l32k_sparse_rows(layer):
+    """Full size (Motif shapes, L = 32768, the block's full-causal layer and a
+    W = 4096 layer): dy is nonzero only on sampled rows, so the oracle's
+    row-restricted backward gives every gradient exactly (dx on all rows,
+    through the keys and values; every weight gradient); the kernels run at
+    full size, unaware of the sparsity."""
+    import time
+    w = configs.WORKLOADS["hybrid_l32k"]
+    s = w.shapes
+    win = w.windows[layer]
+    rows = inputs.sampled_rows(w.L, win, 12, configs.layer_seed(w, layer))
+    print(f"[case] backward hybrid_l32k layer {layer} W={win}, {len(rows)} rows with a gradient", flush=True)
+    Wc = inputs.make_weights(s, configs.layer_seed(w, layer), "bf16")
+    xc = inputs.make_x(w.B, w.L, s["d_model"], w.seed, "bf16")
+    rng = np.random.Generator(np.random.PCG64(91 + layer))
+    dy_rows = inputs.to_storage(rng.standard_normal((w.B, len(rows), s["d_model"]), dtype=np.float32), "bf16")
+    dyc = torch.zeros((w.B, w.L, s["d_model"]), dtype=torch.bfloat16)
+    dyc[:, rows] = dy_rows
+    cfg = gdla.make_config(s, win, "bf16")
+    dx, grads = gdla.backward(cfg, {k: v.to("cuda") for k, v in Wc.items()}, xc.to("cuda"), dyc.to("cuda"))
+    torch.cuda.synchronize()
+    t0 = time.time()
+    ref = R.gdla_layer_backward(inputs.widen(xc), {k: inputs.widen(v) for k, v in Wc.items()},
+                                oracle_cfg(s, win), inputs.widen(dy_rows), rows=rows)
+    print(f"[workload] oracle backward (rows {len(rows)}) in {time.time() - t0:.1f} s", flush=True)
+    check(host64(dx), ref["dx"], "dx")
+    for n in inputs.WEIGHT_NAMES:
+        check(host64(grads[n]), ref[n], n)

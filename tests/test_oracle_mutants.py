@@ -245,18 +245,19 @@ def _rms_backward_no_projection(c, gamma, eps, g):
     return r * g * np.asarray(gamma, np.float64), np.sum((g * c * r).reshape(-1, c.shape[-1]), axis=0)
 
 
-def _attn_backward_no_rowsum(q, kc, kr, v, dH, cfg):
+def _attn_backward_no_rowsum(q, kc, kr, v, dH, cfg, rows=None):
     # dS = P * dP, the softmax's rowsum term dropped
     import math as _m
-    L = q.shape[0]
+    L = kc.shape[0]
+    Rw = np.arange(L) if rows is None else np.asarray(rows)
     scale = 1.0 / _m.sqrt(cfg.d_qk)
     dq = np.zeros_like(q)
     dkc = np.zeros((L, cfg.n_noise, cfg.d_nope))
     dkr = np.zeros((L, cfg.d_rope))
     dv = np.zeros((L, cfg.n_noise, cfg.d_v))
     t = np.arange(L)
-    lo = np.array([R.attended_keys(i, cfg.window)[0] for i in range(L)])
-    allowed = (t[None, :] <= t[:, None]) & (t[None, :] >= lo[:, None])
+    lo = np.array([R.attended_keys(int(i), cfg.window)[0] for i in Rw])
+    allowed = (t[None, :] <= Rw[:, None]) & (t[None, :] >= lo[:, None])
     for h in range(cfg.n_heads):
         n = R.kv_head_of(h, cfg)
         k = np.concatenate([kc[:, n, :], kr], axis=-1)
@@ -272,12 +273,12 @@ def _attn_backward_no_rowsum(q, kc, kr, v, dH, cfg):
     return dq, dkc, dkr, dv
 
 
-def _attn_backward_rotary_key_per_group(q, kc, kr, v, dH, cfg):
+def _attn_backward_rotary_key_per_group(q, kc, kr, v, dH, cfg, rows=None):
     # the rotary key's gradient kept from the noise heads only (not every head)
-    dq, dkc, dkr, dv = _ORIG["attention_heads_backward"](q, kc, kr, v, dH, cfg)
+    dq, dkc, dkr, dv = _ORIG["attention_heads_backward"](q, kc, kr, v, dH, cfg, rows)
     dH2 = np.array(dH)
     dH2[:, :cfg.n_signal] = 0.0
-    _, _, dkr_noise, _ = _ORIG["attention_heads_backward"](q, kc, kr, v, dH2, cfg)
+    _, _, dkr_noise, _ = _ORIG["attention_heads_backward"](q, kc, kr, v, dH2, cfg, rows)
     return dq, dkc, dkr_noise, dv
 
 
