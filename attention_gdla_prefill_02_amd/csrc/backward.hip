@@ -33,8 +33,6 @@ namespace {
 
 constexpr int DN = 128, DR = 64, DQK = DN + DR, DV = 128;
 constexpr int TR = 32;                    // rows of a streamed tile (keys or queries)
-constexpr int QK_LD = DQK + 8;            // LDS row of a [row][d_qk] tile (elements)
-constexpr int V_LD = DV + 8;              // LDS row of a [row][d_v] tile
 constexpr int T_LD = TR + 8;              // LDS row of a transposed [dim][32 rows] tile
 
 // 8 bf16 of a transposed tile row: columns 4q..4q+3 and 16+4q..16+4q+3
@@ -44,24 +42,83 @@ GDLA_DEV bf16x8 tr_cols(const bf16* row, int q4) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// Stage R rows of C 16-byte chunks into LDS rows of C + 1 chunks (the last is
-// padding), 1 KB per load instruction: lane i of a block writes LDS bytes
-// 16i.. of that block, so each lane fetches the chunk that belongs there.
-// src(r, c) returns the global address of chunk c of row r; pad chunks fetch
-// chunk 0 of their row.  Called by all waves; wave w issues blocks w, w+NW..
-template <int R, int C, int NW, class Src>
-GDLA_DEV void stage_rows(unsigned char* lds, int wave, int lane, Src src) {
-  constexpr int CH = R * (C + 1), BLK = (CH + 63) / 64;
+// A tile of R rows of C 16-byte chunks staged into LDS rows of C + 1 chunks
+// (the last is padding), 1 KB per load instruction: lane i of a block writes
+// LDS bytes 16i.. of that block, so each lane fetches the chunk that belongs
+// there.  The region is rounded up to whole blocks, so lanes past the tile
+// write into its slack instead of being switched off.  Wave w issues blocks
+// w, w + NW, ...; the (row, chunk) of each of the lane's blocks is computed
+// once per kernel.
+template <int R, int C, int NW>
+struct Stage {
+  static constexpr int CH = R * (C + 1), BLK = (CH + 63) / 64, NI = (BLK + NW - 1) / NW;
+  static constexpr int BYTES = BLK * 1024;
+  int row[NI], chunk[NI];   // chunk C (the pad) and lanes past the tile read chunk 0
+  GDLA_DEV void init(int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < (BLK + NW - 1) / NW; ++i) {
-    const int blk = wave + NW * i;
-    const int pos = blk * 64 + lane;
-    if (blk < BLK && pos < CH) {
+    for (int i = 0; i < NI; ++i) {
+      const int pos = (wave + NW * i) * 64 + lane;
       const int r = pos / (C + 1), c = pos % (C + 1);
-      g2lds16(src(r, c < C ? c : 0), lds + blk * 1024);
+      row[i] = pos < CH ? r : 0;
+      chunk[i] = pos < CH && c < C ? c : 0;
     }
   }
+  // src(i) gives the global address of block i's chunk for this lane
+  template <class Src>
+  GDLA_DEV void issue(unsigned char* lds, int wave, Src src) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int blk = wave + NW * i;
+      if (blk < BLK) g2lds16(src(i), lds + blk * 1024);
+    }
+  }
+};
+
+// Rows of C = 24 or 16 chunks (d_qk or d_v wide) staged without padding, chunk
+// c of row r at position c ^ swz(r) of the row.  gfx950 serves a 16-byte LDS
+// read in four passes of 16 lanes (lanes 32h + 4j + i, i < 4, with the parity
+// of j fixed); a fragment read of these kernels has lane l on row l & 15
+// (+16) and chunk 4s + (l >> 4), so a pass touches rows {0-3, 8-11} or
+// {4-7, 12-15} at two adjacent chunks.  The swizzle sends those 16 reads to 16
+// distinct 16-byte slots modulo 256 bytes (a padded row leaves 2-way
+// conflicts); it flips chunk bits 1-2 (24-chunk rows) or 1-3 (16-chunk rows),
+// so each row keeps its own chunks.
+template <int C>
+GDLA_DEV int swz(int r) {
+  return C == 24 ? 2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1) : 2 * (r & 3) + 8 * ((r >> 3) & 1);
 }
+
+template <int R, int C, int NW>
+struct SwzStage {
+  static_assert((R * C) % 64 == 0 && (C == 24 || C == 16), "whole 1 KB blocks of 24- or 16-chunk rows");
+  static constexpr int BLK = R * C / 64, NI = (BLK + NW - 1) / NW;
+  static constexpr int BYTES = BLK * 1024;
+  int row[NI], chunk[NI];
+  GDLA_DEV void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int pos = (wave + NW * i) * 64 + lane;
+      const int r = pos / C;
+      row[i] = pos < R * C ? r : 0;
+      chunk[i] = pos < R * C ? (pos % C) ^ swz<C>(r) : 0;
+    }
+  }
+  template <class Src>
+  GDLA_DEV void issue(unsigned char* lds, int wave, Src src) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int blk = wave + NW * i;
+      if (blk < BLK) g2lds16(src(i), lds + blk * 1024);
+    }
+  }
+  // element offsets of this lane's fragment reads: row r16 (+16 u at
+  // 16*C*8 elements), chunk 4s + q4
+  template <int S>
+  GDLA_DEV static void read_offsets(int r16, int q4, int (&off)[S]) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) off[s] = r16 * C * 8 + (((4 * s + q4) ^ swz<C>(r16)) * 8);
+  }
+};
 
 // ------------------------------------------------------------ transpose
 // dst[c][r] = src[r][c] (r < R, c < C); dst[c][r] = 0 for R <= r < Rpad.
@@ -195,7 +252,10 @@ template <int G>
 __global__ void __launch_bounds__(128 * (G + 1), 1)
 attn_bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int NW = 2 * (G + 1);
-  constexpr int K_BYTES = TR * QK_LD * 2, V_BYTES = TR * V_LD * 2, KT_BYTES = DQK * T_LD * 2;
+  using SK = SwzStage<TR, DQK / 8, NW>;
+  using SV = SwzStage<TR, DV / 8, NW>;
+  using SKT = Stage<DQK, TR / 8, NW>;
+  constexpr int K_BYTES = SK::BYTES, V_BYTES = SV::BYTES, KT_BYTES = SKT::BYTES;
   constexpr int BUF = K_BYTES + V_BYTES + KT_BYTES;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -223,21 +283,36 @@ attn_bwd_dq_kernel(AttnBwdArgs a) {
   const int t_lo = (int)((tb + k_lo) / TR), t_hi = (int)cdiv(tb + k_hi, (int64_t)TR);
   const int koff = n * DN, voff = nN * DN + n * DV;
 
+  SK sk;
+  SV sv;
+  SKT skt;
+  sk.init(w, lane);
+  sv.init(w, lane);
+  skt.init(w, lane);
+  int kro[DQK / 32], vro[DV / 32];   // fragment read offsets (elements) in the K and V row tiles
+  SK::read_offsets(r16, q4, kro);
+  SV::read_offsets(r16, q4, vro);
+  const bf16* kvo = a.kv + koff;
+  const bf16* vo = a.kv + voff;
+  const bf16* kto = a.kvT + (int64_t)koff * a.ld_t;
   auto load = [&](int tile, int buf) {
     unsigned char* base = smem + buf * BUF;
     const int64_t r0 = (int64_t)tile * TR;
-    stage_rows<TR, DQK / 8, NW>(base, w, lane, [&](int r, int c) -> const void* {
-      const int64_t row = min(r0 + r, T - 1);
-      return c < DN / 8 ? (const void*)(a.kv + row * a.ld_kv + koff + 8 * c)
-                        : (const void*)(a.kr + row * DR + 8 * (c - DN / 8));
+    const int rmax = (int)min((int64_t)TR - 1, T - 1 - r0);   // rows past the stream repeat its last row
+    const bf16* kvr = kvo + r0 * a.ld_kv;
+    const bf16* krr = a.kr + r0 * DR;
+    sk.issue(base, w, [&](int i) -> const void* {
+      const int r = min(sk.row[i], rmax), c = sk.chunk[i];
+      return c < DN / 8 ? (const void*)(kvr + r * (int)a.ld_kv + 8 * c) : (const void*)(krr + r * DR + 8 * c - DN);
     });
-    stage_rows<TR, DV / 8, NW>(base + K_BYTES, w, lane, [&](int r, int c) -> const void* {
-      const int64_t row = min(r0 + r, T - 1);
-      return a.kv + row * a.ld_kv + voff + 8 * c;
+    const bf16* vr = vo + r0 * a.ld_kv;
+    sv.issue(base + K_BYTES, w, [&](int i) -> const void* {
+      return vr + min(sv.row[i], rmax) * (int)a.ld_kv + 8 * sv.chunk[i];
     });
-    stage_rows<DQK, TR / 8, NW>(base + K_BYTES + V_BYTES, w, lane, [&](int r, int c) -> const void* {
-      return r < DN ? (const void*)(a.kvT + (int64_t)(koff + r) * a.ld_t + r0 + 8 * c)
-                    : (const void*)(a.krT + (int64_t)(r - DN) * a.ld_t + r0 + 8 * c);
+    skt.issue(base + K_BYTES + V_BYTES, w, [&](int i) -> const void* {
+      const int r = skt.row[i];
+      return r < DN ? (const void*)(kto + (int64_t)r * a.ld_t + r0 + 8 * skt.chunk[i])
+                    : (const void*)(a.krT + (int64_t)(r - DN) * a.ld_t + r0 + 8 * skt.chunk[i]);
     });
   };
 
@@ -264,10 +339,10 @@ attn_bwd_dq_kernel(AttnBwdArgs a) {
       dp[u] = f32x4{};
 #pragma unroll
       for (int s = 0; s < DQK / 32; ++s)
-        st[u] = mfma16(*reinterpret_cast<const bf16x8*>(Kt + (16 * u + r16) * QK_LD + 32 * s + 8 * q4), qf[s], st[u]);
+        st[u] = mfma16(*reinterpret_cast<const bf16x8*>(Kt + 16 * u * DQK + kro[s]), qf[s], st[u]);
 #pragma unroll
       for (int s = 0; s < DV / 32; ++s)
-        dp[u] = mfma16(*reinterpret_cast<const bf16x8*>(Vt + (16 * u + r16) * V_LD + 32 * s + 8 * q4), dhf[s], dp[u]);
+        dp[u] = mfma16(*reinterpret_cast<const bf16x8*>(Vt + 16 * u * DV + vro[s]), dhf[s], dp[u]);
     }
     // dS^T = P^T (dP^T - rowsum(dH H)), as the B operand of dQ^T += K^T dS^T
     bf16x8 dsb;
@@ -276,8 +351,8 @@ attn_bwd_dq_kernel(AttnBwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kl = kb + 16 * u + 4 * q4 + j;
-        const float p = visible(ql, kl, L, W) ? fast_exp2(st[u][j] * a.sc - lse) : 0.f;
-        dsb[4 * u + j] = (bf16)(p * (dp[u][j] - dvec));
+        const float e = fast_exp2(st[u][j] * a.sc - lse);   // selected, not branched on
+        dsb[4 * u + j] = (bf16)(visible(ql, kl, L, W) ? e * (dp[u][j] - dvec) : 0.f);
       }
 #pragma unroll
     for (int rt = 0; rt < DQK / 16; ++rt) dq[rt] = mfma16(tr_cols(KT + (16 * rt + r16) * T_LD, q4), dsb, dq[rt]);
@@ -322,8 +397,12 @@ template <int G>
 __global__ void __launch_bounds__(64 * DKV_NW, 1)
 attn_bwd_dkv_kernel(AttnBwdArgs a) {
   constexpr int NW = DKV_NW;
-  constexpr int Q_BYTES = TR * QK_LD * 2, DH_BYTES = TR * V_LD * 2, QT_BYTES = DQK * T_LD * 2,
-                DHT_BYTES = DV * T_LD * 2, ST_BYTES = 2 * TR * 4;
+  using SQ = SwzStage<TR, DQK / 8, NW>;
+  using SD = SwzStage<TR, DV / 8, NW>;
+  using SQT = Stage<DQK, TR / 8, NW>;
+  using SDT = Stage<DV, TR / 8, NW>;
+  constexpr int Q_BYTES = SQ::BYTES, DH_BYTES = SD::BYTES, QT_BYTES = SQT::BYTES, DHT_BYTES = SDT::BYTES,
+                ST_BYTES = 2 * TR * 4;
   constexpr int BUF = Q_BYTES + DH_BYTES + QT_BYTES + DHT_BYTES + ST_BYTES;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -351,23 +430,33 @@ attn_bwd_dkv_kernel(AttnBwdArgs a) {
   const int t_lo = (int)((tb + k0) / TR), t_hi = (int)cdiv(tb + q_hi, (int64_t)TR);
   const int steps = (t_hi - t_lo) * (G + 1);
 
+  SQ sq;
+  SD sd;
+  SQT sqt;
+  SDT sdt;
+  sq.init(w, lane);
+  sd.init(w, lane);
+  sqt.init(w, lane);
+  sdt.init(w, lane);
+  int qro[DQK / 32], dro[DV / 32];   // fragment read offsets (elements) in the Q and dH row tiles
+  SQ::read_offsets(r16, q4, qro);
+  SD::read_offsets(r16, q4, dro);
   auto load = [&](int step, int buf) {
     const int tile = t_lo + step / (G + 1), hs = step % (G + 1);
     const int head = hs < G ? n * G + hs : nS + n;
     unsigned char* base = smem + buf * BUF;
     const int64_t r0 = (int64_t)tile * TR;
-    stage_rows<TR, DQK / 8, NW>(base, w, lane, [&](int r, int c) -> const void* {
-      return a.q + min(r0 + r, T - 1) * a.ld_q + head * DQK + 8 * c;
-    });
-    stage_rows<TR, DV / 8, NW>(base + Q_BYTES, w, lane, [&](int r, int c) -> const void* {
-      return a.dh + min(r0 + r, T - 1) * H * DV + head * DV + 8 * c;
-    });
-    stage_rows<DQK, TR / 8, NW>(base + Q_BYTES + DH_BYTES, w, lane, [&](int r, int c) -> const void* {
-      return a.qT + (int64_t)(head * DQK + r) * a.ld_t + r0 + 8 * c;
-    });
-    stage_rows<DV, TR / 8, NW>(base + Q_BYTES + DH_BYTES + QT_BYTES, w, lane, [&](int r, int c) -> const void* {
-      return a.dhT + (int64_t)(head * DV + r) * a.ld_t + r0 + 8 * c;
-    });
+    const int rmax = (int)min((int64_t)TR - 1, T - 1 - r0);   // rows past the stream repeat its last row
+    const bf16* qr = a.q + r0 * a.ld_q + head * DQK;
+    sq.issue(base, w, [&](int i) -> const void* { return qr + min(sq.row[i], rmax) * (int)a.ld_q + 8 * sq.chunk[i]; });
+    const bf16* dr = a.dh + r0 * H * DV + head * DV;
+    sd.issue(base + Q_BYTES, w, [&](int i) -> const void* { return dr + min(sd.row[i], rmax) * H * DV + 8 * sd.chunk[i]; });
+    const bf16* qto = a.qT + (int64_t)head * DQK * a.ld_t + r0;
+    sqt.issue(base + Q_BYTES + DH_BYTES, w,
+              [&](int i) -> const void* { return qto + (int64_t)sqt.row[i] * a.ld_t + 8 * sqt.chunk[i]; });
+    const bf16* dto = a.dhT + (int64_t)head * DV * a.ld_t + r0;
+    sdt.issue(base + Q_BYTES + DH_BYTES + QT_BYTES, w,
+              [&](int i) -> const void* { return dto + (int64_t)sdt.row[i] * a.ld_t + 8 * sdt.chunk[i]; });
   };
   // the rows' log-sum-exp and rowsum(dH H) go through registers (strided in HBM)
   float st_lse = 0.f, st_dv = 0.f;
@@ -426,10 +515,10 @@ attn_bwd_dkv_kernel(AttnBwdArgs a) {
         dp[u] = f32x4{};
 #pragma unroll
         for (int s = 0; s < DQK / 32; ++s)
-          s_[u] = mfma16(*reinterpret_cast<const bf16x8*>(Qt + (16 * u + r16) * QK_LD + 32 * s + 8 * q4), kf[s], s_[u]);
+          s_[u] = mfma16(*reinterpret_cast<const bf16x8*>(Qt + 16 * u * DQK + qro[s]), kf[s], s_[u]);
 #pragma unroll
         for (int s = 0; s < DV / 32; ++s)
-          dp[u] = mfma16(*reinterpret_cast<const bf16x8*>(Dt + (16 * u + r16) * V_LD + 32 * s + 8 * q4), vf[s], dp[u]);
+          dp[u] = mfma16(*reinterpret_cast<const bf16x8*>(Dt + 16 * u * DV + dro[s]), vf[s], dp[u]);
       }
       bf16x8 pb, dsb;
 #pragma unroll
@@ -439,9 +528,10 @@ attn_bwd_dkv_kernel(AttnBwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int qlq = qb + 16 * u + 4 * q4 + j;
-          const float p = visible(qlq, kl, L, W) ? fast_exp2(s_[u][j] * a.sc - lse4[j]) : 0.f;
-          pb[4 * u + j] = (bf16)p;
-          dsb[4 * u + j] = (bf16)(p * (dp[u][j] - dv4[j]));
+          const bool vis = visible(qlq, kl, L, W);
+          const float e = fast_exp2(s_[u][j] * a.sc - lse4[j]);   // selected, not branched on
+          pb[4 * u + j] = (bf16)(vis ? e : 0.f);
+          dsb[4 * u + j] = (bf16)(vis ? e * (dp[u][j] - dv4[j]) : 0.f);
         }
       }
 #pragma unroll
@@ -587,8 +677,12 @@ hipError_t set_lds(K kernel, size_t bytes) {
 
 template <int G>
 hipError_t attn_bwd_g(const AttnBwdArgs& a, hipStream_t s) {
-  constexpr size_t dq_lds = 2 * (size_t)(TR * QK_LD * 2 + TR * V_LD * 2 + DQK * T_LD * 2);
-  constexpr size_t dkv_lds = 2 * (size_t)(TR * QK_LD * 2 + TR * V_LD * 2 + DQK * T_LD * 2 + DV * T_LD * 2 + 2 * TR * 4);
+  constexpr int NWQ = 2 * (G + 1);
+  constexpr size_t dq_lds = 2 * (size_t)(SwzStage<TR, DQK / 8, NWQ>::BYTES + SwzStage<TR, DV / 8, NWQ>::BYTES +
+                                         Stage<DQK, TR / 8, NWQ>::BYTES);
+  constexpr size_t dkv_lds = 2 * (size_t)(SwzStage<TR, DQK / 8, DKV_NW>::BYTES + SwzStage<TR, DV / 8, DKV_NW>::BYTES +
+                                          Stage<DQK, TR / 8, DKV_NW>::BYTES + Stage<DV, TR / 8, DKV_NW>::BYTES +
+                                          2 * TR * 4);
   static bool attr = false;
   hipError_t e;
   if (!attr) {
