@@ -5,8 +5,10 @@
 //    workgroup (8 waves as 2 x 4, each wave 128 x 64 = 4 x 2 tiles of the
 //    32x32x16 bf16 instruction), K staged through LDS 64 at a time with two
 //    buffers so the global loads of step k+1 overlap the MFMAs of step k.
-//    Rows are padded by 16 bytes so the 16-byte fragment reads of 8
-//    consecutive rows hit distinct banks.  Tiles are ordered so each XCD
+//    Tile rows are 128 bytes, unpadded; the 16-byte chunk c of row r sits at
+//    position c ^ ((r >> 1) & 7) of its row, which keeps the fragment reads
+//    conflict-free and lets each 4-lane group of a tile load fetch one
+//    aligned 64-byte piece of a row.  Tiles are ordered so each XCD
 //    (blockIdx % 8) owns a contiguous, L2-friendly band of output tiles.
 //  * gemm_f32: plain vector-ALU tiled GEMM for the fp32 path.
 //
@@ -26,53 +28,87 @@ struct EpiMfma {
   const float* rope; int q_cols, d_qk, d_nope, d_rope;
   float* G; int64_t ldg;
   int Npad;   // columns [N, Npad) are stored as zeros
-  bool vecC, vecG;   // row strides allow 4-element vector stores
+  bool vecC, vecG, vecR;   // row strides and bases allow 4-element vector accesses
+  bool vecRope;            // the cos/sin table allows 16-byte loads
 
-  // v0[e] belongs to (row, n + e) and v1[e] to (row, n + 32 + e), e = 0..3; n0 is
-  // the first column of the 64-wide window holding both quads (n is 4-aligned).
-  GDLA_DEV void quads(int row, int n, int n0, f32x4 v0, f32x4 v1) const {
-    if (row >= M) return;
-    if (kind == EPI_QG) {
-      if (n0 < q_cols) {
-        if ((n0 % d_qk) == d_nope) {
-          const float* cs = rope + ((int64_t)row * (d_rope / 2) + (n - n0)) * 2;
+  // Register phase, one output row of a wave's 64-column window: v0[i][e]
+  // belongs to column n + 8 i + e and v1[i][e] to column n + 8 i + 32 + e
+  // (i, e = 0..3), where n is 4-aligned and n0 <= n < n0 + 8 is the window's
+  // first column (the window decides the column kind, so branches on it are
+  // wave-uniform).  Applies RoPE to rotary windows and the sigmoid to gate
+  // windows; the values then go to LDS and out through store().
+  GDLA_DEV void transform(int row, int n, int n0, f32x4 (&v0)[4], f32x4 (&v1)[4]) const {
+    if (kind != EPI_QG || row >= M) return;
+    if (n0 >= q_cols) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float c = cs[2 * e], sn = cs[2 * e + 1];
-            const float x1 = v0[e], x2 = v1[e];
-            v0[e] = x1 * c - x2 * sn;
-            v1[e] = x2 * c + x1 * sn;
-          }
-        }
-      } else {
-        float* g = G + (int64_t)row * ldg - q_cols;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          v0[e] = sigmoidf_(v0[e]);
-          v1[e] = sigmoidf_(v1[e]);
+          v0[i][e] = sigmoidf_(v0[i][e]);
+          v1[i][e] = sigmoidf_(v1[i][e]);
         }
-        store4(g, n, v0, N, vecG);
-        store4(g, n + 32, v1, N, vecG);
-        return;
+      return;
+    }
+    if ((n0 % d_qk) != d_nope) return;
+    // rotate-half pairs (n + e, n + 32 + e); the table holds (cos, sin) of
+    // frequency n - n0 + e at floats 2 (n - n0 + e), 2 (n - n0 + e) + 1
+    const float* cs = rope + ((int64_t)row * (d_rope / 2) + (n - n0)) * 2;
+    f32x4 t[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (vecRope) {
+          t[i][h] = *reinterpret_cast<const f32x4*>(cs + 16 * i + 4 * h);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t[i][h][e] = cs[16 * i + 4 * h + e];
+        }
       }
-    }
-    OT* c = C + (int64_t)row * ldc;
-    if (R) {
-      const OT* r = R + (int64_t)row * ldr;
-      add4(r, n, v0);
-      add4(r, n + 32, v1);
-    }
-    store4(c, n, v0, Npad, vecC);
-    store4(c, n + 32, v1, Npad, vecC);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float c = t[i][e >> 1][2 * (e & 1)], sn = t[i][e >> 1][2 * (e & 1) + 1];
+        const float x1 = v0[i][e], x2 = v1[i][e];
+        v0[i][e] = x1 * c - x2 * sn;
+        v1[i][e] = x2 * c + x1 * sn;
+      }
   }
+
+  // Store phase: columns col .. col + 3 (col 4-aligned) of one row.  A wave
+  // stores whole rows of the tile, so vector stores cover whole 128-byte lines
+  // and go out with the non-temporal policy.
+  GDLA_DEV void store(int row, int col, f32x4 v) const {
+    if (row >= M) return;
+    if (kind == EPI_QG && col >= q_cols) {
+      store4(G + (int64_t)row * ldg - q_cols, col, v, N, vecG);
+      return;
+    }
+    store4(C + (int64_t)row * ldc, col, v, Npad, vecC);
+  }
+  // the residual at the same columns, in its own type (zero without one, or
+  // past M / N)
+  typedef typename std::conditional<sizeof(OT) == 2, bf16x4, f32x4>::type Quad;
+  GDLA_DEV Quad residual(int row, int col) const {
+    Quad q = {};
+    if (!R || row >= M) return q;
+    const OT* r = R + (int64_t)row * ldr;
+    if (vecR && col + 3 < N) return *reinterpret_cast<const Quad*>(r + col);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (col + e < N) q[e] = r[col + e];
+    return q;
+  }
+  static GDLA_DEV f32x4 widen(Quad q) { return f32x4{(float)q[0], (float)q[1], (float)q[2], (float)q[3]}; }
   template <class T>
   GDLA_DEV void store4(T* p, int n, f32x4 v, int lim, bool vec) const {
     if (vec && n + 3 < N) {
       if constexpr (sizeof(T) == 2) {
         bf16x4 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-        *reinterpret_cast<bf16x4*>(p + n) = b;
+        __builtin_nontemporal_store(b, reinterpret_cast<bf16x4*>(p + n));
       } else {
-        *reinterpret_cast<f32x4*>(p + n) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p + n));
       }
     } else {
 #pragma unroll
@@ -80,21 +116,19 @@ struct EpiMfma {
         if (n + e < lim) p[n + e] = from_f32<T>(n + e < N ? v[e] : 0.f);
     }
   }
-  GDLA_DEV void add4(const OT* r, int n, f32x4& v) const {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (n + e < N) v[e] += to_f32(r[n + e]);
-  }
 };
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, PAD = 8, LDR = BK + PAD, NT = 512;
-constexpr int ROW_CH = LDR / 8;                   // 9 chunks of 16 B per padded row (1 pad)
-constexpr int OP_CH = BM * ROW_CH;                // 2304 chunks per operand tile
-constexpr int OP_KB = OP_CH / 64;                 // 36 one-KB blocks per operand tile
-constexpr int STAGE_BYTES = 2 * OP_CH * 16;       // A and B tiles of one K step (72 KB)
-static_assert(OP_CH % 64 == 0, "operand tiles must be whole 1 KB blocks");
+constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
+constexpr int ROW_BYTES = BK * 2;                 // 128 B: 8 chunks of 16 B per tile row
+constexpr int OP_BYTES = BM * ROW_BYTES;          // 32 KB per operand tile
+constexpr int OP_KB = OP_BYTES / 1024;            // 32 one-KB blocks (8 rows each) per operand tile
+constexpr int STAGE_BYTES = 2 * OP_BYTES;         // A and B tiles of one K step (64 KB)
+static_assert(BM == BN, "both operand tiles have BM rows");
+
+// position of 16-byte chunk c within tile row r
+GDLA_DEV int chunk_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // blockIdx.x -> (tile_m, tile_n): XCD-contiguous bands, then groups of 8 tile
 // rows walked column by column so concurrent tiles share A rows and B columns.
@@ -115,7 +149,7 @@ __device__ __forceinline__ void tile_of(int id, int nt, int tiles_m, int tiles_n
 // window sit in the same lane (the RoPE pairs).  Tiles move global -> LDS with
 // global_load_lds (no staging registers), double buffered: the loads of step
 // k+1 are in flight while step k's 32 MFMAs per wave run.
-template <class OT>
+template <class OT, bool RES>
 __global__ void __launch_bounds__(NT, 1)
 gemm_bf16_kernel(const bf16* __restrict__ A, int64_t lda, int64_t sA,
                  const bf16* __restrict__ B, int64_t ldb, int64_t sB,
@@ -135,20 +169,21 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int64_t lda, int64_t sA,
   epi.C += bz * sC;
   if (epi.R) epi.R += bz * sR;
 
-  // Each wave loads 1 KB blocks wave + 8i (i < 9) of the stage: blocks 0..35
-  // are the activation tile, 36..71 the weight tile.  The per-lane source of
-  // each block is fixed for the whole tile except for the K offset, so it is
-  // computed once (rows past M / N are clamped to a valid row: their results
-  // are never stored; the pad chunk of each row re-reads chunk 7).
-  constexpr int NLB = 2 * OP_KB / (NT / 64);   // 9 blocks per wave per stage
+  // Each wave loads 1 KB blocks wave + 8i (i < 8) of the stage: blocks 0..31
+  // are the activation tile, 32..63 the weight tile.  Lane l of a block fills
+  // position l % 8 of row l / 8 of the block, i.e. the chunk whose position
+  // that is.  The per-lane source of each block is fixed for the whole tile
+  // except for the K offset, so it is computed once (rows past M / N are
+  // clamped to a valid row: their results are never stored).
+  constexpr int NLB = 2 * OP_KB / (NT / 64);   // 8 blocks per wave per stage
   static_assert(2 * OP_KB % (NT / 64) == 0, "blocks must divide evenly over waves");
   const bf16* lsrc[NLB];
 #pragma unroll
   for (int i = 0; i < NLB; ++i) {
     const int blk = wave + (NT / 64) * i;
     const bool isB = blk >= OP_KB;
-    const int pos = (isB ? blk - OP_KB : blk) * 64 + lane;
-    const int r = pos / ROW_CH, c = min(pos % ROW_CH, ROW_CH - 2);
+    const int r = (isB ? blk - OP_KB : blk) * 8 + (lane >> 3);
+    const int c = chunk_pos(r, lane & 7);
     if (!isB) {
       lsrc[i] = A + (int64_t)min(m0 + r, M - 1) * lda + c * 8;
     } else {
@@ -165,9 +200,15 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int64_t lda, int64_t sA,
 #pragma unroll
     for (int i = 0; i < NLB; ++i) {
       const int blk = wave + (NT / 64) * i;
-      g2lds16(lsrc[i] + (blk >= OP_KB ? kb : ka), base + blk * 1024);
+      g2lds16_explicit(lsrc[i] + (blk >= OP_KB ? kb : ka), base + blk * 1024);
     }
   };
+  // fragment reads: lane row l32 of each 32-row sub-tile (sub-tiles start at
+  // multiples of 32 rows, so the row's swizzle is that of l32), k chunk
+  // 2 ks + hi of the 16-wide sub-step ks
+  int xo[BK / 16];
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) xo[ks] = l32 * ROW_BYTES + chunk_pos(l32, 2 * ks + hi) * 16;
 
   f32x16 acc[2][4];   // [n sub-tile][m sub-tile]
 #pragma unroll
@@ -182,15 +223,17 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int64_t lda, int64_t sA,
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < KT) load_stage((kt + 1) * BK, cur ^ 1);
-    const bf16* As = reinterpret_cast<const bf16*>(gsm + cur * STAGE_BYTES) + (wm * 128 + l32) * LDR + hi * 8;
-    const bf16* Bs = reinterpret_cast<const bf16*>(gsm + cur * STAGE_BYTES + OP_CH * 16) + (wn * 64 + l32) * LDR + hi * 8;
+    const unsigned char* As = gsm + cur * STAGE_BYTES + wm * 128 * ROW_BYTES;
+    const unsigned char* Bs = gsm + cur * STAGE_BYTES + OP_BYTES + wn * 64 * ROW_BYTES;
     bf16x8 wf[BK / 16][2], af[BK / 16][4];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn) wf[ks][tn] = *reinterpret_cast<const bf16x8*>(Bs + tn * 32 * LDR + ks * 16);
+      for (int tn = 0; tn < 2; ++tn)
+        wf[ks][tn] = *reinterpret_cast<const bf16x8*>(Bs + tn * 32 * ROW_BYTES + xo[ks]);
 #pragma unroll
-      for (int tm = 0; tm < 4; ++tm) af[ks][tm] = *reinterpret_cast<const bf16x8*>(As + tm * 32 * LDR + ks * 16);
+      for (int tm = 0; tm < 4; ++tm)
+        af[ks][tm] = *reinterpret_cast<const bf16x8*>(As + tm * 32 * ROW_BYTES + xo[ks]);
     }
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks)
@@ -215,18 +258,53 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int64_t lda, int64_t sA,
     __syncthreads();
   }
 
-  // D[n][m]: lane holds column m = 32*tm + l32, rows n = 32*tn + 8i + 4hi + j
+  // D[n][m]: lane holds column m = 32*tm + l32, rows n = 32*tn + 8i + 4hi + j.
+  // The fp32 results leave through LDS, half a tile (128 rows x 256 columns,
+  // 1 KB rows, 16-byte chunk c of row r at position c ^ (r & 15)) at a time:
+  // the waves holding those rows write them, then every wave stores whole rows.
   const int nw0 = n0 + wn * 64;
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm) {
-    const int row = m0 + wm * 128 + tm * 32 + l32;
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = nw0 + 8 * i + 4 * hi;
-      const f32x4 v0 = {acc[0][tm][4 * i], acc[0][tm][4 * i + 1], acc[0][tm][4 * i + 2], acc[0][tm][4 * i + 3]};
-      const f32x4 v1 = {acc[1][tm][4 * i], acc[1][tm][4 * i + 1], acc[1][tm][4 * i + 2], acc[1][tm][4 * i + 3]};
-      epi.quads(row, n, nw0, v0, v1);
+      for (int tm = 0; tm < 4; ++tm) {
+        f32x4 v0[4], v1[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v0[i] = f32x4{acc[0][tm][4 * i], acc[0][tm][4 * i + 1], acc[0][tm][4 * i + 2], acc[0][tm][4 * i + 3]};
+          v1[i] = f32x4{acc[1][tm][4 * i], acc[1][tm][4 * i + 1], acc[1][tm][4 * i + 2], acc[1][tm][4 * i + 3]};
+        }
+        const int r = tm * 32 + l32;
+        epi.transform(m0 + h * 128 + r, nw0 + 4 * hi, nw0, v0, v1);
+        unsigned char* lrow = gsm + r * 1024;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = wn * 16 + 2 * i + hi;   // 16-byte chunk of column wn*64 + 8i + 4hi
+          *reinterpret_cast<f32x4*>(lrow + ((ch ^ (r & 15)) * 16)) = v0[i];
+          *reinterpret_cast<f32x4*>(lrow + (((ch + 8) ^ (r & 15)) * 16)) = v1[i];
+        }
+      }
     }
+    // with a residual (RES; bf16 output), this thread's residual chunks, all
+    // loads in flight together
+    constexpr int NJ = 128 * 64 / NT;
+    typename EpiMfma<OT>::Quad res[RES ? NJ : 1];
+    if constexpr (RES) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int q = j * NT + tid;
+        res[j] = epi.residual(m0 + h * 128 + (q >> 6), n0 + (q & 63) * 4);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int q = j * NT + tid, r = q >> 6, ch = q & 63;
+      f32x4 v = *reinterpret_cast<const f32x4*>(gsm + r * 1024 + ((ch ^ (r & 15)) * 16));
+      if constexpr (RES) v += EpiMfma<OT>::widen(res[j]);
+      epi.store(m0 + h * 128 + r, n0 + ch * 4, v);
+    }
+    __syncthreads();
   }
 }
 
@@ -295,41 +373,49 @@ __global__ void qg_finish_f32(float* q, int64_t ldq, float* g, int64_t ldg, int6
   for (int c = threadIdx.x; c < gate_cols; c += blockDim.x) g[t * ldg + c] = sigmoidf_(g[t * ldg + c]);
 }
 
-template <class OT>
+template <class OT, bool RES>
 hipError_t set_gemm_lds() {
   static bool done = false;
   if (done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<OT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     2 * STAGE_BYTES);
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<OT, RES>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE_BYTES);
   if (e == hipSuccess) done = true;
   return e;
 }
 
+template <class OT, bool RES>
+hipError_t launch_gemm(const GemmArgs& a, const EpiMfma<OT>& e, int nb2, int nb3, hipStream_t s) {
+  hipError_t err = set_gemm_lds<OT, RES>();
+  if (err != hipSuccess) return err;
+  dim3 grid(cdiv(a.M, BM) * cdiv(a.N, BN), a.batch), block(NT);
+  hipLaunchKernelGGL((gemm_bf16_kernel<OT, RES>), grid, block, 2 * STAGE_BYTES, s, (const bf16*)a.A, a.lda,
+                     a.strideA, (const bf16*)a.B, a.ldb, a.strideB, (const bf16*)a.B2, nb2, (const bf16*)a.B3, nb3,
+                     a.M, a.N, a.K, a.kwrapA, a.kwrapB, a.strideC, a.strideC, e);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// 4-element vector accesses at 4-aligned columns of rows ld elements apart
+// need an aligned base and a row stride divisible by 4
+static bool vec_ok(const void* p, int64_t ld, int align) {
+  return ((uintptr_t)p % align) == 0 && ld % 4 == 0;
+}
 
 hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;
   const int nb2 = a.B2 ? a.nb2 : a.N, nb3 = a.B3 ? a.nb3 : a.N;
-  hipError_t err = a.epi == EPI_F32 ? set_gemm_lds<float>() : set_gemm_lds<bf16>();
-  if (err != hipSuccess) return err;
-  const int tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
-  dim3 grid(tiles, a.batch), block(NT);
   if (a.epi == EPI_F32) {
-    EpiMfma<float> e{(float*)a.C, a.ldc, (const float*)a.R, a.ldr, a.M, a.N, a.epi, a.rope, a.q_cols, a.d_qk,
-                     a.d_nope, a.d_rope, a.G, a.ldg, a.Npad > a.N ? a.Npad : a.N, a.ldc % 4 == 0,
-                     a.ldg % 4 == 0};
-    hipLaunchKernelGGL(gemm_bf16_kernel<float>, grid, block, 2 * STAGE_BYTES, s, (const bf16*)a.A, a.lda, a.strideA,
-                       (const bf16*)a.B, a.ldb, a.strideB, (const bf16*)a.B2, nb2, (const bf16*)a.B3, nb3,
-                       a.M, a.N, a.K, a.kwrapA, a.kwrapB, a.strideC, a.strideC, e);
-  } else {
-    EpiMfma<bf16> e{(bf16*)a.C, a.ldc, (const bf16*)a.R, a.ldr, a.M, a.N, a.epi, a.rope, a.q_cols, a.d_qk,
-                    a.d_nope, a.d_rope, a.G, a.ldg, a.Npad > a.N ? a.Npad : a.N, a.ldc % 4 == 0,
-                    a.ldg % 4 == 0};
-    hipLaunchKernelGGL(gemm_bf16_kernel<bf16>, grid, block, 2 * STAGE_BYTES, s, (const bf16*)a.A, a.lda, a.strideA,
-                       (const bf16*)a.B, a.ldb, a.strideB, (const bf16*)a.B2, nb2, (const bf16*)a.B3, nb3,
-                       a.M, a.N, a.K, a.kwrapA, a.kwrapB, a.strideC, a.strideC, e);
+    if (a.R) return hipErrorInvalidValue;   // the fp32 epilogue takes no residual
+    EpiMfma<float> e{(float*)a.C, a.ldc, nullptr, 0, a.M, a.N, a.epi, a.rope, a.q_cols, a.d_qk,
+                     a.d_nope, a.d_rope, a.G, a.ldg, a.Npad > a.N ? a.Npad : a.N, vec_ok(a.C, a.ldc, 16),
+                     vec_ok(a.G, a.ldg, 16), false, vec_ok(a.rope, 0, 16)};
+    return launch_gemm<float, false>(a, e, nb2, nb3, s);
   }
-  return hipGetLastError();
+  EpiMfma<bf16> e{(bf16*)a.C, a.ldc, (const bf16*)a.R, a.ldr, a.M, a.N, a.epi, a.rope, a.q_cols, a.d_qk,
+                  a.d_nope, a.d_rope, a.G, a.ldg, a.Npad > a.N ? a.Npad : a.N, vec_ok(a.C, a.ldc, 8),
+                  vec_ok(a.G, a.ldg, 16), vec_ok(a.R, a.ldr, 8), vec_ok(a.rope, 0, 16)};
+  return a.R ? launch_gemm<bf16, true>(a, e, nb2, nb3, s) : launch_gemm<bf16, false>(a, e, nb2, nb3, s);
 }
 
 hipError_t gemm_f32(const GemmArgs& a, hipStream_t s) {
