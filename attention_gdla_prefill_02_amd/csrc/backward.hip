@@ -13,16 +13,20 @@
 //   RoPE, RMSNorm, the up- and down-projections: transposed rotations,
 //   the RMSNorm Jacobian, and GEMMs against the transposed weights.
 //
-// Attention backward on the 16x16x32 bf16 MFMA, in two kernels so that no
-// gradient needs atomics: attn_bwd_dq_kernel owns a 32-query block of one KV
-// group (its g+1 heads share every staged key tile, as in the forward) and
-// sweeps the key tiles; attn_bwd_dkv_kernel owns a 128-key block (16 keys per
-// wave) and sweeps (query tile, head) pairs, so dK and dV of the group's
-// shared keys accumulate in registers across all g+1 heads.  Products whose
-// reduction runs over keys (dQ) or queries (dK, dV) take their A operand from
-// a transposed copy of K, Q or dH staged in LDS, read as two 8-byte halves
-// at keys/queries 4q..4q+3 and 16+4q..16+4q+3, the order in which the
-// score-shaped registers (rows 4q+j of two 16-row tiles) become a B operand.
+// Attention backward in two kernels, so that no gradient needs atomics.
+// attn_bwd_dq32_kernel owns a 32-query block of one KV group (its g+1 heads
+// share every staged key tile, as in the forward) and sweeps the key tiles on
+// the 32x32x16 bf16 MFMA: key rows are read in a permuted order so the score
+// registers are directly the B operand of dQ^T += K^T dS^T, whose A operand is
+// the same K tile read transposed (gfx950's transposing LDS read).
+// attn_bwd_dkv_kernel owns a 128-key block (16 keys per wave, 16x16x32 MFMA)
+// and sweeps (query tile, head) pairs, so dK and dV of the group's shared keys
+// accumulate in registers across all g+1 heads; its dK and dV products take
+// their A operand from transposed copies of Q and dH staged in LDS, read as
+// two 8-byte halves at queries 4q..4q+3 and 16+4q..16+4q+3, the order in
+// which the score-shaped registers (rows 4q+j of two 16-row tiles) become a B
+// operand.  (A 32-key-per-wave form of the dK/dV kernel needs 160 accumulator
+// registers per wave and ran slower at one wave per SIMD.)
 #include <cmath>
 
 #include "backward.h"
@@ -230,7 +234,7 @@ struct AttnBwdArgs {
   const bf16* q; int64_t ld_q;          // [T, H*d_qk], rotary parts RoPE'd
   const bf16* kv; int64_t ld_kv;        // [T, nN*d_nope | nN*d_v]: K^C, then V
   const bf16* kr;                       // [T, d_rope]
-  const bf16* kvT; const bf16* krT; const bf16* qT; const bf16* dhT; int64_t ld_t;   // transposed, [dim][Tp]
+  const bf16* qT; const bf16* dhT; int64_t ld_t;   // transposed, [dim][Tp]
   const bf16* dh;                       // [T, H*d_v]
   const float* lse; const float* dvec;  // [T, H]
   const float* rope;                    // [T, d_rope/2, 2]
@@ -243,148 +247,6 @@ struct AttnBwdArgs {
 
 GDLA_DEV bool visible(int ql, int kl, int L, int W) {
   return (unsigned)ql < (unsigned)L && kl <= ql && kl >= 0 && (W <= 0 || ql - kl < W);
-}
-
-// dQ: workgroup = (sequence, KV group n, 32 queries); wave = (head slot, 16
-// queries).  Key tiles of 32 stream rows through LDS: K rows (score A
-// operand), V rows (dP A operand) and K^T (dQ A operand).
-template <int G>
-__global__ void __launch_bounds__(128 * (G + 1), 1)
-attn_bwd_dq_kernel(AttnBwdArgs a) {
-  constexpr int NW = 2 * (G + 1);
-  using SK = SwzStage<TR, DQK / 8, NW>;
-  using SV = SwzStage<TR, DV / 8, NW>;
-  using SKT = Stage<DQK, TR / 8, NW>;
-  constexpr int K_BYTES = SK::BYTES, V_BYTES = SV::BYTES, KT_BYTES = SKT::BYTES;
-  constexpr int BUF = K_BYTES + V_BYTES + KT_BYTES;
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int r16 = lane & 15, q4 = lane >> 4;
-  const int hs = w % (G + 1), qg = w / (G + 1);
-  const int nN = a.nN, nS = G * nN, H = nS + nN, L = a.L, W = a.window;
-  const int nqb = cdiv(L, 32);
-  const int qb = blockIdx.x % nqb, rest = blockIdx.x / nqb, n = rest % nN, b = rest / nN;
-  const int64_t tb = (int64_t)b * L, T = a.T;
-  const int head = hs < G ? n * G + hs : nS + n;
-  const int q0 = qb * 32, ql = q0 + 16 * qg + r16;        // this lane's query (score column)
-  const int64_t qrow = tb + min(ql, L - 1);
-
-  bf16x8 qf[DQK / 32], dhf[DV / 32];
-#pragma unroll
-  for (int s = 0; s < DQK / 32; ++s)
-    qf[s] = *reinterpret_cast<const bf16x8*>(a.q + qrow * a.ld_q + head * DQK + 32 * s + 8 * q4);
-#pragma unroll
-  for (int s = 0; s < DV / 32; ++s)
-    dhf[s] = *reinterpret_cast<const bf16x8*>(a.dh + qrow * H * DV + head * DV + 32 * s + 8 * q4);
-  const float lse = a.lse[qrow * H + head], dvec = a.dvec[qrow * H + head];
-
-  // key tiles (32 stream rows, aligned to the stream) that hold keys of this block
-  const int k_lo = W > 0 ? max(0, q0 - W + 1) : 0, k_hi = min(L, q0 + 32);
-  const int t_lo = (int)((tb + k_lo) / TR), t_hi = (int)cdiv(tb + k_hi, (int64_t)TR);
-  const int koff = n * DN, voff = nN * DN + n * DV;
-
-  SK sk;
-  SV sv;
-  SKT skt;
-  sk.init(w, lane);
-  sv.init(w, lane);
-  skt.init(w, lane);
-  int kro[DQK / 32], vro[DV / 32];   // fragment read offsets (elements) in the K and V row tiles
-  SK::read_offsets(r16, q4, kro);
-  SV::read_offsets(r16, q4, vro);
-  const bf16* kvo = a.kv + koff;
-  const bf16* vo = a.kv + voff;
-  const bf16* kto = a.kvT + (int64_t)koff * a.ld_t;
-  auto load = [&](int tile, int buf) {
-    unsigned char* base = smem + buf * BUF;
-    const int64_t r0 = (int64_t)tile * TR;
-    const int rmax = (int)min((int64_t)TR - 1, T - 1 - r0);   // rows past the stream repeat its last row
-    const bf16* kvr = kvo + r0 * a.ld_kv;
-    const bf16* krr = a.kr + r0 * DR;
-    sk.issue(base, w, [&](int i) -> const void* {
-      const int r = min(sk.row[i], rmax), c = sk.chunk[i];
-      return c < DN / 8 ? (const void*)(kvr + r * (int)a.ld_kv + 8 * c) : (const void*)(krr + r * DR + 8 * c - DN);
-    });
-    const bf16* vr = vo + r0 * a.ld_kv;
-    sv.issue(base + K_BYTES, w, [&](int i) -> const void* {
-      return vr + min(sv.row[i], rmax) * (int)a.ld_kv + 8 * sv.chunk[i];
-    });
-    skt.issue(base + K_BYTES + V_BYTES, w, [&](int i) -> const void* {
-      const int r = skt.row[i];
-      return r < DN ? (const void*)(kto + (int64_t)r * a.ld_t + r0 + 8 * skt.chunk[i])
-                    : (const void*)(a.krT + (int64_t)(r - DN) * a.ld_t + r0 + 8 * skt.chunk[i]);
-    });
-  };
-
-  f32x4 dq[DQK / 16];
-#pragma unroll
-  for (int i = 0; i < DQK / 16; ++i) dq[i] = f32x4{};
-
-  load(t_lo, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int tile = t_lo; tile < t_hi; ++tile) {
-    const int buf = (tile - t_lo) & 1;
-    if (tile + 1 < t_hi) load(tile + 1, buf ^ 1);
-    const unsigned char* base = smem + buf * BUF;
-    const bf16* Kt = reinterpret_cast<const bf16*>(base);
-    const bf16* Vt = reinterpret_cast<const bf16*>(base + K_BYTES);
-    const bf16* KT = reinterpret_cast<const bf16*>(base + K_BYTES + V_BYTES);
-    const int kb = (int)((int64_t)tile * TR - tb);   // first key of the tile, within the sequence
-    // S^T (keys x this wave's queries) and dP^T = V dH^T
-    f32x4 st[2], dp[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      st[u] = f32x4{};
-      dp[u] = f32x4{};
-#pragma unroll
-      for (int s = 0; s < DQK / 32; ++s)
-        st[u] = mfma16(*reinterpret_cast<const bf16x8*>(Kt + 16 * u * DQK + kro[s]), qf[s], st[u]);
-#pragma unroll
-      for (int s = 0; s < DV / 32; ++s)
-        dp[u] = mfma16(*reinterpret_cast<const bf16x8*>(Vt + 16 * u * DV + vro[s]), dhf[s], dp[u]);
-    }
-    // dS^T = P^T (dP^T - rowsum(dH H)), as the B operand of dQ^T += K^T dS^T
-    bf16x8 dsb;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kl = kb + 16 * u + 4 * q4 + j;
-        const float e = fast_exp2(st[u][j] * a.sc - lse);   // selected, not branched on
-        dsb[4 * u + j] = (bf16)(visible(ql, kl, L, W) ? e * (dp[u][j] - dvec) : 0.f);
-      }
-#pragma unroll
-    for (int rt = 0; rt < DQK / 16; ++rt) dq[rt] = mfma16(tr_cols(KT + (16 * rt + r16) * T_LD, q4), dsb, dq[rt]);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-
-  // dQ = c dS K; RoPE's backward on the rotary dims (pairs i, i + 32 of the
-  // rotary block sit in tiles rt and rt + 2 of the same lane)
-  if ((unsigned)ql < (unsigned)L) {
-    const int64_t row = tb + ql;
-#pragma unroll
-    for (int rt = 0; rt < DQK / 16; ++rt) dq[rt] *= a.scale;
-#pragma unroll
-    for (int rt = DN / 16; rt < DN / 16 + 2; ++rt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 16 * (rt - DN / 16) + 4 * q4 + j;
-        const float c = a.rope[(row * (DR / 2) + i) * 2], s = a.rope[(row * (DR / 2) + i) * 2 + 1];
-        const float g1 = dq[rt][j], g2 = dq[rt + 2][j];
-        dq[rt][j] = g1 * c + g2 * s;
-        dq[rt + 2][j] = g2 * c - g1 * s;
-      }
-    bf16* out = a.dq + row * a.ld_dq + head * DQK;
-#pragma unroll
-    for (int rt = 0; rt < DQK / 16; ++rt) {
-      bf16x4 v;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = (bf16)dq[rt][j];
-      *reinterpret_cast<bf16x4*>(out + 16 * rt + 4 * q4) = v;
-    }
-  }
 }
 
 // dK, dV: workgroup = (sequence, KV group n, 128 keys), wave = 16 keys; the
@@ -570,6 +432,211 @@ attn_bwd_dkv_kernel(AttnBwdArgs a) {
   }
 }
 
+// ------------------------------------------------------------ attention backward on 32x32x16
+// Streamed tiles of 32 rows x C 16-byte chunks (C = 24: d_qk wide, C = 16:
+// d_v wide), unpadded, chunk c of row r at position c ^ sw32<C>(r).  Two
+// kinds of reads hit them:
+//  (a) A-operand rows of a 32x32x16 product: lane l reads tile row
+//      perm32(l % 32), chunk 2 s + (l >> 5) (16 bytes);
+//  (b) the tile read transposed (ds_read_b64_tr_b16): in each 16-lane group a
+//      4 x 16 block of (rows, dims) goes out one dim per lane, so lane l gets
+//      dim 32 mt + (l % 32) of rows 16 s + 8 (l >> 5) + 4 t + 0..3 (t = 0, 1).
+// gfx950 serves a 16-byte read in passes of 16 lanes (lanes 32 h + 4 j + i,
+// i < 4, parity of j fixed) and an 8-byte read in passes of 32 lanes; the
+// swizzles were searched so that every pass of both kinds hits distinct
+// 16-byte (8-byte) slots modulo 256 bytes.
+template <int C>
+GDLA_DEV int sw32(int r) {
+  if constexpr (C == 24) return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
+  else return (r & 3) | (((r ^ (r >> 2)) & 3) << 2);
+}
+// Score rows: the product's D row rho is tile row perm32(rho) (bits 2 and 3
+// swapped), so a lane's score registers (i, j) of k-half s' = i >> 1 are
+// rows 16 s' + 8 (l >> 5) + 4 (i & 1) + j: exactly the B operand of the next
+// product over those rows, element 4 (i & 1) + j.
+GDLA_DEV int perm32(int r) { return (r & 19) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+template <int C, int NW>
+struct Tile32 {
+  static constexpr int BLK = C / 2, NI = (BLK + NW - 1) / NW;
+  static constexpr int BYTES = BLK * 1024;
+  int row[NI], chunk[NI];   // the (row, chunk) this lane fetches for block wave + NW i
+  GDLA_DEV void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int pos = (wave + NW * i) * 64 + lane;
+      const int r = pos / C;
+      row[i] = pos < 32 * C ? r : 0;
+      chunk[i] = pos < 32 * C ? (pos % C) ^ sw32<C>(r) : 0;
+    }
+  }
+  template <class Src>
+  GDLA_DEV void issue(unsigned char* lds, int wave, Src src) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int blk = wave + NW * i;
+      if (blk < BLK) g2lds16(src(i), lds + blk * 1024);
+    }
+  }
+  GDLA_DEV static int off(int r, int c) { return r * C * 16 + ((c ^ sw32<C>(r)) << 4); }
+  // (a): byte offsets of chunk 2 s + hi of row perm32(l32), s < C / 2
+  GDLA_DEV static void a_offsets(int l32, int hi, int (&o)[C / 2]) {
+#pragma unroll
+    for (int s = 0; s < C / 2; ++s) o[s] = off(perm32(l32), 2 * s + hi);
+  }
+  // (b): byte offset of this lane's 8-byte piece for dims block mt, rows
+  // 16 sp + 8 hi + 4 t (.. + 3); lane (g = (l >> 4) & 1, i = l & 15) points at
+  // row + (i >> 2), dims 32 mt + 16 g + 4 (i & 3)
+  GDLA_DEV static int b_offset(int mt, int sp, int t, int hi, int g, int i16) {
+    const int r = 16 * sp + 8 * hi + 4 * t + (i16 >> 2);
+    return off(r, 4 * mt + 2 * g + ((i16 & 3) >> 1)) + 8 * (i16 & 1);
+  }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// two transposed 8-byte reads (rows +0..3 at p0, +4..7 at p1) as one A operand
+GDLA_DEV bf16x8 tr_a(const unsigned char* p0, const unsigned char* p1) {
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p0);
+  const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p1);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 c = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// dQ: workgroup = (sequence, KV group n, 32 queries), wave = head slot (its 32
+// queries).  Key tiles of 32 rows stream through LDS: K rows (score A operand
+// and, read transposed, the dQ A operand) and V rows (dP A operand).
+template <int G>
+__global__ void __launch_bounds__(64 * (G + 1), 2)
+attn_bwd_dq32_kernel(AttnBwdArgs a) {
+  constexpr int NW = G + 1;
+  using TK = Tile32<DQK / 8, NW>;
+  using TV = Tile32<DV / 8, NW>;
+  constexpr int BUF = TK::BYTES + TV::BYTES;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5, g = (lane >> 4) & 1, i16 = lane & 15;
+  const int nN = a.nN, nS = G * nN, H = nS + nN, L = a.L, W = a.window;
+  const int nqb = cdiv(L, 32);
+  const int qb = blockIdx.x % nqb, rest = blockIdx.x / nqb, n = rest % nN, b = rest / nN;
+  const int64_t tb = (int64_t)b * L, T = a.T;
+  const int head = w < G ? n * G + w : nS + n;
+  const int q0 = qb * 32, ql = q0 + l32;                  // this lane's query (score column)
+  const int64_t qrow = tb + min(ql, L - 1);
+
+  bf16x8 qf[DQK / 16], dhf[DV / 16];
+#pragma unroll
+  for (int s = 0; s < DQK / 16; ++s)
+    qf[s] = *reinterpret_cast<const bf16x8*>(a.q + qrow * a.ld_q + head * DQK + 16 * s + 8 * hi);
+#pragma unroll
+  for (int s = 0; s < DV / 16; ++s)
+    dhf[s] = *reinterpret_cast<const bf16x8*>(a.dh + qrow * H * DV + head * DV + 16 * s + 8 * hi);
+  const float lse = a.lse[qrow * H + head], dvec = a.dvec[qrow * H + head];
+
+  const int k_lo = W > 0 ? max(0, q0 - W + 1) : 0, k_hi = min(L, q0 + 32);
+  const int t_lo = (int)((tb + k_lo) / TR), t_hi = (int)cdiv(tb + k_hi, (int64_t)TR);
+  const int koff = n * DN, voff = nN * DN + n * DV;
+
+  TK tk;
+  TV tv;
+  tk.init(w, lane);
+  tv.init(w, lane);
+  // (a) offsets: K rows (C = 24, swizzle < 8) repeat every 4 sub-steps at +128 bytes
+  int ka[4], va[DV / 16];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) ka[v] = TK::off(perm32(l32), 2 * v + hi);
+  TV::a_offsets(l32, hi, va);
+  int kb4[4];   // transposed reads: [mt & 1][t], mt >> 1 and sp as immediate offsets
+#pragma unroll
+  for (int x = 0; x < 4; ++x) kb4[x] = TK::b_offset(x >> 1, 0, x & 1, hi, g, i16);
+  const bf16* kvo = a.kv + koff;
+  const bf16* vo = a.kv + voff;
+  auto load = [&](int tile, int buf) {
+    unsigned char* base = smem + buf * BUF;
+    const int64_t r0 = (int64_t)tile * TR;
+    const int rmax = (int)min((int64_t)TR - 1, T - 1 - r0);   // rows past the stream repeat its last row
+    const bf16* kvr = kvo + r0 * a.ld_kv;
+    const bf16* krr = a.kr + r0 * DR;
+    tk.issue(base, w, [&](int i) -> const void* {
+      const int r = min(tk.row[i], rmax), c = tk.chunk[i];
+      return c < DN / 8 ? (const void*)(kvr + r * (int)a.ld_kv + 8 * c) : (const void*)(krr + r * DR + 8 * c - DN);
+    });
+    const bf16* vr = vo + r0 * a.ld_kv;
+    tv.issue(base + TK::BYTES, w, [&](int i) -> const void* {
+      return vr + min(tv.row[i], rmax) * (int)a.ld_kv + 8 * tv.chunk[i];
+    });
+  };
+
+  f32x16 dq[DQK / 32];
+#pragma unroll
+  for (int i = 0; i < DQK / 32; ++i) dq[i] = f32x16{};
+
+  load(t_lo, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int tile = t_lo; tile < t_hi; ++tile) {
+    const int buf = (tile - t_lo) & 1;
+    if (tile + 1 < t_hi) load(tile + 1, buf ^ 1);
+    const unsigned char* Kt = smem + buf * BUF;
+    const unsigned char* Vt = Kt + TK::BYTES;
+    const int kb = (int)((int64_t)tile * TR - tb);   // first key of the tile, within the sequence
+    f32x16 st = {}, dp = {};
+#pragma unroll
+    for (int s = 0; s < DQK / 16; ++s)
+      st = mfma32(*reinterpret_cast<const bf16x8*>(Kt + ka[s & 3] + 128 * (s >> 2)), qf[s], st);
+#pragma unroll
+    for (int s = 0; s < DV / 16; ++s) dp = mfma32(*reinterpret_cast<const bf16x8*>(Vt + va[s]), dhf[s], dp);
+    // dS^T = P^T (dP^T - rowsum(dH H)); register (i, j) is key kb + 16 (i >> 1) + 8 hi + 4 (i & 1) + j
+    bf16x8 ds[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kl = kb + 16 * (i >> 1) + 8 * hi + 4 * (i & 1) + j;
+        const float e = fast_exp2(st[4 * i + j] * a.sc - lse);   // selected, not branched on
+        ds[i >> 1][4 * (i & 1) + j] = (bf16)(visible(ql, kl, L, W) ? e * (dp[4 * i + j] - dvec) : 0.f);
+      }
+    // dQ^T += K^T dS^T, K^T read transposed from the K rows
+#pragma unroll
+    for (int mt = 0; mt < DQK / 32; ++mt)
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        const unsigned char* p = Kt + 128 * (mt >> 1) + 32 * DQK * sp;   // 16 rows of 384 bytes per sp
+        dq[mt] = mfma32(tr_a(p + kb4[2 * (mt & 1)], p + kb4[2 * (mt & 1) + 1]), ds[sp], dq[mt]);
+      }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // dQ = c dS K; RoPE's backward on the rotary dims: dims 128 + p and 160 + p
+  // sit in blocks 4 and 5 at the same register (p = 8 i + 4 hi + j)
+  if ((unsigned)ql < (unsigned)L) {
+    const int64_t row = tb + ql;
+#pragma unroll
+    for (int mt = 0; mt < DQK / 32; ++mt) dq[mt] *= a.scale;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = 8 * i + 4 * hi + j;
+        const float c = a.rope[(row * (DR / 2) + p) * 2], s = a.rope[(row * (DR / 2) + p) * 2 + 1];
+        const float g1 = dq[DN / 32][4 * i + j], g2 = dq[DN / 32 + 1][4 * i + j];
+        dq[DN / 32][4 * i + j] = g1 * c + g2 * s;
+        dq[DN / 32 + 1][4 * i + j] = g2 * c - g1 * s;
+      }
+    bf16* out = a.dq + row * a.ld_dq + head * DQK;
+#pragma unroll
+    for (int mt = 0; mt < DQK / 32; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bf16x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = (bf16)dq[mt][4 * i + j];
+        *reinterpret_cast<bf16x4*>(out + 32 * mt + 8 * i + 4 * hi) = v;
+      }
+  }
+}
+
 // ------------------------------------------------------------ RMSNorm, RoPE, gains
 struct PrepBwdArgs {
   const float* down; int64_t ld_down;   // [T, ...]: raw c_Q | c_KV (the forward's fp32 down-projection)
@@ -677,21 +744,19 @@ hipError_t set_lds(K kernel, size_t bytes) {
 
 template <int G>
 hipError_t attn_bwd_g(const AttnBwdArgs& a, hipStream_t s) {
-  constexpr int NWQ = 2 * (G + 1);
-  constexpr size_t dq_lds = 2 * (size_t)(SwzStage<TR, DQK / 8, NWQ>::BYTES + SwzStage<TR, DV / 8, NWQ>::BYTES +
-                                         Stage<DQK, TR / 8, NWQ>::BYTES);
+  constexpr size_t dq_lds = 2 * (size_t)(Tile32<DQK / 8, G + 1>::BYTES + Tile32<DV / 8, G + 1>::BYTES);
   constexpr size_t dkv_lds = 2 * (size_t)(SwzStage<TR, DQK / 8, DKV_NW>::BYTES + SwzStage<TR, DV / 8, DKV_NW>::BYTES +
                                           Stage<DQK, TR / 8, DKV_NW>::BYTES + Stage<DV, TR / 8, DKV_NW>::BYTES +
                                           2 * TR * 4);
   static bool attr = false;
   hipError_t e;
   if (!attr) {
-    if ((e = set_lds(attn_bwd_dq_kernel<G>, dq_lds)) != hipSuccess) return e;
+    if ((e = set_lds(attn_bwd_dq32_kernel<G>, dq_lds)) != hipSuccess) return e;
     if ((e = set_lds(attn_bwd_dkv_kernel<G>, dkv_lds)) != hipSuccess) return e;
     attr = true;
   }
   const int64_t gq = (int64_t)a.B * a.nN * cdiv(a.L, 32), gk = (int64_t)a.B * a.nN * cdiv(a.L, DKV_KEYS);
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<G>, dim3((unsigned)gq), dim3(128 * (G + 1)), dq_lds, s, a);
+  hipLaunchKernelGGL(attn_bwd_dq32_kernel<G>, dim3((unsigned)gq), dim3(64 * (G + 1)), dq_lds, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(attn_bwd_dkv_kernel<G>, dim3((unsigned)gk), dim3(64 * DKV_NW), dkv_lds, s, a);
   return hipGetLastError();
@@ -745,7 +810,6 @@ BackwardLayout backward_layout(const BwdDims& D, int64_t T) {
   P.dhT = take((size_t)D.H * DV * Tp * 2);
   P.dvec = take((size_t)T * D.H * 4);
   P.qT = take((size_t)D.nq * Tp * 2);
-  P.krT = take((size_t)DR * Tp * 2);
   P.dqg = take((size_t)T * nqg * 2);
   P.dkv = take((size_t)T * nkv * 2);
   P.dkrp = take((size_t)D.nN * T * DR * 4);
@@ -880,13 +944,12 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
   if ((e = transpose_bf16(ws + P.q, D.nq, ws + P.qT, Tp, (int)T, (int)D.nq, (int)Tp, s)) != hipSuccess) return e;
   if ((e = transpose_bf16(ws + P.dh, D.H * DV, ws + P.dhT, Tp, (int)T, (int)(D.H * DV), (int)Tp, s)) != hipSuccess)
     return e;
-  if ((e = transpose_bf16(ws + P.kr, DR, ws + P.krT, Tp, (int)T, DR, (int)Tp, s)) != hipSuccess) return e;
   {
     AttnBwdArgs a{};
     a.q = (const bf16*)(ws + P.q); a.ld_q = D.nq;
     a.kv = (const bf16*)(ws + P.kv); a.ld_kv = nkv;
     a.kr = (const bf16*)(ws + P.kr);
-    a.kvT = (const bf16*)(ws + P.kvT); a.krT = (const bf16*)(ws + P.krT); a.qT = (const bf16*)(ws + P.qT);
+    a.qT = (const bf16*)(ws + P.qT);
     a.dhT = (const bf16*)(ws + P.dhT); a.ld_t = Tp;
     a.dh = (const bf16*)(ws + P.dh);
     a.lse = (const float*)(ws + P.lse); a.dvec = (const float*)(ws + P.dvec);
