@@ -19,7 +19,7 @@ struct BackwardLayout {
   int64_t Tp, ndp, prep_blocks;
   size_t down, cqn, ckvn, kr, lam, rope, q, gate, kv, kvT, z, hall, lse;
   size_t woT, wuqgT, wukvT, wdownT;
-  size_t dz, dyT, zT, dh, dhT, dvec, qT, dqg, dkv, dkrp, dcqn, dckvn, dqgT, cqnT, dkvT, ckvnT, ddown, ddownT, xT,
+  size_t dz, dyT, zT, dh, dvec, dqg, dkv, dkrp, dcqn, dckvn, dqgT, cqnT, dkvT, ckvnT, ddown, ddownT, xT,
       gpart;
   size_t total;
 };

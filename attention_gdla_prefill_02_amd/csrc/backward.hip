@@ -37,59 +37,33 @@ namespace {
 
 constexpr int DN = 128, DR = 64, DQK = DN + DR, DV = 128;
 constexpr int TR = 32;                    // rows of a streamed tile (keys or queries)
-constexpr int T_LD = TR + 8;              // LDS row of a transposed [dim][32 rows] tile
-
-// 8 bf16 of a transposed tile row: columns 4q..4q+3 and 16+4q..16+4q+3
-GDLA_DEV bf16x8 tr_cols(const bf16* row, int q4) {
-  const bf16x4 a = *reinterpret_cast<const bf16x4*>(row + 4 * q4);
-  const bf16x4 b = *reinterpret_cast<const bf16x4*>(row + 16 + 4 * q4);
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// gfx950 transposing LDS read: in each group of 16 lanes, lane i points at 4
+// consecutive 16-bit values (row i >> 2 of a 4 x 16 block, columns
+// 4 (i & 3) .. + 3) and receives column i of the block, rows 0..3.  Two such
+// reads (rows +0..3 at p0, another 4 rows at p1) make one 8-element MFMA
+// operand.
+GDLA_DEV bf16x8 tr_a(const unsigned char* p0, const unsigned char* p1) {
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p0);
+  const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p1);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 c = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(bf16x8, c);
 }
-
-// A tile of R rows of C 16-byte chunks staged into LDS rows of C + 1 chunks
-// (the last is padding), 1 KB per load instruction: lane i of a block writes
-// LDS bytes 16i.. of that block, so each lane fetches the chunk that belongs
-// there.  The region is rounded up to whole blocks, so lanes past the tile
-// write into its slack instead of being switched off.  Wave w issues blocks
-// w, w + NW, ...; the (row, chunk) of each of the lane's blocks is computed
-// once per kernel.
-template <int R, int C, int NW>
-struct Stage {
-  static constexpr int CH = R * (C + 1), BLK = (CH + 63) / 64, NI = (BLK + NW - 1) / NW;
-  static constexpr int BYTES = BLK * 1024;
-  int row[NI], chunk[NI];   // chunk C (the pad) and lanes past the tile read chunk 0
-  GDLA_DEV void init(int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int pos = (wave + NW * i) * 64 + lane;
-      const int r = pos / (C + 1), c = pos % (C + 1);
-      row[i] = pos < CH ? r : 0;
-      chunk[i] = pos < CH && c < C ? c : 0;
-    }
-  }
-  // src(i) gives the global address of block i's chunk for this lane
-  template <class Src>
-  GDLA_DEV void issue(unsigned char* lds, int wave, Src src) const {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int blk = wave + NW * i;
-      if (blk < BLK) g2lds16(src(i), lds + blk * 1024);
-    }
-  }
-};
 
 // Rows of C = 24 or 16 chunks (d_qk or d_v wide) staged without padding, chunk
 // c of row r at position c ^ swz(r) of the row.  gfx950 serves a 16-byte LDS
 // read in four passes of 16 lanes (lanes 32h + 4j + i, i < 4, with the parity
-// of j fixed); a fragment read of these kernels has lane l on row l & 15
-// (+16) and chunk 4s + (l >> 4), so a pass touches rows {0-3, 8-11} or
-// {4-7, 12-15} at two adjacent chunks.  The swizzle sends those 16 reads to 16
-// distinct 16-byte slots modulo 256 bytes (a padded row leaves 2-way
-// conflicts); it flips chunk bits 1-2 (24-chunk rows) or 1-3 (16-chunk rows),
-// so each row keeps its own chunks.
+// of j fixed) and an 8-byte read in two passes of 32 lanes.  These tiles are
+// read two ways: 16-byte fragment reads with lane l on row l & 15 (+16) and
+// chunk 4s + (l >> 4), and transposed 8-byte reads with lane l on row
+// 4 (l >> 4) + ((l & 15) >> 2) (+16) and chunk 2 rt + ((l & 3) >> 1).  The
+// swizzle (found by search) sends every pass of both kinds to distinct slots
+// modulo 256 bytes; it does not depend on row bit 4, so the two 16-row halves
+// share offsets.
 template <int C>
 GDLA_DEV int swz(int r) {
-  return C == 24 ? 2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1) : 2 * (r & 3) + 8 * ((r >> 3) & 1);
+  return C == 24 ? (r & 6) : ((r & 7) << 1);
 }
 
 template <int R, int C, int NW>
@@ -234,7 +208,6 @@ struct AttnBwdArgs {
   const bf16* q; int64_t ld_q;          // [T, H*d_qk], rotary parts RoPE'd
   const bf16* kv; int64_t ld_kv;        // [T, nN*d_nope | nN*d_v]: K^C, then V
   const bf16* kr;                       // [T, d_rope]
-  const bf16* qT; const bf16* dhT; int64_t ld_t;   // transposed, [dim][Tp]
   const bf16* dh;                       // [T, H*d_v]
   const float* lse; const float* dvec;  // [T, H]
   const float* rope;                    // [T, d_rope/2, 2]
@@ -251,8 +224,8 @@ GDLA_DEV bool visible(int ql, int kl, int L, int W) {
 
 // dK, dV: workgroup = (sequence, KV group n, 128 keys), wave = 16 keys; the
 // workgroup sweeps (query tile, head) pairs, staging per pair the head's Q and
-// dH rows (score and dP A operands), Q^T and dH^T (dK and dV A operands),
-// and the rows' log-sum-exp and rowsum(dH H).
+// dH rows (score and dP A operands; read transposed, the dK and dV A
+// operands) and the rows' log-sum-exp and rowsum(dH H).
 constexpr int DKV_KEYS = 128, DKV_NW = DKV_KEYS / 16;
 
 template <int G>
@@ -261,11 +234,8 @@ attn_bwd_dkv_kernel(AttnBwdArgs a) {
   constexpr int NW = DKV_NW;
   using SQ = SwzStage<TR, DQK / 8, NW>;
   using SD = SwzStage<TR, DV / 8, NW>;
-  using SQT = Stage<DQK, TR / 8, NW>;
-  using SDT = Stage<DV, TR / 8, NW>;
-  constexpr int Q_BYTES = SQ::BYTES, DH_BYTES = SD::BYTES, QT_BYTES = SQT::BYTES, DHT_BYTES = SDT::BYTES,
-                ST_BYTES = 2 * TR * 4;
-  constexpr int BUF = Q_BYTES + DH_BYTES + QT_BYTES + DHT_BYTES + ST_BYTES;
+  constexpr int Q_BYTES = SQ::BYTES, DH_BYTES = SD::BYTES, ST_BYTES = 2 * TR * 4;
+  constexpr int BUF = Q_BYTES + DH_BYTES + ST_BYTES;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
@@ -294,15 +264,22 @@ attn_bwd_dkv_kernel(AttnBwdArgs a) {
 
   SQ sq;
   SD sd;
-  SQT sqt;
-  SDT sdt;
   sq.init(w, lane);
   sd.init(w, lane);
-  sqt.init(w, lane);
-  sdt.init(w, lane);
   int qro[DQK / 32], dro[DV / 32];   // fragment read offsets (elements) in the Q and dH row tiles
   SQ::read_offsets(r16, q4, qro);
   SD::read_offsets(r16, q4, dro);
+  // transposed reads (bytes): row 4 q4 + (r16 >> 2) (+16 for the second half),
+  // chunk 2 rt + ((r16 & 3) >> 1), half r16 & 1; the Q swizzle (< 8) repeats
+  // every 4 rt at +128 bytes
+  int qtr[4], dtr[DV / 16];
+  {
+    const int r = 4 * q4 + (r16 >> 2), c0 = (r16 & 3) >> 1, half = 8 * (r16 & 1);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) qtr[x] = r * DQK * 2 + (((2 * x + c0) ^ swz<DQK / 8>(r)) << 4) + half;
+#pragma unroll
+    for (int x = 0; x < DV / 16; ++x) dtr[x] = r * DV * 2 + (((2 * x + c0) ^ swz<DV / 8>(r)) << 4) + half;
+  }
   auto load = [&](int step, int buf) {
     const int tile = t_lo + step / (G + 1), hs = step % (G + 1);
     const int head = hs < G ? n * G + hs : nS + n;
@@ -313,12 +290,6 @@ attn_bwd_dkv_kernel(AttnBwdArgs a) {
     sq.issue(base, w, [&](int i) -> const void* { return qr + min(sq.row[i], rmax) * (int)a.ld_q + 8 * sq.chunk[i]; });
     const bf16* dr = a.dh + r0 * H * DV + head * DV;
     sd.issue(base + Q_BYTES, w, [&](int i) -> const void* { return dr + min(sd.row[i], rmax) * H * DV + 8 * sd.chunk[i]; });
-    const bf16* qto = a.qT + (int64_t)head * DQK * a.ld_t + r0;
-    sqt.issue(base + Q_BYTES + DH_BYTES, w,
-              [&](int i) -> const void* { return qto + (int64_t)sqt.row[i] * a.ld_t + 8 * sqt.chunk[i]; });
-    const bf16* dto = a.dhT + (int64_t)head * DV * a.ld_t + r0;
-    sdt.issue(base + Q_BYTES + DH_BYTES + QT_BYTES, w,
-              [&](int i) -> const void* { return dto + (int64_t)sdt.row[i] * a.ld_t + 8 * sdt.chunk[i]; });
   };
   // the rows' log-sum-exp and rowsum(dH H) go through registers (strided in HBM)
   float st_lse = 0.f, st_dv = 0.f;
@@ -332,7 +303,7 @@ attn_bwd_dkv_kernel(AttnBwdArgs a) {
     }
   };
   auto store_stats = [&](int buf) {
-    float* st = reinterpret_cast<float*>(smem + buf * BUF + Q_BYTES + DH_BYTES + QT_BYTES + DHT_BYTES);
+    float* st = reinterpret_cast<float*>(smem + buf * BUF + Q_BYTES + DH_BYTES);
     if (tid < TR) {
       st[tid] = st_lse;
       st[TR + tid] = st_dv;
@@ -366,9 +337,7 @@ attn_bwd_dkv_kernel(AttnBwdArgs a) {
       const unsigned char* base = smem + buf * BUF;
       const bf16* Qt = reinterpret_cast<const bf16*>(base);
       const bf16* Dt = reinterpret_cast<const bf16*>(base + Q_BYTES);
-      const bf16* QT = reinterpret_cast<const bf16*>(base + Q_BYTES + DH_BYTES);
-      const bf16* DT = reinterpret_cast<const bf16*>(base + Q_BYTES + DH_BYTES + QT_BYTES);
-      const float* st = reinterpret_cast<const float*>(base + Q_BYTES + DH_BYTES + QT_BYTES + DHT_BYTES);
+      const float* st = reinterpret_cast<const float*>(base + Q_BYTES + DH_BYTES);
       // S (queries x this wave's keys) and dP = dH V^T
       f32x4 s_[2], dp[2];
 #pragma unroll
@@ -397,9 +366,15 @@ attn_bwd_dkv_kernel(AttnBwdArgs a) {
         }
       }
 #pragma unroll
-      for (int rt = 0; rt < DV / 16; ++rt) dv[rt] = mfma16(tr_cols(DT + (16 * rt + r16) * T_LD, q4), pb, dv[rt]);
+      for (int rt = 0; rt < DV / 16; ++rt) {
+        const unsigned char* p = base + Q_BYTES + dtr[rt];
+        dv[rt] = mfma16(tr_a(p, p + 16 * DV * 2), pb, dv[rt]);
+      }
 #pragma unroll
-      for (int rt = 0; rt < DQK / 16; ++rt) dk[rt] = mfma16(tr_cols(QT + (16 * rt + r16) * T_LD, q4), dsb, dk[rt]);
+      for (int rt = 0; rt < DQK / 16; ++rt) {
+        const unsigned char* p = base + qtr[rt & 3] + 128 * (rt >> 2);
+        dk[rt] = mfma16(tr_a(p, p + 16 * DQK * 2), dsb, dk[rt]);
+      }
     }
     if (step + 1 < steps) store_stats(buf ^ 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -493,15 +468,6 @@ struct Tile32 {
   }
 };
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-// two transposed 8-byte reads (rows +0..3 at p0, +4..7 at p1) as one A operand
-GDLA_DEV bf16x8 tr_a(const unsigned char* p0, const unsigned char* p1) {
-  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p0);
-  const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p1);
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const s16x8 c = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-  return __builtin_bit_cast(bf16x8, c);
-}
 
 // dQ: workgroup = (sequence, KV group n, 32 queries), wave = head slot (its 32
 // queries).  Key tiles of 32 rows stream through LDS: K rows (score A operand
@@ -745,9 +711,8 @@ hipError_t set_lds(K kernel, size_t bytes) {
 template <int G>
 hipError_t attn_bwd_g(const AttnBwdArgs& a, hipStream_t s) {
   constexpr size_t dq_lds = 2 * (size_t)(Tile32<DQK / 8, G + 1>::BYTES + Tile32<DV / 8, G + 1>::BYTES);
-  constexpr size_t dkv_lds = 2 * (size_t)(SwzStage<TR, DQK / 8, DKV_NW>::BYTES + SwzStage<TR, DV / 8, DKV_NW>::BYTES +
-                                          Stage<DQK, TR / 8, DKV_NW>::BYTES + Stage<DV, TR / 8, DKV_NW>::BYTES +
-                                          2 * TR * 4);
+  constexpr size_t dkv_lds =
+      2 * (size_t)(SwzStage<TR, DQK / 8, DKV_NW>::BYTES + SwzStage<TR, DV / 8, DKV_NW>::BYTES + 2 * TR * 4);
   static bool attr = false;
   hipError_t e;
   if (!attr) {
@@ -807,9 +772,7 @@ BackwardLayout backward_layout(const BwdDims& D, int64_t T) {
   P.dyT = take((size_t)D.d * Tp * 2);
   P.zT = take((size_t)D.ngate * Tp * 2);
   P.dh = take((size_t)T * D.H * DV * 2);
-  P.dhT = take((size_t)D.H * DV * Tp * 2);
   P.dvec = take((size_t)T * D.H * 4);
-  P.qT = take((size_t)D.nq * Tp * 2);
   P.dqg = take((size_t)T * nqg * 2);
   P.dkv = take((size_t)T * nkv * 2);
   P.dkrp = take((size_t)D.nN * T * DR * 4);
@@ -940,17 +903,12 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     hipLaunchKernelGGL(epi_bwd_kernel, dim3((unsigned)cdiv(T, 4)), dim3(256), 0, s, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // 5. attention backward (transposed Q, dH and k_R staged first)
-  if ((e = transpose_bf16(ws + P.q, D.nq, ws + P.qT, Tp, (int)T, (int)D.nq, (int)Tp, s)) != hipSuccess) return e;
-  if ((e = transpose_bf16(ws + P.dh, D.H * DV, ws + P.dhT, Tp, (int)T, (int)(D.H * DV), (int)Tp, s)) != hipSuccess)
-    return e;
+  // 5. attention backward
   {
     AttnBwdArgs a{};
     a.q = (const bf16*)(ws + P.q); a.ld_q = D.nq;
     a.kv = (const bf16*)(ws + P.kv); a.ld_kv = nkv;
     a.kr = (const bf16*)(ws + P.kr);
-    a.qT = (const bf16*)(ws + P.qT);
-    a.dhT = (const bf16*)(ws + P.dhT); a.ld_t = Tp;
     a.dh = (const bf16*)(ws + P.dh);
     a.lse = (const float*)(ws + P.lse); a.dvec = (const float*)(ws + P.dvec);
     a.rope = (const float*)(ws + P.rope);
