@@ -241,6 +241,105 @@ latent_norm_kernel(LatentNormArgs a) {
   }
 }
 
+
+// bf16 rows whose latent widths are multiples of 256: the same steps with
+// 16-byte loads of the fp32 row (kept in registers between the sum of squares
+// and the scaling) and 8-byte bf16 stores, each lane owning 4 consecutive
+// columns of every 256-column group.
+constexpr int VEC_QMAX = 8, VEC_KMAX = 4;   // q_rank <= 2048, kv_rank <= 1024
+__global__ void __launch_bounds__(256)
+rowprep_vec_kernel(RowPrepArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const float* row = a.down + t * a.ld_down;
+  const int nq = a.q_rank / 256, nk = a.kv_rank / 256;
+  f32x4 vq[VEC_QMAX], vk[VEC_KMAX];
+#pragma unroll
+  for (int k = 0; k < VEC_QMAX; ++k)
+    if (k < nq) vq[k] = *reinterpret_cast<const f32x4*>(row + 256 * k + 4 * lane);
+#pragma unroll
+  for (int k = 0; k < VEC_KMAX; ++k)
+    if (k < nk) vk[k] = *reinterpret_cast<const f32x4*>(row + a.q_rank + 256 * k + 4 * lane);
+  const bf16* gq = (const bf16*)a.g_q;
+  const bf16* gkv = (const bf16*)a.g_kv;
+  int64_t p;
+  bf16* crow = locate_row<bf16>(a, t, &p);
+
+  // query latent
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < VEC_QMAX; ++k)
+    if (k < nq) ss += vq[k][0] * vq[k][0] + vq[k][1] * vq[k][1] + vq[k][2] * vq[k][2] + vq[k][3] * vq[k][3];
+  float r = 1.0f / sqrtf(wave_sum(ss) / a.q_rank + a.eps);
+  bf16* cqn = (bf16*)a.cqn + t * a.q_rank;
+#pragma unroll
+  for (int k = 0; k < VEC_QMAX; ++k)
+    if (k < nq) {
+      const int c = 256 * k + 4 * lane;
+      const bf16x4 g = *reinterpret_cast<const bf16x4*>(gq + c);
+      bf16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (bf16)(vq[k][e] * r * (float)g[e]);
+      *reinterpret_cast<bf16x4*>(cqn + c) = o;
+    }
+
+  // KV latent (split rows [hi | lo] as in rowprep_kernel)
+  ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < VEC_KMAX; ++k)
+    if (k < nk) ss += vk[k][0] * vk[k][0] + vk[k][1] * vk[k][1] + vk[k][2] * vk[k][2] + vk[k][3] * vk[k][3];
+  r = 1.0f / sqrtf(wave_sum(ss) / a.kv_rank + a.eps);
+  bf16* ckvn = (bf16*)a.ckvn + t * (a.split_kv ? 2 * a.kv_rank : a.kv_rank);
+#pragma unroll
+  for (int k = 0; k < VEC_KMAX; ++k)
+    if (k < nk) {
+      const int c = 256 * k + 4 * lane;
+      const bf16x4 g = *reinterpret_cast<const bf16x4*>(gkv + c);
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f = vk[k][e] * r * (float)g[e];
+        hi[e] = (bf16)f;
+        lo[e] = (bf16)(f - (float)hi[e]);
+      }
+      *reinterpret_cast<bf16x4*>(ckvn + c) = hi;
+      if (a.split_kv) *reinterpret_cast<bf16x4*>(ckvn + a.kv_rank + c) = lo;
+      if (crow) *reinterpret_cast<bf16x4*>(crow + c) = hi;
+    }
+
+  // rotary key and the RoPE table of this position
+  const float* kr = row + a.q_rank + a.kv_rank;
+  const int half = a.d_rope / 2;
+  bf16* krow = (bf16*)a.kr + t * a.d_rope;
+  for (int i = lane; i < half; i += 64) {
+    float c, sn;
+    rope_cos_sin(a, i, p, &c, &sn);
+    *reinterpret_cast<float2*>(a.rope + (t * half + i) * 2) = float2{c, sn};
+    const float x1 = kr[i], x2 = kr[i + half];
+    const bf16 o1 = (bf16)(x1 * c - x2 * sn), o2 = (bf16)(x2 * c + x1 * sn);
+    krow[i] = o1;
+    krow[i + half] = o2;
+    if (crow) {
+      crow[a.kv_rank + i] = o1;
+      crow[a.kv_rank + i + half] = o2;
+    }
+  }
+
+  // lambda
+  const float* ll = kr + a.d_rope;
+  for (int i = lane; i < a.nS; i += 64) a.lam[t * a.nS + i] = sigmoidf_(ll[i]);
+}
+
+// the vector kernel's layout conditions
+bool rowprep_vec_ok(const RowPrepArgs& a) {
+  auto al = [](const void* q, int n) { return ((uintptr_t)q % n) == 0; };
+  return a.nsplit <= 1 && a.q_rank % 256 == 0 && a.q_rank / 256 <= VEC_QMAX && a.kv_rank % 256 == 0 &&
+         a.kv_rank / 256 <= VEC_KMAX && a.ld_down % 4 == 0 && al(a.down, 16) && al(a.g_q, 8) && al(a.g_kv, 8) &&
+         al(a.cqn, 8) && al(a.ckvn, 8) && al(a.rope, 8) && (a.cache.base == nullptr || (al(a.cache.base, 8) &&
+         (a.kv_rank + a.d_rope) % 4 == 0));
+}
+
 }  // namespace
 
 hipError_t rowprep(const RowPrepArgs& a, bool bf16, hipStream_t s) {
@@ -254,6 +353,10 @@ hipError_t rowprep(const RowPrepArgs& a, bool bf16, hipStream_t s) {
     return hipGetLastError();
   }
   dim3 grid((unsigned)cdiv(a.T, 4)), block(256);
+  if (bf16 && rowprep_vec_ok(a)) {
+    hipLaunchKernelGGL(rowprep_vec_kernel, grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   const size_t lds = a.nsplit > 1 ? 4 * (size_t)a.ld_down * sizeof(float) : 0;
   if (bf16)
     hipLaunchKernelGGL(rowprep_kernel<__bf16>, grid, block, lds, s, a);
