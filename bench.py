@@ -41,8 +41,8 @@ HBM_PEAK_GBS = 8000.0                # MI355X HBM3E
 # the ratio of bytes to counter reading of a device copy of known size timed in
 # the same pass (--copy-probe-mib).  Tied to the kernel source it was measured
 # on: reported as null once that source changes.
-ATTN_TRAFFIC = {"source_sha256": "7883de408d2d36528c57ae82f3459493457bc6412ce8e09f5142234e7aca1fe3",
-                "fetch_bytes": 4066677971, "write_bytes": 402653184}
+ATTN_TRAFFIC = {"source_sha256": "90e750f2ad773a2235d84752e565b637f082379830f00438c814a11d35a39306",
+                "fetch_bytes": 4067162928, "write_bytes": 402653184}
 ATTN_SOURCES = ("attention_gdla_prefill_02_amd/csrc/attn.hip", "attention_gdla_prefill_02_amd/csrc/common.h")
 
 
