@@ -453,6 +453,12 @@ struct Tile32 {
       if (blk < BLK) g2lds16(src(i), lds + blk * 1024);
     }
   }
+  // the (row, chunk) of block wave + NW i for this lane, recomputed (as init)
+  GDLA_DEV static void rc(int wave, int lane, int i, int& r, int& c) {
+    const int pos = (wave + NW * i) * 64 + lane;
+    r = pos < 32 * C ? pos / C : 0;
+    c = pos < 32 * C ? (pos % C) ^ sw32<C>(pos / C) : 0;
+  }
   GDLA_DEV static int off(int r, int c) { return r * C * 16 + ((c ^ sw32<C>(r)) << 4); }
   // (a): byte offsets of chunk 2 s + hi of row perm32(l32), s < C / 2
   GDLA_DEV static void a_offsets(int l32, int hi, int (&o)[C / 2]) {
@@ -505,8 +511,6 @@ attn_bwd_dq32_kernel(AttnBwdArgs a) {
 
   TK tk;
   TV tv;
-  tk.init(w, lane);
-  tv.init(w, lane);
   // (a) offsets: K rows (C = 24, swizzle < 8) repeat every 4 sub-steps at +128 bytes
   int ka[4], va[DV / 16];
 #pragma unroll
@@ -517,19 +521,49 @@ attn_bwd_dq32_kernel(AttnBwdArgs a) {
   for (int x = 0; x < 4; ++x) kb4[x] = TK::b_offset(x >> 1, 0, x & 1, hi, g, i16);
   const bf16* kvo = a.kv + koff;
   const bf16* vo = a.kv + voff;
+  // this lane's load sources at stream row 0 and the row stride of each (a K
+  // chunk comes from the content rows or the rotary rows); a full tile only
+  // adds its first row times the stride
+  const bf16* ksrc[TK::NI];
+  int kstr[TK::NI];
+#pragma unroll
+  for (int i = 0; i < TK::NI; ++i) {
+    int r, c;
+    TK::rc(w, lane, i, r, c);
+    const bool content = c < DN / 8;
+    ksrc[i] = content ? kvo + (int64_t)r * a.ld_kv + 8 * c : a.kr + (int64_t)r * DR + 8 * c - DN;
+    kstr[i] = content ? (int)a.ld_kv : DR;
+  }
+  const bf16* vsrc[TV::NI];
+#pragma unroll
+  for (int i = 0; i < TV::NI; ++i) {
+    int r, c;
+    TV::rc(w, lane, i, r, c);
+    vsrc[i] = vo + (int64_t)r * a.ld_kv + 8 * c;
+  }
   auto load = [&](int tile, int buf) {
     unsigned char* base = smem + buf * BUF;
     const int64_t r0 = (int64_t)tile * TR;
-    const int rmax = (int)min((int64_t)TR - 1, T - 1 - r0);   // rows past the stream repeat its last row
+    if (r0 + TR <= T) {
+      tk.issue(base, w, [&](int i) -> const void* { return ksrc[i] + r0 * kstr[i]; });
+      tv.issue(base + TK::BYTES, w, [&](int i) -> const void* { return vsrc[i] + r0 * a.ld_kv; });
+      return;
+    }
+    // the stream's last, partial tile: rows past the stream repeat its last row
+    const int rmax = (int)(T - 1 - r0);
     const bf16* kvr = kvo + r0 * a.ld_kv;
     const bf16* krr = a.kr + r0 * DR;
     tk.issue(base, w, [&](int i) -> const void* {
-      const int r = min(tk.row[i], rmax), c = tk.chunk[i];
+      int r, c;
+      TK::rc(w, lane, i, r, c);
+      r = min(r, rmax);
       return c < DN / 8 ? (const void*)(kvr + r * (int)a.ld_kv + 8 * c) : (const void*)(krr + r * DR + 8 * c - DN);
     });
     const bf16* vr = vo + r0 * a.ld_kv;
     tv.issue(base + TK::BYTES, w, [&](int i) -> const void* {
-      return vr + min(tv.row[i], rmax) * (int)a.ld_kv + 8 * tv.chunk[i];
+      int r, c;
+      TV::rc(w, lane, i, r, c);
+      return vr + min(r, rmax) * (int)a.ld_kv + 8 * c;
     });
   };
 
