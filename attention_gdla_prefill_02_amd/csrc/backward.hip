@@ -280,15 +280,26 @@ attn_bwd_dkv_kernel(AttnBwdArgs a) {
 #pragma unroll
     for (int x = 0; x < DV / 16; ++x) dtr[x] = r * DV * 2 + (((2 * x + c0) ^ swz<DV / 8>(r)) << 4) + half;
   }
+  // this lane's element offsets from a tile's first row (full tiles)
+  int qoff[SQ::NI], doff[SD::NI];
+#pragma unroll
+  for (int i = 0; i < SQ::NI; ++i) qoff[i] = sq.row[i] * (int)a.ld_q + 8 * sq.chunk[i];
+#pragma unroll
+  for (int i = 0; i < SD::NI; ++i) doff[i] = sd.row[i] * H * DV + 8 * sd.chunk[i];
   auto load = [&](int step, int buf) {
     const int tile = t_lo + step / (G + 1), hs = step % (G + 1);
     const int head = hs < G ? n * G + hs : nS + n;
     unsigned char* base = smem + buf * BUF;
     const int64_t r0 = (int64_t)tile * TR;
-    const int rmax = (int)min((int64_t)TR - 1, T - 1 - r0);   // rows past the stream repeat its last row
     const bf16* qr = a.q + r0 * a.ld_q + head * DQK;
-    sq.issue(base, w, [&](int i) -> const void* { return qr + min(sq.row[i], rmax) * (int)a.ld_q + 8 * sq.chunk[i]; });
     const bf16* dr = a.dh + r0 * H * DV + head * DV;
+    if (r0 + TR <= T) {
+      sq.issue(base, w, [&](int i) -> const void* { return qr + qoff[i]; });
+      sd.issue(base + Q_BYTES, w, [&](int i) -> const void* { return dr + doff[i]; });
+      return;
+    }
+    const int rmax = (int)(T - 1 - r0);   // the stream's last tile: rows past it repeat its last row
+    sq.issue(base, w, [&](int i) -> const void* { return qr + min(sq.row[i], rmax) * (int)a.ld_q + 8 * sq.chunk[i]; });
     sd.issue(base + Q_BYTES, w, [&](int i) -> const void* { return dr + min(sd.row[i], rmax) * H * DV + 8 * sd.chunk[i]; });
   };
   // the rows' log-sum-exp and rowsum(dH H) go through registers (strided in HBM)
