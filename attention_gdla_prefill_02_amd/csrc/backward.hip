@@ -446,25 +446,19 @@ template <int C, int NW>
 struct Tile32 {
   static constexpr int BLK = C / 2, NI = (BLK + NW - 1) / NW;
   static constexpr int BYTES = BLK * 1024;
-  int row[NI], chunk[NI];   // the (row, chunk) this lane fetches for block wave + NW i
-  GDLA_DEV void init(int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int pos = (wave + NW * i) * 64 + lane;
-      const int r = pos / C;
-      row[i] = pos < 32 * C ? r : 0;
-      chunk[i] = pos < 32 * C ? (pos % C) ^ sw32<C>(r) : 0;
-    }
-  }
+  // 1 KB load blocks wave, wave + NW, ...: lane l of block b writes LDS bytes
+  // [1024 b + 16 l, + 16), so it fetches the chunk whose position that is;
+  // src(i) gives that chunk's global address for block wave + NW i
   template <class Src>
-  GDLA_DEV void issue(unsigned char* lds, int wave, Src src) const {
+  GDLA_DEV static void issue(unsigned char* lds, int wave, Src src) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int blk = wave + NW * i;
       if (blk < BLK) g2lds16(src(i), lds + blk * 1024);
     }
   }
-  // the (row, chunk) of block wave + NW i for this lane, recomputed (as init)
+  // the (row, chunk) this lane fetches for block wave + NW i (lanes past the
+  // tile fetch row 0, chunk 0 of their block's slack)
   GDLA_DEV static void rc(int wave, int lane, int i, int& r, int& c) {
     const int pos = (wave + NW * i) * 64 + lane;
     r = pos < 32 * C ? pos / C : 0;
@@ -520,8 +514,6 @@ attn_bwd_dq32_kernel(AttnBwdArgs a) {
   const int t_lo = (int)((tb + k_lo) / TR), t_hi = (int)cdiv(tb + k_hi, (int64_t)TR);
   const int koff = n * DN, voff = nN * DN + n * DV;
 
-  TK tk;
-  TV tv;
   // (a) offsets: K rows (C = 24, swizzle < 8) repeat every 4 sub-steps at +128 bytes
   int ka[4], va[DV / 16];
 #pragma unroll
@@ -556,22 +548,22 @@ attn_bwd_dq32_kernel(AttnBwdArgs a) {
     unsigned char* base = smem + buf * BUF;
     const int64_t r0 = (int64_t)tile * TR;
     if (r0 + TR <= T) {
-      tk.issue(base, w, [&](int i) -> const void* { return ksrc[i] + r0 * kstr[i]; });
-      tv.issue(base + TK::BYTES, w, [&](int i) -> const void* { return vsrc[i] + r0 * a.ld_kv; });
+      TK::issue(base, w, [&](int i) -> const void* { return ksrc[i] + r0 * kstr[i]; });
+      TV::issue(base + TK::BYTES, w, [&](int i) -> const void* { return vsrc[i] + r0 * a.ld_kv; });
       return;
     }
     // the stream's last, partial tile: rows past the stream repeat its last row
     const int rmax = (int)(T - 1 - r0);
     const bf16* kvr = kvo + r0 * a.ld_kv;
     const bf16* krr = a.kr + r0 * DR;
-    tk.issue(base, w, [&](int i) -> const void* {
+    TK::issue(base, w, [&](int i) -> const void* {
       int r, c;
       TK::rc(w, lane, i, r, c);
       r = min(r, rmax);
       return c < DN / 8 ? (const void*)(kvr + r * (int)a.ld_kv + 8 * c) : (const void*)(krr + r * DR + 8 * c - DN);
     });
     const bf16* vr = vo + r0 * a.ld_kv;
-    tv.issue(base + TK::BYTES, w, [&](int i) -> const void* {
+    TV::issue(base + TK::BYTES, w, [&](int i) -> const void* {
       int r, c;
       TV::rc(w, lane, i, r, c);
       return vr + min(r, rmax) * (int)a.ld_kv + 8 * c;
