@@ -9,14 +9,14 @@
 // with A(t) = {s <= t} (full) or {t - W < s <= t} (window W).
 //
 // bf16 kernel (d_nope = 128, d_rope = 64, d_v = 128), one workgroup per
-// (sequence, KV head n, 64-query block; 32-query block when g = 4, with one
-// wave per head -- see halves() below):
-//  * 2(g+1) waves: wave w handles query head slot w/2 (g signal heads, then
-//    the noise head) for 32 consecutive queries.  All g+1 heads of the group
-//    read the same content key, rotary key and value, so each 64-key tile of
-//    [K^C | k_R] (64 x 192) and V^T (128 x 64) is staged in LDS once (double
-//    buffered, loads of tile j+1 in flight during tile j) and reused by every
-//    wave.
+// (sequence, KV head n, query block of 64; 32 when g = 4 -- see halves()):
+//  * 2(g+1) waves (g + 1 for g = 4): wave w handles query head slot w % (g+1)
+//    (g signal heads, then the noise head) for 32 consecutive queries.  All
+//    g+1 heads of the group read the same content key, rotary key and value,
+//    so each 32-key tile of [K^C | k_R] (32 x 192) and V^T (128 x 32) is
+//    staged in LDS once and reused by every wave.  Tiles go HBM -> LDS with
+//    global_load_lds (no register staging) into a three-slot ring: step t
+//    issues tile t+2's loads while it computes with tiles t and t+1.
 //  * Scores are formed transposed, S^T = K Q^T, on the 32x32x16 bf16 MFMA:
 //    the 192-wide key row is the A operand (read from LDS), the wave's query
 //    rows are the B operand held in registers for the whole sweep.  Each lane
@@ -31,12 +31,16 @@
 //    than 8 (so P <= 256); the decision is per query but the rescale branch is
 //    wave-uniform and rare after the first tiles.
 //  * Causal / window tile skipping: the workgroup walks only the key tiles
-//    that intersect [q0 - W + 1, q0 + 63]; masks are applied only on tiles
-//    that straddle a boundary, and a wave skips tiles none of its 32 queries
-//    sees.
+//    that intersect [q0 - W + 1, q0 + BQ - 1]; masks are applied only on
+//    tiles that straddle a boundary.  A wave computes every tile of the
+//    workgroup's range; on a tile none of its queries sees, the mask makes
+//    every P zero.
+//  * The two waves sharing a SIMD (query halves 0 and 1 of a head) order each
+//    step differently, so one runs its Q K^T MFMAs while the other runs the
+//    softmax on the vector ALU.
 //  * Epilogue: H = O / l; the noise waves publish H_N through LDS, the signal
 //    waves form gate * (H_S - lambda * H_N) in fp32 and stage bf16 Z rows in
-//    LDS, then the workgroup writes 64 contiguous Z rows (g*d_v wide) with
+//    LDS, then the workgroup writes BQ contiguous Z rows (g*d_v wide) with
 //    16-byte coalesced stores.
 //  * Workgroups are numbered so XCD x (blockIdx % 8) processes whole KV
 //    heads, query blocks in descending order (longest causal rows first);
@@ -57,7 +61,6 @@ constexpr int K_LD = DQK + 8;        // LDS row of a key (elements), padded
 constexpr int V_LD = BKV + 8;        // LDS row of V^T (one value dim, BKV keys)
 constexpr int K_TILE = BKV * K_LD;   // elements
 constexpr int V_TILE = DV * V_LD;
-constexpr int KV_CHUNKS = BKV * (DQK / 8) + DV * (BKV / 8);   // 16-byte chunks per tile
 constexpr float NEG_INIT = -1.0e30f;
 
 __host__ __device__ constexpr int z_ld(int g) { return g * DV + 8; }
@@ -457,13 +460,10 @@ attn_f32_kernel(AttnArgs a) {
 template <int G>
 hipError_t launch_g(const AttnArgs& a, hipStream_t s) {
   const size_t lds = lds_bytes(G);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<G>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set on every call: no process-wide state, and correct on every device
+  hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<G>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
   const int64_t slots = a.plan ? a.items_cap : (int64_t)a.B * cdiv(a.L, 32 * halves<G>());
   const int64_t blocks = slots * a.nN;
   if (blocks <= 0) return hipSuccess;
@@ -590,13 +590,9 @@ hipError_t attn_plan(const int32_t* cu, int nseq, int64_t T, int g, int* plan, h
   const int nlev = (int)((T + bq - 1) / bq);
   if (nlev + 1 + 2 * PLAN_THREADS > PLAN_LDS_INTS) return hipErrorInvalidValue;
   const size_t lds = ((size_t)nlev + 1 + 2 * PLAN_THREADS) * sizeof(int);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       PLAN_LDS_INTS * (int)sizeof(int));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = hipFuncSetAttribute((const void*)attn_plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     PLAN_LDS_INTS * (int)sizeof(int));
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(PLAN_THREADS), lds, s, cu, nseq, (int)T, bq, nlev, plan);
   return hipGetLastError();
 }

@@ -750,13 +750,9 @@ hipError_t attn_bwd_g(const AttnBwdArgs& a, hipStream_t s) {
   constexpr size_t dq_lds = 2 * (size_t)(Tile32<DQK / 8, G + 1>::BYTES + Tile32<DV / 8, G + 1>::BYTES);
   constexpr size_t dkv_lds =
       2 * (size_t)(SwzStage<TR, DQK / 8, DKV_NW>::BYTES + SwzStage<TR, DV / 8, DKV_NW>::BYTES + 2 * TR * 4);
-  static bool attr = false;
-  hipError_t e;
-  if (!attr) {
-    if ((e = set_lds(attn_bwd_dq32_kernel<G>, dq_lds)) != hipSuccess) return e;
-    if ((e = set_lds(attn_bwd_dkv_kernel<G>, dkv_lds)) != hipSuccess) return e;
-    attr = true;
-  }
+  hipError_t e;   // set on every call: no process-wide state, and correct on every device
+  if ((e = set_lds(attn_bwd_dq32_kernel<G>, dq_lds)) != hipSuccess) return e;
+  if ((e = set_lds(attn_bwd_dkv_kernel<G>, dkv_lds)) != hipSuccess) return e;
   const int64_t gq = (int64_t)a.B * a.nN * cdiv(a.L, 32), gk = (int64_t)a.B * a.nN * cdiv(a.L, DKV_KEYS);
   hipLaunchKernelGGL(attn_bwd_dq32_kernel<G>, dim3((unsigned)gq), dim3(64 * (G + 1)), dq_lds, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;

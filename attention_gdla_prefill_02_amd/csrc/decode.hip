@@ -82,7 +82,7 @@ __device__ __forceinline__ bf16x8 tr_pair(const bf16* p0, const bf16* p1) {
 // bank quads and every fragment read is conflict-free.  64 KB of LDS: two
 // workgroups per CU.
 enum SkinnyMode { SK_PARTIAL = 0, SK_QG = 1, SK_ZGATE = 2 };
-constexpr int SK_KC = 64, SK_NSTG = 4;
+constexpr int SK_KC = 64;
 constexpr int SK_CH = SK_KC / 8;          // 16-byte chunks per tile row
 constexpr int SK_RPB = 64 / SK_CH;        // tile rows per 1 KB block
 constexpr int SK_BPW = SK_CH / 4;         // blocks per wave per operand (16 rows)

@@ -375,12 +375,9 @@ __global__ void qg_finish_f32(float* q, int64_t ldq, float* g, int64_t ldg, int6
 
 template <class OT, bool RES>
 hipError_t set_gemm_lds() {
-  static bool done = false;
-  if (done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<OT, RES>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE_BYTES);
-  if (e == hipSuccess) done = true;
-  return e;
+  // set on every launch: no process-wide state, and correct on every device
+  return hipFuncSetAttribute((const void*)gemm_bf16_kernel<OT, RES>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             2 * STAGE_BYTES);
 }
 
 template <class OT, bool RES>

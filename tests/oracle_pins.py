@@ -419,6 +419,58 @@ def pin_hybrid_schedule():
     assert R.hybrid_windows(8, 128) == [0, 128, 128, 128, 0, 128, 128, 128]
 
 
+def _zero_out_proj(W):
+    return dict(W, w_o=np.zeros_like(W["w_o"]))
+
+
+def pin_block_residual_and_schedule():
+    """The hybrid block ([M3-arch]) joins its layers by x_{l+1} = x_l + y_l
+    and runs layer 0 full causal, layers 1-3 windowed.  With every output
+    projection zero each y_l = 0, so the block is the identity; with only
+    layer k's projection non-zero the block is x + layer_k(x) at that layer's
+    window (full for k = 0, W otherwise), and every other layer output is 0;
+    with layers 0 and 1 non-zero, layer 1 sees x + y_0."""
+    window = 3
+    Ws = [tiny_weights(seed=60 + l) for l in range(4)]
+    x = tiny_x(B=2, seed=64)
+    full_cfg, win_cfg = replace(TINY, window=0), replace(TINY, window=window)
+    # the window must matter at this size, or the schedule would go unchecked
+    assert np.max(np.abs(R.gdla_layer(x, Ws[1], full_cfg)["y"] - R.gdla_layer(x, Ws[1], win_cfg)["y"])) > 1e-6
+    outs, xf = R.gdla_block(x, [_zero_out_proj(W) for W in Ws], TINY, window)
+    assert len(outs) == 4
+    close(xf, x, 0.0)
+    for y in outs:
+        assert np.all(y == 0.0)
+    for k in range(4):
+        Wk = [W if l == k else _zero_out_proj(W) for l, W in enumerate(Ws)]
+        outs, xf = R.gdla_block(x, Wk, TINY, window)
+        yk = R.gdla_layer(x, Ws[k], full_cfg if k == 0 else win_cfg)["y"]
+        close(outs[k], yk, 1e-12)
+        close(xf, x + yk, 1e-12)
+        for l in range(4):
+            if l != k:
+                assert np.all(outs[l] == 0.0), f"layer {l} output with a zero projection"
+    W01 = [Ws[0], Ws[1], _zero_out_proj(Ws[2]), _zero_out_proj(Ws[3])]
+    outs, xf = R.gdla_block(x, W01, TINY, window)
+    y0 = R.gdla_layer(x, Ws[0], full_cfg)["y"]
+    y1 = R.gdla_layer(x + y0, Ws[1], win_cfg)["y"]
+    close(outs[1], y1, 1e-12)
+    close(xf, x + y0 + y1, 1e-12)
+
+
+def pin_block_causality():
+    """Every layer of the block is causal, so changing x at s > t leaves
+    rows 0..t of the block's output unchanged, while row t itself depends on x_t."""
+    Ws = [tiny_weights(seed=70 + l) for l in range(4)]
+    x = tiny_x(B=1, seed=74)
+    t = 6
+    _, base = R.gdla_block(x, Ws, TINY, 2)
+    x2 = x.copy(); x2[0, t + 1:] += 3.0
+    close(R.gdla_block(x2, Ws, TINY, 2)[1][0, :t + 1], base[0, :t + 1], 1e-12)
+    x3 = x.copy(); x3[0, t] += 3.0
+    assert np.max(np.abs(R.gdla_block(x3, Ws, TINY, 2)[1][0, t] - base[0, t])) > 1e-3
+
+
 # YaRN ([OSM-yarn]) with the long-context settings of [M3-ctx]: factor 64 over
 # a native 4096, beta_fast 32, beta_slow 1, on a 64-wide rotary part, base 1e4.
 YARN = (64.0, 4096.0, 32.0, 1.0)

@@ -69,6 +69,13 @@ def test_backward_motif_shapes():
     run(configs.MOTIF_SHAPES, 1, 200, 0, seed=84)
 
 
+def test_backward_motif_shapes_l4096_dense():
+    """Motif shapes at L = 4096 with a dense upstream gradient on every row:
+    the dK/dV accumulation over 4096 query rows (128 query tiles per key
+    block) and every weight gradient against the oracle's full backward."""
+    run(configs.MOTIF_SHAPES, 1, 4096, 0, seed=85)
+
+
 @pytest.mark.parametrize("layer", [0, 1])
 def test_backward_hybrid_l32k_sparse_rows(layer):
     """Full size (Motif shapes, L = 32768, the block's full-causal layer and a

@@ -3,6 +3,8 @@ cache, HIP path through the C ABI vs the oracle's plain (non-absorbed) decode
 on the same bits; the appended cache rows; prefill -> decode consistency; the
 batch-64 workload with a 32K-row cache on a seeded sample of sequences."""
 
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -89,22 +91,95 @@ def test_prefill_then_decode_matches_prefill(window):
                  tol=dict(max_abs=2e-2, rel_l2=1e-2))
 
 
-def test_decode_workload_b64_sampled():
-    """Batch 64 with a 32768-row cache and contexts U{1024..32768} (the timed
-    decode workload); 8 seeded sequences are checked against the oracle."""
-    w = configs.WORKLOADS["decode_b64"]
+def oracle_decode_all(xc, W64, shapes, window, cache_c, lens, chunk=8):
+    """The oracle's decode of every sequence of a batch, in chunks of `chunk`
+    sequences (bounds the float64 copy of the cache)."""
+    B = xc.shape[0]
+    lens = np.asarray(lens)
+    ys, rows = [], []
+    t0 = time.time()
+    for b0 in range(0, B, chunk):
+        sel = list(range(b0, min(B, b0 + chunk)))
+        cap = int(lens[sel].max()) + 1
+        ref = R.gdla_decode(inputs.widen(xc[sel]), W64, oracle_cfg(shapes, window), inputs.widen(cache_c[sel, :cap]),
+                            lens[sel])
+        ys.append(ref["y"])
+        rows.append(ref["new_rows"])
+    print(f"[workload] oracle decode of {B} sequences (W={window}): {time.time() - t0:.1f} s", flush=True)
+    return dict(y=np.concatenate(ys), new_rows=np.concatenate(rows))
+
+
+def nan_pool(cache, lens, page_rows, seed):
+    """The rows of a dense device cache [B, capacity, row] below cache_lens,
+    moved into a shuffled pool of page_rows-row pages (inputs.page_table, with
+    a page for each sequence's new row); every other pool row is NaN.
+    Returns (pool, block_table on the device, block_table on the host)."""
+    B, cap, RL = cache.shape
+    ln = [int(v) for v in lens]
+    bt, npages = inputs.page_table([n + 1 for n in ln], page_rows, seed)
+    pool = torch.full((npages, page_rows, RL), float("nan"), dtype=cache.dtype, device=cache.device)
+    src, dst = [], []
+    for b, n in enumerate(ln):
+        for j in range((n + page_rows) // page_rows):
+            src.append(b * (cap // page_rows) + j)
+            dst.append(int(bt[b, j]))
+    pos = torch.arange(cap, device=cache.device)[None, :]
+    masked = torch.where((pos < lens.to(cache.device)[:, None])[..., None], cache,
+                         torch.tensor(float("nan"), dtype=cache.dtype, device=cache.device))
+    pool[torch.tensor(dst, device=cache.device)] = masked.reshape(B * (cap // page_rows), page_rows, RL)[
+        torch.tensor(src, device=cache.device)]
+    del masked
+    return pool, torch.from_numpy(bt).to(cache.device), bt
+
+
+def check_batch(name, y, pool_or_cache, lens, ref, bt=None, page_rows=0):
+    """y of every sequence and every appended row against the oracle."""
+    assert_close(host64(y), ref["y"], "bf16", f"{name}: y of all {y.shape[0]} sequences")
+    got = []
+    for b, n in enumerate(int(v) for v in lens):
+        if bt is None:
+            got.append(host64(pool_or_cache[b, n]))
+        else:
+            pg, rr = R.paged_slot(bt, page_rows, b, n)
+            got.append(host64(pool_or_cache[pg, rr]))
+    assert_close(np.stack(got), ref["new_rows"], "bf16", f"{name}: appended rows")
+
+
+def run_batch_decode(name, paged_too=False):
+    """A batch-64 decode workload scored on all 64 sequences, full and
+    windowed layers; with paged_too the same state is also decoded from a
+    shuffled NaN-filled pool of 64-row pages and scored against the same
+    oracle result."""
+    w = configs.WORKLOADS[name]
     s = w.shapes
     cache_c, lens = inputs.make_decode_state(w.B, w.capacity, s["kv_rank"], s["d_rope"], w.ctx_range, w.seed, "bf16")
     Wd, W64 = make_layer(s, configs.layer_seed(w, 0), "bf16")
     xc = inputs.make_x(w.B, 1, s["d_model"], w.seed, "bf16")[:, 0].contiguous()
-    rng = np.random.Generator(np.random.PCG64(w.seed + 77))
-    sel = sorted(int(v) for v in rng.choice(w.B, size=8, replace=False))
+    page_rows = w.page_rows or 64
     for window in w.windows:
-        cache = cache_c.to("cuda")
+        print(f"[case] {name} W={window} (all {w.B} sequences{', dense and paged' if paged_too else ''})", flush=True)
+        ref = oracle_decode_all(xc, W64, s, window, cache_c, lens.numpy())
         cfg = gdla.make_config(s, window, "bf16")
-        y = gdla.decode(cfg, Wd, xc.to("cuda"), cache, lens.to("cuda"))
-        torch.cuda.synchronize()
-        ref = R.gdla_decode(inputs.widen(xc[sel]), W64, oracle_cfg(s, window), inputs.widen(cache_c[sel]),
-                            lens.numpy()[sel])
-        assert_close(host64(y)[sel], ref["y"], "bf16", f"decode b64 W={window} (8 sampled sequences)")
+        lens_d = lens.to("cuda")
+        if not w.page_rows:
+            cache = cache_c.to("cuda")
+            y = gdla.decode(cfg, Wd, xc.to("cuda"), cache, lens_d)
+            torch.cuda.synchronize()
+            check_batch(f"{name} dense W={window}", y, cache, lens, ref)
+            if not paged_too:
+                del cache
+                continue
+        else:
+            cache = cache_c.to("cuda")
+        pool, bt_d, bt = nan_pool(cache, lens, page_rows, w.seed)
         del cache
+        y = gdla.decode_paged(cfg, Wd, xc.to("cuda"), pool, bt_d, lens_d)
+        torch.cuda.synchronize()
+        check_batch(f"{name} paged W={window}", y, pool, lens, ref, bt=bt, page_rows=page_rows)
+        del pool
+
+
+def test_decode_workload_b64_all():
+    """Batch 64 with a 32768-row cache and contexts U{1024..32768} (the timed
+    decode workload), every sequence against the oracle."""
+    run_batch_decode("decode_b64")

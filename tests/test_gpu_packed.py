@@ -14,6 +14,7 @@ import torch
 from attention_gdla_prefill_02_amd import configs, gdla, inputs
 from oracle import gdla_ref as R
 from tests.helpers import SMALL, assert_close, host64, make_layer, oracle_cfg
+from tests.test_gpu_decode import run_batch_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -272,3 +273,10 @@ def test_packed_hybrid_l32k_sampled_rows():
                 assert_close(got, ref["y"][0], "bf16", f"packed block layer {l} sequence {b} ({len(rows)} rows)")
         x = gdla.prefill_packed(cfg, Wd, x, cu_d, residual=x, workspace=ws)
     assert bool(torch.isfinite(x).all())
+
+
+def test_paged_decode_b64_all():
+    """The timed paged decode workload (64 heads, 512-wide latent, contexts
+    U{1024..32768}, 64-row pages in a shuffled pool whose unowned rows are
+    NaN), every sequence against the oracle, full and W=4096 layers."""
+    run_batch_decode("paged_decode_b64")

@@ -1,7 +1,7 @@
 """Parity at the report's own layer shapes (group size 4: 64 signal + 16 noise
 = 80 query heads, query rank 1024, sliding windows of 128): small shapes over
 every row, the report shapes on short sequences over every row, the hybrid
-32K block on sampled rows per layer, and batch-64 decode on sampled sequences.
+32K block on sampled rows per layer, and batch-64 decode, dense and paged, on every sequence.
 """
 
 import numpy as np
@@ -11,7 +11,7 @@ import torch
 from attention_gdla_prefill_02_amd import configs, gdla, inputs
 from oracle import gdla_ref as R
 from tests.helpers import SMALL, assert_close, host64, make_layer, oracle_cfg
-from tests.test_gpu_decode import run_decode
+from tests.test_gpu_decode import run_batch_decode, run_decode
 from tests.test_gpu_prefill import run_layer
 from tests.test_gpu_workloads import _block_parity
 
@@ -53,21 +53,8 @@ def test_report_hybrid_l32k_sampled_rows():
     _block_parity("report_hybrid_l32k")
 
 
-def test_report_decode_b64_sampled():
-    """Batch 64 with a 32768-row cache at the report's shapes (80 query heads);
-    8 seeded sequences checked against the oracle, full and W=128 layers."""
-    w = configs.WORKLOADS["report_decode_b64"]
-    s = w.shapes
-    cache_c, lens = inputs.make_decode_state(w.B, w.capacity, s["kv_rank"], s["d_rope"], w.ctx_range, w.seed, "bf16")
-    Wd, W64 = make_layer(s, configs.layer_seed(w, 0), "bf16")
-    xc = inputs.make_x(w.B, 1, s["d_model"], w.seed, "bf16")[:, 0].contiguous()
-    rng = np.random.Generator(np.random.PCG64(w.seed + 77))
-    sel = sorted(int(v) for v in rng.choice(w.B, size=8, replace=False))
-    for window in w.windows:
-        cache = cache_c.to("cuda")
-        y = gdla.decode(gdla.make_config(s, window, "bf16"), Wd, xc.to("cuda"), cache, lens.to("cuda"))
-        torch.cuda.synchronize()
-        ref = R.gdla_decode(inputs.widen(xc[sel]), W64, oracle_cfg(s, window), inputs.widen(cache_c[sel]),
-                            lens.numpy()[sel])
-        assert_close(host64(y)[sel], ref["y"], "bf16", f"report decode b64 W={window} (8 sampled sequences)")
-        del cache
+def test_report_decode_b64_all():
+    """Batch 64 with a 32768-row cache at the report's shapes (80 query heads),
+    every sequence against the oracle, full and W=128 layers, from the dense
+    cache and from a shuffled NaN-filled pool of 64-row pages."""
+    run_batch_decode("report_decode_b64", paged_too=True)

@@ -163,6 +163,36 @@ def _hybrid_last_full(n, w):
     return [0 if (l % 4) == 3 else int(w) for l in range(n)]
 
 
+def _block_no_residual(x, Ws, cfg, window):
+    # each layer replaces the stream instead of adding to it
+    x = np.asarray(x, np.float64)
+    outs = []
+    for W, win in zip(Ws, R.hybrid_windows(len(Ws), window)):
+        y = R.gdla_layer(x, W, R._with_window(cfg, win))["y"]
+        outs.append(y)
+        x = y
+    return outs, x
+
+
+def _block_residual_from_input(x, Ws, cfg, window):
+    # every layer reads the block input, not the running stream
+    x0 = np.asarray(x, np.float64)
+    outs = [R.gdla_layer(x0, W, R._with_window(cfg, win))["y"]
+            for W, win in zip(Ws, R.hybrid_windows(len(Ws), window))]
+    return outs, x0 + sum(outs)
+
+
+def _block_all_full(x, Ws, cfg, window):
+    # the schedule's windows dropped
+    x = np.asarray(x, np.float64)
+    outs = []
+    for W in Ws:
+        y = R.gdla_layer(x, W, R._with_window(cfg, 0))["y"]
+        outs.append(y)
+        x = x + y
+    return outs, x
+
+
 _orig_yif = R.yarn_inv_freq
 
 
@@ -304,6 +334,9 @@ MUTANTS = {
     "linear_transposed": ("linear", _linear_transposed),
     "latent_expand_swapped": ("latent_expand", _latent_expand_swapped),
     "hybrid_last_full": ("hybrid_windows", _hybrid_last_full),
+    "block_no_residual": ("gdla_block", _block_no_residual),
+    "block_residual_from_input": ("gdla_block", _block_residual_from_input),
+    "block_all_full": ("gdla_block", _block_all_full),
     "yarn_ramp_reversed": ("yarn_inv_freq", _yarn_ramp_reversed),
     "yarn_times_s": ("yarn_inv_freq", _yarn_times_s),
     "yarn_mscale_sqrt": ("yarn_mscale", _yarn_mscale_sqrt),
