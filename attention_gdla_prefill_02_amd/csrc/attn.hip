@@ -57,6 +57,7 @@ namespace {
 
 constexpr int DN = 128, DR = 64, DQK = DN + DR, DV = 128;
 constexpr int BQ = 64, BKV = 32;
+constexpr int NBUF = 3;              // LDS ring slots of K/V tiles; loads run NBUF - 1 tiles ahead
 constexpr int K_LD = DQK + 8;        // LDS row of a key (elements), padded
 constexpr int V_LD = BKV + 8;        // LDS row of V^T (one value dim, BKV keys)
 constexpr int K_TILE = BKV * K_LD;   // elements
@@ -65,7 +66,7 @@ constexpr float NEG_INIT = -1.0e30f;
 
 __host__ __device__ constexpr int z_ld(int g) { return g * DV + 8; }
 __host__ __device__ constexpr size_t lds_bytes(int g) {
-  const size_t kv = 3 * (size_t)(K_TILE + V_TILE) * 2;
+  const size_t kv = NBUF * (size_t)(K_TILE + V_TILE) * 2;
   const size_t ep = (size_t)BQ * (DV + 4) * 4 + (size_t)BQ * z_ld(g) * 2;
   return kv > ep ? kv : ep;
 }
@@ -99,7 +100,7 @@ __device__ __forceinline__ float xor32(float v) {
 // consecutive rows bank-conflict free with compile-time offsets.  Tiles are
 // filled with global_load_lds: lane i of a wave writes bytes 16i..16i+15 of a
 // 1 KB LDS block, so each lane fetches the global chunk that belongs at its
-// position; lanes on a pad chunk fetch a valid dummy chunk, lanes past the
+// position; lanes on a pad chunk (never read) and lanes past the
 // tile end are switched off.
 constexpr int KROW_CH = K_LD / 8;                 // 25 chunks per padded key row
 constexpr int VROW_CH = V_LD / 8;                 // 5 chunks per padded value row
@@ -178,28 +179,52 @@ attn_bf16_kernel(AttnArgs a) {
   const bf16* kr = (const bf16*)a.kr;
   const bf16* vt = (const bf16*)a.vt + (int64_t)n * DV * a.ld_vt;
 
-  // issue the loads of one tile into LDS buffer buf (1 KB blocks round-robin over waves)
-  auto load_tile = [&](int tile, int buf) {
-    const int64_t kb = (int64_t)tile * BKV;
-    unsigned char* base = smem_raw + buf * TILE_BYTES;
+  // Tile loads: 1 KB LDS block blk of a tile is filled by wave blk % NW, whose
+  // slot j is block w + NW*j; lane i of the block fetches the global chunk
+  // that belongs at byte 16i.  A lane's source for stream tile `tile` is
+  // src_base + tile * src_step bytes (rows of a tile are consecutive stream
+  // rows), so the per-lane offsets are computed once here.  Only a tile that
+  // runs past the stream's last row T - 1 takes the clamped path, where such
+  // rows repeat row T - 1 (masked in the scores; their value columns lie in
+  // the zero padding of V^T).
+  constexpr int NSLOT = (TILE_KB + NW - 1) / NW;
+  const int wu = __builtin_amdgcn_readfirstlane(w);   // wave index as a scalar (LDS addresses go to M0)
+  const char* src_base[NSLOT];
+  uint32_t src_step[NSLOT];
+  bool src_on[NSLOT];
+  auto chunk_src = [&](int pos, int64_t kb) -> const void* {   // global chunk at tile position pos, tile row kb
+    if (pos < K_CHUNKS) {
+      const int r = pos / KROW_CH, c = pos % KROW_CH;              // c == 24: pad chunk (never loaded)
+      const int64_t key = min(kb + r, T - 1);
+      return c < DN / 8 ? (const void*)(kc + key * a.ld_kc + c * 8)
+                        : (const void*)(kr + key * DR + min(c - DN / 8, DR / 8 - 1) * 8);
+    }
+    const int pv = pos - K_CHUNKS;
+    const int d = pv / VROW_CH, c = min(pv % VROW_CH, VROW_CH - 2);   // pad chunk (never loaded) -> chunk 3
+    return vt + (int64_t)d * a.ld_vt + kb + c * 8;
+  };
 #pragma unroll
-    for (int blk = w; blk < TILE_KB; blk += NW) {
-      const int pos = blk * 64 + lane;             // 16-byte chunk position in the tile
-      if (pos < T_CHUNKS) {
-        const void* src;
-        if (pos < K_CHUNKS) {
-          const int r = pos / KROW_CH, c = pos % KROW_CH;   // c == 24: pad chunk
-          const int64_t key = min(kb + r, T - 1);  // rows past the stream repeat a valid row (masked)
-          src = c < DN / 8 ? (const void*)(kc + (int64_t)key * a.ld_kc + c * 8)
-                           : (const void*)(kr + (int64_t)key * DR + min(c - DN / 8, DR / 8 - 1) * 8);
-        } else {
-          const int pv = pos - K_CHUNKS;
-          const int d = pv / VROW_CH, c = min(pv % VROW_CH, VROW_CH - 2);   // pad chunk -> chunk 3
-          // value columns past T lie in the zero-filled padding of V^T
-          src = vt + (int64_t)d * a.ld_vt + kb + c * 8;
-        }
-        g2lds16(src, base + blk * 1024);
-      }
+  for (int j = 0; j < NSLOT; ++j) {
+    const int pos = (wu + NW * j) * 64 + lane;
+    // pad chunks (the last of each padded key or value row) are never read: skipped
+    const bool pad = pos < K_CHUNKS ? pos % KROW_CH == KROW_CH - 1 : (pos - K_CHUNKS) % VROW_CH == VROW_CH - 1;
+    src_on[j] = wu + NW * j < TILE_KB && pos < T_CHUNKS && !pad;
+    const int p = min(pos, T_CHUNKS - 1);
+    src_base[j] = (const char*)chunk_src(p, 0);
+    src_step[j] = p < K_CHUNKS ? (p % KROW_CH < DN / 8 ? BKV * (uint32_t)a.ld_kc * 2 : BKV * DR * 2) : BKV * 2;
+  }
+  auto load_tile = [&](int tile, int buf) {
+    unsigned char* base = smem_raw + buf * TILE_BYTES;
+    if ((int64_t)(tile + 1) * BKV > T) {   // the stream's last tile: rows clamped to T - 1
+#pragma unroll
+      for (int j = 0; j < NSLOT; ++j)
+        if (wu + NW * j < TILE_KB && src_on[j])
+          g2lds16_explicit(chunk_src((wu + NW * j) * 64 + lane, (int64_t)tile * BKV), base + (wu + NW * j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NSLOT; ++j)
+        if (wu + NW * j < TILE_KB && src_on[j])
+          g2lds16_explicit(src_base[j] + (uint64_t)(uint32_t)tile * src_step[j], base + (wu + NW * j) * 1024);
     }
   };
 
@@ -248,15 +273,15 @@ attn_bf16_kernel(AttnArgs a) {
     }
   };
   // softmax, second half: P = exp2(s*sc - m) in bf16 and the running sum (no branches)
+  // The running sum adds the bf16 P that P V multiplies (one dot2 per pair with
+  // (1, 1)), so l normalizes exactly the weights applied to V.
   auto softmax_exp = [&](const f32x16& s, bf16x8 (&p)[2]) {
-    float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pe = fast_exp2(fmaf(s[e], sc, -m));
-      acc += pe;
-      p[e >> 3][e & 7] = (bf16)pe;
-    }
-    lsum += acc;
+    for (int e = 0; e < 16; ++e) p[e >> 3][e & 7] = (bf16)fast_exp2(fmaf(s[e], sc, -m));
+    const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+    for (int e = 0; e < 16; e += 2)
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[e >> 3][e & 7], p[e >> 3][(e & 7) + 1]}, one, lsum, false);
   };
   auto pv = [&](int buf, const bf16x8 (&p)[2]) {
     const bf16* V = reinterpret_cast<const bf16*>(smem_raw + buf * TILE_BYTES + K_BYTES) + l32 * V_LD + hi * 8;
@@ -269,38 +294,48 @@ attn_bf16_kernel(AttnArgs a) {
       }
   };
 
-  // Pipeline over tiles, LDS buffer of tile t = t % 3, one barrier per tile.
-  // Step t issues the loads of tile t+2 (direct to LDS; buffer (t+2) % 3 last
-  // held tile t-1) and computes Q K^T of tile t+1, the softmax of tile t and
-  // P V of tile t.  Tile t+1 was loaded during step t-1 and published by that
-  // step's closing wait + barrier.  The two waves that share a SIMD (query
-  // halves 0 and 1 of one head) order the step differently -- half 0 starts
-  // with the Q K^T MFMAs, half 1 with the softmax on the vector ALU -- so the
-  // matrix cores and the vector ALU of the SIMD work at the same time.  Tiles
+  // Pipeline over tiles, LDS slot of tile t = t % NBUF, one barrier per tile.
+  // Step t issues the loads of tile t + NBUF - 1 (direct to LDS; its slot last
+  // held tile t - 1), then, in one branch-free stretch, the exponentials of
+  // tile t (its max and any rescale were settled in step t-1), Q K^T of tile
+  // t+1 and P V of tile t, so the vector ALU works on the exponentials while
+  // the matrix core runs the Q K^T chain, and P V follows.  The tail masks
+  // tile t+1's scores if it straddles a boundary, takes its max and, rarely,
+  // raises the running max (rescaling O and l, which by then hold tile t).
+  // The step ends by waiting for this wave's loads of tile t+2 (issued
+  // NBUF - 3 steps earlier; the loads issued in this step stay in flight: the
+  // tile loads are issued from inline assembly, so vmcnt counts only them)
+  // and a barrier, which publishes tile t+2 and frees tile t's slot.  Tiles
   // a wave cannot see are still computed: their masked scores give P = 0.
-  const bool lead = half == 0;
+  static_assert(NBUF >= 3, "the ring holds tiles t, t+1 and the one in flight");
+  int my_loads = 0;   // tile loads this wave issues per tile (uniform)
+#pragma unroll
+  for (int j = 0; j < NSLOT; ++j) my_loads += wu + NW * j < TILE_KB;
   f32x16 sA, sB;
   bf16x8 p[2];
-  load_tile(t_lo, t_lo % 3);
-  if (t_lo + 1 < t_hi) load_tile(t_lo + 1, (t_lo + 1) % 3);
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (t_lo + i < t_hi) load_tile(t_lo + i, (t_lo + i) % NBUF);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  qk(t_lo % 3, sA);
+  qk(t_lo % NBUF, sA);
+  softmax_max(sA, (int)((int64_t)t_lo * BKV - tb));
   auto step = [&](int tile, f32x16& cur, f32x16& nxt, bool has_next) {
-    const int kb = (int)((int64_t)tile * BKV - tb);
-    if (tile + 2 < t_hi) load_tile(tile + 2, (tile + 2) % 3);
-    if (lead) {
-      if (has_next) qk((tile + 1) % 3, nxt);
-      softmax_max(cur, kb);
-      softmax_exp(cur, p);
-      pv(tile % 3, p);
-    } else {
-      softmax_max(cur, kb);
-      softmax_exp(cur, p);
-      pv(tile % 3, p);
-      if (has_next) qk((tile + 1) % 3, nxt);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const bool issue = tile + NBUF - 1 < t_hi;
+    if (issue) load_tile(tile + NBUF - 1, (tile + NBUF - 1) % NBUF);
+    softmax_exp(cur, p);
+    if (has_next) qk((tile + 1) % NBUF, nxt);
+    pv(tile % NBUF, p);
+    if (has_next) softmax_max(nxt, (int)((int64_t)(tile + 1) * BKV - tb));
+    // loads allowed in flight: those of tiles t+3 .. t+NBUF-1, issued in the
+    // last NBUF - 3 steps (all of them issued, since this one was)
+    const int ahead = issue ? (NBUF - 3) * my_loads : 0;
+    if (ahead == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (ahead == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if (ahead == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else if (ahead == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if (ahead == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
   int tile = t_lo;
