@@ -20,7 +20,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "libgdla.so")
-SOURCES = ["api.cpp", "gemm.hip", "rowprep.hip", "attn.hip", "decode.hip", "backward.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "rowprep.hip", "attn.hip", "decode.hip", "backward.hip", "noalloc.cpp"]
 ARCH = "gfx950"
 
 

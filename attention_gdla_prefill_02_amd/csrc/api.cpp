@@ -283,6 +283,18 @@ gdla_status run_prefill(const gdla_config* cfg, const gdla_weights* w, const Str
 
 }  // namespace
 
+namespace gdla {
+
+// thread-local error detail for entry points outside this file
+gdla_status report_error(gdla_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+}  // namespace gdla
+
 extern "C" {
 
 const char* gdla_status_string(gdla_status s) {

@@ -18,4 +18,7 @@ size_t decode_workspace_bytes(const gdla_config* cfg, int B);
 hipError_t decode_step(const gdla_config* cfg, const gdla_weights* w, int B, const void* x, void* y,
                        const CacheView& cache, const int32_t* cache_lens, void* workspace, hipStream_t s);
 
+// Sets the thread-local detail string gdla_last_error returns; returns s.
+gdla_status report_error(gdla_status s, const char* fmt, ...);
+
 }  // namespace gdla

@@ -22,7 +22,9 @@ STAGE_DOWN, STAGE_PREP, STAGE_EXPAND, STAGE_QG, STAGE_ATTN, STAGE_OUT, STAGE_ALL
 EXPORTED = ("gdla_prefill_workspace_size", "gdla_prefill", "gdla_prefill_stages", "gdla_prefill_workspace_layout",
             "gdla_decode_workspace_size", "gdla_decode", "gdla_latent_expand", "gdla_status_string",
             "gdla_last_error", "gdla_version", "gdla_prefill_packed_workspace_size", "gdla_prefill_packed",
-            "gdla_decode_paged", "gdla_backward_workspace_size", "gdla_backward")
+            "gdla_decode_paged", "gdla_backward_workspace_size", "gdla_backward", "gdla_decode_noalloc")
+# bytes of the library-owned device array gdla_decode_noalloc uses as its workspace
+DECODE_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class GdlaError(RuntimeError):
@@ -87,6 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdla_decode_workspace_size.restype = sz
     lib.gdla_decode.argtypes = [cfgp, wp, i32, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.gdla_decode.restype = ctypes.c_int
+    lib.gdla_decode_noalloc.argtypes = [cfgp, wp, i32, vp, vp, vp, vp, i32, vp]
+    lib.gdla_decode_noalloc.restype = ctypes.c_int
     pcp = ctypes.POINTER(PagedCache)
     lib.gdla_prefill_packed_workspace_size.argtypes = [cfgp, i32, i64]
     lib.gdla_prefill_packed_workspace_size.restype = sz
@@ -189,6 +193,15 @@ def decode(cfg: Config, W: dict, x: torch.Tensor, cache: torch.Tensor, cache_len
         workspace = alloc_workspace(decode_workspace_size(cfg, B), x.device)
     _check(load().gdla_decode(ctypes.byref(cfg), ctypes.byref(weights_struct(W)), B, _ptr(x), _ptr(y), _ptr(cache),
                               _ptr(cache_lens), cache.shape[1], _ptr(workspace), workspace.numel(), _stream(stream)))
+    return y
+
+
+def decode_noalloc(cfg: Config, W: dict, x: torch.Tensor, cache: torch.Tensor, cache_lens: torch.Tensor, *,
+                   y: torch.Tensor, stream=None) -> torch.Tensor:
+    """gdla_decode with the library's own device scratch as workspace: nothing
+    is allocated, so y must be given."""
+    _check(load().gdla_decode_noalloc(ctypes.byref(cfg), ctypes.byref(weights_struct(W)), x.shape[0], _ptr(x),
+                                      _ptr(y), _ptr(cache), _ptr(cache_lens), cache.shape[1], _stream(stream)))
     return y
 
 

@@ -212,6 +212,30 @@ gdla_status gdla_decode(const gdla_config* cfg, const gdla_weights* w, int32_t B
                         int32_t capacity, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* gdla_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same step with the same results as gdla_decode (same checks, limits and
+ * kernels), but its workspace is a library-owned device array of
+ * GDLA_DECODE_NOALLOC_SCRATCH_BYTES per GPU instead of a caller buffer; the
+ * caller still passes x, y, the cache and cache_lens.  The array is set aside
+ * by the loader the first time a process uses this entry point on a device
+ * and held until the process ends.
+ *   - GDLA_ERR_WORKSPACE (nothing launched) when gdla_decode_workspace_size
+ *     of cfg and B exceeds the array: B <= 64 fits at 80 query heads and a
+ *     512-wide latent, about B <= 100 at 64 heads.
+ *   - stream must belong to the current device (GDLA_ERR_INVALID_ARG
+ *     otherwise); NULL is the current device's default stream.
+ *   - Every call on one GPU shares that GPU's array, and nothing in it
+ *     survives between calls that the step needs: calls whose work overlaps
+ *     in time on one GPU (different streams, or unordered host threads) race
+ *     on it and give undefined results; order them on one stream.
+ * The library allocates nothing on this path (no hipMalloc, hipFree or
+ * allocating library call). */
+#define GDLA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gdla_status gdla_decode_noalloc(const gdla_config* cfg, const gdla_weights* w, int32_t B,
+                                const void* x, void* y, void* cache, const int32_t* cache_lens,
+                                int32_t capacity, void* stream);
+
 /* A paged latent cache ("Open-Source Frontier Models: Architecture and
  * Benchmarks of Rnj-1 and Motif-2", section 2, prefill sequence diagram: the
  * normalized KV rows are stored in the blocks of a PagedAttention cache).

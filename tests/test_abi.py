@@ -241,3 +241,20 @@ def test_paged_decode_rejects_bad_arguments():
     assert call(paged(), wsb=ws - 1) == gdla.GDLA_ERR_WORKSPACE
     for bad in (paged(page_rows=16), paged(bt=0), paged(num_pages=-1), paged(max_pages=0)):
         assert call(bad) == gdla.GDLA_ERR_INVALID_ARG
+
+
+def test_decode_noalloc_host_checks():
+    """The no-allocation decode rejects a batch whose workspace exceeds the
+    library's scratch array before any device work, and B = 0 is a no-op."""
+    L_ = lib()
+    w = FakeW().struct()
+    c = _cfg(group=4)
+    assert L_.gdla_decode_workspace_size(ctypes.byref(c), 512) > gdla.DECODE_NOALLOC_SCRATCH_BYTES
+    assert L_.gdla_decode_workspace_size(ctypes.byref(c), 64) <= gdla.DECODE_NOALLOC_SCRATCH_BYTES
+    st = L_.gdla_decode_noalloc(ctypes.byref(c), ctypes.byref(w), 512, 0x100000, 0x200000, 0x400000, 0x500000, 64,
+                                None)
+    assert st == gdla.GDLA_ERR_WORKSPACE
+    assert b"scratch holds" in L_.gdla_last_error()
+    assert L_.gdla_decode_noalloc(ctypes.byref(c), ctypes.byref(w), 0, None, None, None, None, 0, None) == gdla.GDLA_OK
+    assert L_.gdla_decode_noalloc(ctypes.byref(c), ctypes.byref(w), -1, None, None, None, None, 0, None) == \
+        gdla.GDLA_ERR_INVALID_ARG
