@@ -41,8 +41,8 @@ HBM_PEAK_GBS = 8000.0                # MI355X HBM3E
 # the ratio of bytes to counter reading of a device copy of known size timed in
 # the same pass (--copy-probe-mib).  Tied to the kernel source it was measured
 # on: reported as null once that source changes.
-ATTN_TRAFFIC = {"source_sha256": "90e750f2ad773a2235d84752e565b637f082379830f00438c814a11d35a39306",
-                "fetch_bytes": 4067162928, "write_bytes": 402653184}
+ATTN_TRAFFIC = {"source_sha256": "a565fabeea6039c5c3bebece3f4d3ae262ef6ed434fdf2b27b281e0c56e43d41",
+                "fetch_bytes": 4019631176, "write_bytes": 402653184}
 ATTN_SOURCES = ("attention_gdla_prefill_02_amd/csrc/attn.hip", "attention_gdla_prefill_02_amd/csrc/common.h")
 
 
@@ -107,6 +107,35 @@ def cpu_baseline(w, Wc0, x_cpu, sample_L: int):
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"fp64 oracle, first {sample_L} tokens of the full-causal layer, all rows, "
                       f"{flop / 1e9:.1f} GFLOP in {dt:.1f} s on {len(os.sched_getaffinity(0))} host cores"}
+
+
+def cpu_baseline_decode(sample_seqs: int):
+    """The fp64 oracle on the first sample_seqs sequences of the batch-64
+    decode workload's full-causal layer (the new token of each, attending its
+    whole cached context); returns tokens/s of that sample and its size."""
+    import numpy as np
+
+    import oracle.gdla_ref as R
+    from attention_gdla_prefill_02_amd import configs, inputs
+    w = configs.WORKLOADS["decode_b64"]
+    s = w.shapes
+    cache, lens = inputs.make_decode_state(w.B, w.capacity, s["kv_rank"], s["d_rope"], w.ctx_range, w.seed, "bf16")
+    Wc = inputs.make_weights(s, configs.layer_seed(w, 0), "bf16")
+    x = inputs.make_x(w.B, 1, s["d_model"], w.seed, "bf16")[:, 0]
+    sel = list(range(sample_seqs))
+    ln = lens.numpy()[sel]
+    cap = int(ln.max()) + 1
+    W64 = {k: inputs.widen(v) for k, v in Wc.items()}
+    x64, c64 = inputs.widen(x[sel]), inputs.widen(cache[sel, :cap])
+    del cache
+    t0 = time.perf_counter()
+    R.gdla_decode(x64, W64, R.Cfg(**configs.cfg_dict(w, 0)), c64, ln)
+    dt = time.perf_counter() - t0
+    rows = int(np.sum(ln + 1))
+    return {"value": sample_seqs / dt, "unit": "tokens/s", "kind": "oracle",
+            "sample": f"fp64 oracle decode, full-causal layer, the first {sample_seqs} of the 64 sequences of the "
+                      f"batch-64 workload ({rows} attended cache rows, every one expanded through W_UKV), "
+                      f"{dt:.1f} s"}
 
 
 def bench_prefill(args, torch, gdla, configs, inputs, name="hybrid_l32k", steps=None, warmup=None):
@@ -386,6 +415,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-decode-seqs", type=int, default=16, help="sequences of the decode workload the oracle times")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-report-shapes", action="store_true", help="skip the report-shape (g=4, W=128) workloads")
     ap.add_argument("--decode-only", action="store_true", help="time only the decode steps (for profiling)")
@@ -470,6 +500,10 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens")
         cpu = cpu_baseline(w, Wc0, x_cpu, args.cpu_sample_tokens)
+        if not args.no_decode:
+            log(f"[bench] cpu baseline: oracle decode on {args.cpu_decode_seqs} sequences")
+            cpu["decode"] = cpu_baseline_decode(args.cpu_decode_seqs)
+            cpu["decode"]["cores"] = cpu["cores"]
 
     n_attn_launch = len(w.windows)
     line = {
