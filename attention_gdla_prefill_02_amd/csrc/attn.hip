@@ -9,8 +9,8 @@
 // with A(t) = {s <= t} (full) or {t - W < s <= t} (window W).
 //
 // bf16 kernel (d_nope = 128, d_rope = 64, d_v = 128), one workgroup per
-// (sequence, KV head n, query block of 64; 32 when g = 4 -- see halves()):
-//  * 2(g+1) waves (g + 1 for g = 4): wave w handles query head slot w % (g+1)
+// (sequence, KV head n, query block of 64; g = 4 runs as two launches -- see Shape):
+//  * 2(g+1) waves for g <= 3: wave w handles query head slot w % (g+1)
 //    (g signal heads, then the noise head) for 32 consecutive queries.  All
 //    g+1 heads of the group read the same content key, rotary key and value,
 //    so each 32-key tile of [K^C | k_R] (32 x 192) and V^T (128 x 32) is
@@ -35,13 +35,15 @@
 //    tiles that straddle a boundary.  A wave computes every tile of the
 //    workgroup's range; on a tile none of its queries sees, the mask makes
 //    every P zero.
-//  * The two waves sharing a SIMD (query halves 0 and 1 of a head) order each
-//    step differently, so one runs its Q K^T MFMAs while the other runs the
-//    softmax on the vector ALU.
-//  * Epilogue: H = O / l; the noise waves publish H_N through LDS, the signal
-//    waves form gate * (H_S - lambda * H_N) in fp32 and stage bf16 Z rows in
-//    LDS, then the workgroup writes BQ contiguous Z rows (g*d_v wide) with
-//    16-byte coalesced stores.
+//  * Each 32-key step runs, in one branch-free stretch, the exponentials of
+//    tile t, Q K^T of tile t+1 and P V of tile t; the boundary mask, the max
+//    and the rare rescale of tile t+1 follow (see the pipeline below).
+//  * Epilogue: H = O / l; the noise waves publish H_N through LDS (for
+//    g = 4 the noise launch stores it in fp32 in the group's Z rows and the
+//    signal launch reads it back), the signal waves form
+//    gate * (H_S - lambda * H_N) in fp32 and stage bf16 Z rows in LDS, then
+//    the workgroup writes BQ contiguous Z rows (g*d_v wide) with 16-byte
+//    coalesced stores.
 //  * Workgroups are numbered so XCD x (blockIdx % 8) processes whole KV
 //    heads, query blocks in descending order (longest causal rows first);
 //    neighbouring query blocks of a head then stream the same key tiles
@@ -49,6 +51,8 @@
 //
 // The fp32 kernel is a plain vector-ALU version (three passes per query and
 // head) for the fp32 configuration.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -65,9 +69,12 @@ constexpr int V_TILE = DV * V_LD;
 constexpr float NEG_INIT = -1.0e30f;
 
 __host__ __device__ constexpr int z_ld(int g) { return g * DV + 8; }
-__host__ __device__ constexpr size_t lds_bytes(int g) {
+// LDS of a workgroup: the K/V tile ring, reused by the epilogue (AM_FUSED: the
+// noise head's H [64][DV + 4] fp32 then the Z rows [64][g*DV + 8]; AM_SIGNAL:
+// the Z rows; AM_NOISE: nothing)
+__host__ __device__ constexpr size_t lds_bytes(int g, int mode) {
   const size_t kv = NBUF * (size_t)(K_TILE + V_TILE) * 2;
-  const size_t ep = (size_t)BQ * (DV + 4) * 4 + (size_t)BQ * z_ld(g) * 2;
+  const size_t ep = mode == 1 ? 0 : (mode == 0 ? (size_t)BQ * (DV + 4) * 4 : 0) + (size_t)BQ * z_ld(g) * 2;
   return kv > ep ? kv : ep;
 }
 
@@ -110,21 +117,34 @@ constexpr int K_BYTES = K_CHUNKS * 16;            // 12.5 KB
 constexpr int TILE_BYTES = T_CHUNKS * 16;         // 22.5 KB
 constexpr int TILE_KB = (T_CHUNKS + 63) / 64;     // 23 load instructions per tile
 
-// HV query halves of 32 per workgroup: 2 for g <= 3 (2(g+1) <= 8 waves, two
-// per SIMD within the 256-register budget); 1 for g = 4, whose 10 waves would
-// put three on a SIMD and cut the budget to 168 registers.
-template <int G> constexpr int halves() { return G <= 3 ? 2 : 1; }
+// Workgroup shapes.  AM_FUSED: the g + 1 heads of a KV group for 64 queries,
+// 2(g+1) waves (g <= 3: at most two waves per SIMD, 256 registers each).  For
+// g = 4 ten waves would leave 168 registers per wave, so the group runs as
+// two launches of eight waves: AM_NOISE computes the noise head for 256
+// queries (one 32-query slot per wave) and stores its H_N in fp32 in the
+// first half of the group's Z row segment; AM_SIGNAL then computes the four
+// signal heads for 64 queries, reads H_N back, and overwrites that segment
+// with the group's Z.  Each K/V tile in LDS thus serves 256 query rows in
+// every shape but the g = 1, 2 fused ones.
+enum AttnMode { AM_FUSED = 0, AM_NOISE = 1, AM_SIGNAL = 2 };
+template <int G, int M> struct Shape {
+  static constexpr int NH = M == AM_FUSED ? G + 1 : (M == AM_SIGNAL ? G : 1);   // heads per workgroup
+  static constexpr int QS = M == AM_NOISE ? 8 : 2;                              // 32-query slots
+  static constexpr int NW = NH * QS, BQ = 32 * QS;
+};
+constexpr int BQ_NOISE = Shape<4, AM_NOISE>::BQ;
 
-template <int G>
-__global__ void __launch_bounds__(64 * halves<G>() * (G + 1), 1)
+template <int G, int MODE>
+__global__ void __launch_bounds__((64 * Shape<G, MODE>::NW), 1)
 attn_bf16_kernel(AttnArgs a) {
-  constexpr int HV = halves<G>(), BQ = 32 * HV;
-  constexpr int NW = HV * (G + 1), NT = 64 * NW;
+  using S_ = Shape<G, MODE>;
+  constexpr int NH = S_::NH, BQ = S_::BQ;
+  constexpr int NW = S_::NW, NT = 64 * NW;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // wave w: query head slot w % (G+1), query half w / (G+1); waves w and w+4 share a SIMD
-  const int hs = w % (G + 1), half = HV == 2 ? w / (G + 1) : 0;
+  // wave w: head slot w % NH, 32-query slot w / NH
+  const int hs = w % NH, half = w / NH;
   const int l32 = lane & 31, hi = lane >> 5;
 
   // workgroup -> (KV head n, work slot); XCD x = blockIdx % 8 keeps whole KV heads
@@ -155,7 +175,9 @@ attn_bf16_kernel(AttnArgs a) {
     tb = (int64_t)b * L;
   }
   const int64_t T = a.T;
-  const int head = hs < G ? n * G + hs : nS + n;
+  constexpr bool NOISE_ONLY = MODE == AM_NOISE;
+  const int head = NOISE_ONLY ? nS + n : (MODE == AM_SIGNAL || hs < G ? n * G + hs : nS + n);
+  const bool noise_wave = NOISE_ONLY || (MODE == AM_FUSED && hs == G);
   const int qw0 = q0 + 32 * half;                 // first query of this wave (within the sequence)
   const int qme = qw0 + l32;                       // this lane's query
   const int qlast = min(qw0 + 31, L - 1);
@@ -368,10 +390,27 @@ attn_bf16_kernel(AttnArgs a) {
       }
     if (hi == 0) a.lse_out[(tb + qme) * (int64_t)(nS + nN) + head] = m + log2f(ltot);
   }
-  float* sH = reinterpret_cast<float*>(smem_raw);                          // [BQ][DV + 4]
-  bf16* sZ = reinterpret_cast<bf16*>(smem_raw + (size_t)BQ * (DV + 4) * 4);  // [BQ][g*DV + 8]
+  // this row's H_N of the group, fp32, in the first half of its Z segment
+  // (between the AM_NOISE and AM_SIGNAL launches of g = 4)
+  auto hn_row = [&](int64_t t) {
+    return reinterpret_cast<float*>((bf16*)a.z + t * (int64_t)(nS * DV) + (int64_t)n * G * DV);
+  };
+  if constexpr (NOISE_ONLY) {
+    if (qme < L) {
+      float* hn = hn_row(tb + qme);
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<f32x4*>(hn + d * 32 + 8 * i + 4 * hi) =
+              f32x4{o[d][4 * i] * inv, o[d][4 * i + 1] * inv, o[d][4 * i + 2] * inv, o[d][4 * i + 3] * inv};
+    }
+    return;
+  }
+  float* sH = reinterpret_cast<float*>(smem_raw);                          // [BQ][DV + 4] (AM_FUSED)
+  bf16* sZ = reinterpret_cast<bf16*>(smem_raw + (MODE == AM_FUSED ? (size_t)BQ * (DV + 4) * 4 : 0));  // [BQ][g*DV + 8]
   const int qrow = 32 * half + l32;
-  if (hs == G) {
+  if (MODE == AM_FUSED && noise_wave) {
 #pragma unroll
     for (int d = 0; d < DV / 32; ++d)
 #pragma unroll
@@ -380,18 +419,20 @@ attn_bf16_kernel(AttnArgs a) {
         *reinterpret_cast<f32x4*>(sH + qrow * (DV + 4) + d * 32 + 8 * i + 4 * hi) = h4;
       }
   }
-  __syncthreads();
-  if (hs < G) {
+  if (MODE == AM_FUSED) __syncthreads();
+  if (!noise_wave) {
     const int64_t t = tb + min(qme, L - 1);
     const int j = n * G + hs;
     const float lam = a.lam[t * nS + j];
     const float* gate = a.gate + t * a.ld_gate + (int64_t)j * DV;
+    const float* hng = MODE == AM_SIGNAL ? hn_row(t) : nullptr;
 #pragma unroll
     for (int d = 0; d < DV / 32; ++d)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int dv = d * 32 + 8 * i + 4 * hi;
-        const f32x4 hn4 = *reinterpret_cast<const f32x4*>(sH + qrow * (DV + 4) + dv);
+        const f32x4 hn4 = MODE == AM_SIGNAL ? *reinterpret_cast<const f32x4*>(hng + dv)
+                                            : *reinterpret_cast<const f32x4*>(sH + qrow * (DV + 4) + dv);
         const f32x4 g4 = *reinterpret_cast<const f32x4*>(gate + dv);
         bf16x4 z4;
 #pragma unroll
@@ -399,7 +440,7 @@ attn_bf16_kernel(AttnArgs a) {
         *reinterpret_cast<bf16x4*>(sZ + qrow * z_ld(G) + hs * DV + dv) = z4;
       }
   }
-  __syncthreads();
+  __syncthreads();   // (AM_SIGNAL: every H_N read of these rows is done before Z overwrites them)
   {
     constexpr int CPRZ = G * DV / 8;    // 16-byte chunks per Z row of this group
     bf16* z = (bf16*)a.z;
@@ -492,18 +533,21 @@ attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int G>
-hipError_t launch_g(const AttnArgs& a, hipStream_t s) {
-  const size_t lds = lds_bytes(G);
+template <int G, int MODE>
+hipError_t launch_mode(const AttnArgs& a, const int* plan, int64_t items_cap, hipStream_t s) {
+  using S_ = Shape<G, MODE>;
+  const size_t lds = lds_bytes(G, MODE);
   // set on every call: no process-wide state, and correct on every device
-  hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<G>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<G, MODE>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const int64_t slots = a.plan ? a.items_cap : (int64_t)a.B * cdiv(a.L, 32 * halves<G>());
+  AttnArgs k = a;
+  k.plan = plan;
+  const int64_t slots = plan ? items_cap : (int64_t)a.B * cdiv(a.L, S_::BQ);
   const int64_t blocks = slots * a.nN;
   if (blocks <= 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_bf16_kernel<G>, dim3((unsigned)blocks), dim3(64 * halves<G>() * (G + 1)), lds, s, a);
+  hipLaunchKernelGGL((attn_bf16_kernel<G, MODE>), dim3((unsigned)blocks), dim3(64 * S_::NW), lds, s, k);
   return hipGetLastError();
 }
 
@@ -600,30 +644,24 @@ attn_plan_kernel(const int32_t* cu, int nseq, int T, int bq, int nlev, int* plan
 
 size_t attn_bf16_lds_bytes(int g) {
   switch (g) {
-    case 1: return lds_bytes(1);
-    case 2: return lds_bytes(2);
-    case 3: return lds_bytes(3);
-    case 4: return lds_bytes(4);
+    case 1: return lds_bytes(1, AM_FUSED);
+    case 2: return lds_bytes(2, AM_FUSED);
+    case 3: return lds_bytes(3, AM_FUSED);
+    case 4: return std::max(lds_bytes(4, AM_NOISE), lds_bytes(4, AM_SIGNAL));
     default: return 0;
   }
 }
 
-int attn_block_q(int g) { return g <= 3 ? 64 : 32; }
-
-int attn_plan_items(int nseq, int64_t T, int g) {
-  return (int)((T + attn_block_q(g) - 1) / attn_block_q(g)) + nseq;
+namespace {
+// ints of one work list for query blocks of bq, rounded up to 16 bytes
+size_t plan_ints(int nseq, int64_t T, int bq) {
+  const int64_t cap = (T + bq - 1) / bq + nseq;
+  return (4 + 4 * (size_t)cap + (size_t)nseq + 3) / 4 * 4;
 }
-
-size_t attn_plan_bytes(int nseq, int64_t T, int g) {
-  const int64_t nlev = (T + attn_block_q(g) - 1) / attn_block_q(g);
-  if (nlev + 1 + 2 * PLAN_THREADS > PLAN_LDS_INTS) return 0;
-  return (4 + 4 * (size_t)attn_plan_items(nseq, T, g) + (size_t)nseq) * sizeof(int);
-}
-
-hipError_t attn_plan(const int32_t* cu, int nseq, int64_t T, int g, int* plan, hipStream_t s) {
-  const int bq = attn_block_q(g);
+bool plan_fits(int64_t T, int bq) { return (T + bq - 1) / bq + 1 + 2 * PLAN_THREADS <= PLAN_LDS_INTS; }
+hipError_t plan_one(const int32_t* cu, int nseq, int64_t T, int bq, int* plan, hipStream_t s) {
   const int nlev = (int)((T + bq - 1) / bq);
-  if (nlev + 1 + 2 * PLAN_THREADS > PLAN_LDS_INTS) return hipErrorInvalidValue;
+  if (!plan_fits(T, bq)) return hipErrorInvalidValue;
   const size_t lds = ((size_t)nlev + 1 + 2 * PLAN_THREADS) * sizeof(int);
   hipError_t e = hipFuncSetAttribute((const void*)attn_plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      PLAN_LDS_INTS * (int)sizeof(int));
@@ -631,14 +669,41 @@ hipError_t attn_plan(const int32_t* cu, int nseq, int64_t T, int g, int* plan, h
   hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(PLAN_THREADS), lds, s, cu, nseq, (int)T, bq, nlev, plan);
   return hipGetLastError();
 }
+}  // namespace
+
+// The fused and signal work items cover 64 queries; g = 4 has a second list
+// for its noise launch (256 queries per item) right after the first.
+int attn_block_q(int) { return 64; }
+
+int attn_plan_items(int nseq, int64_t T, int g) {
+  return (int)((T + attn_block_q(g) - 1) / attn_block_q(g)) + nseq;
+}
+
+size_t attn_plan_bytes(int nseq, int64_t T, int g) {
+  if (!plan_fits(T, attn_block_q(g))) return 0;
+  return (plan_ints(nseq, T, attn_block_q(g)) + (g == 4 ? plan_ints(nseq, T, BQ_NOISE) : 0)) * sizeof(int);
+}
+
+hipError_t attn_plan(const int32_t* cu, int nseq, int64_t T, int g, int* plan, hipStream_t s) {
+  hipError_t e = plan_one(cu, nseq, T, attn_block_q(g), plan, s);
+  if (e != hipSuccess || g != 4) return e;
+  return plan_one(cu, nseq, T, BQ_NOISE, plan + plan_ints(nseq, T, attn_block_q(g)), s);
+}
 
 hipError_t attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   switch (a.g) {
-    case 1: return launch_g<1>(a, s);
-    case 2: return launch_g<2>(a, s);
-    case 3: return launch_g<3>(a, s);
-    case 4: return launch_g<4>(a, s);
+    case 1: return launch_mode<1, AM_FUSED>(a, a.plan, a.items_cap, s);
+    case 2: return launch_mode<2, AM_FUSED>(a, a.plan, a.items_cap, s);
+    case 3: return launch_mode<3, AM_FUSED>(a, a.plan, a.items_cap, s);
+    case 4: {
+      // noise head first (H_N into the Z rows), then the signal heads
+      const int* nplan = a.plan ? a.plan + plan_ints(a.nseq, a.T, attn_block_q(4)) : nullptr;
+      const int64_t ncap = (a.T + BQ_NOISE - 1) / BQ_NOISE + a.nseq;
+      hipError_t e = launch_mode<4, AM_NOISE>(a, nplan, ncap, s);
+      if (e != hipSuccess) return e;
+      return launch_mode<4, AM_SIGNAL>(a, a.plan, a.items_cap, s);
+    }
     default: return hipErrorInvalidValue;
   }
 }

@@ -100,7 +100,9 @@ template <> GDLA_DEV float from_f32<float>(float v) { return v; }
 template <> GDLA_DEV bf16 from_f32<bf16>(float v) { return (bf16)v; }   // round to nearest even
 
 GDLA_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-GDLA_DEV float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// sigmoid with the hardware reciprocal (1 ulp) instead of the correctly rounded
+// division sequence: 1/(1 + e^-z) saturates to 0 and 1 through rcp(inf) = 0
+GDLA_DEV float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 GDLA_DEV float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
