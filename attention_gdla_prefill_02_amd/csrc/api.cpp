@@ -193,6 +193,7 @@ gdla_status run_prefill(const gdla_config* cfg, const gdla_weights* w, const Str
     r.cqn = ws + P.cqn; r.ckvn = ws + P.ckvn; r.kr = ws + P.kr; r.lam = (float*)(ws + P.lam);
     r.rope = (float*)(ws + P.rope); r.cache = cache;
     r.split_kv = bf;
+    r.kr_f16 = bf;   // the attention's rotary keys in fp16 (the cache rows stay bf16)
     if ((err = rowprep(r, bf, s)) != hipSuccess) return hip_fail(err, "row prep");
   }
   // 3. latent expansion: K^C = c_KVn W_UK^T (token-major), V^T = W_UV c_KVn^T
@@ -206,6 +207,7 @@ gdla_status run_prefill(const gdla_config* cfg, const gdla_weights* w, const Str
     g.B = w->w_ukv; g.ldb = D.rkv; g.kwrapB = bf ? (int)D.rkv : 0;
     g.C = ws + P.kc; g.ldc = D.nN * D.dn;
     g.M = (int)T; g.N = (int)(D.nN * D.dn); g.K = (int)kk; g.batch = 1; g.epi = EPI_STORE;
+    g.out_f16 = bf;   // content keys in fp16 (score operand)
     if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "latent expand (keys)");
     GemmArgs v{};
     v.A = (const char*)w->w_ukv + (size_t)D.nN * D.dn * D.rkv * e; v.lda = D.rkv;
@@ -227,6 +229,7 @@ gdla_status run_prefill(const gdla_config* cfg, const gdla_weights* w, const Str
       g.C = ws + P.q; g.ldc = D.nq;
       g.G = (float*)(ws + P.gate); g.ldg = D.ngate;
       g.M = (int)T; g.N = (int)(D.nq + D.ngate); g.K = (int)D.rq; g.batch = 1; g.epi = EPI_QG;
+      g.out_f16 = true;   // queries in fp16 (score operand); the gate stays fp32
       g.rope = (const float*)(ws + P.rope); g.q_cols = (int)D.nq;
       g.d_qk = (int)D.dqk; g.d_nope = (int)D.dn; g.d_rope = (int)D.dr;
       if ((err = gemm(g, s)) != hipSuccess) return hip_fail(err, "query/gate projection");
@@ -260,6 +263,7 @@ gdla_status run_prefill(const gdla_config* cfg, const gdla_weights* w, const Str
     a.nN = (int)D.nN; a.g = (int)D.g; a.window = cfg->window;
     a.d_nope = (int)D.dn; a.d_rope = (int)D.dr; a.d_v = (int)D.dv;
     a.scale = (float)(1.0 / std::sqrt((double)D.dqk));
+    a.qk_f16 = bf;
     if (bf && S.cu) {
       int* plan = (int*)(ws + P.plan);
       if ((err = attn_plan(S.cu, S.nseq, T, (int)D.g, plan, s)) != hipSuccess) return hip_fail(err, "attention plan");

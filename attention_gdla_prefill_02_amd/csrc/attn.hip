@@ -17,9 +17,12 @@
 //    staged in LDS once and reused by every wave.  Tiles go HBM -> LDS with
 //    global_load_lds (no register staging) into a three-slot ring: step t
 //    issues tile t+2's loads while it computes with tiles t and t+1.
-//  * Scores are formed transposed, S^T = K Q^T, on the 32x32x16 bf16 MFMA:
-//    the 192-wide key row is the A operand (read from LDS), the wave's query
-//    rows are the B operand held in registers for the whole sweep.  Each lane
+//  * Scores are formed transposed, S^T = K Q^T, on the 32x32x16 MFMA (fp16
+//    queries and keys on the inference path, whose 11-bit significands keep
+//    the score error an eighth of bf16's; bf16 when the training forward
+//    runs): the 192-wide key row is the A operand (read from LDS), the wave's
+//    query rows are the B operand held in registers for the whole sweep.
+//    P and V stay bf16.  Each lane
 //    then owns one query column, so the softmax row max needs one exchange
 //    with lane l^32 and the row sum needs none until the end.
 //  * Key rows are fed to the A operand with bits 2 and 3 of the in-tile index
@@ -52,6 +55,7 @@
 // The fp32 kernel is a plain vector-ALU version (three passes per query and
 // head) for the fp32 configuration.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -134,10 +138,14 @@ template <int G, int M> struct Shape {
 };
 constexpr int BQ_NOISE = Shape<4, AM_NOISE>::BQ;
 
-template <int G, int MODE>
+template <int G, int MODE, bool F16QK>
 __global__ void __launch_bounds__((64 * Shape<G, MODE>::NW), 1)
 attn_bf16_kernel(AttnArgs a) {
   using S_ = Shape<G, MODE>;
+  // element type of the queries and keys (the score operands): fp16 on the
+  // inference path, bf16 when the backward recomputes the forward
+  using QE = typename std::conditional<F16QK, f16, bf16>::type;
+  using QV = typename std::conditional<F16QK, f16x8, bf16x8>::type;
   constexpr int NH = S_::NH, BQ = S_::BQ;
   constexpr int NW = S_::NW, NT = 64 * NW;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
@@ -184,11 +192,11 @@ attn_bf16_kernel(AttnArgs a) {
   const float sc = a.scale * 1.4426950408889634f;  // exp2 domain
 
   // this wave's query fragments, B operand: column = query, k = 16s + 8hi + e
-  bf16x8 qf[DQK / 16];
+  QV qf[DQK / 16];
   {
-    const bf16* qp = (const bf16*)a.q + (tb + min(qme, L - 1)) * a.ld_q + (int64_t)head * DQK + hi * 8;
+    const QE* qp = (const QE*)a.q + (tb + min(qme, L - 1)) * a.ld_q + (int64_t)head * DQK + hi * 8;
 #pragma unroll
-    for (int s = 0; s < DQK / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+    for (int s = 0; s < DQK / 16; ++s) qf[s] = *reinterpret_cast<const QV*>(qp + 16 * s);
   }
 
   // key tiles this workgroup visits: 32-row tiles of the stream (aligned to the
@@ -261,11 +269,11 @@ attn_bf16_kernel(AttnArgs a) {
 
   // S^T tile of 32 keys: key kb + key_of(e, hi) in element e, column = this lane's query
   auto qk = [&](int buf, f32x16& s) {
-    const bf16* K = reinterpret_cast<const bf16*>(smem_raw + buf * TILE_BYTES) + arow * K_LD + hi * 8;
+    const QE* K = reinterpret_cast<const QE*>(smem_raw + buf * TILE_BYTES) + arow * K_LD + hi * 8;
     s = f32x16{};
 #pragma unroll
     for (int st = 0; st < DQK / 16; ++st) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(K + 16 * st);
+      const QV kf = *reinterpret_cast<const QV*>(K + 16 * st);
       s = mfma32(kf, qf[st], s);
     }
   };
@@ -533,12 +541,12 @@ attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int G, int MODE>
+template <int G, int MODE, bool F16QK>
 hipError_t launch_mode(const AttnArgs& a, const int* plan, int64_t items_cap, hipStream_t s) {
   using S_ = Shape<G, MODE>;
   const size_t lds = lds_bytes(G, MODE);
   // set on every call: no process-wide state, and correct on every device
-  hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<G, MODE>,
+  hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<G, MODE, F16QK>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   AttnArgs k = a;
@@ -547,7 +555,7 @@ hipError_t launch_mode(const AttnArgs& a, const int* plan, int64_t items_cap, hi
   const int64_t blocks = slots * a.nN;
   if (blocks <= 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_bf16_kernel<G, MODE>), dim3((unsigned)blocks), dim3(64 * S_::NW), lds, s, k);
+  hipLaunchKernelGGL((attn_bf16_kernel<G, MODE, F16QK>), dim3((unsigned)blocks), dim3(64 * S_::NW), lds, s, k);
   return hipGetLastError();
 }
 
@@ -690,22 +698,29 @@ hipError_t attn_plan(const int32_t* cu, int nseq, int64_t T, int g, int* plan, h
   return plan_one(cu, nseq, T, BQ_NOISE, plan + plan_ints(nseq, T, attn_block_q(g)), s);
 }
 
-hipError_t attn_bf16(const AttnArgs& a, hipStream_t s) {
-  if (a.T <= 0) return hipSuccess;
+namespace {
+template <bool F16QK>
+hipError_t attn_bf16_t(const AttnArgs& a, hipStream_t s) {
   switch (a.g) {
-    case 1: return launch_mode<1, AM_FUSED>(a, a.plan, a.items_cap, s);
-    case 2: return launch_mode<2, AM_FUSED>(a, a.plan, a.items_cap, s);
-    case 3: return launch_mode<3, AM_FUSED>(a, a.plan, a.items_cap, s);
+    case 1: return launch_mode<1, AM_FUSED, F16QK>(a, a.plan, a.items_cap, s);
+    case 2: return launch_mode<2, AM_FUSED, F16QK>(a, a.plan, a.items_cap, s);
+    case 3: return launch_mode<3, AM_FUSED, F16QK>(a, a.plan, a.items_cap, s);
     case 4: {
       // noise head first (H_N into the Z rows), then the signal heads
       const int* nplan = a.plan ? a.plan + plan_ints(a.nseq, a.T, attn_block_q(4)) : nullptr;
       const int64_t ncap = (a.T + BQ_NOISE - 1) / BQ_NOISE + a.nseq;
-      hipError_t e = launch_mode<4, AM_NOISE>(a, nplan, ncap, s);
+      hipError_t e = launch_mode<4, AM_NOISE, F16QK>(a, nplan, ncap, s);
       if (e != hipSuccess) return e;
-      return launch_mode<4, AM_SIGNAL>(a, a.plan, a.items_cap, s);
+      return launch_mode<4, AM_SIGNAL, F16QK>(a, a.plan, a.items_cap, s);
     }
     default: return hipErrorInvalidValue;
   }
+}
+}  // namespace
+
+hipError_t attn_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  return a.qk_f16 ? attn_bf16_t<true>(a, s) : attn_bf16_t<false>(a, s);
 }
 
 hipError_t attn_f32(const AttnArgs& a, hipStream_t s) {

@@ -7,6 +7,9 @@
 #include <type_traits>
 
 typedef __bf16 bf16;
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -31,6 +34,10 @@ GDLA_DEV void static_for(F&& f) {
 //             column l%32, rows 8*i + 4*(l/32) + j in element 4*i + j.
 GDLA_DEV f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// The same shape with fp16 inputs (the same rate).
+GDLA_DEV f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 //   16x16x32: A lane l supplies row l%16, k = 8*(l/16)+e; B column l%16;
 //             D lane l holds column l%16, rows 4*(l/16) + j.
@@ -98,6 +105,7 @@ GDLA_DEV float to_f32(float v) { return v; }
 template <class T> GDLA_DEV T from_f32(float v);
 template <> GDLA_DEV float from_f32<float>(float v) { return v; }
 template <> GDLA_DEV bf16 from_f32<bf16>(float v) { return (bf16)v; }   // round to nearest even
+template <> GDLA_DEV f16 from_f32<f16>(float v) { return (f16)v; }     // round to nearest even
 
 GDLA_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // sigmoid with the hardware reciprocal (1 ulp) instead of the correctly rounded

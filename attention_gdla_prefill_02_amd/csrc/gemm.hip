@@ -16,7 +16,8 @@
 // optional residual add (latent expansion, output projection), and the
 // query/gate epilogue: RoPE on each head's rotary block (rotate-half: pair
 // (i, i + 32) of the 64-wide block, cos/sin from the per-token table) and a
-// sigmoid on the gate columns.
+// sigmoid on the gate columns.  With bf16 operands the element-type store can
+// also write fp16 (the attention's score operands: content keys, queries).
 #include "common.h"
 #include "kernels.h"
 
@@ -104,7 +105,10 @@ struct EpiMfma {
   template <class T>
   GDLA_DEV void store4(T* p, int n, f32x4 v, int lim, bool vec) const {
     if (vec && n + 3 < N) {
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (std::is_same<T, f16>::value) {
+        f16x4 b = {(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+        __builtin_nontemporal_store(b, reinterpret_cast<f16x4*>(p + n));
+      } else if constexpr (sizeof(T) == 2) {
         bf16x4 b = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
         __builtin_nontemporal_store(b, reinterpret_cast<bf16x4*>(p + n));
       } else {
@@ -408,6 +412,13 @@ hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
                      a.d_nope, a.d_rope, a.G, a.ldg, a.Npad > a.N ? a.Npad : a.N, vec_ok(a.C, a.ldc, 16),
                      vec_ok(a.G, a.ldg, 16), false, vec_ok(a.rope, 0, 16)};
     return launch_gemm<float, false>(a, e, nb2, nb3, s);
+  }
+  if (a.out_f16) {   // fp16 output (queries, content keys of the attention), no residual
+    if (a.R) return hipErrorInvalidValue;
+    EpiMfma<f16> e{(f16*)a.C, a.ldc, nullptr, 0, a.M, a.N, a.epi, a.rope, a.q_cols, a.d_qk,
+                   a.d_nope, a.d_rope, a.G, a.ldg, a.Npad > a.N ? a.Npad : a.N, vec_ok(a.C, a.ldc, 8),
+                   vec_ok(a.G, a.ldg, 16), false, vec_ok(a.rope, 0, 16)};
+    return launch_gemm<f16, false>(a, e, nb2, nb3, s);
   }
   EpiMfma<bf16> e{(bf16*)a.C, a.ldc, (const bf16*)a.R, a.ldr, a.M, a.N, a.epi, a.rope, a.q_cols, a.d_qk,
                   a.d_nope, a.d_rope, a.G, a.ldg, a.Npad > a.N ? a.Npad : a.N, vec_ok(a.C, a.ldc, 8),

@@ -28,6 +28,7 @@ struct GemmArgs {
   int M, N, K, batch;
   int Npad;               // EPI_STORE: columns [N, Npad) are written as zeros (0 = none)
   int epi;
+  bool out_f16;           // bf16 operands: C (EPI_STORE without residual, EPI_QG queries) stored as fp16
   // EPI_QG
   const float* rope;      // [rows][d_rope/2] (cos, sin) pairs
   int q_cols;             // columns [0, q_cols) are query heads (to C), the rest gate (to G)
@@ -85,6 +86,7 @@ struct RowPrepArgs {
   void* cqn; void* ckvn; void* kr; float* lam; float* rope;
   bool split_kv;                         // ckvn rows are [hi | lo] (2*kv_rank wide)
   CacheView cache;                       // base nullable: no cache rows written
+  bool kr_f16;                           // bf16 rows: the rotary key for attention (kr) as fp16 (cache rows stay bf16)
   const int32_t* pos_dev;                // decode: per-row positions (device), else null;
                                          // row b is then sequence b at position pos_dev[b]
   int nsplit; int64_t split_stride;      // down holds nsplit partial sums (elements apart); 0/1 = one
@@ -123,6 +125,8 @@ struct AttnArgs {
   // training forward (bf16, nullable): per-head outputs H [T, H, d_v] bf16 and
   // the exp2-domain log-sum-exp of each (row, head) [T, H] fp32
   void* h_out; float* lse_out;
+  // bf16 kernel: queries, content keys and rotary keys are fp16 (values stay bf16)
+  bool qk_f16;
 };
 hipError_t attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t attn_f32(const AttnArgs& a, hipStream_t s);

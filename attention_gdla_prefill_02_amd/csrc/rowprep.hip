@@ -115,15 +115,22 @@ rowprep_kernel(RowPrepArgs a) {
   const float* kr = ckv + a.kv_rank;
   const int half = a.d_rope / 2;
   T* krow = (T*)a.kr + t * a.d_rope;
+  f16* krow16 = (f16*)a.kr + t * a.d_rope;
   for (int i = lane; i < half; i += 64) {
     float c, s;
     rope_cos_sin(a, i, p, &c, &s);
     a.rope[(t * half + i) * 2] = c;
     a.rope[(t * half + i) * 2 + 1] = s;
     const float x1 = kr[i], x2 = kr[i + half];
-    const T o1 = from_f32<T>(x1 * c - x2 * s), o2 = from_f32<T>(x2 * c + x1 * s);
-    krow[i] = o1;
-    krow[i + half] = o2;
+    const float f1 = x1 * c - x2 * s, f2 = x2 * c + x1 * s;
+    const T o1 = from_f32<T>(f1), o2 = from_f32<T>(f2);
+    if (sizeof(T) == 2 && a.kr_f16) {
+      krow16[i] = (f16)f1;
+      krow16[i + half] = (f16)f2;
+    } else {
+      krow[i] = o1;
+      krow[i + half] = o2;
+    }
     if (crow) {
       crow[a.kv_rank + i] = o1;
       crow[a.kv_rank + i + half] = o2;
@@ -199,15 +206,22 @@ rowprep_block_kernel(RowPrepArgs a) {
   const float* kr = ckv + a.kv_rank;
   const int half = a.d_rope / 2;
   T* krow = (T*)a.kr + t * a.d_rope;
+  f16* krow16 = (f16*)a.kr + t * a.d_rope;
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
     float c, s;
     rope_cos_sin(a, i, p, &c, &s);
     a.rope[(t * half + i) * 2] = c;
     a.rope[(t * half + i) * 2 + 1] = s;
     const float x1 = kr[i], x2 = kr[i + half];
-    const T o1 = from_f32<T>(x1 * c - x2 * s), o2 = from_f32<T>(x2 * c + x1 * s);
-    krow[i] = o1;
-    krow[i + half] = o2;
+    const float f1 = x1 * c - x2 * s, f2 = x2 * c + x1 * s;
+    const T o1 = from_f32<T>(f1), o2 = from_f32<T>(f2);
+    if (sizeof(T) == 2 && a.kr_f16) {
+      krow16[i] = (f16)f1;
+      krow16[i + half] = (f16)f2;
+    } else {
+      krow[i] = o1;
+      krow[i + half] = o2;
+    }
     if (crow) {
       crow[a.kv_rank + i] = o1;
       crow[a.kv_rank + i + half] = o2;
@@ -312,14 +326,21 @@ rowprep_vec_kernel(RowPrepArgs a) {
   const float* kr = row + a.q_rank + a.kv_rank;
   const int half = a.d_rope / 2;
   bf16* krow = (bf16*)a.kr + t * a.d_rope;
+  f16* krow16 = (f16*)a.kr + t * a.d_rope;
   for (int i = lane; i < half; i += 64) {
     float c, sn;
     rope_cos_sin(a, i, p, &c, &sn);
     *reinterpret_cast<float2*>(a.rope + (t * half + i) * 2) = float2{c, sn};
     const float x1 = kr[i], x2 = kr[i + half];
-    const bf16 o1 = (bf16)(x1 * c - x2 * sn), o2 = (bf16)(x2 * c + x1 * sn);
-    krow[i] = o1;
-    krow[i + half] = o2;
+    const float f1 = x1 * c - x2 * sn, f2 = x2 * c + x1 * sn;
+    const bf16 o1 = (bf16)f1, o2 = (bf16)f2;
+    if (a.kr_f16) {
+      krow16[i] = (f16)f1;
+      krow16[i + half] = (f16)f2;
+    } else {
+      krow[i] = o1;
+      krow[i + half] = o2;
+    }
     if (crow) {
       crow[a.kv_rank + i] = o1;
       crow[a.kv_rank + i + half] = o2;

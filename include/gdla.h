@@ -117,7 +117,13 @@ typedef struct {          /* device pointers, all [out, in] row-major, dtype of 
 /* Support limits of the bf16 path (the fp32 path takes any positive sizes with
  * d_rope even, d_nope + d_rope <= 256, d_v <= 256, and L <= 8192):
  *   d_nope = 128, d_rope = 64, d_v = 128, group + 1 <= 8,
- *   d_model, q_rank, kv_rank and nS * d_v multiples of 64.            */
+ *   d_model, q_rank, kv_rank and nS * d_v multiples of 64.
+ * Prefill (gdla_prefill, gdla_prefill_packed) stores the score operands --
+ * queries, content keys, rotary keys -- as fp16: 11-bit significands cut
+ * the score rounding error 8x against bf16, but every query and key element
+ * must stay below 65504 in magnitude (beyond it the element becomes +-inf
+ * and the output of that row NaN).  The cache rows, values and Z stay bf16;
+ * decode and the training forward keep bf16 queries and keys.        */
 
 /* Bytes of workspace gdla_prefill needs for B sequences of L tokens
  * (0 if the configuration is invalid). */
@@ -169,18 +175,21 @@ gdla_status gdla_prefill_stages(const gdla_config* cfg, const gdla_weights* w, i
 
 /* Byte offsets of the intermediates inside the prefill workspace after a call
  * (for inspection and tests).  T = B*L tokens; elements are in the config
- * dtype unless marked fp32.
+ * dtype unless marked fp32 -- except that in the bf16 configuration the
+ * score operands q, kc and kr are fp16 (11-bit significands: the scores
+ * carry an eighth of the bf16 rounding error; values must stay below 65504
+ * in magnitude).
  *   down   [T, q_rank + kv_rank + d_rope + nS] fp32: c_Q | c_KV | k_R | lambda logit
  *   cqn    [T, q_rank]            normalized query latent
  *   ckvn   bf16: [T, 2*kv_rank]   normalized KV latent as hi | lo, where
  *                                 hi = bf16(c_KVn) and lo = bf16(c_KVn - hi);
  *          fp32: [T, kv_rank]
- *   kr     [T, d_rope]            RoPE'd rotary key
+ *   kr     [T, d_rope]            RoPE'd rotary key (fp16 in the bf16 configuration)
  *   lam    [T, nS] fp32           lambda
  *   rope   [T, d_rope/2, 2] fp32  cos, sin of each position's RoPE angles
- *   q      [T, H*(d_nope+d_rope)] query heads, rotary parts RoPE'd
+ *   q      [T, H*(d_nope+d_rope)] query heads, rotary parts RoPE'd (fp16 in the bf16 configuration)
  *   gate   [T, nS*d_v] fp32       sigmoid gate
- *   kc     [T, nN*d_nope]         content keys
+ *   kc     [T, nN*d_nope]         content keys (fp16 in the bf16 configuration)
  *   vt     [nN*d_v, Tp]           values transposed: token t in column t;
  *                                 Tp = T rounded up to 64, columns T.. zero
  *   z      [T, nS*d_v]            gate * D                                     */
