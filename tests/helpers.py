@@ -12,6 +12,11 @@ from oracle import gdla_ref as R
 
 TOL = {"fp32": dict(max_abs=1e-4, rel_l2=1e-5), "bf16": dict(max_abs=2e-2, rel_l2=5e-3)}
 
+# Guard band: a check also fails once its error uses more than this fraction
+# of a bar, so a change that eats the precision margin (one more rounding, a
+# reordered sum) shows up before the bar itself is crossed.
+GUARD = 0.95
+
 # bf16 shapes with the real head dims and small widths: spans several tiles of
 # every kernel while the oracle finishes in well under a second.
 SMALL = dict(d_model=256, q_rank=128, kv_rank=128, n_noise=2, group=3, d_nope=128, d_rope=64, d_v=128)
@@ -37,6 +42,9 @@ def assert_close(got, ref, dtype, what="", tol=None):
     assert np.all(np.isfinite(np.asarray(got, np.float64))), f"{what}: non-finite output"
     assert ma <= t["max_abs"], f"{what}: max_abs {ma:.3e} > {t['max_abs']:.1e}"
     assert rl <= t["rel_l2"], f"{what}: rel_l2 {rl:.3e} > {t['rel_l2']:.1e}"
+    assert ma <= GUARD * t["max_abs"] and rl <= GUARD * t["rel_l2"], (
+        f"{what}: within the bar but inside the {1 - GUARD:.0%} guard band "
+        f"(max_abs {ma / t['max_abs']:.3f}, rel_l2 {rl / t['rel_l2']:.3f} of the bar)")
 
 
 def oracle_cfg(shapes, window=0, rope_base=10000.0, rms_eps=1e-6):
