@@ -433,8 +433,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the GDLA path here is built and timed on a single MI355X; "
-              "runs on more than one GPU are not part of this build (see the sharding notes in DESIGN.md).",
+        print("bench.py measures one GPU: the GDLA path is built and timed on a single MI355X, and "
+              "runs on more than one GPU are not supported (--gpus must be 1).",
               file=sys.stderr)
         sys.exit(2)
 
