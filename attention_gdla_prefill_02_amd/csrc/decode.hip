@@ -20,9 +20,10 @@
 //                 new row [c_KVn | RoPE(k_R)] to the cache (one block per row)
 //   skinny_gemm   c_Qn -> q (RoPE) and gate (sigmoid, fp32)
 //   absorb        q~ for every head (W_UK read transposed from LDS with the
-//                 gfx950 transpose read), packed with q^R into 576-wide rows
-//   plan          per-sequence attended range; the 32-row tiles of all
-//                 sequences are split evenly over up to 512 workgroups
+//                 gfx950 transpose read), packed with q^R into 576-wide rows;
+//                 one extra workgroup of the launch builds the plan
+//                 (per-sequence attended range; the 32-row tiles of all
+//                 sequences split evenly over up to 512 workgroups)
 //   dec_attn      one workgroup per tile range, all heads: cache tiles go
 //                 HBM -> LDS directly (double buffered); scores on the
 //                 16x16x32 MFMA with the cache rows as A operand; P V with the
@@ -313,54 +314,77 @@ struct AbsorbArgs {
   const bf16* w_ukv; int kv_rank;     // content-key rows of W_UKV: [nN*128, kv_rank]
   int B, nN, g, nS, H;
   bf16* qlat;                          // [B, H, kv_rank + 64]
+  // the latent attention's plan, built by one extra workgroup of the same
+  // launch (it depends on the positions only)
+  const int32_t* lens; int64_t cap; int window; int* plan;
 };
+
+__device__ void plan_body(const int32_t* lens, int B, int64_t cap, int window, int* plan, int* sc);
 
 // row stride 192 B: the four rows a 32-lane transposed read pass touches
 // (64 B each) fall on disjoint quarters of the 64 four-byte LDS banks
 constexpr int AB_LD = 96;
 
-// grid (kv_rank/64, nN, cdiv(B*(g+1), 256)); C[(b,h), r] = sum_i q^C[b,h,i] W_UK,n[i, r]
+// grid (kv_rank/64 + 1, nN, cdiv(B*(g+1), 256)); C[(b,h), r] = sum_i q^C[b,h,i] W_UK,n[i, r].
+// Workgroup (kv_rank/64, 0, 0) builds the plan instead; the rest of that
+// column of the grid has nothing to do.
 __global__ void __launch_bounds__(256)
 absorb_kernel(AbsorbArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 w[DN * AB_LD];
+  if (blockIdx.x == gridDim.x - 1) {
+    if (blockIdx.y == 0 && blockIdx.z == 0) {
+      plan_body(a.lens, a.B, a.cap, a.window, a.plan, reinterpret_cast<int*>(w));
+    }
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5, r16 = lane & 15, g16 = lane >> 4;
   const int r0 = blockIdx.x * 64, n = blockIdx.y;
   const int mbase = blockIdx.z * 256 + wave * 64;
   const int RL = a.kv_rank + DR;
   const int Mtot = a.B * (a.g + 1);
-  for (int c = tid; c < DN * 8; c += 256) {
-    const int i = c >> 3, cc = c & 7;
-    *reinterpret_cast<bf16x8*>(w + i * AB_LD + cc * 8) =
-        *reinterpret_cast<const bf16x8*>(a.w_ukv + (int64_t)(n * DN + i) * a.kv_rank + r0 + cc * 8);
-  }
-  __syncthreads();
   auto head_of = [&](int m, int* b) {
     *b = m / (a.g + 1);
     const int hs = m % (a.g + 1);
     return hs < a.g ? n * a.g + hs : a.nS + n;
   };
+  // this lane's query fragments first: their loads are in flight together
+  // with the weight slice's
+  const bf16x8 zero8 = {};
+  bf16x8 af[DN / 16][2];
+#pragma unroll
+  for (int tm = 0; tm < 2; ++tm) {
+    const int m = mbase + 32 * tm + l32;
+    const bool ok = m < Mtot;
+    int b;
+    const int h = head_of(ok ? m : 0, &b);
+    const bf16* arow = a.q + (int64_t)b * a.ldq + (int64_t)h * DQK + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < DN / 16; ++s) af[s][tm] = ok ? *reinterpret_cast<const bf16x8*>(arow + 16 * s) : zero8;
+  }
+  {
+    constexpr int NC = DN * 8 / 256;   // 16-byte chunks per thread, all loads issued before the first store
+    bf16x8 wv[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = tid + 256 * j, i = c >> 3, cc = c & 7;
+      wv[j] = *reinterpret_cast<const bf16x8*>(a.w_ukv + (int64_t)(n * DN + i) * a.kv_rank + r0 + cc * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = tid + 256 * j, i = c >> 3, cc = c & 7;
+      *reinterpret_cast<bf16x8*>(w + i * AB_LD + cc * 8) = wv[j];
+    }
+  }
+  __syncthreads();
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  const bf16* arow[2];
-  bool aok[2];
-#pragma unroll
-  for (int tm = 0; tm < 2; ++tm) {
-    const int m = mbase + 32 * tm + l32;
-    aok[tm] = m < Mtot;
-    int b;
-    const int h = head_of(aok[tm] ? m : 0, &b);
-    arow[tm] = a.q + (int64_t)b * a.ldq + (int64_t)h * DQK;
-  }
-  const bf16x8 zero8 = {};
 #pragma unroll
   for (int s = 0; s < DN / 16; ++s) {
-    bf16x8 af[2], bfr[2];
-#pragma unroll
-    for (int tm = 0; tm < 2; ++tm) af[tm] = aok[tm] ? *reinterpret_cast<const bf16x8*>(arow[tm] + 16 * s + 8 * hi) : zero8;
+    bf16x8 bfr[2];
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn) {
       // B operand: column = r (32*tn + 16*(g16&1) + r16), k = 16s + 8*(g16>>1) + e
@@ -372,7 +396,7 @@ absorb_kernel(AbsorbArgs a) {
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn) acc[tm][tn] = mfma32(af[tm], bfr[tn], acc[tm][tn]);
+      for (int tn = 0; tn < 2; ++tn) acc[tm][tn] = mfma32(af[s][tm], bfr[tn], acc[tm][tn]);
   }
 #pragma unroll
   for (int tm = 0; tm < 2; ++tm)
@@ -460,9 +484,8 @@ __device__ int block_incl_scan(int v, int* sc, int* total) {
   return r;
 }
 
-__global__ void __launch_bounds__(256)
-plan_kernel(const int32_t* lens, int B, int64_t cap, int window, int* plan) {
-  __shared__ int sc[256];
+// One 256-thread workgroup; sc: 256 ints of LDS.
+__device__ void plan_body(const int32_t* lens, int B, int64_t cap, int window, int* plan, int* sc) {
   int* tstart = plan + 2;
   int* lo = tstart + B + 1;
   int* len = lo + B;
@@ -1005,15 +1028,13 @@ hipError_t decode_step(const gdla_config* c, const gdla_weights* w, int B, const
   // 4. absorption
   {
     AbsorbArgs k{(const bf16*)(ws + Lw.q), H * DQK, (const bf16*)w->w_ukv, rkv, B, nN, g, nS, H,
-                 (bf16*)(ws + Lw.qlat)};
-    hipLaunchKernelGGL(absorb_kernel, dim3(rkv / 64, nN, cdiv((int64_t)B * (g + 1), 256)), dim3(256), 0, s, k);
+                 (bf16*)(ws + Lw.qlat), cache_lens, (int64_t)cache.page_rows * cache.max_pages, c->window,
+                 (int*)(ws + Lw.plan)};
+    hipLaunchKernelGGL(absorb_kernel, dim3(rkv / 64 + 1, nN, cdiv((int64_t)B * (g + 1), 256)), dim3(256), 0, s, k);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  // 5. plan and latent attention
+  // 5. latent attention
   int* plan = (int*)(ws + Lw.plan);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, cache_lens, B,
-                     (int64_t)cache.page_rows * cache.max_pages, c->window, plan);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
   {
     DecAttnArgs k{(const bf16*)(ws + Lw.qlat), cache, (int)((int64_t)B * cache.max_pages * 4),
                   cache.bt ? __builtin_ctz((unsigned)cache.page_rows) : 0, B, H, plan, (float*)(ws + Lw.ml),
