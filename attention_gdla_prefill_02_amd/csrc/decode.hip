@@ -869,7 +869,7 @@ combine_kernel(CombineArgs a) {
     if ((slot & 3) == 3 || slot == a.g) __syncthreads();
   }
   // weighted sums: thread t owns latent dims 2t, 2t + 1 of every head slot; the
-  // loads of two segments x all slots are issued before any is consumed
+  // loads of four segments x all slots are issued before any is consumed
   const int d = 2 * threadIdx.x;
   float2 acc[5] = {};
   int hs[5];
@@ -879,31 +879,23 @@ combine_kernel(CombineArgs a) {
     auto seg_row = [&](int c, int slot) {
       return reinterpret_cast<const float2*>(a.part_o + ((int64_t)(c0 + c) * a.H + hs[slot]) * a.kv_rank + d);
     };
-    int c = 0;
-    for (; c + 2 <= nch; c += 2) {
-      float2 p0[5], p1[5];
+    constexpr int U = 4;
+    for (int c = 0; c < nch; c += U) {
+      float2 p[U][5];
 #pragma unroll
-      for (int slot = 0; slot < 5; ++slot)
-        if (slot <= a.g) {
-          p0[slot] = *seg_row(c, slot);
-          p1[slot] = *seg_row(c + 1, slot);
-        }
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int slot = 0; slot < 5; ++slot)
-        if (slot <= a.g) {
-          const float w0 = wts[slot][c], w1 = wts[slot][c + 1];
-          acc[slot].x += w0 * p0[slot].x + w1 * p1[slot].x;
-          acc[slot].y += w0 * p0[slot].y + w1 * p1[slot].y;
-        }
-    }
-    if (c < nch) {
+        for (int slot = 0; slot < 5; ++slot)
+          p[u][slot] = (slot <= a.g && c + u < nch) ? *seg_row(c + u, slot) : float2{0.f, 0.f};
 #pragma unroll
-      for (int slot = 0; slot < 5; ++slot)
-        if (slot <= a.g) {
-          const float2 p = *seg_row(c, slot);
-          acc[slot].x += wts[slot][c] * p.x;
-          acc[slot].y += wts[slot][c] * p.y;
-        }
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int slot = 0; slot < 5; ++slot)
+          if (slot <= a.g && c + u < nch) {
+            const float wv = wts[slot][c + u];
+            acc[slot].x += wv * p[u][slot].x;
+            acc[slot].y += wv * p[u][slot].y;
+          }
     }
 #pragma unroll
     for (int slot = 0; slot < 4; ++slot) {
