@@ -67,10 +67,12 @@ signal head j and noise head j//g both use KV head j//g; window W means keys
 s with t - W < s <= t (W <= 0 or W >= L: full causal); no biases; weights are
 [out, in] (y = x W^T); W_UKV rows are all content-key heads then all value
 heads.  YaRN (when cfg.yarn_factor > 1, full-causal layers only): the
-frequency table and the cos/sin multiplier m of the listing in [OSM-yarn],
-applied to the rotary parts, so the rotary part of every logit scales by m^2
-(the page's prose writes the temperature as sqrt(1 + 0.1 ln s) on the logits;
-the listing is the executable statement and is the reading taken).
+frequency table of the listing in [OSM-yarn]; its temperature m = 1 + 0.1 ln s
+either multiplies cos and sin (cfg.yarn_temperature "rotary", the listing, the
+default: the rotary part of every logit scales by m^2) or the whole logit by
+m^2 ("logit": the page's prose puts the temperature on the softmax logits,
+garbled as sqrt(1 + 0.1 ln s), and [M3-ctx] names the DeepSeek form of YaRN,
+which scales the softmax by the square of the same m).
 Packed sequences ([M3-pack]): sequence b of a packed stream holds rows
 cu[b] .. cu[b+1]-1, its positions restart at pos_offsets[b], and its tokens
 attend only to earlier tokens of the same sequence -- each sequence is the
@@ -110,6 +112,13 @@ class Cfg:
     yarn_orig_len: int = 4096    # native context length
     yarn_beta_fast: float = 32.0
     yarn_beta_slow: float = 1.0
+    # where YaRN's temperature m = 1 + 0.1 ln s goes: "rotary" multiplies cos
+    # and sin by m (the listing of [OSM-yarn]; with the decoupled rotary part
+    # only the rotary term of each logit scales, by m^2); "logit" multiplies
+    # the whole logit by m^2 and leaves cos and sin unscaled (the prose of
+    # [OSM-yarn] applies the temperature to the softmax logits, and [M3-ctx]
+    # names the DeepSeek form of YaRN)
+    yarn_temperature: str = "rotary"
 
     @property
     def n_signal(self) -> int:
@@ -185,14 +194,39 @@ def yarn_mscale(s):
     return 1.0 + 0.1 * math.log(s)
 
 
+def yarn_active(cfg: Cfg) -> bool:
+    """YaRN applies on full-causal layers only ([M3-ctx])."""
+    return cfg.yarn_factor > 1.0 and cfg.window <= 0
+
+
 def rope_params(cfg: Cfg):
     """(base, yarn) for rope(): yarn is None for plain RoPE, else
-    (s, orig_len, beta_fast, beta_slow).  YaRN only on full-causal layers
-    ([M3-ctx])."""
-    if cfg.yarn_factor > 1.0 and cfg.window <= 0:
+    (s, orig_len, beta_fast, beta_slow, m) with m the cos/sin multiplier:
+    yarn_mscale(s) for the "rotary" temperature, 1 for "logit"."""
+    if yarn_active(cfg):
+        m = yarn_mscale(cfg.yarn_factor) if cfg.yarn_temperature == "rotary" else 1.0
         return cfg.rope_base, (float(cfg.yarn_factor), float(cfg.yarn_orig_len),
-                               float(cfg.yarn_beta_fast), float(cfg.yarn_beta_slow))
+                               float(cfg.yarn_beta_fast), float(cfg.yarn_beta_slow), m)
     return cfg.rope_base, None
+
+
+def logit_scale(cfg: Cfg) -> float:
+    """Multiplier of q . k in the softmax: 1/sqrt(d_qk) ([OSM-1]), times m^2
+    on a YaRN layer with the "logit" temperature ([OSM-yarn])."""
+    scale = 1.0 / math.sqrt(cfg.d_qk)
+    if yarn_active(cfg) and cfg.yarn_temperature == "logit":
+        scale *= yarn_mscale(cfg.yarn_factor) ** 2
+    return scale
+
+
+def _yarn_table(d, base, yarn):
+    """(frequencies, cos/sin multiplier) of a rope() yarn argument: None, or
+    (s, orig_len, beta_fast, beta_slow[, m]); m defaults to yarn_mscale(s)."""
+    if yarn is None:
+        return rope_inv_freq(d, base), 1.0
+    s_, orig, bf, bs = yarn[:4]
+    m = yarn[4] if len(yarn) > 4 else yarn_mscale(s_)
+    return yarn_inv_freq(d, base, s_, orig, bf, bs), m
 
 
 def rope(u, pos, base, yarn=None):
@@ -201,17 +235,13 @@ def rope(u, pos, base, yarn=None):
     For each i < d_rope/2 the pair (u_i, u_{i+d/2}) is rotated by angle
     pos * theta_i:  u_i' = u_i cos - u_{i+d/2} sin,
                     u_{i+d/2}' = u_{i+d/2} cos + u_i sin.
-    With yarn = (s, orig_len, beta_fast, beta_slow) the frequencies are YaRN's
-    and cos, sin carry the factor m = 1 + 0.1 ln s ([OSM-yarn]).
+    With yarn = (s, orig_len, beta_fast, beta_slow[, m]) the frequencies are
+    YaRN's and cos, sin carry the factor m (default 1 + 0.1 ln s, [OSM-yarn]).
     """
     u = _f64(u)
     d = u.shape[-1]
     half = d // 2
-    if yarn is None:
-        inv, m = rope_inv_freq(d, base), 1.0
-    else:
-        s_, orig, bf, bs = yarn
-        inv, m = yarn_inv_freq(d, base, s_, orig, bf, bs), yarn_mscale(s_)
+    inv, m = _yarn_table(d, base, yarn)
     ang = _f64(pos)[:, None] * inv[None, :]      # [T, d/2]
     cos, sin = m * np.cos(ang), m * np.sin(ang)
     u1, u2 = u[..., :half], u[..., half:]
@@ -317,15 +347,17 @@ def _consecutive_runs(rows, max_len):
     return runs
 
 
-def attention_heads(q, kc, kr, v, rows, cfg: Cfg):
+def attention_heads(q, kc, kr, v, rows, cfg: Cfg, scale=None):
     """Per-head causal / sliding-window softmax attention ([OSM-1], [M3-eq]).
 
     q [R, H, d_qk] for query positions `rows`; kc [L, nN, d_nope]; kr [L, d_rope]
     (one rotary key per token, shared by all heads); v [L, nN, d_v].
-    H[r, h] = sum_{s in A(t)} softmax_s(q_h . [k^C_n,s | k_R,s] / sqrt(d_qk)) v_n,s
-    with n = kv_head_of(h), A(t) = attended_keys(t, window).
+    H[r, h] = sum_{s in A(t)} softmax_s(scale q_h . [k^C_n,s | k_R,s]) v_n,s
+    with n = kv_head_of(h), A(t) = attended_keys(t, window), scale =
+    logit_scale(cfg) unless given.
     """
-    scale = 1.0 / math.sqrt(cfg.d_qk)
+    if scale is None:
+        scale = logit_scale(cfg)
     out = np.zeros((len(rows), cfg.n_heads, cfg.d_v))
     index = {t: i for i, t in enumerate(rows)}
     runs = _consecutive_runs(rows, 128)
@@ -433,7 +465,7 @@ def gdla_decode(x_new, W, cfg: Cfg, cache, cache_lens):
         kr = rows[:, cfg.kv_rank:]
         # keys are indexed relative to lo, so the query sits at hi-1-lo
         Hh = attention_heads(pr["q"], kc, kr, v, [hi - 1 - lo],
-                             _with_window(cfg, 0))[0]
+                             _with_window(cfg, 0), scale=logit_scale(cfg))[0]
         y, Z, _ = differential_gate_out(Hh[None, :cfg.n_signal], Hh[None, cfg.n_signal:],
                                         pr["lam"], pr["gate"], W["w_o"], cfg)
         ys.append(y[0])
@@ -552,11 +584,7 @@ def rope_backward(g, pos, base, yarn=None):
     g = _f64(g)
     d = g.shape[-1]
     half = d // 2
-    if yarn is None:
-        inv, m = rope_inv_freq(d, base), 1.0
-    else:
-        s_, orig, bf, bs = yarn
-        inv, m = yarn_inv_freq(d, base, s_, orig, bf, bs), yarn_mscale(s_)
+    inv, m = _yarn_table(d, base, yarn)
     ang = _f64(pos)[:, None] * inv[None, :]
     cos, sin = m * np.cos(ang), m * np.sin(ang)
     g1, g2 = g[..., :half], g[..., half:]
@@ -574,7 +602,7 @@ def attention_heads_backward(q, kc, kr, v, dH, cfg: Cfg, rows=None):
     dkc [L, nN, d_nope], dkr [L, d_rope], dv [L, nN, d_v]."""
     L = kc.shape[0]
     R = np.arange(L) if rows is None else np.asarray(rows)
-    scale = 1.0 / math.sqrt(cfg.d_qk)
+    scale = logit_scale(cfg)
     dq = np.zeros_like(_f64(q))
     dkc = np.zeros((L, cfg.n_noise, cfg.d_nope))
     dkr = np.zeros((L, cfg.d_rope))

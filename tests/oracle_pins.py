@@ -543,6 +543,51 @@ def pin_yarn_full_layers_only():
     assert np.max(np.abs(full - R.gdla_layer(x, W, TINY)["y"])) > 1e-6
 
 
+YARN_TINY = dict(yarn_factor=64.0, yarn_orig_len=4, yarn_beta_fast=2.0, yarn_beta_slow=0.5)
+
+
+def pin_yarn_logit_temperature_two_keys():
+    """With the "logit" temperature every logit of a YaRN layer is multiplied
+    by m^2 = (1 + 0.1 ln 64)^2: row 1 seeing keys 0 and 1 gives
+    H = v0 + sigmoid(m^2 (s1 - s0) / sqrt(d_qk)) (v1 - v0).  The "rotary"
+    temperature (the listing) puts m on cos and sin instead, so on given
+    rotated queries and keys its attention carries no extra factor; nor does a
+    windowed layer (YaRN only on full-causal layers)."""
+    m2 = (1.0 + 0.1 * math.log(64.0)) ** 2
+    q, kc, kr, v = _rand_qkv(TINY, 2, seed=23)
+    for temp, win, f in (("logit", 0, m2), ("rotary", 0, 1.0), ("logit", 3, 1.0)):
+        cfg = replace(TINY, window=win, yarn_temperature=temp, **YARN_TINY)
+        H = R.attention_heads(q[1:2], kc, kr, v, [1], cfg)[0]
+        for h in range(cfg.n_heads):
+            n = h // cfg.group if h < cfg.n_signal else h - cfg.n_signal
+            k0 = np.concatenate([kc[0, n], kr[0]])
+            k1 = np.concatenate([kc[1, n], kr[1]])
+            a = 1.0 / (1.0 + math.exp(-f * (q[1, h] @ k1 - q[1, h] @ k0) / math.sqrt(cfg.d_qk)))
+            close(H[h], v[0, n] + a * (v[1, n] - v[0, n]), 1e-12)
+
+
+def pin_yarn_temperature_modes():
+    """The two temperatures differ only in where m goes.  The "logit" one
+    leaves cos and sin unscaled (rotated vectors keep their length), the
+    "rotary" one scales them by m.  With the content keys zeroed (the content
+    rows of W_UKV), every logit is its rotary term, which both scale by m^2,
+    so the two layers agree; with content keys they differ."""
+    m = 1.0 + 0.1 * math.log(64.0)
+    u = np.random.Generator(np.random.PCG64(6)).standard_normal((3, 4))
+    pos = np.array([0.0, 3.0, 50.0])
+    cfg_l = replace(TINY, yarn_temperature="logit", **YARN_TINY)
+    cfg_r = replace(TINY, yarn_temperature="rotary", **YARN_TINY)
+    for cfg, f in ((cfg_l, 1.0), (cfg_r, m)):
+        r = R.rope(u, pos, *R.rope_params(cfg))
+        close(np.linalg.norm(r, axis=-1), f * np.linalg.norm(u, axis=-1), 1e-12)
+    W = tiny_weights(seed=40)
+    x = tiny_x(B=1, L=7, seed=41)
+    assert np.max(np.abs(R.gdla_layer(x, W, cfg_l)["y"] - R.gdla_layer(x, W, cfg_r)["y"])) > 1e-6
+    W0 = dict(W, w_ukv=W["w_ukv"].copy())
+    W0["w_ukv"][:TINY.n_noise * TINY.d_nope] = 0.0
+    close(R.gdla_layer(x, W0, cfg_l)["y"], R.gdla_layer(x, W0, cfg_r)["y"], 1e-12)
+
+
 # ------------------------------------------- packed sequences and the paged cache
 PACK_LENS = (3, 1, 5, 0, 2)
 PACK_POS = (0, 7, 2, 9, 4)
@@ -736,9 +781,11 @@ def pin_backward_finite_differences_window_batch():
 
 
 def pin_backward_finite_differences_yarn():
-    """The same with YaRN frequencies and the cos/sin factor on a full layer."""
+    """The same with YaRN frequencies and the cos/sin factor on a full layer,
+    and with the temperature on the whole logit instead."""
     cfg = replace(TINY, yarn_factor=8.0, yarn_orig_len=8, yarn_beta_fast=32.0, yarn_beta_slow=1.0)
     _fd_check(cfg, pos_offset=3, seed=31)
+    _fd_check(replace(cfg, yarn_temperature="logit"), pos_offset=3, seed=32)
 
 
 def pin_rope_backward_is_adjoint():

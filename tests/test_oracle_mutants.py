@@ -119,14 +119,14 @@ def _query_rope_on_content(x, W, cfg, pos):
 _orig_attn = R.attention_heads
 
 
-def _attn_scale_dnope(q, kc, kr, v, rows, cfg):
+def _attn_scale_dnope(q, kc, kr, v, rows, cfg, scale=None):
     # a scale of 1/sqrt(d_nope) instead of 1/sqrt(d_nope + d_rope)
     f = math.sqrt(cfg.d_nope / cfg.d_qk)
-    return _orig_attn(np.asarray(q) / f, kc, kr, v, rows, cfg)
+    return _orig_attn(np.asarray(q) / f, kc, kr, v, rows, cfg, scale)
 
 
-def _attn_drop_rope_term(q, kc, kr, v, rows, cfg):
-    return _orig_attn(q, kc, np.zeros_like(np.asarray(kr, np.float64)), v, rows, cfg)
+def _attn_drop_rope_term(q, kc, kr, v, rows, cfg, scale=None):
+    return _orig_attn(q, kc, np.zeros_like(np.asarray(kr, np.float64)), v, rows, cfg, scale)
 
 
 _orig_decode = R.gdla_decode
@@ -219,6 +219,20 @@ def _rope_params_every_layer(cfg):
         return cfg.rope_base, (float(cfg.yarn_factor), float(cfg.yarn_orig_len),
                                float(cfg.yarn_beta_fast), float(cfg.yarn_beta_slow))
     return cfg.rope_base, None
+
+
+def _logit_scale_without_temperature(cfg):
+    # the "logit" temperature forgotten: plain 1/sqrt(d_qk) everywhere
+    return 1.0 / math.sqrt(cfg.d_qk)
+
+
+_orig_rope_params = R.rope_params
+
+
+def _rope_params_m_in_both_modes(cfg):
+    # cos and sin scaled by m under the "logit" temperature too
+    base, yarn = _orig_rope_params(cfg)
+    return base, (None if yarn is None else yarn[:4])
 
 
 def _packed_global_positions(x, W, cfg, cu_seqlens, pos_offsets=None):
@@ -341,6 +355,8 @@ MUTANTS = {
     "yarn_times_s": ("yarn_inv_freq", _yarn_times_s),
     "yarn_mscale_sqrt": ("yarn_mscale", _yarn_mscale_sqrt),
     "yarn_on_window_layers": ("rope_params", _rope_params_every_layer),
+    "yarn_logit_temperature_dropped": ("logit_scale", _logit_scale_without_temperature),
+    "yarn_m_on_rope_in_logit_mode": ("rope_params", _rope_params_m_in_both_modes),
     "packed_global_positions": ("gdla_layer_packed", _packed_global_positions),
     "packed_leaky": ("gdla_layer_packed", _packed_leaky),
     "packed_segments_skip_first": ("packed_segments", _packed_segments_skip_first),
