@@ -66,6 +66,8 @@ gdla_status check_config(const gdla_config* c) {
       !(std::isfinite(c->yarn_factor) && c->yarn_orig_len > 0 && std::isfinite(c->yarn_beta_fast) &&
         c->yarn_beta_slow > 0.f && c->yarn_beta_fast > c->yarn_beta_slow))
     return fail(GDLA_ERR_INVALID_ARG, "YaRN needs a finite factor, yarn_orig_len > 0 and beta_fast > beta_slow > 0");
+  if (c->yarn_temperature != GDLA_YARN_TEMP_ROTARY && c->yarn_temperature != GDLA_YARN_TEMP_LOGIT)
+    return fail(GDLA_ERR_INVALID_ARG, "unknown yarn_temperature %d", (int)c->yarn_temperature);
   const int64_t H = (int64_t)c->group * c->n_noise + c->n_noise;
   if (H * (c->d_nope + c->d_rope) > (1 << 24)) return fail(GDLA_ERR_INVALID_ARG, "too many query heads");
   if (c->dtype == GDLA_BF16) {
@@ -189,7 +191,7 @@ gdla_status run_prefill(const gdla_config* cfg, const gdla_weights* w, const Str
     r.q_rank = (int)D.rq; r.kv_rank = (int)D.rkv; r.d_rope = (int)D.dr; r.nS = (int)D.nS;
     r.g_q = w->g_q; r.g_kv = w->g_kv; r.eps = cfg->rms_eps;
     set_rope(r, cfg->rope_base, cfg->window, cfg->yarn_factor, cfg->yarn_orig_len, cfg->yarn_beta_fast,
-             cfg->yarn_beta_slow);
+             cfg->yarn_beta_slow, cfg->yarn_temperature);
     r.cqn = ws + P.cqn; r.ckvn = ws + P.ckvn; r.kr = ws + P.kr; r.lam = (float*)(ws + P.lam);
     r.rope = (float*)(ws + P.rope); r.cache = cache;
     r.split_kv = bf;
@@ -262,7 +264,8 @@ gdla_status run_prefill(const gdla_config* cfg, const gdla_weights* w, const Str
     a.cu = S.cu; a.nseq = S.nseq;
     a.nN = (int)D.nN; a.g = (int)D.g; a.window = cfg->window;
     a.d_nope = (int)D.dn; a.d_rope = (int)D.dr; a.d_v = (int)D.dv;
-    a.scale = (float)(1.0 / std::sqrt((double)D.dqk));
+    a.scale = (float)(yarn_logit_multiplier(cfg->yarn_factor, cfg->window, cfg->yarn_temperature) /
+                      std::sqrt((double)D.dqk));
     a.qk_f16 = bf;
     if (bf && S.cu) {
       int* plan = (int*)(ws + P.plan);
@@ -314,7 +317,7 @@ const char* gdla_status_string(gdla_status s) {
 
 const char* gdla_last_error(void) { return g_err; }
 
-int32_t gdla_version(void) { return 103; }   // 1.03: layer backward
+int32_t gdla_version(void) { return 104; }   // 1.04: YaRN temperature setting in gdla_config
 
 size_t gdla_prefill_workspace_size(const gdla_config* cfg, int32_t B, int32_t L) {
   if (check_config(cfg) != GDLA_OK || B < 0 || L < 0) return 0;

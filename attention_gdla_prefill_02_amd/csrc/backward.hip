@@ -828,6 +828,8 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
   const int64_t T = c.T, Tp = P.Tp;
   const int64_t nkv = D.nN * (D.dn + D.dv), nqg = D.nq + D.ngate;
   const int rq = (int)D.rq, rkv = (int)D.rkv, d = (int)D.d, nS = (int)D.nS;
+  // YaRN's temperature on the whole logit, when configured so (else 1)
+  const double logit_mult = yarn_logit_multiplier(c.cfg->yarn_factor, c.cfg->window, c.cfg->yarn_temperature);
   hipError_t e;
   // 1. recompute the forward: down-projection, row prep, expansion (token-major
   //    and transposed), query/gate, attention with per-head outputs
@@ -848,7 +850,7 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     r.q_rank = rq; r.kv_rank = rkv; r.d_rope = DR; r.nS = nS;
     r.g_q = c.w->g_q; r.g_kv = c.w->g_kv; r.eps = c.cfg->rms_eps;
     set_rope(r, c.cfg->rope_base, c.cfg->window, c.cfg->yarn_factor, c.cfg->yarn_orig_len, c.cfg->yarn_beta_fast,
-             c.cfg->yarn_beta_slow);
+             c.cfg->yarn_beta_slow, c.cfg->yarn_temperature);
     r.cqn = ws + P.cqn; r.ckvn = ws + P.ckvn; r.kr = ws + P.kr; r.lam = (float*)(ws + P.lam);
     r.rope = (float*)(ws + P.rope); r.split_kv = true;
     if ((e = rowprep(r, true, s)) != hipSuccess) return e;
@@ -891,7 +893,7 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     a.T = T; a.B = c.B; a.L = c.L;
     a.nN = (int)D.nN; a.g = (int)D.g; a.window = c.cfg->window;
     a.d_nope = DN; a.d_rope = DR; a.d_v = DV;
-    a.scale = (float)(1.0 / std::sqrt((double)DQK));
+    a.scale = (float)(logit_mult / std::sqrt((double)DQK));
     a.h_out = ws + P.hall; a.lse_out = (float*)(ws + P.lse);
     if ((e = attn_bf16(a, s)) != hipSuccess) return e;
   }
@@ -949,8 +951,8 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     a.dkv = (bf16*)(ws + P.dkv);
     a.dkr_part = (float*)(ws + P.dkrp);
     a.T = T; a.B = c.B; a.L = c.L; a.nN = (int)D.nN; a.window = c.cfg->window;
-    a.scale = (float)(1.0 / std::sqrt((double)DQK));
-    a.sc = (float)(1.4426950408889634 / std::sqrt((double)DQK));
+    a.scale = (float)(logit_mult / std::sqrt((double)DQK));
+    a.sc = (float)(1.4426950408889634 * logit_mult / std::sqrt((double)DQK));
     switch (D.g) {
       case 1: e = attn_bwd_g<1>(a, s); break;
       case 2: e = attn_bwd_g<2>(a, s); break;

@@ -1002,7 +1002,8 @@ hipError_t decode_step(const gdla_config* c, const gdla_weights* w, int B, const
     r.down = (const float*)(ws + Lw.down); r.ld_down = ndown; r.nsplit = sp_down; r.split_stride = (int64_t)B * ndown;
     r.T = B; r.L = 1; r.q_rank = rq; r.kv_rank = rkv; r.d_rope = DR; r.nS = nS;
     r.g_q = w->g_q; r.g_kv = w->g_kv; r.eps = c->rms_eps;
-    set_rope(r, c->rope_base, c->window, c->yarn_factor, c->yarn_orig_len, c->yarn_beta_fast, c->yarn_beta_slow);
+    set_rope(r, c->rope_base, c->window, c->yarn_factor, c->yarn_orig_len, c->yarn_beta_fast, c->yarn_beta_slow,
+             c->yarn_temperature);
     r.cqn = ws + Lw.cqn; r.ckvn = ws + Lw.ckvn; r.kr = ws + Lw.kr; r.lam = (float*)(ws + Lw.lam);
     r.rope = (float*)(ws + Lw.rope); r.cache = cache; r.pos_dev = cache_lens;
     if ((err = rowprep(r, true, s)) != hipSuccess) return err;
@@ -1030,7 +1031,8 @@ hipError_t decode_step(const gdla_config* c, const gdla_weights* w, int B, const
   {
     DecAttnArgs k{(const bf16*)(ws + Lw.qlat), cache, (int)((int64_t)B * cache.max_pages * 4),
                   cache.bt ? __builtin_ctz((unsigned)cache.page_rows) : 0, B, H, plan, (float*)(ws + Lw.ml),
-                  (float*)(ws + Lw.po), (float)(1.4426950408889634 / std::sqrt((double)DQK))};
+                  (float*)(ws + Lw.po), (float)(1.4426950408889634 * yarn_logit_multiplier(c->yarn_factor, c->window, c->yarn_temperature) /
+                          std::sqrt((double)DQK))};
     const int grid = DEC_WGS;
     switch (rkv) {
       case 128: err = dec_attn_kvr<128>(k, grid, s); break;

@@ -92,9 +92,13 @@ struct RowPrepArgs {
   int nsplit; int64_t split_stride;      // down holds nsplit partial sums (elements apart); 0/1 = one
 };
 hipError_t rowprep(const RowPrepArgs& a, bool bf16, hipStream_t s);
-// RoPE fields of the row prep: base, and YaRN when factor > 1 on a full-causal layer
+// RoPE fields of the row prep: base, and YaRN when factor > 1 on a full-causal
+// layer; temperature 0 puts YaRN's m on cos and sin, 1 leaves them unscaled
+// (the logit then carries m^2, see yarn_logit_multiplier)
 void set_rope(RowPrepArgs& r, double base, int window, float yarn_factor, int yarn_orig_len, float beta_fast,
-              float beta_slow);
+              float beta_slow, int temperature);
+// factor on q . k / sqrt(d_qk): m^2 on a YaRN layer with temperature 1, else 1
+double yarn_logit_multiplier(float yarn_factor, int window, int temperature);
 
 struct LatentNormArgs {
   const void* c; int64_t ldc; int64_t T; int kv_rank;

@@ -397,15 +397,21 @@ hipError_t latent_norm(const LatentNormArgs& a, bool bf16, hipStream_t s) {
 }
 
 void set_rope(RowPrepArgs& r, double base, int window, float yarn_factor, int yarn_orig_len, float beta_fast,
-              float beta_slow) {
+              float beta_slow, int temperature) {
   r.rope_base = base;
   r.yarn_s = 0.0;
   if (yarn_factor > 1.f && window <= 0) {   // full-causal layers only
     r.yarn_s = yarn_factor;
     r.yarn_short = (double)yarn_orig_len / beta_fast;
     r.yarn_long = (double)yarn_orig_len / beta_slow;
-    r.yarn_m = 1.0 + 0.1 * std::log((double)yarn_factor);
+    r.yarn_m = temperature == 1 ? 1.0 : 1.0 + 0.1 * std::log((double)yarn_factor);
   }
+}
+
+double yarn_logit_multiplier(float yarn_factor, int window, int temperature) {
+  if (!(yarn_factor > 1.f && window <= 0) || temperature != 1) return 1.0;
+  const double m = 1.0 + 0.1 * std::log((double)yarn_factor);
+  return m * m;
 }
 
 }  // namespace gdla

@@ -40,7 +40,8 @@ class Config(ctypes.Structure):
                 ("d_rope", ctypes.c_int32), ("d_v", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int),
                 ("yarn_factor", ctypes.c_float), ("yarn_orig_len", ctypes.c_int32),
-                ("yarn_beta_fast", ctypes.c_float), ("yarn_beta_slow", ctypes.c_float)]
+                ("yarn_beta_fast", ctypes.c_float), ("yarn_beta_slow", ctypes.c_float),
+                ("yarn_temperature", ctypes.c_int32)]
 
 
 WEIGHT_FIELDS = ("w_dq", "g_q", "w_dkv", "g_kv", "w_lambda", "w_uq", "w_ukv", "w_gate", "w_o")
@@ -129,15 +130,19 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+YARN_TEMPERATURES = {"rotary": 0, "logit": 1}
+
+
 def make_config(shapes: dict, window: int = 0, dtype: str = "bf16", rope_base: float = 10000.0,
-                rms_eps: float = 1e-6, yarn=None) -> Config:
+                rms_eps: float = 1e-6, yarn=None, yarn_temperature: str = "rotary") -> Config:
     """yarn: None, or (factor, orig_len, beta_fast, beta_slow); the library
-    applies it on full-causal layers (window <= 0) only."""
+    applies it on full-causal layers (window <= 0) only.  yarn_temperature:
+    "rotary" (m on cos and sin) or "logit" (m^2 on the whole logit)."""
     yf, yl, ybf, ybs = (0.0, 0, 0.0, 0.0) if not yarn else yarn
     return Config(shapes["d_model"], shapes["q_rank"], shapes["kv_rank"], shapes["n_noise"], shapes["group"],
                   shapes["d_nope"], shapes["d_rope"], shapes["d_v"], int(window), float(rope_base),
                   float(rms_eps), GDLA_BF16 if dtype == "bf16" else GDLA_FP32,
-                  float(yf), int(yl), float(ybf), float(ybs))
+                  float(yf), int(yl), float(ybf), float(ybs), YARN_TEMPERATURES[yarn_temperature])
 
 
 def weights_struct(W: dict) -> Weights:

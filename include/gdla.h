@@ -72,6 +72,12 @@ typedef enum {
   GDLA_FP32 = 1    /* fp32 storage and arithmetic (vector-ALU path) */
 } gdla_dtype;
 
+/* Where YaRN's temperature m = 1 + 0.1 ln s is applied (see gdla_config). */
+typedef enum {
+  GDLA_YARN_TEMP_ROTARY = 0,   /* cos and sin times m: the rotary term of each logit scales by m^2 */
+  GDLA_YARN_TEMP_LOGIT = 1     /* the whole logit times m^2; cos and sin unscaled */
+} gdla_yarn_temperature;
+
 typedef struct {
   int32_t d_model;   /* token width */
   int32_t q_rank;    /* query latent width */
@@ -93,13 +99,20 @@ typedef struct {
    * fields mean plain RoPE.  Pair i of wavelength l_i = 2 pi / theta_i keeps
    * theta_i below yarn_orig_len / yarn_beta_fast, becomes theta_i / s above
    * yarn_orig_len / yarn_beta_slow and is interpolated linearly in l_i in
-   * between; cos and sin are multiplied by m = 1 + 0.1 ln s, so the rotary
-   * part of every logit scales by m^2.  Invalid when yarn_factor > 1 unless
-   * yarn_orig_len > 0 and yarn_beta_fast > yarn_beta_slow > 0. */
+   * between.  The temperature m = 1 + 0.1 ln s goes where yarn_temperature
+   * says: GDLA_YARN_TEMP_ROTARY (0, the listing) multiplies cos and sin by
+   * m, so only the rotary part of every logit scales, by m^2 (the content
+   * part of a GDLA head carries no rotation); GDLA_YARN_TEMP_LOGIT (1, the
+   * page's prose, which puts the temperature on the softmax logits, and the
+   * DeepSeek form of YaRN the report names) multiplies the whole logit by
+   * m^2 and leaves cos and sin unscaled.  Invalid when yarn_factor > 1 unless
+   * yarn_orig_len > 0 and yarn_beta_fast > yarn_beta_slow > 0, or when
+   * yarn_temperature is neither value. */
   float yarn_factor;       /* s */
   int32_t yarn_orig_len;   /* native context length */
   float yarn_beta_fast;
   float yarn_beta_slow;
+  int32_t yarn_temperature;   /* gdla_yarn_temperature */
 } gdla_config;
 
 typedef struct {          /* device pointers, all [out, in] row-major, dtype of the config */

@@ -40,7 +40,11 @@ def test_exports_every_declared_function():
 
 def test_header_compiles_as_c(tmp_path):
     src = tmp_path / "t.c"
-    src.write_text('#include "gdla.h"\nint main(void){ gdla_config c; (void)c; return 0; }\n')
+    # the layout the Python binding declares (Config): 17 four-byte fields
+    src.write_text('#include "gdla.h"\n#include <stddef.h>\n'
+                   'typedef char size_ok[sizeof(gdla_config) == 68 ? 1 : -1];\n'
+                   'typedef char temp_ok[offsetof(gdla_config, yarn_temperature) == 64 ? 1 : -1];\n'
+                   'int main(void){ gdla_config c; size_ok a; temp_ok b; (void)c; (void)a; (void)b; return 0; }\n')
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), "-c", str(src),
                         "-o", str(tmp_path / "t.o")], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
@@ -127,6 +131,20 @@ def test_yarn_settings_validated():
     off = _cfg()
     off.yarn_factor, off.yarn_orig_len = 1.0, 0    # factor <= 1: plain RoPE, other fields ignored
     assert lib().gdla_prefill_workspace_size(ctypes.byref(off), 1, 16) > 0
+    for temp, expect in ((0, gdla.GDLA_OK), (1, gdla.GDLA_OK), (2, gdla.GDLA_ERR_INVALID_ARG),
+                         (-1, gdla.GDLA_ERR_INVALID_ARG)):
+        c = _cfg()
+        c.yarn_temperature = temp
+        st, msg = call_prefill(c, w, B=0, x=0, y=0, ws=0)
+        assert st == expect, (temp, st, msg)
+        if expect != gdla.GDLA_OK:
+            assert "yarn_temperature" in msg, msg
+
+
+def test_config_struct_layout():
+    """The binding's gdla_config matches the header's: 17 four-byte fields."""
+    assert ctypes.sizeof(gdla.Config) == 17 * 4
+    assert gdla.Config.yarn_temperature.offset == 16 * 4
 
 
 def test_empty_inputs_are_noops():

@@ -30,20 +30,20 @@ def check(got, ref, what):
     assert ma <= GRAD_TOL["max_rel"] * scale, f"{what}: max_abs {ma:.3e} > {GRAD_TOL['max_rel']} x {scale:.3e}"
 
 
-def run(shapes, B, L, window, seed, pos_offset=0, yarn=None):
+def run(shapes, B, L, window, seed, pos_offset=0, yarn=None, temp="rotary"):
     print(f"[case] backward shapes={shapes['d_model']}/{shapes['group']} B={B} L={L} W={window} "
-          f"pos={pos_offset} yarn={yarn}", flush=True)
+          f"pos={pos_offset} yarn={yarn} temperature={temp}", flush=True)
     Wd, W64 = make_layer(shapes, seed, "bf16", gamma="random")
     xc = inputs.make_x(B, L, shapes["d_model"], seed, "bf16")
     dyc = inputs.make_x(B, L, shapes["d_model"], seed + 1000, "bf16")
-    cfg = gdla.make_config(shapes, window, "bf16", yarn=yarn)
+    cfg = gdla.make_config(shapes, window, "bf16", yarn=yarn, yarn_temperature=temp)
     dx, grads = gdla.backward(cfg, Wd, xc.to("cuda"), dyc.to("cuda"), pos_offset=pos_offset)
     torch.cuda.synchronize()
     ocfg = oracle_cfg(shapes, window)
     if yarn:
         from dataclasses import replace
         ocfg = replace(ocfg, yarn_factor=yarn[0], yarn_orig_len=yarn[1], yarn_beta_fast=yarn[2],
-                       yarn_beta_slow=yarn[3])
+                       yarn_beta_slow=yarn[3], yarn_temperature=temp)
     ref = R.gdla_layer_backward(inputs.widen(xc), W64, ocfg, inputs.widen(dyc), pos_offset=pos_offset)
     check(host64(dx), ref["dx"], "dx")
     for n in inputs.WEIGHT_NAMES:
@@ -55,8 +55,9 @@ def test_backward_small(B, L, window):
     run(SMALL, B, L, window, seed=81 + L)
 
 
-def test_backward_position_offset_and_yarn():
-    run(SMALL, 2, 130, 0, seed=82, pos_offset=70000, yarn=(64.0, 4096, 32.0, 1.0))
+@pytest.mark.parametrize("temp", ["rotary", "logit"])
+def test_backward_position_offset_and_yarn(temp):
+    run(SMALL, 2, 130, 0, seed=82, pos_offset=70000, yarn=(64.0, 4096, 32.0, 1.0), temp=temp)
 
 
 @pytest.mark.parametrize("window", [0, 64])
