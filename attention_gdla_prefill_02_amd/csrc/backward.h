@@ -20,7 +20,7 @@ struct BackwardLayout {
   size_t down, cqn, ckvn, kr, lam, rope, q, gate, kv, kvT, z, hall, lse;
   size_t woT, wuqgT, wukvT, wdownT;
   size_t dz, dyT, zT, dh, dvec, dqg, dkv, dkrp, dcqn, dckvn, dqgT, cqnT, dkvT, ckvnT, ddown, ddownT, xT,
-      gpart;
+      gpart, wpart;
   size_t total;
 };
 

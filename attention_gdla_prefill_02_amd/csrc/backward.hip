@@ -27,6 +27,7 @@
 // which the score-shaped registers (rows 4q+j of two 16-row tiles) become a B
 // operand.  (A 32-key-per-wave form of the dK/dV kernel needs 160 accumulator
 // registers per wave and ran slower at one wave per SIMD.)
+#include <algorithm>
 #include <cmath>
 
 #include "backward.h"
@@ -762,6 +763,49 @@ hipError_t attn_bwd_g(const AttnBwdArgs& a, hipStream_t s) {
 
 size_t a256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Weight gradients C[M, N] = A[M, K] B[N, K]^T reduce over K = the token
+// count: a handful of 256 x 256 output tiles with a long K would leave most of
+// the 256 CUs idle, so K is cut into S chunks that run as a batch of fp32
+// partials, summed in chunk order afterwards.  S doubles (up to 16) while the
+// grid is under four rounds of the chip, chunks stay >= 1024 columns and whole
+// 64-column steps.
+constexpr int WG_TILE = 256, WG_MAX_SPLIT = 16;
+int wgrad_split(int M, int N, int64_t K) {
+  const int64_t tiles = (int64_t)cdiv(M, WG_TILE) * cdiv(N, WG_TILE);
+  int S = 1;
+  while (S < WG_MAX_SPLIT && tiles * S < 1024 && K % (2 * S * 64) == 0 && K / (2 * S) >= 1024) S *= 2;
+  return S;
+}
+size_t wgrad_part_bytes(int M, int N, int64_t K) {
+  const int S = wgrad_split(M, N, K);
+  return S > 1 ? (size_t)S * M * N * 4 : 0;
+}
+
+// out[i] = sum over z < S of part[z * MN + i], in z order (float4 per thread)
+__global__ void __launch_bounds__(256)
+wgrad_sum_kernel(const float* __restrict__ part, int S, int64_t MN, float* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= MN) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
+  for (int z = 1; z < S; ++z) acc += *reinterpret_cast<const f32x4*>(part + z * MN + i);
+  *reinterpret_cast<f32x4*>(out + i) = acc;
+}
+
+// g describes C = A B^T over the full K with C = out (contiguous [M, N] fp32)
+hipError_t wgrad_gemm(GemmArgs g, char* part, hipStream_t s) {
+  const int S = wgrad_split(g.M, g.N, g.K);
+  if (S == 1) return gemm_bf16(g, s);
+  float* out = (float*)g.C;
+  const int64_t MN = (int64_t)g.M * g.N;
+  g.C = part; g.ldc = g.N; g.strideC = MN;
+  g.K /= S; g.strideA = g.K; g.strideB = g.K; g.batch = S;
+  hipError_t e = gemm_bf16(g, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(wgrad_sum_kernel, dim3((unsigned)cdiv(MN / 4, 256)), dim3(256), 0, s, (const float*)part, S, MN,
+                     out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t transpose_bf16(const void* src, int64_t ld_src, void* dst, int64_t ld_dst, int R, int C, int Rpad,
@@ -819,6 +863,15 @@ BackwardLayout backward_layout(const BwdDims& D, int64_t T) {
   P.ddownT = take((size_t)P.ndp * Tp * 2);
   P.xT = take((size_t)D.d * Tp * 2);
   P.gpart = take((size_t)P.prep_blocks * (D.rq + D.rkv) * 4);
+  {
+    // split-K partials of the largest weight gradient
+    const int dims[7][2] = {{(int)D.d, (int)D.ngate}, {(int)D.nq, (int)D.rq}, {(int)D.ngate, (int)D.rq},
+                            {(int)nkv, (int)D.rkv}, {(int)D.rq, (int)D.d}, {(int)(D.rkv + DR), (int)D.d},
+                            {(int)D.nS, (int)D.d}};
+    size_t wp = 0;
+    for (const auto& md : dims) wp = std::max(wp, wgrad_part_bytes(md[0], md[1], Tp));
+    P.wpart = take(wp);
+  }
   P.total = o;
   return P;
 }
@@ -928,7 +981,7 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     g.B = ws + P.zT; g.ldb = Tp;
     g.C = c.grads->w_o; g.ldc = D.ngate;
     g.M = d; g.N = (int)D.ngate; g.K = (int)Tp; g.batch = 1; g.epi = EPI_F32;
-    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
   }
   // 4. gate and differential
   {
@@ -979,10 +1032,10 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     g.B = ws + P.cqnT; g.ldb = Tp;
     g.C = c.grads->w_uq; g.ldc = rq;
     g.M = (int)D.nq; g.N = rq; g.K = (int)Tp; g.batch = 1; g.epi = EPI_F32;
-    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
     g.A = ws + P.dqgT + (size_t)D.nq * Tp * 2;
     g.C = c.grads->w_gate; g.M = (int)D.ngate;
-    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
   }
   // 7. KV side: dc_KVn = [dK^C | dV] W_UKV; dW_UKV = [dK^C | dV]^T c_KVn
   {
@@ -1001,7 +1054,7 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     g.B = ws + P.ckvnT; g.ldb = Tp;
     g.C = c.grads->w_ukv; g.ldc = rkv;
     g.M = (int)nkv; g.N = rkv; g.K = (int)Tp; g.batch = 1; g.epi = EPI_F32;
-    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
   }
   // 8. RMSNorms, the rotary key's RoPE, gains
   {
@@ -1039,11 +1092,11 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     g.B = ws + P.xT; g.ldb = Tp;
     g.C = c.grads->w_dq; g.ldc = d;
     g.M = rq; g.N = d; g.K = (int)Tp; g.batch = 1; g.epi = EPI_F32;
-    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
     g.A = ws + P.ddownT + (size_t)rq * Tp * 2; g.C = c.grads->w_dkv; g.M = rkv + DR;
-    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
     g.A = ws + P.ddownT + (size_t)(rq + rkv + DR) * Tp * 2; g.C = c.grads->w_lambda; g.M = nS;
-    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
   }
   return hipSuccess;
 }
