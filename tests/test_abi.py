@@ -85,6 +85,21 @@ def call_prefill(cfg, w, B=1, L=16, pos=0, x=0x100000, y=0x200000, res=None, cac
     return st, L_.gdla_last_error().decode()
 
 
+def test_prefill_stages_rejects_unknown_bits():
+    w = FakeW().struct()
+    cfg = _cfg()
+    L_ = lib()
+    wsb = L_.gdla_prefill_workspace_size(ctypes.byref(cfg), 1, 16)
+    for bits in (64, 1 << 31, 63 | 128):
+        st = L_.gdla_prefill_stages(ctypes.byref(cfg), ctypes.byref(w), 1, 16, 0, 0x100000, 0x200000, None, None, 0,
+                                    0x300000, wsb, None, bits)
+        assert st == gdla.GDLA_ERR_INVALID_ARG, (bits, st)
+        assert "stage" in L_.gdla_last_error().decode()
+    # no stage at all: nothing to launch, and no pointer is touched
+    st = L_.gdla_prefill_stages(ctypes.byref(cfg), ctypes.byref(w), 0, 16, 0, 0, 0, None, None, 0, 0, 0, None, 0)
+    assert st == gdla.GDLA_OK
+
+
 def test_prefill_rejects_bad_arguments():
     lib()
     w = FakeW().struct()

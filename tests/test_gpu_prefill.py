@@ -88,6 +88,48 @@ def test_determinism_bf16():
     assert torch.equal(a, b)
 
 
+def _ws_view(ws, off, n, dtype, shape):
+    esize = torch.tensor([], dtype=dtype).element_size()
+    return ws[off:off + n * esize].view(dtype).reshape(shape)
+
+
+def test_prefill_stages_compose_and_intermediates():
+    """gdla_prefill_stages run one stage per call on one workspace gives gdla_prefill's
+    y bit for bit, and the intermediates gdla_prefill_workspace_layout names hold
+    what the oracle computes: lambda and the sigmoid gate (fp32), the RoPE'd
+    queries, content keys and rotary key (fp16 in the bf16 configuration)."""
+    B, L, window = 2, 200, 0
+    Wd, W64 = make_layer(SMALL, 17, "bf16")
+    xc = inputs.make_x(B, L, SMALL["d_model"], 17, "bf16")
+    x = xc.to("cuda")
+    cfg = gdla.make_config(SMALL, window, "bf16")
+    y_all = gdla.prefill(cfg, Wd, x)
+    ws = gdla.alloc_workspace(gdla.prefill_workspace_size(cfg, B, L))
+    y = torch.empty_like(x)
+    for st in (gdla.STAGE_DOWN, gdla.STAGE_PREP, gdla.STAGE_EXPAND, gdla.STAGE_QG, gdla.STAGE_ATTN, gdla.STAGE_OUT):
+        gdla.prefill(cfg, Wd, x, y=y, workspace=ws, stages=st)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_all), "stage-by-stage calls must reproduce gdla_prefill"
+    lay = gdla.prefill_layout(cfg, B, L)
+    T, H, nS, nN = B * L, SMALL["group"] * SMALL["n_noise"] + SMALL["n_noise"], SMALL["group"] * SMALL["n_noise"], \
+        SMALL["n_noise"]
+    ocfg = oracle_cfg(SMALL, window)
+    x64 = inputs.widen(xc)
+    pos = np.arange(L, dtype=np.float64)
+    refs = [R.project_tokens(x64[b], W64, ocfg, pos) for b in range(B)]
+    lam = _ws_view(ws, lay["lam"], T * nS, torch.float32, (T, nS))
+    gate = _ws_view(ws, lay["gate"], T * nS * 128, torch.float32, (T, nS * 128))
+    q = _ws_view(ws, lay["q"], T * H * 192, torch.float16, (T, H, 192))
+    kc = _ws_view(ws, lay["kc"], T * nN * 128, torch.float16, (T, nN, 128))
+    kr = _ws_view(ws, lay["kr"], T * 64, torch.float16, (T, 64))
+    assert_close(host64(lam), np.concatenate([r["lam"] for r in refs]), "bf16", "workspace lambda")
+    assert_close(host64(gate), np.concatenate([r["gate"] for r in refs]), "bf16", "workspace gate")
+    assert_close(host64(q), np.concatenate([r["q"] for r in refs]), "bf16", "workspace queries (fp16)")
+    assert_close(host64(kr), np.concatenate([r["kr"] for r in refs]), "bf16", "workspace rotary key (fp16)")
+    kc_ref = np.concatenate([R.latent_expand_from_norm(r["ckvn"], W64["w_ukv"], ocfg)[0] for r in refs])
+    assert_close(host64(kc), kc_ref, "bf16", "workspace content keys (fp16)")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_latent_expand(dtype):
     shapes = SMALL if dtype == "bf16" else configs.TINY_SHAPES
