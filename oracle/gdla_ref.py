@@ -711,6 +711,28 @@ def gdla_layer_backward(x, W, cfg: Cfg, dy, pos_offset=0, rows=None):
     return dict(dx=dx, **grads)
 
 
+def gdla_layer_packed_backward(x, W, cfg: Cfg, dy, cu_seqlens, pos_offsets=None):
+    """Backward of gdla_layer_packed ([M3-pack] streams in the training pass of
+    [M3-train]): every sequence of the stream is the layer applied to it
+    alone, so its rows of dx are that sequence's dx and each weight gradient
+    is the sum of the sequences' gradients.  x, dy [T, d_model]; returns dict
+    dx [T, d_model] and one entry per weight name."""
+    x, dy = _f64(x), _f64(dy)
+    segs = packed_segments(cu_seqlens)
+    if pos_offsets is None:
+        pos_offsets = [0] * len(segs)
+    grads = {k: np.zeros_like(_f64(v)) for k, v in W.items()}
+    dx = np.zeros_like(x)
+    for (s0, s1), p0 in zip(segs, pos_offsets):
+        if s1 <= s0:
+            continue
+        g = gdla_layer_backward(x[None, s0:s1], W, cfg, dy[None, s0:s1], pos_offset=int(p0))
+        dx[s0:s1] = g["dx"][0]
+        for k in grads:
+            grads[k] += g[k]
+    return dict(dx=dx, **grads)
+
+
 # --------------------------------------------------------------------------
 # Hybrid block ([M3-arch]): 1 full-causal layer then 3 sliding-window layers
 # --------------------------------------------------------------------------

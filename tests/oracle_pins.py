@@ -788,6 +788,54 @@ def pin_backward_finite_differences_yarn():
     _fd_check(replace(cfg, yarn_temperature="logit"), pos_offset=3, seed=32)
 
 
+def pin_packed_backward_finite_differences():
+    """The packed backward ([M3-pack] in the training pass) against central
+    finite differences of sum(dy * y) through the packed forward: x and every
+    weight, a stream of PACK_LENS (one sequence empty) at PACK_POS, full
+    causal and windowed."""
+    cu, x = _pack(PACK_LENS, seed=51)
+    rng = np.random.Generator(np.random.PCG64(52))
+    dy = rng.standard_normal(x.shape)
+    h = 1e-5
+    for cfg in (TINY, replace(TINY, window=2)):
+        W = tiny_weights(cfg, seed=53)
+        grads = R.gdla_layer_packed_backward(x, W, cfg, dy, cu, PACK_POS)
+
+        def loss(x_, W_):
+            return float(np.sum(dy * R.gdla_layer_packed(x_, W_, cfg, cu, PACK_POS)["y"]))
+
+        for name, arr, key in [("dx", x, None)] + [(k, W[k], k) for k in sorted(W)]:
+            for idx in rng.choice(np.arange(arr.size), size=min(5, arr.size), replace=False):
+                i = np.unravel_index(idx, arr.shape)
+                plus, minus = arr.copy(), arr.copy()
+                plus[i] += h
+                minus[i] -= h
+                if key is None:
+                    fd = (loss(plus, W) - loss(minus, W)) / (2 * h)
+                else:
+                    fd = (loss(x, dict(W, **{key: plus})) - loss(x, dict(W, **{key: minus}))) / (2 * h)
+                got = grads["dx" if key is None else key][i]
+                scale = max(1.0, float(np.max(np.abs(grads["dx" if key is None else key]))))
+                assert abs(got - fd) <= 2e-6 * scale, f"packed {name}{i}: analytic {got:.9e} vs {fd:.9e}"
+
+
+def pin_packed_backward_equal_lengths_is_the_batch():
+    """Equal lengths packed end to end are the batched layer: dx is the
+    batched dx row for row and each weight gradient the batched one (the
+    batch sums over its sequences)."""
+    B, L = 3, 5
+    W = tiny_weights(seed=54)
+    x = tiny_x(B=B, L=L, seed=55)
+    dy = np.random.Generator(np.random.PCG64(56)).standard_normal(x.shape)
+    cu = [i * L for i in range(B + 1)]
+    for cfg in (TINY, replace(TINY, window=2)):
+        batched = R.gdla_layer_backward(x, W, cfg, dy, pos_offset=4)
+        packed = R.gdla_layer_packed_backward(x.reshape(B * L, -1), W, cfg, dy.reshape(B * L, -1), cu, [4] * B)
+        close(packed["dx"], batched["dx"].reshape(B * L, -1), 1e-12)
+        for k in W:
+            close(packed[k], batched[k], 1e-12)
+
+
 def pin_rope_backward_is_adjoint():
     """<rope(u), g> = <u, rope_backward(g)> for plain and YaRN frequencies."""
     rng = np.random.Generator(np.random.PCG64(41))

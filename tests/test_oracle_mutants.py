@@ -235,6 +235,21 @@ def _rope_params_m_in_both_modes(cfg):
     return base, (None if yarn is None else yarn[:4])
 
 
+_orig_packed_bwd = R.gdla_layer_packed_backward
+
+
+def _packed_backward_last_sequence_grads(x, W, cfg, dy, cu_seqlens, pos_offsets=None):
+    # weight gradients of the last non-empty sequence only (overwritten, not summed)
+    out = _orig_packed_bwd(x, W, cfg, dy, cu_seqlens, pos_offsets)
+    segs = R.packed_segments(cu_seqlens)
+    b = max(i for i, (s0, s1) in enumerate(segs) if s1 > s0)
+    s0, s1 = segs[b]
+    p0 = 0 if pos_offsets is None else int(pos_offsets[b])
+    last = R.gdla_layer_backward(np.asarray(x, np.float64)[None, s0:s1], W, cfg,
+                                 np.asarray(dy, np.float64)[None, s0:s1], pos_offset=p0)
+    return dict(out, **{k: last[k] for k in W})
+
+
 def _packed_global_positions(x, W, cfg, cu_seqlens, pos_offsets=None):
     # positions run on through the stream instead of restarting per sequence
     segs = R.packed_segments(cu_seqlens)
@@ -360,6 +375,7 @@ MUTANTS = {
     "packed_global_positions": ("gdla_layer_packed", _packed_global_positions),
     "packed_leaky": ("gdla_layer_packed", _packed_leaky),
     "packed_segments_skip_first": ("packed_segments", _packed_segments_skip_first),
+    "packed_backward_last_sequence_grads": ("gdla_layer_packed_backward", _packed_backward_last_sequence_grads),
     "paged_slot_swapped": ("paged_slot", _paged_slot_swapped),
     "paged_slot_no_table": ("paged_slot", _paged_slot_no_table),
     "rope_backward_forward_rotation": ("rope_backward", _rope_backward_forward_rotation),
