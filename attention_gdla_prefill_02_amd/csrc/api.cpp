@@ -534,15 +534,12 @@ size_t gdla_backward_workspace_size(const gdla_config* cfg, int32_t B, int32_t L
   return gdla::backward_layout(bwd_dims(cfg), (int64_t)B * L).total;
 }
 
-gdla_status gdla_backward(const gdla_config* cfg, const gdla_weights* w, int32_t B, int32_t L, int64_t pos_offset,
-                          const void* x, const void* dy, void* dx, const gdla_grads* grads, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  gdla_status st = check_backward_shape(cfg, B, L);
-  if (st != GDLA_OK) return st;
-  if (pos_offset < 0) return fail(GDLA_ERR_INVALID_ARG, "pos_offset must be >= 0");
-  if (B == 0 || L == 0) return GDLA_OK;
-  if (pos_offset + L > (int64_t)1 << 30) return fail(GDLA_ERR_INVALID_ARG, "positions beyond 2^30");
-  st = check_weights(w);
+namespace {
+
+// Pointer and workspace checks shared by the uniform and the packed backward.
+gdla_status check_backward_buffers(const gdla_weights* w, const void* x, const void* dy, void* dx,
+                                   const gdla_grads* grads, void* workspace, size_t workspace_bytes, size_t need) {
+  gdla_status st = check_weights(w);
   if (st != GDLA_OK) return st;
   if (!x || !dy || !dx || !grads) return fail(GDLA_ERR_INVALID_ARG, "x, dy, dx and grads must be non-NULL");
   if (!aligned16(x) || !aligned16(dy) || !aligned16(dx))
@@ -554,15 +551,65 @@ gdla_status gdla_backward(const gdla_config* cfg, const gdla_weights* w, int32_t
     if (!p) return fail(GDLA_ERR_INVALID_ARG, "every gradient pointer must be non-NULL");
     if (!aligned16(p)) return fail(GDLA_ERR_INVALID_ARG, "gradient buffers must be 16-byte aligned");
   }
+  if (!workspace) return fail(GDLA_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", need);
+  if (((uintptr_t)workspace & 255) != 0) return fail(GDLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need) return fail(GDLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  return GDLA_OK;
+}
+
+gdla_status check_backward_packed_shape(const gdla_config* cfg, int32_t n_seq, int64_t T) {
+  gdla_status st = check_backward_shape(cfg, 0, 0);
+  if (st != GDLA_OK) return st;
+  if (n_seq < 0 || T < 0) return fail(GDLA_ERR_INVALID_ARG, "n_seq and T must be >= 0");
+  if (T > ((int64_t)1 << 22)) return fail(GDLA_ERR_UNSUPPORTED, "packed backward supports T <= 2^22");
+  if (n_seq > (1 << 20)) return fail(GDLA_ERR_UNSUPPORTED, "packed backward supports n_seq <= 2^20");
+  return GDLA_OK;
+}
+
+}  // namespace
+
+gdla_status gdla_backward(const gdla_config* cfg, const gdla_weights* w, int32_t B, int32_t L, int64_t pos_offset,
+                          const void* x, const void* dy, void* dx, const gdla_grads* grads, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  gdla_status st = check_backward_shape(cfg, B, L);
+  if (st != GDLA_OK) return st;
+  if (pos_offset < 0) return fail(GDLA_ERR_INVALID_ARG, "pos_offset must be >= 0");
+  if (B == 0 || L == 0) return GDLA_OK;
+  if (pos_offset + L > (int64_t)1 << 30) return fail(GDLA_ERR_INVALID_ARG, "positions beyond 2^30");
   const gdla::BwdDims D = bwd_dims(cfg);
   const gdla::BackwardLayout P = gdla::backward_layout(D, (int64_t)B * L);
-  if (!workspace) return fail(GDLA_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", P.total);
-  if (((uintptr_t)workspace & 255) != 0) return fail(GDLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (workspace_bytes < P.total)
-    return fail(GDLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, P.total);
-  const gdla::BwdCall c{cfg, w, grads, B, L, (int64_t)B * L, pos_offset, x, dy, dx, workspace};
+  st = check_backward_buffers(w, x, dy, dx, grads, workspace, workspace_bytes, P.total);
+  if (st != GDLA_OK) return st;
+  const gdla::BwdCall c{cfg, w, grads, B, L, (int64_t)B * L, pos_offset, x, dy, dx, workspace, nullptr, nullptr, 0};
   hipError_t err = gdla::backward_step(D, P, c, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "backward");
+  return GDLA_OK;
+}
+
+size_t gdla_backward_packed_workspace_size(const gdla_config* cfg, int32_t n_seq, int64_t T) {
+  if (check_backward_packed_shape(cfg, n_seq, T) != GDLA_OK || n_seq == 0) return 0;
+  return gdla::backward_layout(bwd_dims(cfg), T, n_seq).total;
+}
+
+gdla_status gdla_backward_packed(const gdla_config* cfg, const gdla_weights* w, int32_t n_seq, int64_t T,
+                                 const int32_t* cu_seqlens, const int32_t* pos_offsets, const void* x,
+                                 const void* dy, void* dx, const gdla_grads* grads, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  gdla_status st = check_backward_packed_shape(cfg, n_seq, T);
+  if (st != GDLA_OK) return st;
+  if (T == 0) return GDLA_OK;
+  if (n_seq == 0) return fail(GDLA_ERR_INVALID_ARG, "T = %lld tokens but no sequences", (long long)T);
+  if (!cu_seqlens) return fail(GDLA_ERR_INVALID_ARG, "cu_seqlens must be non-NULL");
+  if (((uintptr_t)cu_seqlens & 3) || ((uintptr_t)pos_offsets & 3))
+    return fail(GDLA_ERR_INVALID_ARG, "cu_seqlens and pos_offsets must be 4-byte aligned");
+  const gdla::BwdDims D = bwd_dims(cfg);
+  const gdla::BackwardLayout P = gdla::backward_layout(D, T, n_seq);
+  if (P.total == 0) return fail(GDLA_ERR_UNSUPPORTED, "stream too long for the work-list kernel");
+  st = check_backward_buffers(w, x, dy, dx, grads, workspace, workspace_bytes, P.total);
+  if (st != GDLA_OK) return st;
+  const gdla::BwdCall c{cfg, w, grads, 0, 0, T, 0, x, dy, dx, workspace, cu_seqlens, pos_offsets, n_seq};
+  hipError_t err = gdla::backward_step(D, P, c, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "packed backward");
   return GDLA_OK;
 }
 

@@ -698,6 +698,16 @@ hipError_t attn_plan(const int32_t* cu, int nseq, int64_t T, int g, int* plan, h
   return plan_one(cu, nseq, T, BQ_NOISE, plan + plan_ints(nseq, T, attn_block_q(g)), s);
 }
 
+size_t block_plan_bytes(int nseq, int64_t T, int rows) {
+  return plan_fits(T, rows) ? plan_ints(nseq, T, rows) * sizeof(int) : 0;
+}
+
+int64_t block_plan_items(int nseq, int64_t T, int rows) { return (T + rows - 1) / rows + nseq; }
+
+hipError_t block_plan(const int32_t* cu, int nseq, int64_t T, int rows, int* plan, hipStream_t s) {
+  return plan_one(cu, nseq, T, rows, plan, s);
+}
+
 namespace {
 template <bool F16QK>
 hipError_t attn_bf16_t(const AttnArgs& a, hipStream_t s) {

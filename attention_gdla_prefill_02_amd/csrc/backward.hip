@@ -217,6 +217,9 @@ struct AttnBwdArgs {
   float* dkr_part;                      // out: [nN, T, d_rope], one slice per KV group
   int64_t T; int B, L, nN, window;
   float scale, sc;                      // 1/sqrt(d_qk), and times log2(e)
+  // packed stream: work lists of 32-query blocks (dQ) and DKV_KEYS-key blocks
+  // (dK/dV), block_plan's layout, and their slot counts; nullptr: B x L
+  const int* plan_q; const int* plan_k; int64_t items_q, items_k;
 };
 
 GDLA_DEV bool visible(int ql, int kl, int L, int W) {
@@ -240,11 +243,27 @@ attn_bwd_dkv_kernel(AttnBwdArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
-  const int nN = a.nN, nS = G * nN, H = nS + nN, L = a.L, W = a.window;
-  const int nkb = cdiv(L, DKV_KEYS);
-  const int kbk = blockIdx.x % nkb, rest = blockIdx.x / nkb, n = rest % nN, b = rest / nN;
-  const int64_t tb = (int64_t)b * L, T = a.T;
-  const int k0 = kbk * DKV_KEYS, kw = k0 + 16 * w, kl = kw + r16;   // this lane's key (score column)
+  const int nN = a.nN, nS = G * nN, H = nS + nN, W = a.window;
+  int L, k0, n;
+  int64_t tb;
+  if (a.plan_k) {   // packed stream: work item (sequence, key block) of the list, KV group n
+    const int slot = blockIdx.x / nN;
+    n = blockIdx.x % nN;
+    if (slot >= a.plan_k[0]) return;
+    const int4 it = reinterpret_cast<const int4*>(a.plan_k + 4)[slot];
+    tb = it.x;
+    L = it.y;
+    k0 = it.z;
+  } else {
+    L = a.L;
+    const int nkb = cdiv(L, DKV_KEYS);
+    const int kbk = blockIdx.x % nkb, rest = blockIdx.x / nkb;
+    n = rest % nN;
+    tb = (int64_t)(rest / nN) * L;
+    k0 = kbk * DKV_KEYS;
+  }
+  const int64_t T = a.T;
+  const int kw = k0 + 16 * w, kl = kw + r16;   // this lane's key (score column)
   const int64_t krow = tb + min(kl, L - 1);
   const int koff = n * DN, voff = nN * DN + n * DV;
 
@@ -494,12 +513,28 @@ attn_bwd_dq32_kernel(AttnBwdArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5, g = (lane >> 4) & 1, i16 = lane & 15;
-  const int nN = a.nN, nS = G * nN, H = nS + nN, L = a.L, W = a.window;
-  const int nqb = cdiv(L, 32);
-  const int qb = blockIdx.x % nqb, rest = blockIdx.x / nqb, n = rest % nN, b = rest / nN;
-  const int64_t tb = (int64_t)b * L, T = a.T;
+  const int nN = a.nN, nS = G * nN, H = nS + nN, W = a.window;
+  int L, q0, n;
+  int64_t tb;
+  if (a.plan_q) {   // packed stream: work item (sequence, 32-query block) of the list, KV group n
+    const int slot = blockIdx.x / nN;
+    n = blockIdx.x % nN;
+    if (slot >= a.plan_q[0]) return;
+    const int4 it = reinterpret_cast<const int4*>(a.plan_q + 4)[slot];
+    tb = it.x;
+    L = it.y;
+    q0 = it.z;
+  } else {
+    L = a.L;
+    const int nqb = cdiv(L, 32);
+    const int qb = blockIdx.x % nqb, rest = blockIdx.x / nqb;
+    n = rest % nN;
+    tb = (int64_t)(rest / nN) * L;
+    q0 = qb * 32;
+  }
+  const int64_t T = a.T;
   const int head = w < G ? n * G + w : nS + n;
-  const int q0 = qb * 32, ql = q0 + l32;                  // this lane's query (score column)
+  const int ql = q0 + l32;                  // this lane's query (score column)
   const int64_t qrow = tb + min(ql, L - 1);
 
   bf16x8 qf[DQK / 16], dhf[DV / 16];
@@ -754,7 +789,10 @@ hipError_t attn_bwd_g(const AttnBwdArgs& a, hipStream_t s) {
   hipError_t e;   // set on every call: no process-wide state, and correct on every device
   if ((e = set_lds(attn_bwd_dq32_kernel<G>, dq_lds)) != hipSuccess) return e;
   if ((e = set_lds(attn_bwd_dkv_kernel<G>, dkv_lds)) != hipSuccess) return e;
-  const int64_t gq = (int64_t)a.B * a.nN * cdiv(a.L, 32), gk = (int64_t)a.B * a.nN * cdiv(a.L, DKV_KEYS);
+  const int64_t gq = a.plan_q ? a.items_q * a.nN : (int64_t)a.B * a.nN * cdiv(a.L, 32);
+  const int64_t gk = a.plan_k ? a.items_k * a.nN : (int64_t)a.B * a.nN * cdiv(a.L, DKV_KEYS);
+  if (gq <= 0 || gk <= 0) return hipSuccess;
+  if (gq > INT32_MAX || gk > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_bwd_dq32_kernel<G>, dim3((unsigned)gq), dim3(64 * (G + 1)), dq_lds, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(attn_bwd_dkv_kernel<G>, dim3((unsigned)gk), dim3(64 * DKV_NW), dkv_lds, s, a);
@@ -819,7 +857,7 @@ hipError_t transpose_bf16(const void* src, int64_t ld_src, void* dst, int64_t ld
 }
 
 // ------------------------------------------------------------ the backward step
-BackwardLayout backward_layout(const BwdDims& D, int64_t T) {
+BackwardLayout backward_layout(const BwdDims& D, int64_t T, int nseq) {
   BackwardLayout P;
   const int64_t Tp = (T + 63) / 64 * 64;
   const int64_t nkv = D.nN * (D.dn + D.dv), nqg = D.nq + D.ngate;
@@ -872,6 +910,18 @@ BackwardLayout backward_layout(const BwdDims& D, int64_t T) {
     for (const auto& md : dims) wp = std::max(wp, wgrad_part_bytes(md[0], md[1], Tp));
     P.wpart = take(wp);
   }
+  P.plan_f = P.plan_q = P.plan_k = 0;
+  if (nseq > 0) {
+    const size_t f = attn_plan_bytes(nseq, T, (int)D.g), q = block_plan_bytes(nseq, T, 32),
+                 k = block_plan_bytes(nseq, T, DKV_KEYS);
+    if (!f || !q || !k) {   // the stream is too long for the plan kernel
+      P.total = 0;
+      return P;
+    }
+    P.plan_f = take(f);
+    P.plan_q = take(q);
+    P.plan_k = take(k);
+  }
   P.total = o;
   return P;
 }
@@ -900,6 +950,7 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     RowPrepArgs r{};
     r.down = (const float*)(ws + P.down); r.ld_down = D.ndown;
     r.T = T; r.L = c.L; r.pos_offset = c.pos_offset;
+    r.cu = c.nseq > 0 ? c.cu : nullptr; r.nseq = c.nseq; r.seq_pos = c.seq_pos;
     r.q_rank = rq; r.kv_rank = rkv; r.d_rope = DR; r.nS = nS;
     r.g_q = c.w->g_q; r.g_kv = c.w->g_kv; r.eps = c.cfg->rms_eps;
     set_rope(r, c.cfg->rope_base, c.cfg->window, c.cfg->yarn_factor, c.cfg->yarn_orig_len, c.cfg->yarn_beta_fast,
@@ -948,6 +999,13 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     a.d_nope = DN; a.d_rope = DR; a.d_v = DV;
     a.scale = (float)(logit_mult / std::sqrt((double)DQK));
     a.h_out = ws + P.hall; a.lse_out = (float*)(ws + P.lse);
+    if (c.nseq > 0) {
+      int* plan = (int*)(ws + P.plan_f);
+      if ((e = attn_plan(c.cu, c.nseq, T, (int)D.g, plan, s)) != hipSuccess) return e;
+      a.cu = c.cu; a.nseq = c.nseq;
+      a.plan = plan;
+      a.items_cap = attn_plan_items(c.nseq, T, (int)D.g);
+    }
     if ((e = attn_bf16(a, s)) != hipSuccess) return e;
   }
   // 2. transposed weights: W_O^T, [W_UQ; W_G]^T, W_UKV^T, [W_DQ; W_DKV; W_lambda]^T (zero-padded)
@@ -1006,6 +1064,14 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     a.T = T; a.B = c.B; a.L = c.L; a.nN = (int)D.nN; a.window = c.cfg->window;
     a.scale = (float)(logit_mult / std::sqrt((double)DQK));
     a.sc = (float)(1.4426950408889634 * logit_mult / std::sqrt((double)DQK));
+    if (c.nseq > 0) {
+      int* pq = (int*)(ws + P.plan_q);
+      int* pk = (int*)(ws + P.plan_k);
+      if ((e = block_plan(c.cu, c.nseq, T, 32, pq, s)) != hipSuccess) return e;
+      if ((e = block_plan(c.cu, c.nseq, T, DKV_KEYS, pk, s)) != hipSuccess) return e;
+      a.plan_q = pq; a.items_q = block_plan_items(c.nseq, T, 32);
+      a.plan_k = pk; a.items_k = block_plan_items(c.nseq, T, DKV_KEYS);
+    }
     switch (D.g) {
       case 1: e = attn_bwd_g<1>(a, s); break;
       case 2: e = attn_bwd_g<2>(a, s); break;

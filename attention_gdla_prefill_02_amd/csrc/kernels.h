@@ -143,5 +143,12 @@ int attn_block_q(int g);
 size_t attn_plan_bytes(int nseq, int64_t T, int g);
 int attn_plan_items(int nseq, int64_t T, int g);
 hipError_t attn_plan(const int32_t* cu, int nseq, int64_t T, int g, int* plan, hipStream_t s);
+// The same work list for blocks of `rows` rows (queries or keys) of each
+// sequence: items {first stream row, length, first row of the block, 0}.
+// bytes: 0 if the stream is too long for the plan kernel; items: the slot
+// count a grid over the list needs.
+size_t block_plan_bytes(int nseq, int64_t T, int rows);
+int64_t block_plan_items(int nseq, int64_t T, int rows);
+hipError_t block_plan(const int32_t* cu, int nseq, int64_t T, int rows, int* plan, hipStream_t s);
 
 }  // namespace gdla

@@ -22,7 +22,8 @@ STAGE_DOWN, STAGE_PREP, STAGE_EXPAND, STAGE_QG, STAGE_ATTN, STAGE_OUT, STAGE_ALL
 EXPORTED = ("gdla_prefill_workspace_size", "gdla_prefill", "gdla_prefill_stages", "gdla_prefill_workspace_layout",
             "gdla_decode_workspace_size", "gdla_decode", "gdla_latent_expand", "gdla_status_string",
             "gdla_last_error", "gdla_version", "gdla_prefill_packed_workspace_size", "gdla_prefill_packed",
-            "gdla_decode_paged", "gdla_backward_workspace_size", "gdla_backward", "gdla_decode_noalloc")
+            "gdla_decode_paged", "gdla_backward_workspace_size", "gdla_backward", "gdla_decode_noalloc",
+            "gdla_backward_packed_workspace_size", "gdla_backward_packed")
 # bytes of the library-owned device array gdla_decode_noalloc uses as its workspace
 DECODE_NOALLOC_SCRATCH_BYTES = 128 << 20
 
@@ -103,6 +104,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdla_backward_workspace_size.restype = sz
     lib.gdla_backward.argtypes = [cfgp, wp, i32, i32, i64, vp, vp, vp, ctypes.POINTER(Grads), vp, sz, vp]
     lib.gdla_backward.restype = ctypes.c_int
+    lib.gdla_backward_packed_workspace_size.argtypes = [cfgp, i32, i64]
+    lib.gdla_backward_packed_workspace_size.restype = sz
+    lib.gdla_backward_packed.argtypes = [cfgp, wp, i32, i64, vp, vp, vp, vp, vp, ctypes.POINTER(Grads), vp, sz, vp]
+    lib.gdla_backward_packed.restype = ctypes.c_int
     lib.gdla_latent_expand.argtypes = [cfgp, i64, vp, i64, vp, vp, vp, vp, vp, vp]
     lib.gdla_latent_expand.restype = ctypes.c_int
     lib.gdla_status_string.argtypes = [ctypes.c_int]
@@ -272,6 +277,30 @@ def backward(cfg: Config, W: dict, x: torch.Tensor, dy: torch.Tensor, *, pos_off
     ws = wstruct if wstruct is not None else weights_struct(W)
     _check(load().gdla_backward(ctypes.byref(cfg), ctypes.byref(ws), B, L, int(pos_offset), _ptr(x), _ptr(dy),
                                 _ptr(dx), ctypes.byref(gs), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dx, grads
+
+
+def backward_packed_workspace_size(cfg: Config, n_seq: int, T: int) -> int:
+    return int(load().gdla_backward_packed_workspace_size(ctypes.byref(cfg), n_seq, T))
+
+
+def backward_packed(cfg: Config, W: dict, x: torch.Tensor, dy: torch.Tensor, cu_seqlens: torch.Tensor, *,
+                    pos_offsets=None, dx=None, grads=None, workspace=None, stream=None, wstruct=None):
+    """Backward of the layer over a packed stream: x, dy [T, d_model] (cu_seqlens,
+    pos_offsets: device int32) -> (dx [T, d_model], dict of fp32 weight gradients)."""
+    T = x.shape[0]
+    n = cu_seqlens.numel() - 1
+    if dx is None:
+        dx = torch.empty_like(x)
+    if grads is None:
+        grads = {k: torch.empty(W[k].shape, dtype=torch.float32, device=x.device) for k in WEIGHT_FIELDS}
+    if workspace is None:
+        workspace = alloc_workspace(backward_packed_workspace_size(cfg, n, T), x.device)
+    gs = Grads(*[grads[k].data_ptr() for k in WEIGHT_FIELDS])
+    ws = wstruct if wstruct is not None else weights_struct(W)
+    _check(load().gdla_backward_packed(ctypes.byref(cfg), ctypes.byref(ws), n, T, _ptr(cu_seqlens),
+                                       _ptr(pos_offsets), _ptr(x), _ptr(dy), _ptr(dx), ctypes.byref(gs),
+                                       _ptr(workspace), workspace.numel(), _stream(stream)))
     return dx, grads
 
 

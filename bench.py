@@ -41,8 +41,8 @@ HBM_PEAK_GBS = 8000.0                # MI355X HBM3E
 # the ratio of bytes to counter reading of a device copy of known size timed in
 # the same pass (--copy-probe-mib).  Tied to the kernel source it was measured
 # on: reported as null once that source changes.
-ATTN_TRAFFIC = {"source_sha256": "842fc3b1776f5ff706e54576a47209ef3118df8b1c3583d47c005c6f591173e5",
-                "fetch_bytes": 4018401259, "write_bytes": 402653184}
+ATTN_TRAFFIC = {"source_sha256": "367b18ae881e70e1af48f28642ec968e4c61b22245e291e9132fcb3a8ea78e92",
+                "fetch_bytes": 4020303158, "write_bytes": 402653184}
 ATTN_SOURCES = ("attention_gdla_prefill_02_amd/csrc/attn.hip", "attention_gdla_prefill_02_amd/csrc/common.h")
 
 
@@ -259,6 +259,26 @@ def bench_packed(args, torch, gdla, configs, inputs, name="packed_hybrid_l32k", 
     proj = proj_flop_per_token(s) * T * len(w.windows)
     attn = attn_flop_per_pair(s) * sum(attended_pairs(n, win) for n in lens for win in w.windows)
     total = proj + attn
+
+    # the block's backward over the same stream: one gdla_backward_packed call
+    # per layer (forward recomputed inside), on the layer inputs of the forward
+    del ws
+    dy = inputs.make_x(1, T, s["d_model"], w.seed + 1000, "bf16")[0].to("cuda")
+    dx = torch.empty_like(x0)
+    grads = {n: torch.empty(Wd[0][n].shape, dtype=torch.float32, device="cuda") for n in gdla.WEIGHT_FIELDS}
+    wsb = gdla.alloc_workspace(max(gdla.backward_packed_workspace_size(c, len(lens), T) for c in cfgs))
+
+    def backward_step():
+        for l in range(len(cfgs)):
+            gdla.backward_packed(cfgs[l], None, xs[l], dy, cu_d, dx=dx, grads=grads, workspace=wsb,
+                                 wstruct=wstructs[l])
+
+    t_bwd = timed(backward_step)
+    hs = s["n_noise"] * (s["group"] + 1)
+    bwd_pair = hs * (6 * (s["d_nope"] + s["d_rope"]) + 4 * s["d_v"])
+    bwd_total = 3 * proj + (attn_flop_per_pair(s) + bwd_pair) * sum(attended_pairs(n, win) for n in lens
+                                                                     for win in w.windows)
+    del wsb
     out = {"workload": f"{name}: {w.note}", "sequences": len(lens), "tokens": T,
            "lengths": f"U{{{w.len_range[0]}..{w.len_range[1]}}} seeded, min {min(lens)}, max {max(lens)}",
            "ms_per_step": round(t_packed * 1e3, 3), "tokens_per_s": round(T / t_packed, 1),
@@ -267,7 +287,12 @@ def bench_packed(args, torch, gdla, configs, inputs, name="packed_hybrid_l32k", 
            "algorithmic_tflop_per_step": round(total / 1e12, 3), "attn_share_of_flop": round(attn / total, 4),
            "per_sequence_calls_ms_per_step": round(t_seq * 1e3, 3),
            "speedup_vs_per_sequence_calls": round(t_seq / t_packed, 3),
-           "output_finite": bool(torch.isfinite(xs[-1]).all().item())}
+           "output_finite": bool(torch.isfinite(xs[-1]).all().item()),
+           "backward": {"ms_per_step": round(t_bwd * 1e3, 3),
+                        "algorithmic_tflop_per_step": round(bwd_total / 1e12, 3),
+                        "tflops": round(bwd_total / t_bwd / 1e12, 2),
+                        "frac_of_peak": round(bwd_total / t_bwd / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "finite": bool(torch.isfinite(dx).all().item())}}
     log(f"[bench] packed block: {out}")
     return out
 

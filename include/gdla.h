@@ -356,6 +356,35 @@ gdla_status gdla_backward(const gdla_config* cfg, const gdla_weights* w, int32_t
                           const gdla_grads* grads, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Bytes of workspace gdla_backward_packed needs for n_seq sequences holding
+ * T tokens (0 if unsupported, or if n_seq = 0). */
+size_t gdla_backward_packed_workspace_size(const gdla_config* cfg, int32_t n_seq, int64_t T);
+
+/* gdla_backward over a packed stream: gdla_prefill_packed's layer (report,
+ * long-context training paragraph: complete sequences packed together;
+ * training-infrastructure paragraph: activations recomputed for the backward
+ * pass).  Each sequence is differentiated as the layer applied to it alone:
+ * its rows of dx are its own, and every weight gradient is the sum over the
+ * sequences.
+ *   cu_seqlens, pos_offsets  as in gdla_prefill_packed (device int32, read on
+ *                the device only; other values cause no access outside the
+ *                buffers, but rows no sequence holds get unspecified dx and
+ *                the weight gradients then include their contributions)
+ *   x, dy        [T, d_model], config dtype
+ *   dx           [T, d_model] out; must not alias x or dy
+ *   grads        as in gdla_backward (overwritten)
+ *   workspace    at least gdla_backward_packed_workspace_size bytes, 256-byte
+ *                aligned
+ * The attention backward runs one work item per (sequence, block of 32
+ * queries) for dQ and per (sequence, block of 128 keys) for dK and dV.
+ * Limits: bf16 only, the shape limits of gdla_backward, T <= 2^22 (T = 0 is
+ * a no-op), n_seq <= 2^20.  All pointers 16-byte aligned except cu_seqlens
+ * and pos_offsets (4-byte). */
+gdla_status gdla_backward_packed(const gdla_config* cfg, const gdla_weights* w, int32_t n_seq, int64_t T,
+                                 const int32_t* cu_seqlens, const int32_t* pos_offsets, const void* x,
+                                 const void* dy, void* dx, const gdla_grads* grads, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Latent expansion alone (report, GDLA summary and definition paragraphs):
  * c_KVn = RMSNorm(c_KV) * g_kv, [K^C | V] = c_KVn W_UKV^T.
  *   c_kv    [T, ld_c] raw latent (first kv_rank columns used), ld_c >= kv_rank

@@ -100,6 +100,42 @@ def test_prefill_stages_rejects_unknown_bits():
     assert st == gdla.GDLA_OK
 
 
+def test_backward_packed_host_checks():
+    w = FakeW().struct()
+    cfg = _cfg()
+    L_ = lib()
+    assert L_.gdla_backward_packed_workspace_size(ctypes.byref(cfg), 3, 500) > 0
+    assert L_.gdla_backward_packed_workspace_size(ctypes.byref(cfg), 0, 500) == 0
+    assert L_.gdla_backward_packed_workspace_size(ctypes.byref(_cfg(dtype="fp32", d_nope=32, d_rope=16, d_v=32)),
+                                                  3, 500) == 0
+    # the packed layout holds the uniform one plus the work lists
+    assert (L_.gdla_backward_packed_workspace_size(ctypes.byref(cfg), 2, 512) >
+            L_.gdla_backward_workspace_size(ctypes.byref(cfg), 2, 256))
+
+    g = gdla.Grads(*[0x400000 + 0x10000 * i for i in range(9)])
+    wsb = L_.gdla_backward_packed_workspace_size(ctypes.byref(cfg), 2, 64)
+
+    def call(n_seq, T, cu=0x500000, pos=None, x=0x100000, dy=0x200000, dx=0x300000, ws=0x600000, c=cfg):
+        st = L_.gdla_backward_packed(ctypes.byref(c), ctypes.byref(w), n_seq, T, cu, pos, x, dy, dx,
+                                     ctypes.byref(g), ws, wsb, None)
+        return st, L_.gdla_last_error().decode()
+
+    assert call(0, 0)[0] == gdla.GDLA_OK                      # nothing to do
+    assert call(3, 0)[0] == gdla.GDLA_OK
+    st, msg = call(0, 64)
+    assert st == gdla.GDLA_ERR_INVALID_ARG and "no sequences" in msg
+    st, msg = call(2, 64, cu=None)
+    assert st == gdla.GDLA_ERR_INVALID_ARG and "cu_seqlens" in msg
+    st, msg = call(2, 64, cu=0x500002)
+    assert st == gdla.GDLA_ERR_INVALID_ARG and "aligned" in msg
+    st, msg = call(2, 64, dx=0x100000)
+    assert st == gdla.GDLA_ERR_INVALID_ARG and "alias" in msg
+    st, msg = call(2, 64, ws=None)
+    assert st == gdla.GDLA_ERR_WORKSPACE
+    st, msg = call(2, 64, c=_cfg(dtype="fp32", d_nope=32, d_rope=16, d_v=32))
+    assert st == gdla.GDLA_ERR_UNSUPPORTED
+
+
 def test_prefill_rejects_bad_arguments():
     lib()
     w = FakeW().struct()

@@ -66,6 +66,65 @@ def test_backward_report_shapes_g4(window):
     run(s, 1, 160, window, seed=83)
 
 
+def run_packed(shapes, lens, window, seed, pos=None, yarn=None):
+    """The packed backward against the oracle's: sequences of `lens` (empty and
+    one-token ones included) packed into one stream at positions `pos`."""
+    T = int(sum(lens))
+    print(f"[case] packed backward shapes={shapes['d_model']}/{shapes['group']} lens={lens} W={window} "
+          f"pos={pos} yarn={yarn}", flush=True)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pos = [0] * len(lens) if pos is None else list(pos)
+    Wd, W64 = make_layer(shapes, seed, "bf16", gamma="random")
+    xc = inputs.make_x(1, T, shapes["d_model"], seed, "bf16")[0]
+    dyc = inputs.make_x(1, T, shapes["d_model"], seed + 1000, "bf16")[0]
+    cfg = gdla.make_config(shapes, window, "bf16", yarn=yarn)
+    dx, grads = gdla.backward_packed(cfg, Wd, xc.to("cuda"), dyc.to("cuda"), torch.tensor(cu, device="cuda"),
+                                     pos_offsets=torch.tensor(np.asarray(pos, np.int32), device="cuda"))
+    torch.cuda.synchronize()
+    ocfg = oracle_cfg(shapes, window)
+    if yarn:
+        from dataclasses import replace
+        ocfg = replace(ocfg, yarn_factor=yarn[0], yarn_orig_len=yarn[1], yarn_beta_fast=yarn[2],
+                       yarn_beta_slow=yarn[3])
+    ref = R.gdla_layer_packed_backward(inputs.widen(xc), W64, ocfg, inputs.widen(dyc), cu, pos)
+    check(host64(dx), ref["dx"], "packed dx")
+    for n in inputs.WEIGHT_NAMES:
+        check(host64(grads[n]), ref[n], "packed " + n)
+    return dx, grads
+
+
+@pytest.mark.parametrize("window", [0, 40])
+def test_backward_packed_small(window):
+    run_packed(SMALL, [37, 0, 130, 1, 64, 200, 33], window, seed=86, pos=[0, 5, 300, 7, 1000, 0, 64])
+
+
+def test_backward_packed_report_shapes_g4():
+    s = dict(configs.REPORT_SHAPES, d_model=512, q_rank=256)
+    run_packed(s, [150, 97, 1, 129], 64, seed=87, pos=[0, 12, 3, 4000])
+
+
+def test_backward_packed_yarn():
+    run_packed(SMALL, [100, 161, 5], 0, seed=88, pos=[70000, 0, 250000], yarn=(64.0, 4096, 32.0, 1.0))
+
+
+def test_backward_packed_equal_lengths_match_the_batch():
+    """Equal lengths packed end to end give the batched backward's dx and
+    weight gradients (the same per-sequence work, other work lists)."""
+    B, L = 3, 96
+    Wd, _ = make_layer(SMALL, 89, "bf16", gamma="random")
+    xc = inputs.make_x(B, L, SMALL["d_model"], 89, "bf16")
+    dyc = inputs.make_x(B, L, SMALL["d_model"], 1089, "bf16")
+    cfg = gdla.make_config(SMALL, 50, "bf16")
+    x, dy = xc.to("cuda"), dyc.to("cuda")
+    dxb, gb = gdla.backward(cfg, Wd, x, dy)
+    cu = torch.tensor([0, L, 2 * L, 3 * L], dtype=torch.int32, device="cuda")
+    dxp, gp = gdla.backward_packed(cfg, Wd, x.reshape(B * L, -1).contiguous(), dy.reshape(B * L, -1).contiguous(), cu)
+    torch.cuda.synchronize()
+    check(host64(dxp), host64(dxb).reshape(B * L, -1), "packed vs batched dx")
+    for n in inputs.WEIGHT_NAMES:
+        check(host64(gp[n]), host64(gb[n]), "packed vs batched " + n)
+
+
 def test_backward_motif_shapes():
     run(configs.MOTIF_SHAPES, 1, 200, 0, seed=84)
 
