@@ -29,18 +29,21 @@
 //    swapped; with that order the fp32 score registers of a lane, converted
 //    to bf16, are already the B operand of the P V product for 8 consecutive
 //    keys, and V^T fragments are single 16-byte LDS reads.
-//  * Online softmax in the exp2 domain with a lazy rescale: the running max
-//    is only raised (and O, l rescaled) when a tile's max exceeds it by more
-//    than 8 (so P <= 256); the decision is per query but the rescale branch is
-//    wave-uniform and rare after the first tiles.
+//  * Online softmax in the exp2 domain without a per-tile max: P is formed
+//    against the running value m and only the row sum is checked.  While the
+//    sum stays below 2^32 every P is below 2^32, far from overflow in fp32 O
+//    and l, and bf16 P keeps its relative precision at any magnitude; a tile
+//    that pushes the sum past it (the first one always does, m starting at
+//    -1e30) makes the wave take the tile's max, raise m, rescale O and l and
+//    form P again.  The branch is wave-uniform and rare after the first tile.
 //  * Causal / window tile skipping: the workgroup walks only the key tiles
 //    that intersect [q0 - W + 1, q0 + BQ - 1]; masks are applied only on
 //    tiles that straddle a boundary.  A wave computes every tile of the
 //    workgroup's range; on a tile none of its queries sees, the mask makes
 //    every P zero.
-//  * Each 32-key step runs, in one branch-free stretch, the exponentials of
-//    tile t, Q K^T of tile t+1 and P V of tile t; the boundary mask, the max
-//    and the rare rescale of tile t+1 follow (see the pipeline below).
+//  * Each 32-key step masks tile t if it straddles a boundary, then runs
+//    the exponentials of tile t under Q K^T of tile t+1, then P V of tile t
+//    (see the pipeline below).
 //  * Epilogue: H = O / l; the noise waves publish H_N through LDS (for
 //    g = 4 the noise launch stores it in fp32 in the group's Z rows and the
 //    signal launch reads it back), the signal waves form
@@ -277,9 +280,9 @@ attn_bf16_kernel(AttnArgs a) {
       s = mfma32(kf, qf[st], s);
     }
   };
-  // softmax, first half: masks on boundary tiles, tile max, lazy rescale of O
-  // (branches; rare after the first tiles)
-  auto softmax_max = [&](f32x16& s, int kb) {   // kb: first key of the tile, within the sequence
+  // masks on a tile that straddles a boundary of this wave's visible ranges
+  // (a wave-uniform test; most tiles skip it)
+  auto mask_tile = [&](f32x16& s, int kb) {   // kb: first key of the tile, within the sequence
     const bool full = kb >= 0 && kb + BKV - 1 <= qw0 && kb + BKV <= L && (W <= 0 || kb > qlast - W);
     if (!full) {
       const int lo_ok = W > 0 ? max(0, qme - W + 1) : 0;   // keys in [lo_ok, min(qme, L-1)] are visible
@@ -290,28 +293,35 @@ attn_bf16_kernel(AttnArgs a) {
         s[e] = (unsigned)(key - lo_ok) <= span ? s[e] : -INFINITY;
       }
     }
-    float mt = max16(s);
-    mt = fmaxf(mt, xor32(mt)) * sc;
-    const bool raise = mt > m + 8.0f;
-    if (__any(raise)) {
-      const float mn = raise ? mt : m;
-      const float alpha = fast_exp2(m - mn);
-      m = mn;
-      lsum *= alpha;
-#pragma unroll
-      for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
-    }
   };
-  // softmax, second half: P = exp2(s*sc - m) in bf16 and the running sum (no branches)
-  // The running sum adds the bf16 P that P V multiplies (one dot2 per pair with
-  // (1, 1)), so l normalizes exactly the weights applied to V.
-  auto softmax_exp = [&](const f32x16& s, bf16x8 (&p)[2]) {
+  // P = exp2(s*sc - m) in bf16 and the running sum of the bf16 P (one dot2 per
+  // pair with (1, 1)), so l normalizes exactly the weights applied to V
+  auto softmax_exp = [&](const f32x16& s, bf16x8 (&p)[2], float l0) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) p[e >> 3][e & 7] = (bf16)fast_exp2(fmaf(s[e], sc, -m));
     const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+    float l = l0;
 #pragma unroll
     for (int e = 0; e < 16; e += 2)
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[e >> 3][e & 7], p[e >> 3][(e & 7) + 1]}, one, lsum, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[e >> 3][e & 7], p[e >> 3][(e & 7) + 1]}, one, l, false);
+    return l;
+  };
+  // P of a tile against the current m; if the sum leaves [0, 2^32] (m still
+  // at its initial value gives infinite P), raise m to the tile's max, rescale
+  // O and l, and form P again
+  auto softmax_tile = [&](const f32x16& s, bf16x8 (&p)[2]) {
+    float ln = softmax_exp(s, p, lsum);
+    if (__any(!(ln <= 4294967296.0f))) {
+      float mt = max16(s);
+      mt = fmaxf(mt, xor32(mt)) * sc;
+      const float mn = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
+      ln = softmax_exp(s, p, lsum * alpha);
+    }
+    lsum = ln;
   };
   auto pv = [&](int buf, const bf16x8 (&p)[2]) {
     const bf16* V = reinterpret_cast<const bf16*>(smem_raw + buf * TILE_BYTES + K_BYTES) + l32 * V_LD + hi * 8;
@@ -326,12 +336,11 @@ attn_bf16_kernel(AttnArgs a) {
 
   // Pipeline over tiles, LDS slot of tile t = t % NBUF, one barrier per tile.
   // Step t issues the loads of tile t + NBUF - 1 (direct to LDS; its slot last
-  // held tile t - 1), then, in one branch-free stretch, the exponentials of
-  // tile t (its max and any rescale were settled in step t-1), Q K^T of tile
-  // t+1 and P V of tile t, so the vector ALU works on the exponentials while
-  // the matrix core runs the Q K^T chain, and P V follows.  The tail masks
-  // tile t+1's scores if it straddles a boundary, takes its max and, rarely,
-  // raises the running max (rescaling O and l, which by then hold tile t).
+  // held tile t - 1), masks tile t's scores if the tile straddles a boundary,
+  // issues Q K^T of tile t+1 and forms tile t's P, so the vector ALU works on
+  // the exponentials while the matrix core runs the Q K^T chain; then P V of
+  // tile t.  Only the rare overflow check can branch, and it depends on the
+  // exponentials alone, not on the Q K^T chain in flight.
   // The step ends by waiting for this wave's loads of tile t+2 (issued
   // NBUF - 3 steps earlier; the loads issued in this step stay in flight: the
   // tile loads are issued from inline assembly, so vmcnt counts only them)
@@ -349,14 +358,13 @@ attn_bf16_kernel(AttnArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   qk(t_lo % NBUF, sA);
-  softmax_max(sA, (int)((int64_t)t_lo * BKV - tb));
   auto step = [&](int tile, f32x16& cur, f32x16& nxt, bool has_next) {
     const bool issue = tile + NBUF - 1 < t_hi;
     if (issue) load_tile(tile + NBUF - 1, (tile + NBUF - 1) % NBUF);
-    softmax_exp(cur, p);
+    mask_tile(cur, (int)((int64_t)tile * BKV - tb));
     if (has_next) qk((tile + 1) % NBUF, nxt);
+    softmax_tile(cur, p);
     pv(tile % NBUF, p);
-    if (has_next) softmax_max(nxt, (int)((int64_t)(tile + 1) * BKV - tb));
     // loads allowed in flight: those of tiles t+3 .. t+NBUF-1, issued in the
     // last NBUF - 3 steps (all of them issued, since this one was)
     const int ahead = issue ? (NBUF - 3) * my_loads : 0;

@@ -44,9 +44,12 @@ namespace gdla {
 namespace {
 
 constexpr int DN = 128, DR = 64, DQK = DN + DR, DV = 128;
-constexpr int MAX_SPLIT = 8;
+constexpr int MAX_SPLIT = 4;
 
-// largest split count in {8, 4, 2, 1} that cuts K into whole 64-wide blocks
+// largest split count in {4, 2, 1} that cuts K into whole 64-wide blocks
+// (measured on the batch-64 down and output projections, K = 4096 and 6144:
+// four K ranges beat eight by 2-3 us per launch; fewer, longer workgroups
+// amortize the fill and drain of the load pipeline)
 int ksplit(int K) {
   for (int sp = MAX_SPLIT; sp > 1; sp >>= 1)
     if (K % (64 * sp) == 0) return sp;

@@ -41,8 +41,8 @@ HBM_PEAK_GBS = 8000.0                # MI355X HBM3E
 # the ratio of bytes to counter reading of a device copy of known size timed in
 # the same pass (--copy-probe-mib).  Tied to the kernel source it was measured
 # on: reported as null once that source changes.
-ATTN_TRAFFIC = {"source_sha256": "367b18ae881e70e1af48f28642ec968e4c61b22245e291e9132fcb3a8ea78e92",
-                "fetch_bytes": 4020303158, "write_bytes": 402653184}
+ATTN_TRAFFIC = {"source_sha256": "c2e28066af1db6593c9c0e2af1ce34477123f9fee1a777973cd0f6da6f2674c5",
+                "fetch_bytes": 4034294848, "write_bytes": 402653184}
 ATTN_SOURCES = ("attention_gdla_prefill_02_amd/csrc/attn.hip", "attention_gdla_prefill_02_amd/csrc/common.h")
 
 
