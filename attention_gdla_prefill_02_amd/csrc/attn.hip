@@ -58,6 +58,7 @@
 // The fp32 kernel is a plain vector-ALU version (three passes per query and
 // head) for the fp32 configuration.
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -306,12 +307,12 @@ attn_bf16_kernel(AttnArgs a) {
       l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[e >> 3][e & 7], p[e >> 3][(e & 7) + 1]}, one, l, false);
     return l;
   };
-  // P of a tile against the current m; if the sum leaves [0, 2^32] (m still
-  // at its initial value gives infinite P), raise m to the tile's max, rescale
-  // O and l, and form P again
+  // P of a tile against the current m; if the sum leaves [0, sum_limit] (m
+  // still at its initial value gives infinite P), raise m to the tile's max,
+  // rescale O and l, and form P again
   auto softmax_tile = [&](const f32x16& s, bf16x8 (&p)[2]) {
     float ln = softmax_exp(s, p, lsum);
-    if (__any(!(ln <= 4294967296.0f))) {
+    if (__any(!(ln <= a.sum_limit))) {
       float mt = max16(s);
       mt = fmaxf(mt, xor32(mt)) * sc;
       const float mn = fmaxf(m, mt);
@@ -736,9 +737,22 @@ hipError_t attn_bf16_t(const AttnArgs& a, hipStream_t s) {
 }
 }  // namespace
 
+// The row-sum bound of the bf16 kernel's overflow check: 2^32, or for testing
+// the value of GDLA_ATTN_SUM_LIMIT clamped to [1, 2^32] (a small bound sends
+// every tile through the rescale path; results agree to rounding either way)
+static float attn_sum_limit() {
+  constexpr float DEFAULT_LIMIT = 4294967296.0f;
+  const char* e = std::getenv("GDLA_ATTN_SUM_LIMIT");
+  if (!e || !*e) return DEFAULT_LIMIT;
+  const float v = std::strtof(e, nullptr);
+  return v >= 1.0f ? std::min(v, DEFAULT_LIMIT) : (v > 0.0f ? 1.0f : DEFAULT_LIMIT);
+}
+
 hipError_t attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  return a.qk_f16 ? attn_bf16_t<true>(a, s) : attn_bf16_t<false>(a, s);
+  AttnArgs k = a;
+  k.sum_limit = attn_sum_limit();
+  return k.qk_f16 ? attn_bf16_t<true>(k, s) : attn_bf16_t<false>(k, s);
 }
 
 hipError_t attn_f32(const AttnArgs& a, hipStream_t s) {

@@ -131,6 +131,10 @@ struct AttnArgs {
   void* h_out; float* lse_out;
   // bf16 kernel: queries, content keys and rotary keys are fp16 (values stay bf16)
   bool qk_f16;
+  // bf16 kernel: bound on a query's running row sum past which the wave takes
+  // the tile max and rescales (set by attn_bf16: 2^32, or the testing override
+  // GDLA_ATTN_SUM_LIMIT)
+  float sum_limit;
 };
 hipError_t attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t attn_f32(const AttnArgs& a, hipStream_t s);

@@ -41,8 +41,8 @@ HBM_PEAK_GBS = 8000.0                # MI355X HBM3E
 # the ratio of bytes to counter reading of a device copy of known size timed in
 # the same pass (--copy-probe-mib).  Tied to the kernel source it was measured
 # on: reported as null once that source changes.
-ATTN_TRAFFIC = {"source_sha256": "c2e28066af1db6593c9c0e2af1ce34477123f9fee1a777973cd0f6da6f2674c5",
-                "fetch_bytes": 4034294848, "write_bytes": 402653184}
+ATTN_TRAFFIC = {"source_sha256": "015811abb81bd3b886257549b8fdb0bcd3248a46b5f3f7bcaf5264ac1144a779",
+                "fetch_bytes": 4030368618, "write_bytes": 402653184}
 ATTN_SOURCES = ("attention_gdla_prefill_02_amd/csrc/attn.hip", "attention_gdla_prefill_02_amd/csrc/common.h")
 
 

@@ -44,6 +44,12 @@
  * valid until the stream reaches it.  Calls that share output or workspace
  * buffers must be ordered on one stream.
  *
+ * Environment (testing): GDLA_ATTN_SUM_LIMIT sets the bound on a query's
+ * running softmax row sum past which the bf16 prefill attention takes the
+ * tile's max and rescales (default 2^32, clamped to [1, 2^32]; read at every
+ * launch).  A small bound sends every key tile through the rescale path;
+ * results agree to rounding for any value.
+ *
  * Errors: every argument is checked on the host before anything is enqueued;
  * a call that returns non-OK has launched nothing.  GDLA_ERR_HIP means a
  * launch failed; gdla_last_error() has the detail.  Faults that happen
