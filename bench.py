@@ -443,6 +443,7 @@ def main():
     ap.add_argument("--cpu-decode-seqs", type=int, default=16, help="sequences of the decode workload the oracle times")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-report-shapes", action="store_true", help="skip the report-shape (g=4, W=128) workloads")
+    ap.add_argument("--no-long", action="store_true", help="skip the 262,144-token block (one timed step)")
     ap.add_argument("--decode-only", action="store_true", help="time only the decode steps (for profiling)")
     ap.add_argument("--no-packed", action="store_true", help="skip the packed-stream and paged-cache workloads")
     ap.add_argument("--no-backward", action="store_true", help="skip the layer backward")
@@ -513,6 +514,18 @@ def main():
                               "algorithmic_tflop_per_step": round(rp["total_flop"] / 1e12, 3), "stage_ms": rp["kern"]},
                   "decode": rd}
 
+    long_ctx = None
+    if not args.no_long:
+        lp, lw, _, _ = bench_prefill(args, torch, gdla, configs, inputs, name="hybrid_l256k", steps=1, warmup=1)
+        log(f"[bench] 262K prefill: {lp['ms_step']:.1f} ms/step, {lp['tflops']:.1f} TFLOP/s, attention "
+            f"{lp['attn_tflops']:.1f} TFLOP/s, GEMMs+prep {lp['other_tflops']:.1f} TFLOP/s, stages {lp['kern']}")
+        long_ctx = {"workload": f"hybrid_l256k: {lw.note}", "steps": 1, "warmup": 1,
+                    "ms_per_step": round(lp["ms_step"], 2), "block_tflops": round(lp["tflops"], 2),
+                    "frac_of_peak": round(lp["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "attn_tflops": round(lp["attn_tflops"], 2), "gemm_prep_tflops": round(lp["other_tflops"], 2),
+                    "algorithmic_tflop_per_step": round(lp["total_flop"] / 1e12, 3), "stage_ms": lp["kern"],
+                    "output_finite": lp["finite"]}
+
     packed = None
     if not args.no_packed:
         packed = {"prefill": bench_packed(args, torch, gdla, configs, inputs),
@@ -558,6 +571,7 @@ def main():
                     "output_finite": pf["finite"]},
         "decode": decode,
         "report_shapes": report,
+        "long_context": long_ctx,
         "packed_and_paged": packed,
         "backward": backward,
         "cpu_baseline": cpu,
