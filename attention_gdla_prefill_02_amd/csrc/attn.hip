@@ -427,6 +427,28 @@ attn_bf16_kernel(AttnArgs a) {
   float* sH = reinterpret_cast<float*>(smem_raw);                          // [BQ][DV + 4] (AM_FUSED)
   bf16* sZ = reinterpret_cast<bf16*>(smem_raw + (MODE == AM_FUSED ? (size_t)BQ * (DV + 4) * 4 : 0));  // [BQ][g*DV + 8]
   const int qrow = 32 * half + l32;
+  // signal waves: the row's lambda and gate (and, for AM_SIGNAL, H_N) are
+  // loaded before the barrier that publishes H_N, so their latency overlaps
+  // the noise waves' LDS writes
+  f32x4 g4s[DV / 32][4], hn4s[MODE == AM_SIGNAL ? DV / 32 : 1][4];
+  float lam = 0.f;
+  if (!noise_wave) {
+    const int64_t t = tb + min(qme, L - 1);
+    const int j = n * G + hs;
+    lam = a.lam[t * nS + j];
+    const float* gate = a.gate + t * a.ld_gate + (int64_t)j * DV;
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g4s[d][i] = *reinterpret_cast<const f32x4*>(gate + d * 32 + 8 * i + 4 * hi);
+    if constexpr (MODE == AM_SIGNAL) {
+      const float* hng = hn_row(t);
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hn4s[d][i] = *reinterpret_cast<const f32x4*>(hng + d * 32 + 8 * i + 4 * hi);
+    }
+  }
   if (MODE == AM_FUSED && noise_wave) {
 #pragma unroll
     for (int d = 0; d < DV / 32; ++d)
@@ -438,19 +460,15 @@ attn_bf16_kernel(AttnArgs a) {
   }
   if (MODE == AM_FUSED) __syncthreads();
   if (!noise_wave) {
-    const int64_t t = tb + min(qme, L - 1);
-    const int j = n * G + hs;
-    const float lam = a.lam[t * nS + j];
-    const float* gate = a.gate + t * a.ld_gate + (int64_t)j * DV;
-    const float* hng = MODE == AM_SIGNAL ? hn_row(t) : nullptr;
 #pragma unroll
     for (int d = 0; d < DV / 32; ++d)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int dv = d * 32 + 8 * i + 4 * hi;
-        const f32x4 hn4 = MODE == AM_SIGNAL ? *reinterpret_cast<const f32x4*>(hng + dv)
-                                            : *reinterpret_cast<const f32x4*>(sH + qrow * (DV + 4) + dv);
-        const f32x4 g4 = *reinterpret_cast<const f32x4*>(gate + dv);
+        f32x4 hn4;
+        if constexpr (MODE == AM_SIGNAL) hn4 = hn4s[d][i];
+        else hn4 = *reinterpret_cast<const f32x4*>(sH + qrow * (DV + 4) + dv);
+        const f32x4 g4 = g4s[d][i];
         bf16x4 z4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) z4[e] = (bf16)(g4[e] * (o[d][4 * i + e] * inv - lam * hn4[e]));

@@ -41,8 +41,8 @@ HBM_PEAK_GBS = 8000.0                # MI355X HBM3E
 # the ratio of bytes to counter reading of a device copy of known size timed in
 # the same pass (--copy-probe-mib).  Tied to the kernel source it was measured
 # on: reported as null once that source changes.
-ATTN_TRAFFIC = {"source_sha256": "015811abb81bd3b886257549b8fdb0bcd3248a46b5f3f7bcaf5264ac1144a779",
-                "fetch_bytes": 4030368618, "write_bytes": 402653184}
+ATTN_TRAFFIC = {"source_sha256": "0a99dcd0bf6af44572013e085c8d02b737da905034fad3143a1edacaa32fb9ee",
+                "fetch_bytes": 4030208305, "write_bytes": 402653184}
 ATTN_SOURCES = ("attention_gdla_prefill_02_amd/csrc/attn.hip", "attention_gdla_prefill_02_amd/csrc/common.h")
 
 
