@@ -20,7 +20,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "libgdla.so")
-SOURCES = ["api.cpp", "gemm.hip", "rowprep.hip", "attn.hip", "decode.hip", "backward.hip", "noalloc.cpp"]
+SOURCES = ["api.cpp", "gemm.hip", "rowprep.hip", "attn.hip", "decode.hip", "backward.hip", "noalloc.cpp", "blas.cpp"]
 ARCH = "gfx950"
 
 
@@ -55,7 +55,7 @@ def build(jobs: int = 8, verbose: bool = True) -> str:
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-lhipblaslt"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")

@@ -87,7 +87,7 @@ gdla_status check_config(const gdla_config* c) {
 // Prefill workspace: every intermediate of the layer, each 256-byte aligned,
 // for a stream of T tokens; plan_bytes for the packed attention's work list.
 struct PrefillLayout {
-  size_t down, cqn, ckvn, kr, lam, rope, q, gate, kc, vt, z, plan, total;
+  size_t down, cqn, ckvn, kr, lam, rope, q, gate, kc, vt, z, plan, blas, total;
   int64_t vt_ld;
 };
 
@@ -108,6 +108,7 @@ PrefillLayout prefill_layout(const Dims& D, int64_t T, size_t plan_bytes) {
   P.vt = o;   o = align256(o + (size_t)D.nN * D.dv * P.vt_ld * e);
   P.z = o;    o = align256(o + (size_t)T * D.nS * D.dv * e);
   P.plan = o; o = align256(o + plan_bytes);
+  P.blas = o; o = align256(o + (D.elt == 2 ? gdla::blas_workspace_bytes() : 0));   // hipBLASLt's workspace (bf16)
   P.total = o;
   return P;
 }
@@ -275,8 +276,15 @@ gdla_status run_prefill(const gdla_config* cfg, const gdla_weights* w, const Str
     }
     if ((err = bf ? attn_bf16(a, s) : attn_f32(a, s)) != hipSuccess) return hip_fail(err, "attention");
   }
-  // 6. output projection (+ residual)
+  // 6. output projection (+ residual): hipBLASLt for bf16 (a plain GEMM; the
+  //    residual is its C term), the library's GEMM otherwise or as the fallback
   if (stages & GDLA_STAGE_OUT) {
+    if (bf) {
+      err = blas_gemm_bf16(ws + P.z, D.nS * D.dv, w->w_o, D.nS * D.dv, residual, D.d, y, D.d, (int)T, (int)D.d,
+                           (int)(D.nS * D.dv), ws + P.blas, blas_workspace_bytes(), s);
+      if (err == hipSuccess) return GDLA_OK;
+      if (err != hipErrorNotSupported) return hip_fail(err, "output projection (hipBLASLt)");
+    }
     GemmArgs g{};
     g.A = ws + P.z; g.lda = D.nS * D.dv;
     g.B = w->w_o; g.ldb = D.nS * D.dv;

@@ -1,0 +1,110 @@
+// The output projection of the bf16 prefill, y = Z W_O^T (+ residual), through
+// hipBLASLt: a plain GEMM whose only epilogue, the residual, is the library's
+// beta * C term.  Measured on the layer's shapes (32768 tokens, d_model 4096,
+// K = 6144 and 8192) the vendor kernel takes 11-31% less time than the
+// library's own 256 x 256 tile GEMM, which stays in use for every projection
+// with a fused epilogue (RoPE, gate, fp16 or hi/lo operands) and as the fallback
+// when hipBLASLt offers no algorithm for a shape.
+//
+// Row-major D[M, N] = A[M, K] B[N, K]^T + beta C is, in hipBLASLt's
+// column-major terms, D^T = op(B) A^T with B stored K x N (transposed) and A
+// stored K x M: m = N, n = M, k = K.
+//
+// State: per thread, one hipBLASLt handle per device and, per (device, shape,
+// strides, residual or not), the descriptors and the algorithm the heuristic
+// ranks first, all created on first use and kept for the life of the process.
+#include <hip/hip_runtime.h>
+#include <hipblaslt/hipblaslt.h>
+
+#include <cstdlib>
+#include <map>
+#include <tuple>
+
+#include "kernels.h"
+
+namespace gdla {
+namespace {
+
+struct BlasPlan {
+  bool ok = false;
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr, ld = nullptr;
+  hipblasLtMatmulAlgo_t algo{};
+  size_t ws = 0;
+};
+
+using BlasKey = std::tuple<int, int, int, int, int64_t, int64_t, int64_t, int64_t, size_t>;
+
+struct BlasState {
+  std::map<int, hipblasLtHandle_t> handles;
+  std::map<BlasKey, BlasPlan> plans;
+};
+
+// never destroyed: tearing a handle down after the HIP runtime at process exit is unsafe
+BlasState& state() {
+  thread_local BlasState* s = new BlasState();
+  return *s;
+}
+
+bool blas_disabled() {
+  const char* e = std::getenv("GDLA_NO_HIPBLASLT");
+  return e && *e && *e != '0';
+}
+
+BlasPlan make_plan(hipblasLtHandle_t h, int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int64_t ldd,
+                   size_t ws_bytes) {
+  BlasPlan p;
+  if (hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS) return p;
+  const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+  hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta));
+  hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb));
+  if (hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, K, N, ldb) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, K, M, lda) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatrixLayoutCreate(&p.lc, HIP_R_16BF, N, M, ldc) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatrixLayoutCreate(&p.ld, HIP_R_16BF, N, M, ldd) != HIPBLAS_STATUS_SUCCESS)
+    return p;
+  hipblasLtMatmulPreference_t pref = nullptr;
+  if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) return p;
+  hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &ws_bytes, sizeof(ws_bytes));
+  hipblasLtMatmulHeuristicResult_t res{};
+  int got = 0;
+  const hipblasStatus_t st =
+      hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.la, p.lb, p.lc, p.ld, pref, 1, &res, &got);
+  hipblasLtMatmulPreferenceDestroy(pref);
+  if (st != HIPBLAS_STATUS_SUCCESS || got < 1 || res.workspaceSize > ws_bytes) return p;
+  p.algo = res.algo;
+  p.ws = res.workspaceSize;
+  p.ok = true;
+  return p;
+}
+
+}  // namespace
+
+size_t blas_workspace_bytes() { return (size_t)32 << 20; }
+
+hipError_t blas_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc, void* D,
+                          int64_t ldd, int M, int N, int K, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (blas_disabled()) return hipErrorNotSupported;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  BlasState& S = state();
+  auto hit = S.handles.find(dev);
+  if (hit == S.handles.end()) {
+    hipblasLtHandle_t h = nullptr;
+    if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) return hipErrorNotSupported;
+    hit = S.handles.emplace(dev, h).first;
+  }
+  const BlasKey key{dev, M, N, K, lda, ldb, C ? ldc : -1, ldd, ws_bytes};
+  auto pit = S.plans.find(key);
+  if (pit == S.plans.end())
+    pit = S.plans.emplace(key, make_plan(hit->second, M, N, K, lda, ldb, C ? ldc : ldd, ldd, ws_bytes)).first;
+  const BlasPlan& p = pit->second;
+  if (!p.ok) return hipErrorNotSupported;
+  const float alpha = 1.0f, beta = C ? 1.0f : 0.0f;
+  const hipblasStatus_t st = hipblasLtMatmul(hit->second, p.desc, &alpha, B, p.la, A, p.lb, &beta, C ? C : D, p.lc,
+                                             D, p.ld, &p.algo, ws, p.ws, s);
+  return st == HIPBLAS_STATUS_SUCCESS ? hipSuccess : hipErrorLaunchFailure;
+}
+
+}  // namespace gdla

@@ -38,13 +38,20 @@
  *   - RMSNorm: c / sqrt(mean(c^2) + rms_eps) * gain.
  *
  * Ownership and threading: every buffer is device memory owned by the
- * caller.  The library allocates nothing, keeps no state besides a
- * thread-local error string, and never synchronizes: all work is enqueued on
- * `stream` (a hipStream_t; NULL = the default stream) and inputs must stay
- * valid until the stream reaches it.  Calls that share output or workspace
- * buffers must be ordered on one stream.
+ * caller.  The library allocates no device memory for data and never
+ * synchronizes: all work is enqueued on `stream` (a hipStream_t; NULL = the
+ * default stream) and inputs must stay valid until the stream reaches it.
+ * Calls that share output or workspace buffers must be ordered on one stream.
+ * Its state is a thread-local error string and, for the bf16 prefill's output
+ * projection (a plain GEMM run on hipBLASLt, residual as its C term), a
+ * hipBLASLt handle per thread and device and the algorithm chosen per shape,
+ * created on that thread's first such call (which also loads hipBLASLt's
+ * kernels; make it outside any stream capture) and kept until the process
+ * ends.
  *
- * Environment (testing): GDLA_ATTN_SUM_LIMIT sets the bound on a query's
+ * Environment (testing): GDLA_NO_HIPBLASLT=1 runs that output projection on
+ * the library's own GEMM instead (also the fallback when hipBLASLt offers no
+ * algorithm for a shape).  GDLA_ATTN_SUM_LIMIT sets the bound on a query's
  * running softmax row sum past which the bf16 prefill attention takes the
  * tile's max and rescales (default 2^32, clamped to [1, 2^32]; read at every
  * launch).  A small bound sends every key tile through the rescale path;

@@ -37,6 +37,15 @@ SMALL_CASES = [
 
 @pytest.mark.parametrize("B,L,window", SMALL_CASES)
 def test_prefill_small_bf16(B, L, window):
+    run_small(B, L, window)
+
+
+@pytest.mark.parametrize("B,L,window", [(2, 257, 0), (1, 300, 100)])
+def test_prefill_small_bf16_both_output_projections(out_proj, B, L, window):
+    run_small(B, L, window)
+
+
+def run_small(B, L, window):
     r = run_layer(SMALL, "bf16", B, L, window, seed=11)
     assert_close(r["y"], r["ref"]["y"], "bf16", f"y B={B} L={L} W={window}")
     lay = gdla.prefill_layout(r["cfg"], B, L)
@@ -66,7 +75,17 @@ def test_prefill_tiny_fp32_windows(window, L):
     assert_close(r["y"], r["ref"]["y"], "fp32", f"tiny fp32 W={window} L={L}")
 
 
-def test_residual_variant_bf16():
+@pytest.fixture(params=["hipblaslt", "library"])
+def out_proj(request, monkeypatch):
+    """The bf16 output projection runs on hipBLASLt; GDLA_NO_HIPBLASLT selects
+    the library's own GEMM, its fallback.  Both are checked."""
+    if request.param == "library":
+        monkeypatch.setenv("GDLA_NO_HIPBLASLT", "1")
+    print(f"[case] output projection on {request.param}", flush=True)
+    return request.param
+
+
+def test_residual_variant_bf16(out_proj):
     Wd, _ = make_layer(SMALL, 13, "bf16")
     x = inputs.make_x(1, 96, SMALL["d_model"], 13, "bf16").to("cuda")
     cfg = gdla.make_config(SMALL, 0, "bf16")
