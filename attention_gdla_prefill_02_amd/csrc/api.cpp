@@ -280,8 +280,8 @@ gdla_status run_prefill(const gdla_config* cfg, const gdla_weights* w, const Str
   //    residual is its C term), the library's GEMM otherwise or as the fallback
   if (stages & GDLA_STAGE_OUT) {
     if (bf) {
-      err = blas_gemm_bf16(ws + P.z, D.nS * D.dv, w->w_o, D.nS * D.dv, residual, D.d, y, D.d, (int)T, (int)D.d,
-                           (int)(D.nS * D.dv), ws + P.blas, blas_workspace_bytes(), s);
+      err = blas_gemm(ws + P.z, D.nS * D.dv, w->w_o, D.nS * D.dv, residual, D.d, y, D.d, (int)T, (int)D.d,
+                      (int)(D.nS * D.dv), false, ws + P.blas, blas_workspace_bytes(), s);
       if (err == hipSuccess) return GDLA_OK;
       if (err != hipErrorNotSupported) return hip_fail(err, "output projection (hipBLASLt)");
     }

@@ -20,7 +20,7 @@ struct BackwardLayout {
   size_t down, cqn, ckvn, kr, lam, rope, q, gate, kv, kvT, z, hall, lse;
   size_t woT, wuqgT, wukvT, wdownT;
   size_t dz, dyT, zT, dh, dvec, dqg, dkv, dkrp, dcqn, dckvn, dqgT, cqnT, dkvT, ckvnT, ddown, ddownT, xT,
-      gpart, wpart;
+      gpart, wpart, blas;
   size_t plan_f, plan_q, plan_k;   // packed stream: work lists of the forward attention, dQ and dK/dV
   size_t total;
 };

@@ -829,8 +829,27 @@ wgrad_sum_kernel(const float* __restrict__ part, int S, int64_t MN, float* __res
   *reinterpret_cast<f32x4*>(out + i) = acc;
 }
 
-// g describes C = A B^T over the full K with C = out (contiguous [M, N] fp32)
-hipError_t wgrad_gemm(GemmArgs g, char* part, hipStream_t s) {
+// A gradient GEMM without an epilogue (C = A B^T, fp32 or bf16 out):
+// hipBLASLt when it takes the shape, else the library's GEMM
+hipError_t plain_gemm(const GemmArgs& g, char* blas_ws, hipStream_t s) {
+  if (g.batch == 1 && !g.R && !g.B2 && !g.B3 && !g.kwrapA && !g.kwrapB && g.Npad <= g.N && !g.out_f16 &&
+      (g.epi == EPI_F32 || g.epi == EPI_STORE)) {
+    const hipError_t e = blas_gemm(g.A, g.lda, g.B, g.ldb, nullptr, 0, g.C, g.ldc, g.M, g.N, g.K, g.epi == EPI_F32,
+                                   blas_ws, blas_workspace_bytes(), s);
+    if (e != hipErrorNotSupported) return e;
+  }
+  return gemm_bf16(g, s);
+}
+
+// g describes C = A B^T over the full K with C = out (contiguous [M, N] fp32).
+// hipBLASLt takes the whole K when it offers an algorithm (its own kernels
+// split long reductions); else the library's GEMM runs the split below.
+hipError_t wgrad_gemm(GemmArgs g, char* part, char* blas_ws, hipStream_t s) {
+  {
+    const hipError_t e = blas_gemm(g.A, g.lda, g.B, g.ldb, nullptr, 0, g.C, g.ldc, g.M, g.N, g.K, true, blas_ws,
+                                   blas_workspace_bytes(), s);
+    if (e != hipErrorNotSupported) return e;
+  }
   const int S = wgrad_split(g.M, g.N, g.K);
   if (S == 1) return gemm_bf16(g, s);
   float* out = (float*)g.C;
@@ -910,6 +929,7 @@ BackwardLayout backward_layout(const BwdDims& D, int64_t T, int nseq) {
     for (const auto& md : dims) wp = std::max(wp, wgrad_part_bytes(md[0], md[1], Tp));
     P.wpart = take(wp);
   }
+  P.blas = take(blas_workspace_bytes());   // hipBLASLt's workspace for the gradient GEMMs
   P.plan_f = P.plan_q = P.plan_k = 0;
   if (nseq > 0) {
     const size_t f = attn_plan_bytes(nseq, T, (int)D.g), q = block_plan_bytes(nseq, T, 32),
@@ -1029,7 +1049,7 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     g.B = ws + P.woT; g.ldb = d;
     g.C = ws + P.dz; g.ldc = D.ngate;
     g.M = (int)T; g.N = (int)D.ngate; g.K = d; g.batch = 1; g.epi = EPI_F32;
-    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    if ((e = plain_gemm(g, ws + P.blas, s)) != hipSuccess) return e;
   }
   if ((e = transpose_bf16(c.dy, d, ws + P.dyT, Tp, (int)T, d, (int)Tp, s)) != hipSuccess) return e;
   if ((e = transpose_bf16(ws + P.z, D.ngate, ws + P.zT, Tp, (int)T, (int)D.ngate, (int)Tp, s)) != hipSuccess) return e;
@@ -1039,7 +1059,7 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     g.B = ws + P.zT; g.ldb = Tp;
     g.C = c.grads->w_o; g.ldc = D.ngate;
     g.M = d; g.N = (int)D.ngate; g.K = (int)Tp; g.batch = 1; g.epi = EPI_F32;
-    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, ws + P.blas, s)) != hipSuccess) return e;
   }
   // 4. gate and differential
   {
@@ -1088,7 +1108,7 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     g.B = ws + P.wuqgT; g.ldb = nqg;
     g.C = ws + P.dcqn; g.ldc = rq;
     g.M = (int)T; g.N = rq; g.K = (int)nqg; g.batch = 1; g.epi = EPI_F32;
-    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    if ((e = plain_gemm(g, ws + P.blas, s)) != hipSuccess) return e;
   }
   if ((e = transpose_bf16(ws + P.dqg, nqg, ws + P.dqgT, Tp, (int)T, (int)nqg, (int)Tp, s)) != hipSuccess) return e;
   if ((e = transpose_bf16(ws + P.cqn, rq, ws + P.cqnT, Tp, (int)T, rq, (int)Tp, s)) != hipSuccess) return e;
@@ -1098,10 +1118,10 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     g.B = ws + P.cqnT; g.ldb = Tp;
     g.C = c.grads->w_uq; g.ldc = rq;
     g.M = (int)D.nq; g.N = rq; g.K = (int)Tp; g.batch = 1; g.epi = EPI_F32;
-    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, ws + P.blas, s)) != hipSuccess) return e;
     g.A = ws + P.dqgT + (size_t)D.nq * Tp * 2;
     g.C = c.grads->w_gate; g.M = (int)D.ngate;
-    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, ws + P.blas, s)) != hipSuccess) return e;
   }
   // 7. KV side: dc_KVn = [dK^C | dV] W_UKV; dW_UKV = [dK^C | dV]^T c_KVn
   {
@@ -1110,7 +1130,7 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     g.B = ws + P.wukvT; g.ldb = nkv;
     g.C = ws + P.dckvn; g.ldc = rkv;
     g.M = (int)T; g.N = rkv; g.K = (int)nkv; g.batch = 1; g.epi = EPI_F32;
-    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    if ((e = plain_gemm(g, ws + P.blas, s)) != hipSuccess) return e;
   }
   if ((e = transpose_bf16(ws + P.dkv, nkv, ws + P.dkvT, Tp, (int)T, (int)nkv, (int)Tp, s)) != hipSuccess) return e;
   if ((e = transpose_bf16(ws + P.ckvn, 2 * rkv, ws + P.ckvnT, Tp, (int)T, rkv, (int)Tp, s)) != hipSuccess) return e;
@@ -1120,7 +1140,7 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     g.B = ws + P.ckvnT; g.ldb = Tp;
     g.C = c.grads->w_ukv; g.ldc = rkv;
     g.M = (int)nkv; g.N = rkv; g.K = (int)Tp; g.batch = 1; g.epi = EPI_F32;
-    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, ws + P.blas, s)) != hipSuccess) return e;
   }
   // 8. RMSNorms, the rotary key's RoPE, gains
   {
@@ -1147,7 +1167,7 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     g.B = ws + P.wdownT; g.ldb = P.ndp;
     g.C = c.dx; g.ldc = d;
     g.M = (int)T; g.N = d; g.K = (int)P.ndp; g.batch = 1; g.epi = EPI_STORE;
-    if ((e = gemm_bf16(g, s)) != hipSuccess) return e;
+    if ((e = plain_gemm(g, ws + P.blas, s)) != hipSuccess) return e;
   }
   if ((e = transpose_bf16(ws + P.ddown, P.ndp, ws + P.ddownT, Tp, (int)T, (int)P.ndp, (int)Tp, s)) != hipSuccess)
     return e;
@@ -1158,11 +1178,11 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     g.B = ws + P.xT; g.ldb = Tp;
     g.C = c.grads->w_dq; g.ldc = d;
     g.M = rq; g.N = d; g.K = (int)Tp; g.batch = 1; g.epi = EPI_F32;
-    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, ws + P.blas, s)) != hipSuccess) return e;
     g.A = ws + P.ddownT + (size_t)rq * Tp * 2; g.C = c.grads->w_dkv; g.M = rkv + DR;
-    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, ws + P.blas, s)) != hipSuccess) return e;
     g.A = ws + P.ddownT + (size_t)(rq + rkv + DR) * Tp * 2; g.C = c.grads->w_lambda; g.M = nS;
-    if ((e = wgrad_gemm(g, ws + P.wpart, s)) != hipSuccess) return e;
+    if ((e = wgrad_gemm(g, ws + P.wpart, ws + P.blas, s)) != hipSuccess) return e;
   }
   return hipSuccess;
 }

@@ -1,18 +1,20 @@
-// The output projection of the bf16 prefill, y = Z W_O^T (+ residual), through
-// hipBLASLt: a plain GEMM whose only epilogue, the residual, is the library's
-// beta * C term.  Measured on the layer's shapes (32768 tokens, d_model 4096,
-// K = 6144 and 8192) the vendor kernel takes 11-31% less time than the
-// library's own 256 x 256 tile GEMM, which stays in use for every projection
-// with a fused epilogue (RoPE, gate, fp16 or hi/lo operands) and as the fallback
-// when hipBLASLt offers no algorithm for a shape.
+// Plain GEMMs through hipBLASLt: the output projection of the bf16 prefill,
+// y = Z W_O^T (+ residual, the library's beta * C term), and the gradient
+// GEMMs of the backward (fp32 or bf16 out, no epilogue).  Measured on the
+// layer's shapes (32768 tokens, d_model 4096, K = 6144 and 8192) the vendor
+// kernel takes 11-31% less time than the library's own 256 x 256 tile GEMM,
+// which stays in use for every projection with a fused epilogue (RoPE, gate,
+// fp16 or hi/lo operands) and as the fallback when hipBLASLt offers no
+// algorithm for a shape.
 //
 // Row-major D[M, N] = A[M, K] B[N, K]^T + beta C is, in hipBLASLt's
 // column-major terms, D^T = op(B) A^T with B stored K x N (transposed) and A
 // stored K x M: m = N, n = M, k = K.
 //
 // State: per thread, one hipBLASLt handle per device and, per (device, shape,
-// strides, residual or not), the descriptors and the algorithm the heuristic
-// ranks first, all created on first use and kept for the life of the process.
+// strides, residual or not, output type), the descriptors and the algorithm
+// the heuristic ranks first, all created on first use and kept for the life
+// of the process.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
@@ -33,7 +35,7 @@ struct BlasPlan {
   size_t ws = 0;
 };
 
-using BlasKey = std::tuple<int, int, int, int, int64_t, int64_t, int64_t, int64_t, size_t>;
+using BlasKey = std::tuple<int, int, int, int, int64_t, int64_t, int64_t, int64_t, size_t, bool>;
 
 struct BlasState {
   std::map<int, hipblasLtHandle_t> handles;
@@ -52,7 +54,7 @@ bool blas_disabled() {
 }
 
 BlasPlan make_plan(hipblasLtHandle_t h, int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int64_t ldd,
-                   size_t ws_bytes) {
+                   bool d_f32, size_t ws_bytes) {
   BlasPlan p;
   if (hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS) return p;
   const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
@@ -60,8 +62,8 @@ BlasPlan make_plan(hipblasLtHandle_t h, int M, int N, int K, int64_t lda, int64_
   hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb));
   if (hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, K, N, ldb) != HIPBLAS_STATUS_SUCCESS ||
       hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, K, M, lda) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatrixLayoutCreate(&p.lc, HIP_R_16BF, N, M, ldc) != HIPBLAS_STATUS_SUCCESS ||
-      hipblasLtMatrixLayoutCreate(&p.ld, HIP_R_16BF, N, M, ldd) != HIPBLAS_STATUS_SUCCESS)
+      hipblasLtMatrixLayoutCreate(&p.lc, d_f32 ? HIP_R_32F : HIP_R_16BF, N, M, ldc) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatrixLayoutCreate(&p.ld, d_f32 ? HIP_R_32F : HIP_R_16BF, N, M, ldd) != HIPBLAS_STATUS_SUCCESS)
     return p;
   hipblasLtMatmulPreference_t pref = nullptr;
   if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) return p;
@@ -82,8 +84,8 @@ BlasPlan make_plan(hipblasLtHandle_t h, int M, int N, int K, int64_t lda, int64_
 
 size_t blas_workspace_bytes() { return (size_t)32 << 20; }
 
-hipError_t blas_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc, void* D,
-                          int64_t ldd, int M, int N, int K, void* ws, size_t ws_bytes, hipStream_t s) {
+hipError_t blas_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc, void* D,
+                     int64_t ldd, int M, int N, int K, bool d_f32, void* ws, size_t ws_bytes, hipStream_t s) {
   if (blas_disabled()) return hipErrorNotSupported;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -95,10 +97,10 @@ hipError_t blas_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb
     if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) return hipErrorNotSupported;
     hit = S.handles.emplace(dev, h).first;
   }
-  const BlasKey key{dev, M, N, K, lda, ldb, C ? ldc : -1, ldd, ws_bytes};
+  const BlasKey key{dev, M, N, K, lda, ldb, C ? ldc : -1, ldd, ws_bytes, d_f32};
   auto pit = S.plans.find(key);
   if (pit == S.plans.end())
-    pit = S.plans.emplace(key, make_plan(hit->second, M, N, K, lda, ldb, C ? ldc : ldd, ldd, ws_bytes)).first;
+    pit = S.plans.emplace(key, make_plan(hit->second, M, N, K, lda, ldb, C ? ldc : ldd, ldd, d_f32, ws_bytes)).first;
   const BlasPlan& p = pit->second;
   if (!p.ok) return hipErrorNotSupported;
   const float alpha = 1.0f, beta = C ? 1.0f : 0.0f;

@@ -40,12 +40,13 @@ struct GemmArgs {
 hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s);
 // fp32 vector-ALU GEMM (any sizes; EPI_QG is not applied, see qg_finish).
 hipError_t gemm_f32(const GemmArgs& a, hipStream_t s);
-// Row-major D[M, N] = A[M, K] B[N, K]^T (+ C when C != nullptr), bf16 operands
-// and outputs, through hipBLASLt (blas.cpp).  hipErrorNotSupported when
-// hipBLASLt offers no algorithm for the shape, or GDLA_NO_HIPBLASLT is set (the
-// caller then runs gemm_bf16); ws: blas_workspace_bytes() of device memory.
-hipError_t blas_gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc, void* D,
-                          int64_t ldd, int M, int N, int K, void* ws, size_t ws_bytes, hipStream_t s);
+// Row-major D[M, N] = A[M, K] B[N, K]^T (+ C when C != nullptr), bf16
+// operands, D and C bf16 or fp32 (d_f32), through hipBLASLt (blas.cpp).
+// hipErrorNotSupported when hipBLASLt offers no algorithm for the shape, or
+// GDLA_NO_HIPBLASLT is set (the caller then runs gemm_bf16); ws:
+// blas_workspace_bytes() of device memory.
+hipError_t blas_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc, void* D,
+                     int64_t ldd, int M, int N, int K, bool d_f32, void* ws, size_t ws_bytes, hipStream_t s);
 size_t blas_workspace_bytes();
 // fp32 path: RoPE on the query heads' rotary parts and sigmoid on the gate, in place.
 hipError_t qg_finish(float* q, int64_t ldq, float* g, int64_t ldg, int64_t T, int heads, int gate_cols, int d_qk,

@@ -55,6 +55,30 @@ def test_backward_small(B, L, window):
     run(SMALL, B, L, window, seed=81 + L)
 
 
+@pytest.mark.parametrize("B,L,window", [(2, 100, 0), (1, 257, 40)])
+def test_backward_small_library_gemms(monkeypatch, B, L, window):
+    """The gradient GEMMs on the library's own GEMM (GDLA_NO_HIPBLASLT), the
+    fallback of the hipBLASLt path the other tests take."""
+    monkeypatch.setenv("GDLA_NO_HIPBLASLT", "1")
+    run(SMALL, B, L, window, seed=81 + L)
+
+
+def test_backward_deterministic():
+    """Two calls on the same inputs give the same bits (no atomics in any
+    gradient reduction, hipBLASLt's included), at a length whose weight
+    gradients reduce over 4,096 tokens."""
+    Wd, _ = make_layer(SMALL, 90, "bf16", gamma="random")
+    x = inputs.make_x(1, 4096, SMALL["d_model"], 90, "bf16").to("cuda")
+    dy = inputs.make_x(1, 4096, SMALL["d_model"], 1090, "bf16").to("cuda")
+    cfg = gdla.make_config(SMALL, 0, "bf16")
+    dx1, g1 = gdla.backward(cfg, Wd, x, dy)
+    dx2, g2 = gdla.backward(cfg, Wd, x, dy)
+    torch.cuda.synchronize()
+    assert torch.equal(dx1, dx2)
+    for n in inputs.WEIGHT_NAMES:
+        assert torch.equal(g1[n], g2[n]), n
+
+
 @pytest.mark.parametrize("temp", ["rotary", "logit"])
 def test_backward_position_offset_and_yarn(temp):
     run(SMALL, 2, 130, 0, seed=82, pos_offset=70000, yarn=(64.0, 4096, 32.0, 1.0), temp=temp)
