@@ -107,6 +107,23 @@ def test_determinism_bf16():
     assert torch.equal(a, b)
 
 
+def test_full_layer_deterministic_32k():
+    """A 32K full-causal layer at the timed shapes, twice: the same bits, so
+    no kernel on the path (hipBLASLt's stream-K output projection included)
+    reduces in a run-dependent order."""
+    s, T = configs.MOTIF_SHAPES, 32768
+    print(f"[case] full layer twice, L={T}", flush=True)
+    Wd = {k: v.to("cuda") for k, v in inputs.make_weights(s, 31, "bf16").items()}
+    x = inputs.make_x(1, T, s["d_model"], 31, "bf16").to("cuda")
+    cfg = gdla.make_config(s, 0, "bf16")
+    ws = gdla.alloc_workspace(gdla.prefill_workspace_size(cfg, 1, T))
+    y1 = gdla.prefill(cfg, Wd, x, residual=x, workspace=ws)
+    y2 = gdla.prefill(cfg, Wd, x, residual=x, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y1).all()
+    assert torch.equal(y1, y2)
+
+
 def _ws_view(ws, off, n, dtype, shape):
     esize = torch.tensor([], dtype=dtype).element_size()
     return ws[off:off + n * esize].view(dtype).reshape(shape)
