@@ -42,15 +42,15 @@
  * synchronizes: all work is enqueued on `stream` (a hipStream_t; NULL = the
  * default stream) and inputs must stay valid until the stream reaches it.
  * Calls that share output or workspace buffers must be ordered on one stream.
- * Its state is a thread-local error string and, for the bf16 prefill's output
- * projection (a plain GEMM run on hipBLASLt, residual as its C term), a
- * hipBLASLt handle per thread and device and the algorithm chosen per shape,
- * created on that thread's first such call (which also loads hipBLASLt's
- * kernels; make it outside any stream capture) and kept until the process
- * ends.
+ * Its state is a thread-local error string and, for the plain GEMMs it runs
+ * on hipBLASLt (the bf16 prefill's output projection, residual as its C term,
+ * and the backward's gradient GEMMs), a hipBLASLt handle per thread and device
+ * and the algorithm chosen per shape, created on that thread's first such
+ * call (which also loads hipBLASLt's kernels; make it outside any stream
+ * capture) and kept until the process ends.  Decode does not use hipBLASLt.
  *
- * Environment (testing): GDLA_NO_HIPBLASLT=1 runs that output projection on
- * the library's own GEMM instead (also the fallback when hipBLASLt offers no
+ * Environment (testing): GDLA_NO_HIPBLASLT=1 runs those GEMMs on the
+ * library's own GEMM instead (also the fallback when hipBLASLt offers no
  * algorithm for a shape).  GDLA_ATTN_SUM_LIMIT sets the bound on a query's
  * running softmax row sum past which the bf16 prefill attention takes the
  * tile's max and rescales (default 2^32, clamped to [1, 2^32]; read at every
