@@ -11,6 +11,10 @@
 // column-major terms, D^T = op(B) A^T with B stored K x N (transposed) and A
 // stored K x M: m = N, n = M, k = K.
 //
+// Only contiguous outputs (ldd == N, and ldc == N with a C term) go to the
+// vendor library; every call in this library has them, and a strided output
+// returns hipErrorNotSupported so that the caller uses its own GEMM.
+//
 // State: per thread, one hipBLASLt handle per device and, per (device, shape,
 // strides, residual or not, output type), the descriptors and the algorithm
 // the heuristic ranks first, all created on first use and kept for the life
@@ -86,7 +90,7 @@ size_t blas_workspace_bytes() { return (size_t)32 << 20; }
 
 hipError_t blas_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc, void* D,
                      int64_t ldd, int M, int N, int K, bool d_f32, void* ws, size_t ws_bytes, hipStream_t s) {
-  if (blas_disabled()) return hipErrorNotSupported;
+  if (blas_disabled() || ldd != N || (C && ldc != N)) return hipErrorNotSupported;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
