@@ -86,6 +86,11 @@ BlasPlan make_plan(hipblasLtHandle_t h, int M, int N, int K, int64_t lda, int64_
 
 }  // namespace
 
+// hipBLASLt's heuristic does not honour the workspace limit it is given, and
+// a plan whose first-ranked algorithm needs more than this is refused (the
+// caller's own GEMM then runs).  That happens for three of the layer's weight
+// gradients (W_UQ, W_G and W_DQ at K = 32,768 tokens: 40-48 MB), where the
+// library's split-K GEMM is the faster of the two anyway.
 size_t blas_workspace_bytes() { return (size_t)32 << 20; }
 
 hipError_t blas_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc, void* D,
