@@ -502,7 +502,11 @@ struct Tile32 {
 
 // dQ: workgroup = (sequence, KV group n, 32 queries), wave = head slot (its 32
 // queries).  Key tiles of 32 rows stream through LDS: K rows (score A operand
-// and, read transposed, the dQ A operand) and V rows (dP A operand).
+// and, read transposed, the dQ A operand) and V rows (dP A operand).  The
+// wave's dH fragments (the dP B operand, the same for every tile) sit in LDS
+// behind the two tile buffers, one 1 KB block per fragment in lane order:
+// held in registers they pushed the wave past the 256 registers that two
+// workgroups per CU allow, and the compiler spilled them to scratch.
 template <int G>
 __global__ void __launch_bounds__(64 * (G + 1), 2)
 attn_bwd_dq32_kernel(AttnBwdArgs a) {
@@ -537,13 +541,15 @@ attn_bwd_dq32_kernel(AttnBwdArgs a) {
   const int ql = q0 + l32;                  // this lane's query (score column)
   const int64_t qrow = tb + min(ql, L - 1);
 
-  bf16x8 qf[DQK / 16], dhf[DV / 16];
+  bf16x8 qf[DQK / 16];
 #pragma unroll
   for (int s = 0; s < DQK / 16; ++s)
     qf[s] = *reinterpret_cast<const bf16x8*>(a.q + qrow * a.ld_q + head * DQK + 16 * s + 8 * hi);
+  unsigned char* dhs = smem + 2 * BUF + w * (DV / 16) * 1024 + lane * 16;   // this lane's dH fragment slots
 #pragma unroll
   for (int s = 0; s < DV / 16; ++s)
-    dhf[s] = *reinterpret_cast<const bf16x8*>(a.dh + qrow * H * DV + head * DV + 16 * s + 8 * hi);
+    *reinterpret_cast<bf16x8*>(dhs + s * 1024) =
+        *reinterpret_cast<const bf16x8*>(a.dh + qrow * H * DV + head * DV + 16 * s + 8 * hi);
   const float lse = a.lse[qrow * H + head], dvec = a.dvec[qrow * H + head];
 
   const int k_lo = W > 0 ? max(0, q0 - W + 1) : 0, k_hi = min(L, q0 + 32);
@@ -624,7 +630,8 @@ attn_bwd_dq32_kernel(AttnBwdArgs a) {
     for (int s = 0; s < DQK / 16; ++s)
       st = mfma32(*reinterpret_cast<const bf16x8*>(Kt + ka[s & 3] + 128 * (s >> 2)), qf[s], st);
 #pragma unroll
-    for (int s = 0; s < DV / 16; ++s) dp = mfma32(*reinterpret_cast<const bf16x8*>(Vt + va[s]), dhf[s], dp);
+    for (int s = 0; s < DV / 16; ++s)
+      dp = mfma32(*reinterpret_cast<const bf16x8*>(Vt + va[s]), *reinterpret_cast<const bf16x8*>(dhs + s * 1024), dp);
     // dS^T = P^T (dP^T - rowsum(dH H)); register (i, j) is key kb + 16 (i >> 1) + 8 hi + 4 (i & 1) + j
     bf16x8 ds[2];
 #pragma unroll
@@ -783,7 +790,8 @@ hipError_t set_lds(K kernel, size_t bytes) {
 
 template <int G>
 hipError_t attn_bwd_g(const AttnBwdArgs& a, hipStream_t s) {
-  constexpr size_t dq_lds = 2 * (size_t)(Tile32<DQK / 8, G + 1>::BYTES + Tile32<DV / 8, G + 1>::BYTES);
+  constexpr size_t dq_lds = 2 * (size_t)(Tile32<DQK / 8, G + 1>::BYTES + Tile32<DV / 8, G + 1>::BYTES) +
+                            (size_t)(G + 1) * (DV / 16) * 1024;   // + the waves' dH fragments
   constexpr size_t dkv_lds =
       2 * (size_t)(SwzStage<TR, DQK / 8, DKV_NW>::BYTES + SwzStage<TR, DV / 8, DKV_NW>::BYTES + 2 * TR * 4);
   hipError_t e;   // set on every call: no process-wide state, and correct on every device
