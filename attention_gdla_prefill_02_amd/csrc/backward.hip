@@ -740,17 +740,28 @@ prep_bwd_kernel(PrepBwdArgs a) {
     bf16* out = a.ddown + t * a.ld_dd;
     rms_bwd(row, a.dcqn + t * a.q_rank, a.g_q, nq, out, accq);
     rms_bwd(row + a.q_rank, a.dckvn + t * a.kv_rank, a.g_kv, nk, out + a.q_rank, acck);
-    // rotary key: sum over KV groups, then the transposed rotation
-    if (lane < DR / 2) {
-      float g1 = 0.f, g2 = 0.f;
-      for (int n = 0; n < a.nN; ++n) {
-        const float* p = a.dkr_part + ((int64_t)n * a.T + t) * DR;
-        g1 += p[lane];
-        g2 += p[lane + DR / 2];
+    // rotary key: lane l sums column l of the KV groups' slices in group
+    // order (the loads of eight groups in flight), then lane l < 32 takes the
+    // pair (l, l + 32) through the transposed rotation
+    {
+      const float* p = a.dkr_part + t * DR + lane;
+      const int64_t gs = a.T * DR;
+      float gsum = 0.f;
+      int n = 0;
+      for (; n + 8 <= a.nN; n += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = p[(n + u) * gs];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) gsum += v[u];
       }
-      const float c = a.rope[(t * (DR / 2) + lane) * 2], s = a.rope[(t * (DR / 2) + lane) * 2 + 1];
-      out[a.q_rank + a.kv_rank + lane] = (bf16)(g1 * c + g2 * s);
-      out[a.q_rank + a.kv_rank + DR / 2 + lane] = (bf16)(g2 * c - g1 * s);
+      for (; n < a.nN; ++n) gsum += p[n * gs];
+      const float g1 = gsum, g2 = __shfl_down(gsum, DR / 2);
+      if (lane < DR / 2) {
+        const float c = a.rope[(t * (DR / 2) + lane) * 2], s = a.rope[(t * (DR / 2) + lane) * 2 + 1];
+        out[a.q_rank + a.kv_rank + lane] = (bf16)(g1 * c + g2 * s);
+        out[a.q_rank + a.kv_rank + DR / 2 + lane] = (bf16)(g2 * c - g1 * s);
+      }
     }
     for (int col = a.pad_from + lane; col < a.ld_dd; col += 64) out[col] = (bf16)0.f;
   }
@@ -771,16 +782,37 @@ prep_bwd_kernel(PrepBwdArgs a) {
   flush(acck, nk, a.q_rank);
 }
 
-// gain gradients: column sums of the per-block partials
-__global__ void __launch_bounds__(256)
+// gain gradients: column sums of the per-block partials.  A workgroup owns 64
+// columns; wave w sums blocks w, w + 16, ... in that order (the loads of eight
+// blocks in flight), and the 16 waves' sums are added in wave order.
+constexpr int GR_WAVES = 16;
+__global__ void __launch_bounds__(64 * GR_WAVES)
 gain_reduce_kernel(const float* gpart, int blocks, int q_rank, int kv_rank, float* dg_q, float* dg_kv) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
+  __shared__ float part[GR_WAVES][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + lane;
   const int ncol = q_rank + kv_rank;
-  if (col >= ncol) return;
   float s = 0.f;
-  for (int b = 0; b < blocks; ++b) s += gpart[(int64_t)b * ncol + col];
-  if (col < q_rank) dg_q[col] = s;
-  else dg_kv[col - q_rank] = s;
+  if (col < ncol) {
+    const float* p = gpart + col;
+    int b = w;
+    for (; b + GR_WAVES * 7 < blocks; b += GR_WAVES * 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(b + GR_WAVES * u) * ncol];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; b < blocks; b += GR_WAVES) s += p[(int64_t)b * ncol];
+  }
+  part[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && col < ncol) {
+    float t = 0.f;
+    for (int i = 0; i < GR_WAVES; ++i) t += part[i][lane];
+    if (col < q_rank) dg_q[col] = t;
+    else dg_kv[col - q_rank] = t;
+  }
 }
 
 template <class K>
@@ -1163,7 +1195,7 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     k.T = T; k.q_rank = rq; k.kv_rank = rkv;
     hipLaunchKernelGGL(prep_bwd_kernel, dim3((unsigned)P.prep_blocks), dim3(256), 0, s, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(gain_reduce_kernel, dim3((unsigned)cdiv(rq + rkv, 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(gain_reduce_kernel, dim3((unsigned)cdiv(rq + rkv, 64)), dim3(64 * GR_WAVES), 0, s,
                        (const float*)(ws + P.gpart), (int)P.prep_blocks, rq, rkv, c.grads->g_q, c.grads->g_kv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
