@@ -29,6 +29,7 @@
 // registers per wave and ran slower at one wave per SIMD.)
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "backward.h"
 #include "common.h"
@@ -700,37 +701,46 @@ constexpr int PREP_MAXC = 32;   // columns per lane of each latent (q_rank, kv_r
 
 // One wave per token, four waves per workgroup; the gain gradients of the
 // workgroup's tokens are summed in registers (lane l owns columns l + 64 i)
-// and written as one partial row per workgroup.
+// and written as one partial row per workgroup.  NQ, NK: the latents' widths
+// in 64-column chunks when fixed at compile time (the loops then carry no
+// guards, so each pass has all its loads in flight), 0 to read them from the
+// arguments.
+template <int NQ, int NK>
 __global__ void __launch_bounds__(256)
 prep_bwd_kernel(PrepBwdArgs a) {
+  constexpr int MQ = NQ ? NQ : PREP_MAXC, MK = NK ? NK : PREP_MAXC;
   __shared__ float red[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  float accq[PREP_MAXC], acck[PREP_MAXC];
+  float accq[MQ], acck[MK];
 #pragma unroll
-  for (int i = 0; i < PREP_MAXC; ++i) accq[i] = acck[i] = 0.f;
-  const int nq = a.q_rank / 64, nk = a.kv_rank / 64;
+  for (int i = 0; i < MQ; ++i) accq[i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < MK; ++i) acck[i] = 0.f;
+  const int nq = NQ ? NQ : a.q_rank / 64, nk = NK ? NK : a.kv_rank / 64;
   // RMSNorm backward of one latent: dc = r u - c r^3 mean(u c), u = g gamma;
   // gain gradient g c r
-  auto rms_bwd = [&](const float* c, const float* g, const bf16* gamma, int nc, bf16* out, float (&acc)[PREP_MAXC]) {
+  auto rms_bwd = [&](const float* c, const float* g, const bf16* gamma, int nc, bf16* out, auto& acc) {
+    constexpr int M = std::extent<std::remove_reference_t<decltype(acc)>>::value;
+    float cv[M], gv[M], u[M];
     float ss = 0.f, uc = 0.f;
 #pragma unroll
-    for (int i = 0; i < PREP_MAXC; ++i)
+    for (int i = 0; i < M; ++i)
       if (i < nc) {
         const int col = lane + 64 * i;
-        const float cv = c[col], u = g[col] * (float)gamma[col];
-        ss += cv * cv;
-        uc += u * cv;
+        cv[i] = c[col];
+        gv[i] = g[col];
+        u[i] = gv[i] * (float)gamma[col];
+        ss += cv[i] * cv[i];
+        uc += u[i] * cv[i];
       }
     const float ncol = (float)(nc * 64);
     const float r = 1.0f / sqrtf(wave_sum(ss) / ncol + a.eps);
     const float m = wave_sum(uc) / ncol;
 #pragma unroll
-    for (int i = 0; i < PREP_MAXC; ++i)
+    for (int i = 0; i < M; ++i)
       if (i < nc) {
-        const int col = lane + 64 * i;
-        const float cv = c[col], u = g[col] * (float)gamma[col];
-        out[col] = (bf16)(r * u - cv * r * r * r * m);
-        acc[i] += g[col] * cv * r;
+        out[lane + 64 * i] = (bf16)(r * u[i] - cv[i] * r * r * r * m);
+        acc[i] += gv[i] * cv[i] * r;
       }
   };
   for (int k = w; k < PREP_TOK; k += 4) {
@@ -767,9 +777,10 @@ prep_bwd_kernel(PrepBwdArgs a) {
   }
   // the four waves' partial gain sums, one column per lane at a time
   float* gp = a.gpart + (int64_t)blockIdx.x * (a.q_rank + a.kv_rank);
-  auto flush = [&](float (&acc)[PREP_MAXC], int nc, int off) {
+  auto flush = [&](auto& acc, int nc, int off) {
+    constexpr int M = std::extent<std::remove_reference_t<decltype(acc)>>::value;
 #pragma unroll
-    for (int i = 0; i < PREP_MAXC; ++i) {
+    for (int i = 0; i < M; ++i) {
       if (i < nc) {
         red[w][lane] = acc[i];
         __syncthreads();
@@ -1193,7 +1204,10 @@ hipError_t backward_step(const BwdDims& D, const BackwardLayout& P, const BwdCal
     k.ddown = (bf16*)(ws + P.ddown); k.ld_dd = P.ndp; k.pad_from = (int)D.ndown;
     k.gpart = (float*)(ws + P.gpart);
     k.T = T; k.q_rank = rq; k.kv_rank = rkv;
-    hipLaunchKernelGGL(prep_bwd_kernel, dim3((unsigned)P.prep_blocks), dim3(256), 0, s, k);
+    const dim3 pg((unsigned)P.prep_blocks);
+    if (rq == 1536 && rkv == 512) hipLaunchKernelGGL((prep_bwd_kernel<24, 8>), pg, dim3(256), 0, s, k);
+    else if (rq == 1024 && rkv == 512) hipLaunchKernelGGL((prep_bwd_kernel<16, 8>), pg, dim3(256), 0, s, k);
+    else hipLaunchKernelGGL((prep_bwd_kernel<0, 0>), pg, dim3(256), 0, s, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(gain_reduce_kernel, dim3((unsigned)cdiv(rq + rkv, 64)), dim3(64 * GR_WAVES), 0, s,
                        (const float*)(ws + P.gpart), (int)P.prep_blocks, rq, rkv, c.grads->g_q, c.grads->g_kv);
