@@ -257,11 +257,15 @@ attn_bwd_dkv_kernel(AttnBwdArgs a) {
     k0 = it.z;
   } else {
     L = a.L;
+    // KV group fastest: consecutive workgroups go to different XCDs, so each
+    // XCD keeps to the groups n with n % 8 fixed and its L2 serves their Q
+    // and dH tiles to every key block it runs; key blocks in ascending order
+    // (the first ones see the most queries under the causal mask)
     const int nkb = cdiv(L, DKV_KEYS);
-    const int kbk = blockIdx.x % nkb, rest = blockIdx.x / nkb;
-    n = rest % nN;
-    tb = (int64_t)(rest / nN) * L;
-    k0 = kbk * DKV_KEYS;
+    n = (int)(blockIdx.x % nN);
+    const int rest = (int)(blockIdx.x / nN);
+    tb = (int64_t)(rest / nkb) * L;
+    k0 = (rest % nkb) * DKV_KEYS;
   }
   const int64_t T = a.T;
   const int kw = k0 + 16 * w, kl = kw + r16;   // this lane's key (score column)
@@ -531,11 +535,16 @@ attn_bwd_dq32_kernel(AttnBwdArgs a) {
     q0 = it.z;
   } else {
     L = a.L;
+    // KV group fastest (each XCD keeps to the groups n with n % 8 fixed, so
+    // its L2 serves their K and V tiles to every query block it runs); last
+    // query blocks first: they see the most key tiles under the causal mask,
+    // so the longest workgroups start earliest and the launch ends without a
+    // tail
     const int nqb = cdiv(L, 32);
-    const int qb = blockIdx.x % nqb, rest = blockIdx.x / nqb;
-    n = rest % nN;
-    tb = (int64_t)(rest / nN) * L;
-    q0 = qb * 32;
+    n = (int)(blockIdx.x % nN);
+    const int rest = (int)(blockIdx.x / nN);
+    tb = (int64_t)(rest / nqb) * L;
+    q0 = (nqb - 1 - rest % nqb) * 32;
   }
   const int64_t T = a.T;
   const int head = w < G ? n * G + w : nS + n;
