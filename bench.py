@@ -450,6 +450,8 @@ def main():
     ap.add_argument("--backward-only", action="store_true", help="time only the block backward (for profiling)")
     ap.add_argument("--packed-only", action="store_true", help="time only the packed-stream block (for profiling)")
     ap.add_argument("--paged-only", action="store_true", help="time only the paged-cache decode (for profiling)")
+    ap.add_argument("--report-only", action="store_true",
+                    help="time only the report-shape (g=4, W=128) prefill block and decode step (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (hardware-counter calibration)")
     ap.add_argument("--print-attn-sha", action="store_true", help="print the attention source hash and exit")
@@ -493,6 +495,13 @@ def main():
     if args.paged_only:
         print(json.dumps({"paged_decode": bench_decode(torch, gdla, configs, inputs, name="paged_decode_b64",
                                                        fixed_ctx=False, paged=True)}), flush=True)
+        return
+    if args.report_only:
+        rp, _, _, _ = bench_prefill(args, torch, gdla, configs, inputs, name="report_hybrid_l32k")
+        print(json.dumps({"report_prefill": {"ms_per_step": round(rp["ms_step"], 3), "tflops": round(rp["tflops"], 2),
+                                             "attn_tflops": round(rp["attn_tflops"], 2), "stage_ms": rp["kern"]},
+                          "report_decode": bench_decode(torch, gdla, configs, inputs, reps=10,
+                                                        name="report_decode_b64", fixed_ctx=False)}), flush=True)
         return
     pf, w, Wc0, x_cpu = bench_prefill(args, torch, gdla, configs, inputs)
     log(f"[bench] prefill: {pf['ms_step']:.2f} ms/step, {pf['tflops']:.1f} TFLOP/s, attention "
